@@ -1,0 +1,213 @@
+"""The oracle: plain CPU definition of MoE token dispatch and combine.
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may use it; the GPU product path never does.
+It shares no code with the HIP library: its arithmetic lives in ``oracle.c``
+(plain single-threaded C, built with ``gcc -O2 -ffp-contract=off``), and this
+module only marshals numpy arrays in and out.
+
+See ``oracle.c`` for the definitions followed and the page sections they come
+from. Every function here is pinned by the ``-m "not gpu"`` tests against brute
+force, library routines, closed forms and a hand-worked example.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+ST_BAD_EXPERT = 1
+ST_LL_OVERFLOW = 2
+ST_BAD_SLOT = 4
+ST_BAD_REPLICA = 8
+
+
+def build(out: str = LIB, mutant: Optional[int] = None) -> str:
+    """Compile oracle.c into a shared library (optionally with a planted mutant)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+           "-Wall", "-Wextra", "-Werror", "-o", out + ".tmp", SRC]
+    if mutant is not None:
+        cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_P = C.c_void_p
+_I64 = C.c_int64
+_I32 = C.c_int32
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+class Oracle:
+    """ctypes view of one build of oracle.c (the normal build or a mutant)."""
+
+    def __init__(self, path: str = LIB):
+        if not os.path.exists(path):
+            raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build()")
+        self.path = path
+        lib = C.CDLL(path)
+        self.lib = lib
+        lib.oracle_mutant.restype = C.c_int
+        lib.oracle_bf16_from_f32.argtypes = [_P, _P, _I64]
+        lib.oracle_layout.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                      _I64, _P]
+        lib.oracle_ll_layout.argtypes = [_I64, _I32, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P,
+                                         _P, _P]
+        lib.oracle_expert_load.argtypes = [_I64, _I32, _I32, _P, _P, _P]
+        lib.oracle_dispatch.argtypes = [_I64, _I32, _I32, _P, _P, _P, _I64, _P]
+        lib.oracle_combine_f64.argtypes = [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P]
+        lib.oracle_combine_f32.argtypes = [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P]
+        lib.oracle_plan_replicas.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
+        lib.oracle_reroute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]
+        for f in ("oracle_layout", "oracle_ll_layout", "oracle_expert_load", "oracle_dispatch",
+                  "oracle_combine_f64", "oracle_combine_f32", "oracle_plan_replicas",
+                  "oracle_reroute"):
+            getattr(lib, f).restype = C.c_int
+
+    @property
+    def mutant(self) -> int:
+        return int(self.lib.oracle_mutant())
+
+    # -- conversions --------------------------------------------------------
+    def bf16_rne(self, f: np.ndarray) -> np.ndarray:
+        f = np.ascontiguousarray(f, dtype=np.float32)
+        out = np.empty(f.shape, np.uint16)
+        self.lib.oracle_bf16_from_f32(_ptr(f), _ptr(out), f.size)
+        return out
+
+    # -- layout -------------------------------------------------------------
+    def layout(self, idx: np.ndarray, E: int, R: int, A: int = 1) -> dict:
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        T, K = idx.shape
+        count = np.empty(E, np.int32)
+        offset = np.empty(E + 1, np.int32)
+        rtc = np.empty(R, np.int32)
+        in_rank = np.empty((T, R), np.uint8)
+        slot = np.empty((T, K), np.int32)
+        worst = T * K + E * (A - 1)
+        row_src = np.empty(max(worst, 1), np.int32)
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_layout(T, K, E, R, A, _ptr(idx), _ptr(count), _ptr(offset),
+                                    _ptr(rtc), _ptr(in_rank), _ptr(slot), _ptr(row_src),
+                                    row_src.size, _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle_layout rejected its arguments ({rc})")
+        rows = int(offset[E])
+        return dict(count=count, offset=offset, rank_token_count=rtc, is_token_in_rank=in_rank,
+                    slot=slot, row_src=row_src[:rows].copy(), rows=rows,
+                    status=int(status[0]))
+
+    def ll_layout(self, idx: np.ndarray, E: int, R: int, M: int, src_rank: int = 0) -> dict:
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        T, K = idx.shape
+        recv_count = np.empty(E, np.int32)
+        rtc = np.empty(R, np.int32)
+        in_rank = np.empty((T, R), np.uint8)
+        slot = np.empty((T, K), np.int32)
+        row_src = np.empty(E * M, np.int32)
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_ll_layout(T, K, E, R, M, src_rank, _ptr(idx), _ptr(recv_count),
+                                       _ptr(rtc), _ptr(in_rank), _ptr(slot), _ptr(row_src),
+                                       _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle_ll_layout rejected its arguments ({rc})")
+        return dict(recv_count=recv_count, rank_token_count=rtc, is_token_in_rank=in_rank,
+                    slot=slot, row_src=row_src, rows=E * R * M, status=int(status[0]))
+
+    def expert_load(self, idx: np.ndarray, E: int) -> tuple:
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        T, K = idx.shape
+        load = np.empty(E, np.int32)
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_expert_load(T, K, E, _ptr(idx), _ptr(load), _ptr(status))
+        if rc != 0:
+            raise ValueError(rc)
+        return load, int(status[0])
+
+    # -- dispatch / combine -------------------------------------------------
+    def dispatch(self, x: np.ndarray, slot: np.ndarray, rows: int,
+                 fill: Optional[int] = None, out: Optional[np.ndarray] = None) -> tuple:
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        T, H = x.shape
+        K = slot.shape[1]
+        if out is None:
+            out = np.empty((rows, H), np.uint16) if fill is None else \
+                np.full((rows, H), fill, np.uint16)
+        status = np.zeros(1, np.int32)
+        self.lib.oracle_dispatch(T, H, K, _ptr(x), _ptr(slot), _ptr(out), rows, _ptr(status))
+        return out, int(status[0])
+
+    def combine(self, y: np.ndarray, slot: np.ndarray, w: Optional[np.ndarray],
+                acc: str = "f64") -> dict:
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        T, K = slot.shape
+        rows, H = y.shape
+        if w is not None:
+            w = np.ascontiguousarray(w, dtype=np.float32)
+            assert w.shape == (T, K)
+        status = np.zeros(1, np.int32)
+        if acc == "f64":
+            out = np.empty((T, H), np.float64)
+            self.lib.oracle_combine_f64(T, H, K, _ptr(y), rows, _ptr(slot), _ptr(w), _ptr(out),
+                                        _ptr(status))
+            return dict(out_f64=out, status=int(status[0]))
+        if acc == "f32":
+            o32 = np.empty((T, H), np.float32)
+            o16 = np.empty((T, H), np.uint16)
+            self.lib.oracle_combine_f32(T, H, K, _ptr(y), rows, _ptr(slot), _ptr(w), _ptr(o32),
+                                        _ptr(o16), _ptr(status))
+            return dict(out_f32=o32, out_bf16=o16, status=int(status[0]))
+        raise ValueError(acc)
+
+    # -- replicas -----------------------------------------------------------
+    def plan_replicas(self, load: np.ndarray, R: int, C_: int) -> dict:
+        load = np.ascontiguousarray(load, dtype=np.int32)
+        E = load.size
+        rc_ = np.empty(E, np.int32)
+        rp = np.empty((E, 2), np.int32)
+        p2l = np.empty(E + C_, np.int32)
+        rc = self.lib.oracle_plan_replicas(E, R, C_, _ptr(load), _ptr(rc_), _ptr(rp), _ptr(p2l))
+        if rc != 0:
+            raise ValueError(f"oracle_plan_replicas rejected its arguments ({rc})")
+        return dict(replica_count=rc_, replica_phys=rp, phys_to_logical=p2l, E_phys=E + C_,
+                    L_phys=E // R + C_ // R)
+
+    def reroute(self, idx: np.ndarray, E: int, replica_count: np.ndarray,
+                replica_phys: np.ndarray, E_phys: int) -> tuple:
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        T, K = idx.shape
+        out = np.empty((T, K), np.int64)
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_reroute(T, K, E, _ptr(idx),
+                                     _ptr(np.ascontiguousarray(replica_count, np.int32)),
+                                     _ptr(np.ascontiguousarray(replica_phys, np.int32)),
+                                     E_phys, _ptr(out), _ptr(status))
+        if rc != 0:
+            raise ValueError(rc)
+        return out, int(status[0])
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The normal (unmutated) oracle build; built on first use if absent."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build()
+        _default = Oracle(LIB)
+    return _default

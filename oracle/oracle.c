@@ -1,0 +1,425 @@
+/*
+ * The oracle: a plain, slow, single-threaded CPU definition of MoE token
+ * dispatch and combine, written from the problem statement. It is TEST
+ * INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg load it; the GPU library shares no code, header, table or
+ * helper with it.
+ *
+ * Sources (page title, section):
+ *   [P1] NeMo AutoModel API page "nemo_automodel.components.moe.uccl_ep.buffer":
+ *        Buffer.get_dispatch_layout, Buffer.dispatch (topk_idx, expert_alignment,
+ *        num_tokens_per_rank, is_token_in_rank, num_tokens_per_expert),
+ *        Buffer.combine, Buffer.low_latency_dispatch (receive layout
+ *        [num_local_experts, num_ranks * num_max_dispatch_tokens_per_rank, hidden]),
+ *        Buffer.low_latency_combine (reduce with weights, -1 ids allowed).
+ *   [P3] "dots-infra/ultraep architecture": Overview (plan replicas, expand the
+ *        routing before the experts), GPU operations (Load computation,
+ *        Placement planning, Routing expansion).
+ *
+ * Readings of points the pages leave open (each is listed with its reason in
+ * the design notes of this repository):
+ *   - a (token, k) pair with id -1 is not counted and gets slot -1;
+ *   - ids >= E or < -1 are skipped and set status bit 1;
+ *   - rows inside an expert are ordered by pair index t*K+k (stable);
+ *   - per-expert row counts are rounded up to the expert alignment A;
+ *   - combine is weighted (weights NULL = all ones), summed in ascending k;
+ *   - bf16 rounding is round-to-nearest-even, NaN -> 0x7FC0;
+ *   - low-latency row of the j-th pair of expert e sent by rank s is
+ *     (e*R + s)*M + j; pairs with j >= M are dropped and set status bit 2;
+ *   - replica plan: the C most loaded experts (ties -> lower id) get one extra
+ *     physical replica; a pair of token t uses replica (t mod count).
+ *
+ * Arithmetic: combine is provided twice -- in double (the exact definition up
+ * to rounding of a K-term sum), and in float with every product and every sum
+ * rounded to float, in ascending k, no fused multiply-add (build with
+ * -ffp-contract=off).
+ *
+ * Mutants: building with -DORACLE_MUTANT=n plants one known mistake; the test
+ * suite uses those builds to show that its pins catch each of them. A normal
+ * build has ORACLE_MUTANT undefined.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+#define ST_BAD_EXPERT 1
+#define ST_LL_OVERFLOW 2
+#define ST_BAD_SLOT 4
+#define ST_BAD_REPLICA 8
+
+int oracle_mutant(void) { return ORACLE_MUTANT; }
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> f32                                                        */
+/* ------------------------------------------------------------------ */
+
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* Round a float to the nearest bf16, ties to even; any NaN becomes 0x7FC0. */
+static uint16_t f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    uint32_t lsb = (u >> 16) & 1u;
+#if ORACLE_MUTANT == 9
+    lsb = 0; /* mutant: round half up instead of half to even */
+#endif
+    u += 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+void oracle_bf16_from_f32(const float *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(in[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Layout: counts, per-rank token sets, aligned offsets, stable slots  */
+/* ------------------------------------------------------------------ */
+
+static int valid_id(int64_t e, int32_t E) { return e >= 0 && e < E; }
+
+/* Count (token, expert) pairs per expert and mark which ranks each token
+ * reaches. [P1] Buffer.get_dispatch_layout / Buffer.dispatch:
+ * num_tokens_per_expert, is_token_in_rank, num_tokens_per_rank. */
+static void count_pairs(int64_t T, int32_t K, int32_t E, int32_t R, const int64_t *idx,
+                        int32_t *count, int32_t *rank_token_count, uint8_t *in_rank,
+                        int32_t *status) {
+    int32_t L = E / R;
+    for (int32_t e = 0; e < E; ++e) count[e] = 0;
+    uint8_t *mark = (uint8_t *)calloc((size_t)(T > 0 ? T : 1) * (size_t)R, 1);
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t e = idx[t * K + k];
+            if (e == -1) continue;
+            if (!valid_id(e, E)) {
+                if (status) *status |= ST_BAD_EXPERT;
+                continue;
+            }
+            count[e] += 1;
+            mark[t * R + e / L] = 1;
+        }
+    }
+    if (rank_token_count) {
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t n = 0;
+            for (int64_t t = 0; t < T; ++t) n += mark[t * R + r];
+#if ORACLE_MUTANT == 5
+            /* mutant: count pairs per rank instead of distinct tokens */
+            n = 0;
+            for (int32_t e = r * L; e < (r + 1) * L; ++e) n += count[e];
+#endif
+            rank_token_count[r] = n;
+        }
+    }
+    if (in_rank) memcpy(in_rank, mark, (size_t)T * (size_t)R);
+    free(mark);
+}
+
+/* Contiguous layout. offset[0] = 0, offset[e+1] = offset[e] + ceil(count[e]/A)*A
+ * ([P1] Buffer.dispatch, expert_alignment). The j-th pair of expert e in
+ * row-major (t, k) order takes row offset[e] + j. row_src[row] = t*K + k, and
+ * -1 on alignment padding rows in [0, offset[E]). */
+int oracle_layout(int64_t T, int32_t K, int32_t E, int32_t R, int32_t A, const int64_t *idx,
+                  int32_t *count, int32_t *offset, int32_t *rank_token_count, uint8_t *in_rank,
+                  int32_t *slot, int32_t *row_src, int64_t row_src_len, int32_t *status) {
+    if (T < 0 || K < 1 || E < 1 || R < 1 || E % R != 0 || A < 1) return -2;
+    count_pairs(T, K, E, R, idx, count, rank_token_count, in_rank, status);
+
+    offset[0] = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        int32_t c = count[e];
+        int32_t padded = (c + A - 1) / A * A;
+#if ORACLE_MUTANT == 1
+        padded = c; /* mutant: alignment dropped */
+#endif
+        offset[e + 1] = offset[e] + padded;
+    }
+    if (row_src) {
+        if (row_src_len < offset[E]) return -3;
+        for (int32_t r = 0; r < offset[E]; ++r) row_src[r] = -1;
+    }
+
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e) cursor[e] = offset[e];
+#if ORACLE_MUTANT == 2
+    /* mutant: pairs visited in column-major (k, t) order */
+    for (int32_t k = 0; k < K; ++k) {
+        for (int64_t t = 0; t < T; ++t) {
+#else
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+#endif
+            int64_t p = t * K + k;
+            int64_t e = idx[p];
+            if (!valid_id(e, E)) {
+                slot[p] = -1;
+                continue;
+            }
+            int32_t row = cursor[e]++;
+            slot[p] = row;
+            if (row_src) row_src[row] = (int32_t)p;
+        }
+    }
+    free(cursor);
+    return 0;
+}
+
+/* Low-latency padded layout ([P1] Buffer.low_latency_dispatch: each rank
+ * receives [num_local_experts, num_ranks * M, hidden]; taken together the R
+ * receive buffers are [E, R*M, hidden]). This rank is source s; its j-th pair
+ * for expert e lands in row (e*R + s)*M + j. recv_count[e] = pairs that fit
+ * (min(count, M)); pairs with j >= M are dropped with status bit 2.
+ * row_src (optional) is [E*M]: the pair held in stripe row j of expert e, or -1. */
+int oracle_ll_layout(int64_t T, int32_t K, int32_t E, int32_t R, int32_t M, int32_t s,
+                     const int64_t *idx, int32_t *recv_count, int32_t *rank_token_count,
+                     uint8_t *in_rank, int32_t *slot, int32_t *row_src, int32_t *status) {
+    if (T < 0 || K < 1 || E < 1 || R < 1 || E % R != 0 || M < 1) return -2;
+    if (T > M || s < 0 || s >= R) return -4;
+    int32_t *count = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    count_pairs(T, K, E, R, idx, count, rank_token_count, in_rank, status);
+    if (row_src)
+        for (int64_t r = 0; r < (int64_t)E * M; ++r) row_src[r] = -1;
+    int32_t *j = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t p = t * K + k;
+            int64_t e = idx[p];
+            if (!valid_id(e, E)) {
+                slot[p] = -1;
+                continue;
+            }
+            int32_t jj = j[e]++;
+            if (jj >= M) {
+                slot[p] = -1;
+                if (status) *status |= ST_LL_OVERFLOW;
+                continue;
+            }
+            int64_t row = ((int64_t)e * R + s) * M + jj;
+#if ORACLE_MUTANT == 6
+            row = (int64_t)e * R * M + jj; /* mutant: source stripe dropped */
+#endif
+            slot[p] = (int32_t)row;
+            if (row_src) row_src[(int64_t)e * M + jj] = (int32_t)p;
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) recv_count[e] = count[e] < M ? count[e] : M;
+    free(j);
+    free(count);
+    return 0;
+}
+
+/* Per-expert load over the batch ([P3] GPU operations: Load computation). */
+int oracle_expert_load(int64_t T, int32_t K, int32_t E, const int64_t *idx, int32_t *load,
+                       int32_t *status) {
+    if (T < 0 || K < 1 || E < 1) return -2;
+    for (int32_t e = 0; e < E; ++e) load[e] = 0;
+    for (int64_t p = 0; p < T * K; ++p) {
+        int64_t e = idx[p];
+        if (e == -1) continue;
+        if (!valid_id(e, E)) {
+            if (status) *status |= ST_BAD_EXPERT;
+            continue;
+        }
+        load[e] += 1;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dispatch: recv[slot[t,k]] = x[t]                                    */
+/* ------------------------------------------------------------------ */
+
+/* [P1] Buffer.dispatch / Buffer.low_latency_dispatch: each selected (token,
+ * expert) pair sends the token's hidden row; here the row is copied bit for
+ * bit into its slot of the receive buffer. */
+int oracle_dispatch(int64_t T, int32_t H, int32_t K, const uint16_t *x, const int32_t *slot,
+                    uint16_t *recv, int64_t rows, int32_t *status) {
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = slot[t * K + k];
+            if (r == -1) continue;
+            if (r < -1 || r >= rows) {
+                if (status) *status |= ST_BAD_SLOT;
+                continue;
+            }
+            memcpy(recv + (int64_t)r * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Combine: out[t] = sum_k w[t,k] * y[slot[t,k]]                       */
+/* ------------------------------------------------------------------ */
+
+static int32_t k_of(int32_t k, int32_t K) {
+#if ORACLE_MUTANT == 4
+    return K - 1 - k; /* mutant: weight index reversed */
+#else
+    (void)K;
+    return k;
+#endif
+}
+
+static int32_t k_end(int32_t K) {
+#if ORACLE_MUTANT == 3
+    return K - 1; /* mutant: last top-k term dropped */
+#else
+    return K;
+#endif
+}
+
+/* [P1] Buffer.low_latency_combine (reduce with weights) and Buffer.combine:
+ * the expert outputs of a token's selected pairs are summed, each times its
+ * top-k weight, back into the token's row. Exact definition in double. */
+int oracle_combine_f64(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64_t rows,
+                       const int32_t *slot, const float *w, double *out, int32_t *status) {
+    for (int64_t t = 0; t < T; ++t) {
+        double *o = out + t * (int64_t)H;
+        for (int32_t h = 0; h < H; ++h) o[h] = 0.0;
+        for (int32_t k = 0; k < k_end(K); ++k) {
+            int32_t r = slot[t * K + k];
+            if (r == -1) continue;
+            if (r < -1 || r >= rows) {
+                if (status) *status |= ST_BAD_SLOT;
+                continue;
+            }
+            double wk = w ? (double)w[t * K + k_of(k, K)] : 1.0;
+            const uint16_t *yr = y + (int64_t)r * H;
+            for (int32_t h = 0; h < H; ++h) o[h] += wk * (double)bf16_to_f32(yr[h]);
+        }
+    }
+    return 0;
+}
+
+/* Same sum in float: ascending k, each product and each sum rounded to float,
+ * starting from +0. Also returns the bf16 rounding of the float sum. */
+int oracle_combine_f32(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64_t rows,
+                       const int32_t *slot, const float *w, float *out_f32, uint16_t *out_bf16,
+                       int32_t *status) {
+    float *acc = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+        for (int32_t k = 0; k < k_end(K); ++k) {
+            int32_t r = slot[t * K + k];
+            if (r == -1) continue;
+            if (r < -1 || r >= rows) {
+                if (status) *status |= ST_BAD_SLOT;
+                continue;
+            }
+            float wk = w ? w[t * K + k_of(k, K)] : 1.0f;
+            const uint16_t *yr = y + (int64_t)r * H;
+            for (int32_t h = 0; h < H; ++h) {
+                float prod = wk * bf16_to_f32(yr[h]);
+                acc[h] = acc[h] + prod;
+            }
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            if (out_f32) out_f32[t * (int64_t)H + h] = acc[h];
+            if (out_bf16) out_bf16[t * (int64_t)H + h] = f32_to_bf16(acc[h]);
+        }
+    }
+    free(acc);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Replica plan and routing expansion ([P3] Overview; GPU operations:  */
+/* Placement planning, Routing expansion)                              */
+/* ------------------------------------------------------------------ */
+
+static const int32_t *g_load;
+static int cmp_hot(const void *a, const void *b) {
+    int32_t ea = *(const int32_t *)a, eb = *(const int32_t *)b;
+    if (g_load[ea] != g_load[eb]) {
+#if ORACLE_MUTANT == 7
+        return g_load[ea] < g_load[eb] ? -1 : 1; /* mutant: coldest first */
+#else
+        return g_load[ea] > g_load[eb] ? -1 : 1;
+#endif
+    }
+    return ea < eb ? -1 : (ea > eb ? 1 : 0);
+}
+
+/* The C most loaded logical experts (load descending, ties -> lower id) get a
+ * second physical replica. Physical numbering: every rank r holds
+ * L' = L + C/R physical slots; slot r*L' + l (l < L) is the primary of logical
+ * expert r*L + l, and the i-th hottest expert's replica is slot
+ * (i mod R)*L' + L + i/R. replica_phys is [E][2] (-1 where there is no second
+ * replica); phys_to_logical is [E + C]. */
+int oracle_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
+                         int32_t *replica_count, int32_t *replica_phys,
+                         int32_t *phys_to_logical) {
+    if (E < 1 || R < 1 || E % R != 0 || C < 0 || C > E || C % R != 0) return -2;
+    int32_t L = E / R, Lp = L + C / R;
+    int32_t *order = (int32_t *)malloc(sizeof(int32_t) * (size_t)E);
+    for (int32_t e = 0; e < E; ++e) order[e] = e;
+    g_load = load;
+    qsort(order, (size_t)E, sizeof(int32_t), cmp_hot);
+    for (int32_t e = 0; e < E; ++e) {
+        int32_t prim = (e / L) * Lp + e % L;
+        replica_count[e] = 1;
+        replica_phys[2 * e] = prim;
+        replica_phys[2 * e + 1] = -1;
+        phys_to_logical[prim] = e;
+    }
+    for (int32_t i = 0; i < C; ++i) {
+        int32_t e = order[i];
+        int32_t rep = (i % R) * Lp + L + i / R;
+        replica_count[e] = 2;
+        replica_phys[2 * e + 1] = rep;
+        phys_to_logical[rep] = e;
+    }
+    free(order);
+    return 0;
+}
+
+/* Expand logical routing to physical routing: the pair (t, k) on logical
+ * expert e goes to replica (t mod replica_count[e]) of e; -1 stays -1. */
+int oracle_reroute(int64_t T, int32_t K, int32_t E, const int64_t *idx,
+                   const int32_t *replica_count, const int32_t *replica_phys, int32_t E_phys,
+                   int64_t *phys_idx, int32_t *status) {
+    if (T < 0 || K < 1 || E < 1) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t p = t * K + k;
+            int64_t e = idx[p];
+            if (e == -1) {
+                phys_idx[p] = -1;
+                continue;
+            }
+            if (!valid_id(e, E)) {
+                if (status) *status |= ST_BAD_EXPERT;
+                phys_idx[p] = -1;
+                continue;
+            }
+            int32_t c = replica_count[e];
+            if (c < 1 || c > 2) {
+                if (status) *status |= ST_BAD_REPLICA;
+                phys_idx[p] = -1;
+                continue;
+            }
+            int32_t which = (int32_t)(t % c);
+#if ORACLE_MUTANT == 8
+            which = (int32_t)(k % c); /* mutant: replica chosen by k instead of t */
+#endif
+            int32_t ph = replica_phys[2 * e + which];
+            if (ph < 0 || ph >= E_phys) {
+                if (status) *status |= ST_BAD_REPLICA;
+                phys_idx[p] = -1;
+                continue;
+            }
+            phys_idx[p] = ph;
+        }
+    }
+    return 0;
+}

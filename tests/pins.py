@@ -1,0 +1,331 @@
+"""Pins of the oracle: checks against things other than the oracle itself.
+
+Every check takes an ``Oracle`` (the normal build, or a build with a planted
+mistake) and raises ``AssertionError`` when the oracle disagrees with
+
+* the hand-worked example in ``golden/hand_worked_tiny.json``,
+* the sort-based brute force in ``bruteforce.py``,
+* numpy's library routines for the alignment-1 special case
+  (``bincount`` / ``cumsum`` / stable ``argsort``),
+* a dense matrix-product formulation of combine (``numpy`` matmul in f64),
+* closed forms of combine with the identity expert (unit weights give K*x,
+  softmax weights give x back after bf16 rounding, K=1 is a permutation
+  round trip),
+* the float error bound between the f32 and f64 combine sums,
+* torch's CPU float->bf16 cast,
+* invariants (counts sum to the valid pairs; every pair has exactly one row;
+  rows inside an expert increase with the pair index; offsets are multiples
+  of the alignment; the replica tables are a bijection onto physical slots;
+  replicated and unreplicated combine agree bit for bit).
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import bruteforce as bf
+import moe_inputs as mi
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "hand_worked_tiny.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        g = json.load(f)
+    g["idx"] = np.array(g["topk_idx"], np.int64)
+    g["xb"] = mi.to_bf16_bits(np.array(g["x"], np.float32))
+    g["w"] = np.array(g["topk_weights"], np.float32)
+    return g
+
+
+def check_golden(orc):
+    g = _golden()
+    ex = g["expected"]
+    lay = orc.layout(g["idx"], g["E"], g["R"], g["A"])
+    assert lay["count"].tolist() == ex["count"]
+    assert lay["offset"].tolist() == ex["offset"]
+    assert lay["slot"].tolist() == ex["slot"]
+    assert lay["row_src"].tolist() == ex["row_src"]
+    assert lay["is_token_in_rank"].tolist() == ex["is_token_in_rank"]
+    assert lay["rank_token_count"].tolist() == ex["rank_token_count"]
+    assert lay["status"] == 0
+    recv, _ = orc.dispatch(g["xb"], lay["slot"], lay["rows"], fill=0)
+    out = orc.combine(recv, lay["slot"], g["w"], "f64")["out_f64"]
+    assert out.tolist() == ex["combine_identity"]
+    rows = lay["rows"]
+    y = mi.to_bf16_bits(np.array([[r + 1, (r + 1) / 2] for r in range(rows)], np.float32))
+    for acc in ("f64", "f32"):
+        res = orc.combine(y, lay["slot"], g["w"], acc)
+        o = res["out_f64"] if acc == "f64" else res["out_f32"]
+        assert o.tolist() == ex["combine_y_rows"], (acc, o.tolist())
+        res1 = orc.combine(y, lay["slot"], None, acc)
+        o1 = res1["out_f64"] if acc == "f64" else res1["out_f32"]
+        assert o1.tolist() == ex["combine_y_rows_unit_weights"], (acc, o1.tolist())
+    for key, M in (("ll_m4_s1", 4), ("ll_m3_s1", 3)):
+        idx = np.array(ex[key].get("topk_idx", g["topk_idx"]), np.int64)
+        ll = orc.ll_layout(idx, g["E"], g["R"], M, 1)
+        assert ll["slot"].tolist() == ex[key]["slot"], (key, ll["slot"].tolist())
+        assert ll["recv_count"].tolist() == ex[key]["recv_count"]
+        assert ll["status"] == ex[key]["status"]
+    rep = ex["replicas_c2"]
+    plan = orc.plan_replicas(lay["count"], g["R"], 2)
+    assert plan["replica_count"].tolist() == rep["replica_count"]
+    assert plan["replica_phys"].tolist() == rep["replica_phys"]
+    assert plan["phys_to_logical"].tolist() == rep["phys_to_logical"]
+    phys, st = orc.reroute(g["idx"], g["E"], plan["replica_count"], plan["replica_phys"],
+                           plan["E_phys"])
+    assert phys.tolist() == rep["phys_idx"] and st == 0
+
+
+def tiny_cases(n: int, seed: int = 0):
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        R = int(rng.choice([1, 2, 4]))
+        E = R * int(rng.integers(1, 9))
+        K = int(rng.integers(1, 9))
+        T = int(rng.integers(0, 40))
+        A = int(rng.choice([1, 2, 4, 16, 128]))
+        yield mi.random_case(1000 * seed + i, T, 8, E, R, K, A,
+                             neg_frac=float(rng.choice([0, 0.1, 0.5])),
+                             dup_frac=float(rng.choice([0, 0.3])),
+                             bad_frac=float(rng.choice([0, 0, 0.05])))
+
+
+def check_layout_vs_bruteforce(orc, n: int = 150, seed: int = 0):
+    for w in tiny_cases(n, seed):
+        got = orc.layout(w.topk_idx, w.E, w.R, w.A)
+        ref = bf.layout(w.topk_idx, w.E, w.R, w.A)
+        tag = w.name
+        assert got["count"].tolist() == ref["count"], tag
+        assert got["offset"].tolist() == ref["offset"], tag
+        assert got["slot"].tolist() == ref["slot"], tag
+        assert got["row_src"].tolist() == ref["row_src"], tag
+        assert got["is_token_in_rank"].tolist() == ref["is_token_in_rank"], tag
+        assert got["rank_token_count"].tolist() == ref["rank_token_count"], tag
+        assert bool(got["status"] & 1) == ref["bad"], tag
+
+
+def check_ll_vs_bruteforce(orc, n: int = 100, seed: int = 1):
+    rng = np.random.default_rng(seed)
+    for w in tiny_cases(n, seed):
+        if w.T == 0:
+            continue
+        M = int(w.T + rng.integers(0, 3))
+        s = int(rng.integers(0, w.R))
+        got = orc.ll_layout(w.topk_idx, w.E, w.R, M, s)
+        ref = bf.ll_layout(w.topk_idx, w.E, w.R, M, s)
+        assert got["slot"].tolist() == ref["slot"], w.name
+        assert got["row_src"].tolist() == ref["row_src"], w.name
+        assert got["recv_count"].tolist() == ref["recv_count"], w.name
+        assert bool(got["status"] & 2) == ref["overflow"], w.name
+
+
+def check_layout_vs_numpy(orc, workloads):
+    """Alignment 1 reduces the layout to a counting sort of the flattened ids."""
+    for w in workloads:
+        ids = w.topk_idx.ravel()
+        lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+        valid = ids >= 0
+        cnt = np.bincount(ids[valid], minlength=w.E)
+        assert np.array_equal(lay["count"], cnt), w.name
+        assert np.array_equal(lay["offset"], np.concatenate([[0], np.cumsum(cnt)])), w.name
+        order = np.argsort(np.where(valid, ids, w.E), kind="stable")[: int(valid.sum())]
+        assert np.array_equal(lay["row_src"], order), w.name
+        inv = np.full(ids.size, -1, np.int64)
+        inv[order] = np.arange(order.size)
+        assert np.array_equal(lay["slot"].ravel(), inv), w.name
+
+
+def check_layout_invariants(orc, w, A: int = 1):
+    lay = orc.layout(w.topk_idx, w.E, w.R, A)
+    ids = w.topk_idx.ravel()
+    slot = lay["slot"].ravel()
+    valid = (ids >= 0) & (ids < w.E)
+    assert lay["count"].sum() == valid.sum()
+    assert np.all(lay["offset"] % A == 0)
+    assert np.all(np.diff(lay["offset"]) >= lay["count"])
+    assert np.all(np.diff(lay["offset"]) - lay["count"] < A)
+    assert np.all(slot[~valid] == -1)
+    vs = slot[valid]
+    assert np.unique(vs).size == vs.size
+    assert np.array_equal(lay["row_src"][vs], np.nonzero(valid)[0])
+    e = ids[valid]
+    lo = lay["offset"][e]
+    assert np.all(vs >= lo) and np.all(vs < lo + lay["count"][e])
+    # rows rise with the pair index inside each expert
+    order = np.lexsort((np.nonzero(valid)[0], e))
+    assert np.all(np.diff(vs[order])[np.diff(e[order]) == 0] == 1)
+    in_rank = lay["is_token_in_rank"]
+    assert np.array_equal(lay["rank_token_count"], in_rank.sum(axis=0))
+    hit = np.zeros_like(in_rank)
+    t_of = np.repeat(np.arange(w.T), w.K)[valid]
+    hit[t_of, e // w.L] = 1
+    assert np.array_equal(hit, in_rank)
+
+
+def check_dispatch(orc, n: int = 40, seed: int = 2):
+    for w in tiny_cases(n, seed):
+        lay = orc.layout(w.topk_idx, w.E, w.R, w.A)
+        rows = lay["rows"]
+        recv, st = orc.dispatch(w.x, lay["slot"], rows, fill=0xABCD)
+        assert st == 0
+        for t in range(w.T):
+            for k in range(w.K):
+                s = lay["slot"][t, k]
+                if s >= 0:
+                    assert np.array_equal(recv[s], w.x[t]), w.name
+        pad = lay["row_src"] < 0
+        assert np.all(recv[pad] == 0xABCD), w.name
+
+
+def check_combine_dense(orc, n: int = 40, seed: int = 3):
+    for w in tiny_cases(n, seed):
+        lay = orc.layout(w.topk_idx, w.E, w.R, w.A)
+        rows = lay["rows"]
+        rng = np.random.default_rng(w.seed)
+        y = mi.to_bf16_bits(rng.standard_normal((rows, w.H), dtype=np.float32))
+        yf = mi.bf16_bits_to_f32(y)
+        for wt in (w.topk_weights, None):
+            ref = bf.dense_combine(yf, lay["slot"], wt)
+            got = orc.combine(y, lay["slot"], wt, "f64")["out_f64"]
+            assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), w.name
+
+
+def check_combine_closed_forms(orc, seed: int = 4):
+    # K*x with unit weights (exact in f32 and f64), x with softmax weights
+    for K in (1, 2, 6, 8):
+        w = mi.random_case(seed + K, 64, 64, 32, 4, K, 1, distinct=True)
+        lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+        recv, _ = orc.dispatch(w.x, lay["slot"], lay["rows"])
+        xf = mi.bf16_bits_to_f32(w.x)
+        o64 = orc.combine(recv, lay["slot"], None, "f64")["out_f64"]
+        assert np.array_equal(o64, K * xf.astype(np.float64)), K
+        r32 = orc.combine(recv, lay["slot"], None, "f32")
+        assert np.array_equal(r32["out_f32"], (K * xf).astype(np.float32)), K
+        soft = orc.combine(recv, lay["slot"], w.topk_weights, "f32")["out_bf16"]
+        same = (soft == w.x) | ((xf == 0) & (mi.bf16_bits_to_f32(soft) == 0))
+        assert np.all(same), K
+        if K == 1:
+            assert np.array_equal(orc.combine(recv, lay["slot"], None, "f32")["out_bf16"][xf != 0],
+                                  w.x[xf != 0])
+    # tokens whose ids are all -1 come back as +0
+    w = mi.random_case(seed, 16, 16, 8, 2, 4, 1, neg_frac=1.0)
+    lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+    r = orc.combine(np.zeros((1, 16), np.uint16), lay["slot"], w.topk_weights, "f32")
+    assert np.all(r["out_bf16"] == 0)
+
+
+def check_combine_f32_bound(orc, n: int = 30, seed: int = 5):
+    """|f32 sum - f64 sum| <= K * 2^-24 * sum_k |w*y| (a K-term float sum)."""
+    for w in tiny_cases(n, seed):
+        lay = orc.layout(w.topk_idx, w.E, w.R, w.A)
+        rng = np.random.default_rng(w.seed + 7)
+        y = mi.to_bf16_bits(rng.standard_normal((max(lay["rows"], 1), w.H),
+                                                dtype=np.float32) * 100)
+        wt = (w.topk_weights * rng.uniform(-3, 3, w.topk_weights.shape)).astype(np.float32)
+        o64 = orc.combine(y, lay["slot"], wt, "f64")["out_f64"]
+        o32 = orc.combine(y, lay["slot"], wt, "f32")["out_f32"].astype(np.float64)
+        yf = mi.bf16_bits_to_f32(y).astype(np.float64)
+        mag = np.zeros_like(o64)
+        for t in range(w.T):
+            for k in range(w.K):
+                s = lay["slot"][t, k]
+                if s >= 0:
+                    mag[t] += np.abs(wt[t, k] * yf[s])
+        assert np.all(np.abs(o32 - o64) <= (w.K + 1) * 2.0 ** -24 * mag + 1e-30), w.name
+
+
+def check_bf16_vs_torch(orc, n: int = 1 << 22, seed: int = 6):
+    import torch
+
+    rng = np.random.default_rng(seed)
+    pats = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x00000000, 0x80000000, 0x00000001, 0x807fffff, 0x3f808000, 0x3f818000,
+                        0x3f80ffff, 0x3f817fff, 0x7f7fffff, 0x7f800000, 0xff800000, 0x7fc00000,
+                        0xffc00001, 0x7f800001, 0x7f7f8000, 0x00008000, 0x00018000],
+                       dtype=np.uint32)
+    pats = np.concatenate([special, pats])
+    f = pats.view(np.float32)
+    got = orc.bf16_rne(f)
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # the encoding of NaN is not fixed (torch's vector cast gives 0xFFFF, the
+    # oracle the canonical 0x7FC0): NaN must stay NaN, everything else is bitwise
+    nan = np.isnan(f)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(mi.bf16_bits_to_f32(got[nan])))
+
+
+def check_replicas(orc, w, C_: int):
+    lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+    load, st = orc.expert_load(w.topk_idx, w.E)
+    assert np.array_equal(load, lay["count"]) and st == 0
+    plan = orc.plan_replicas(load, w.R, C_)
+    Ep, Lp = plan["E_phys"], plan["L_phys"]
+    # hot set = the first C of a (load desc, id asc) library sort
+    hot = np.lexsort((np.arange(w.E), -load.astype(np.int64)))[:C_]
+    assert np.array_equal(np.sort(np.nonzero(plan["replica_count"] == 2)[0]), np.sort(hot))
+    p2l = plan["phys_to_logical"]
+    rp = plan["replica_phys"]
+    # every physical slot maps back to its logical expert, and each physical
+    # slot is used once
+    used = np.concatenate([rp[:, 0], rp[rp[:, 1] >= 0, 1]])
+    assert np.array_equal(np.sort(used), np.arange(Ep))
+    assert np.all(p2l[rp[:, 0]] == np.arange(w.E))
+    two = rp[:, 1] >= 0
+    assert np.all(p2l[rp[two, 1]] == np.nonzero(two)[0])
+    # primaries stay on the rank that owns the logical expert
+    assert np.all(rp[:, 0] // Lp == np.arange(w.E) // w.L)
+    phys, st = orc.reroute(w.topk_idx, w.E, plan["replica_count"], rp, Ep)
+    assert st == 0
+    v = w.topk_idx >= 0
+    assert np.all(p2l[phys[v]] == w.topk_idx[v]) and np.all(phys[~v] == -1)
+    # replica share = the odd tokens on hot experts
+    plan_lay = orc.layout(phys, Ep, w.R, 1)
+    t_of = np.repeat(np.arange(w.T), w.K).reshape(w.T, w.K)
+    for i, e in enumerate(hot):
+        odd = int(((w.topk_idx == e) & (t_of % 2 == 1)).sum())
+        assert plan_lay["count"][rp[e, 1]] == odd
+        assert plan_lay["count"][rp[e, 0]] + odd == load[e]
+    # identity expert: replicated combine == unreplicated combine, bit for bit
+    r0, _ = orc.dispatch(w.x, lay["slot"], lay["rows"])
+    r1, _ = orc.dispatch(w.x, plan_lay["slot"], plan_lay["rows"])
+    a = orc.combine(r0, lay["slot"], w.topk_weights, "f32")
+    b = orc.combine(r1, plan_lay["slot"], w.topk_weights, "f32")
+    assert np.array_equal(a["out_bf16"], b["out_bf16"])
+    assert np.array_equal(a["out_f32"].view(np.uint32), b["out_f32"].view(np.uint32))
+
+
+def check_ll_matches_contiguous(orc, w):
+    """Source 0's padded layout and the contiguous layout give the same combine."""
+    M = w.M or w.T
+    ll = orc.ll_layout(w.topk_idx, w.E, w.R, M, 0)
+    lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+    assert ll["status"] == 0
+    assert np.array_equal(ll["recv_count"], lay["count"])
+    r_ll, _ = orc.dispatch(w.x, ll["slot"], ll["rows"], fill=0)
+    r_c, _ = orc.dispatch(w.x, lay["slot"], lay["rows"])
+    a = orc.combine(r_ll, ll["slot"], w.topk_weights, "f32")["out_bf16"]
+    b = orc.combine(r_c, lay["slot"], w.topk_weights, "f32")["out_bf16"]
+    assert np.array_equal(a, b)
+    # every used row decodes to (e, s=0, j) with j < recv_count[e]
+    v = ll["slot"] >= 0
+    rows = ll["slot"][v]
+    e = rows // (w.R * M)
+    s = (rows // M) % w.R
+    j = rows % M
+    assert np.array_equal(e, w.topk_idx[v]) and np.all(s == 0)
+    assert np.all(j < ll["recv_count"][e])
+
+
+ALL_SMALL_CHECKS = (
+    check_golden,
+    check_layout_vs_bruteforce,
+    check_ll_vs_bruteforce,
+    check_dispatch,
+    check_combine_dense,
+    check_combine_closed_forms,
+    check_combine_f32_bound,
+)

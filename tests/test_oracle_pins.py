@@ -1,0 +1,90 @@
+"""The oracle against its pins (CPU only). See pins.py for what each pin is."""
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import pins
+
+
+def test_golden_hand_worked(orc):
+    pins.check_golden(orc)
+
+
+def test_layout_vs_bruteforce(orc):
+    pins.check_layout_vs_bruteforce(orc, n=300, seed=0)
+
+
+def test_ll_layout_vs_bruteforce(orc):
+    pins.check_ll_vs_bruteforce(orc, n=200, seed=1)
+
+
+def test_dispatch_rows_and_untouched_padding(orc):
+    pins.check_dispatch(orc, n=60)
+
+
+def test_combine_vs_dense_matmul(orc):
+    pins.check_combine_dense(orc, n=60)
+
+
+def test_combine_closed_forms(orc):
+    pins.check_combine_closed_forms(orc)
+
+
+def test_combine_f32_within_float_bound_of_f64(orc):
+    pins.check_combine_f32_bound(orc, n=60)
+
+
+def test_bf16_rounding_matches_torch_cpu(orc):
+    pins.check_bf16_vs_torch(orc)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3_m16", "c3_m512", "c4", "c5"])
+def test_layout_vs_numpy_library_at_config(orc, name):
+    pins.check_layout_vs_numpy(orc, [mi.by_name(name)])
+
+
+@pytest.mark.parametrize("name,A", [("c1", 1), ("c1", 16), ("c2", 1), ("c2", 128), ("c4", 4),
+                                    ("c5", 1), ("c5", 64)])
+def test_layout_invariants_at_config(orc, name, A):
+    pins.check_layout_invariants(orc, mi.by_name(name), A)
+
+
+@pytest.mark.parametrize("M", mi.C3_SWEEP)
+def test_ll_equals_contiguous_for_source_zero(orc, M):
+    w = mi.config_c3(M)
+    if M >= 256:  # keep the CPU suite quick: the property is per token
+        w.T = 64
+        w.x = w.x[:64]
+        w.topk_idx = w.topk_idx[:64]
+        w.topk_weights = w.topk_weights[:64]
+    pins.check_ll_matches_contiguous(orc, w)
+
+
+def test_replicas_on_c5_routing(orc):
+    w = mi.config_c5(T=1024, H=64)  # routing of the replica workload at reduced size
+    pins.check_replicas(orc, w, 32)
+
+
+def test_replicas_on_random_routing(orc):
+    for s in range(10):
+        w = mi.random_case(s, 50, 16, 16, 4, 3, neg_frac=0.1)
+        pins.check_replicas(orc, w, 4 * (s % 3))
+
+
+def test_bad_ids_and_overflow_status(orc):
+    w = mi.random_case(9, 40, 8, 8, 2, 4, bad_frac=0.2)
+    lay = orc.layout(w.topk_idx, 8, 2, 1)
+    assert lay["status"] & 1
+    bad = (w.topk_idx < -1) | (w.topk_idx >= 8)
+    assert np.all(lay["slot"][bad] == -1)
+    dup = np.zeros((8, 2), np.int64)  # 16 pairs on expert 0, M = 8
+    ll = orc.ll_layout(dup, 4, 2, 8, 1)
+    assert ll["status"] == 2 and ll["recv_count"][0] == 8
+    assert (ll["slot"] >= 0).sum() == 8
+
+
+def test_empty_batch(orc):
+    idx = np.zeros((0, 8), np.int64)
+    lay = orc.layout(idx, 256, 8, 4)
+    assert lay["rows"] == 0 and lay["count"].sum() == 0 and lay["offset"].sum() == 0
+    assert lay["rank_token_count"].sum() == 0
