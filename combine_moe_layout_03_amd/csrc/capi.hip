@@ -1,0 +1,239 @@
+// C-ABI entry points of libmoe_ep.so (declared and documented in moe_ep.h):
+// host-side argument checks, then kernel launches on the caller's stream.
+// Nothing here allocates, frees or synchronises.
+#include <atomic>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "moe_ep.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace moe;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];  // 0 = not checked yet, 1 = gfx950, 2 = other
+
+// The kernels are compiled for gfx950 only; refuse any other current device.
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_DEVICE;
+  int state = dev < kMaxDevices ? g_arch[dev].load(std::memory_order_relaxed) : 0;
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MOE_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    if (dev < kMaxDevices) g_arch[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? MOE_OK : MOE_ERR_ARCH;
+}
+
+int bits_for(int n) {  // bits needed to tell apart the values 0 .. n-1
+  int b = 0;
+  while ((1 << b) < n) ++b;
+  return b;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape checks shared by every call that takes a moe_shape.
+int check_shape(const moe_shape *s, bool need_h) {
+  if (!s) return MOE_ERR_NULL;
+  if (s->T < 0 || s->K < 1 || s->K > 64 || s->E < 1 || s->E > kMaxExperts || s->R < 1 ||
+      s->E % s->R != 0 || s->A < 1 || s->A > (1 << 16))
+    return MOE_ERR_SHAPE;
+  const int64_t worst = (int64_t)s->T * s->K + (int64_t)s->E * (s->A - 1);
+  if (worst >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (need_h) {
+    if (s->H < 8 || s->H > (1 << 20) || s->H % 8 != 0) return MOE_ERR_SHAPE;
+    if ((int64_t)s->T * (s->H / 8) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  }
+  return MOE_OK;
+}
+
+int tokens_per_block(int K) { return kPairsPerBlock / K > 0 ? kPairsPerBlock / K : 1; }
+
+bool one_block(const moe_shape *s) { return (int64_t)s->T * s->K <= kMaxPairsOneBlock; }
+
+size_t workspace_bytes(const moe_shape *s) {
+  if (one_block(s)) return 0;
+  const int64_t tpb = tokens_per_block(s->K);
+  const int64_t nb = (s->T + tpb - 1) / tpb;
+  const int64_t ints = nb * s->E + nb * s->R;
+  return (size_t)((ints * 4 + 255) / 256 * 256);
+}
+
+int layout_common(const moe_shape *s, int mode, int32_t M, int32_t src, const int64_t *idx,
+                  const moe_layout_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s, false);
+  if (rc) return rc;
+  if (!out || !out->count || !out->slot) return MOE_ERR_NULL;
+  if (mode == kModeContiguous && !out->offset) return MOE_ERR_NULL;
+  if (s->T > 0 && !idx) return MOE_ERR_NULL;
+  if (mode == kModeLowLatency) {
+    if (M < 1 || s->T > M || src < 0 || src >= s->R) return MOE_ERR_LL;
+    if ((int64_t)s->E * s->R * M >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  }
+  const size_t need = workspace_bytes(s);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  rc = check_device();
+  if (rc) return rc;
+
+  LayoutParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.idx = idx;
+  p.T = s->T;
+  p.K = s->K;
+  p.E = s->E;
+  p.R = s->R;
+  p.L = s->E / s->R;
+  p.A = mode == kModeContiguous ? s->A : 1;
+  p.mode = mode;
+  p.M = M;
+  p.src = src;
+  p.id_bits = bits_for(s->E);
+  p.rank_bits = bits_for(s->R);
+  p.count = out->count;
+  p.offset = out->offset;
+  p.rank_token_count = out->rank_token_count;
+  p.in_rank = out->is_token_in_rank;
+  p.slot = out->slot;
+  p.row_src = out->row_src;
+  p.status = out->status;
+  hipError_t err;
+  if (one_block(s)) {
+    p.tokens_per_block = s->T > 0 ? s->T : 1;
+    p.nblocks = 1;
+    err = launch_layout_one_block(p, stream);
+  } else {
+    p.tokens_per_block = tokens_per_block(s->K);
+    p.nblocks = (s->T + p.tokens_per_block - 1) / p.tokens_per_block;
+    p.ws_hist = static_cast<int32_t *>(ws);
+    p.ws_rcnt = p.ws_hist + (int64_t)p.nblocks * s->E;
+    err = launch_layout_multi_block(p, stream);
+  }
+  return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+}  // namespace
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_CAPACITY: return "receive buffer size is invalid";
+    case MOE_ERR_LL: return "low latency: T > M or src_rank outside [0, R)";
+    case MOE_ERR_ALIGN: return "a row pointer is not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_ARCH: return "current device is not gfx950";
+    case MOE_ERR_DEVICE: return "HIP runtime query failed";
+    default: return "unknown error code";
+  }
+}
+
+MOE_API int64_t moe_recv_rows_worst(const moe_shape *shape) {
+  if (check_shape(shape, false)) return -1;
+  return (int64_t)shape->T * shape->K + (int64_t)shape->E * (shape->A - 1);
+}
+
+MOE_API int64_t moe_ll_recv_rows(int32_t E, int32_t R, int32_t M) {
+  if (E < 1 || R < 1 || M < 1 || E % R != 0) return -1;
+  return (int64_t)E * R * M;
+}
+
+MOE_API size_t moe_layout_workspace_bytes(const moe_shape *shape) {
+  if (check_shape(shape, false)) return 0;
+  return workspace_bytes(shape);
+}
+
+MOE_API int moe_layout(const moe_shape *shape, const int64_t *topk_idx, const moe_layout_t *out,
+                       void *ws, size_t ws_bytes, hipStream_t stream) {
+  return layout_common(shape, kModeContiguous, 0, 0, topk_idx, out, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank,
+                          const int64_t *topk_idx, const moe_layout_t *out, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return layout_common(shape, kModeLowLatency, M, src_rank, topk_idx, out, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_expert_load(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
+                            int32_t *load, int32_t *status, hipStream_t stream) {
+  if (T < 0 || K < 1 || K > 64 || E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
+  if ((int64_t)T * K >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (!load || (T > 0 && !topk_idx)) return MOE_ERR_NULL;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_expert_load(topk_idx, T, K, E, bits_for(E), load, status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *slot,
+                         uint16_t *recv_x, int64_t recv_rows, int32_t *status,
+                         hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!x || !slot || (!recv_x && recv_rows > 0)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_x)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_dispatch(x, slot, recv_x, shape->T, shape->K, shape->H, recv_rows, status,
+                         stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                        const int32_t *slot, const float *topk_weights, uint16_t *out,
+                        float *out_f32, int32_t *status, hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!slot || !out || (!y && recv_rows > 0)) return MOE_ERR_NULL;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_combine(y, recv_rows, slot, topk_weights, out, out_f32, shape->T, shape->K,
+                        shape->H, status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
+                              int32_t *replica_count, int32_t *replica_phys,
+                              int32_t *phys_to_logical, hipStream_t stream) {
+  if (E < 1 || E > kMaxExperts || R < 1 || E % R != 0 || C < 0 || C > E || C % R != 0)
+    return MOE_ERR_SHAPE;
+  if (!load || !replica_count || !replica_phys || !phys_to_logical) return MOE_ERR_NULL;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_plan_replicas(E, R, C, load, replica_count, replica_phys, phys_to_logical,
+                              stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
+                        const int32_t *replica_count, const int32_t *replica_phys,
+                        int32_t E_phys, int64_t *phys_idx, int32_t *status, hipStream_t stream) {
+  if (T < 0 || K < 1 || K > 64 || E < 1 || E_phys < 1) return MOE_ERR_SHAPE;
+  if ((int64_t)T * K >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !replica_count || !replica_phys || !phys_idx) return MOE_ERR_NULL;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_reroute(T, K, E, topk_idx, replica_count, replica_phys, E_phys, phys_idx, status,
+                        stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}

@@ -1,0 +1,70 @@
+// Internal launch interface between the C-ABI entry points (capi.hip) and the
+// gfx950 kernels (layout.hip, scatter.hip, replica.hip). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// One workgroup of the layout kernels: 16 wave64s.
+constexpr int kLayoutThreads = 1024;
+constexpr int kLayoutWaves = kLayoutThreads / 64;
+// Largest expert count (one expert per layout thread; per-wave counters in LDS).
+constexpr int kMaxExperts = 1024;
+// A batch of up to this many (token, k) pairs is laid out by one workgroup.
+constexpr int kMaxPairsOneBlock = 8192;
+// Above that, each workgroup of the first layout pass takes about this many pairs.
+constexpr int kPairsPerBlock = 1024;
+
+enum LayoutMode : int32_t {
+  kModeContiguous = 0,  // aligned per-expert partitions of one receive buffer
+  kModeLowLatency = 1,  // fixed stripes (e*R + src)*M + j
+};
+
+struct LayoutParams {
+  const int64_t *idx;  // [T*K]
+  int32_t T, K, E, R, L, A;
+  int32_t mode;
+  int32_t M, src;        // low-latency capacity and source rank
+  int32_t id_bits;       // bits needed for an expert id in [0, E)
+  int32_t rank_bits;     // bits needed for a rank id in [0, R)
+  int32_t tokens_per_block;
+  int32_t nblocks;
+  int32_t *count;
+  int32_t *offset;
+  int32_t *rank_token_count;
+  uint8_t *in_rank;
+  int32_t *slot;
+  int32_t *row_src;
+  int32_t *status;
+  int32_t *ws_hist;  // [nblocks][E]  multi-block path only
+  int32_t *ws_rcnt;  // [nblocks][R]  multi-block path only
+};
+
+// Status bits (same values as the MOE_STATUS_* macros of the public header).
+constexpr int32_t kStBadExpert = 1;
+constexpr int32_t kStOverflow = 2;
+constexpr int32_t kStBadSlot = 4;
+constexpr int32_t kStBadReplica = 8;
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_layout_one_block(const LayoutParams &p, hipStream_t s);
+hipError_t launch_layout_multi_block(const LayoutParams &p, hipStream_t s);
+hipError_t launch_expert_load(const int64_t *idx, int32_t T, int32_t K, int32_t E,
+                              int32_t id_bits, int32_t *load, int32_t *status, hipStream_t s);
+
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
+                           int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s);
+hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
+                          uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
+                          int32_t *status, hipStream_t s);
+
+hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
+                                int32_t *replica_count, int32_t *replica_phys,
+                                int32_t *phys_to_logical, hipStream_t s);
+hipError_t launch_reroute(int32_t T, int32_t K, int32_t E, const int64_t *idx,
+                          const int32_t *replica_count, const int32_t *replica_phys,
+                          int32_t E_phys, int64_t *phys_idx, int32_t *status, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,388 @@
+// Dispatch layout on gfx950: per-expert counts, aligned prefix offsets and
+// stable slots for every (token, k) pair, plus per-rank token sets.
+//
+// What is computed follows the NeMo AutoModel page
+// "nemo_automodel.components.moe.uccl_ep.buffer": Buffer.get_dispatch_layout
+// (num_tokens_per_rank, is_token_in_rank, num_tokens_per_expert), Buffer.dispatch
+// (expert_alignment), Buffer.low_latency_dispatch (receive stripes of M rows per
+// source rank and local expert). Rows inside an expert follow pair order t*K+k,
+// which makes the layout unique.
+//
+// How: a wave64 finds the lanes holding the same expert id with one ballot per
+// id bit (gfx950 has no match instruction), so a lane's rank among its peers is
+// a popcount and one leader lane per (wave, expert) touches LDS -- no atomics on
+// a hot expert's counter, whatever the skew. Each wave owns a contiguous segment
+// of pairs and a private row of uint16 counters in LDS; a per-expert prefix over
+// the 16 waves then gives every wave its starting rank. A batch of up to 8192
+// pairs is done by one workgroup; larger batches take three launches (per-block
+// counts and local ranks, one-workgroup scan over blocks, per-pair fix-up), with
+// no inter-workgroup waiting.
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Lanes of this wave holding the same key (only lanes with valid = true take
+// part). Every lane of the wave must call this (the ballots are wave-wide).
+__device__ __forceinline__ uint64_t match_peers(uint32_t key, bool valid, int bits) {
+  uint64_t m = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool one = (key >> b) & 1u;
+    const uint64_t ones = __ballot(one);
+    m &= one ? ones : ~ones;
+  }
+  return valid ? m : 0ull;
+}
+
+__device__ __forceinline__ bool is_leader(uint64_t peers) {
+  return peers != 0ull && (__ffsll((unsigned long long)peers) - 1) == lane_id();
+}
+
+__device__ __forceinline__ int below_me(uint64_t peers) {
+  const uint64_t lt = (1ull << lane_id()) - 1ull;
+  return __popcll(peers & lt);
+}
+
+// Exclusive scan of one int per thread over the 1024 threads of the block.
+__device__ int block_exclusive_scan(int v, int *s_wave, int *total) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kLayoutWaves; ++w) {
+    const int s = s_wave[w];
+    before += (w < wave) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int round_up(int c, int a) { return (c + a - 1) / a * a; }
+
+// One workgroup's share of the layout: tokens [t0, t1).
+// kOneBlock: the workgroup holds the whole batch and writes final slots.
+// Otherwise: it writes its per-expert totals and per-rank token counts to the
+// workspace and its pairs' ranks inside the block to slot[]; the scan and
+// fix-up kernels finish the job.
+template <bool kOneBlock>
+__global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutParams p) {
+  __shared__ int16_t s_ids[kMaxPairsOneBlock];     // validated ids, -1 = none (16 KiB)
+  __shared__ uint16_t s_wc[kLayoutWaves][kMaxExperts];  // per-wave counters (32 KiB)
+  __shared__ int32_t s_base[kMaxExperts];          // first slot of each expert
+  __shared__ int32_t s_cnt[kMaxExperts];           // pairs per expert in this block
+  __shared__ int32_t s_rc[kMaxExperts];            // tokens per rank in this block
+  __shared__ int32_t s_wave[kLayoutWaves];
+  __shared__ int32_t s_status;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int E = p.E, R = p.R, K = p.K;
+  const int t0 = blockIdx.x * p.tokens_per_block;
+  const int t1 = min(p.T, t0 + p.tokens_per_block);
+  const int nt = max(0, t1 - t0);
+  const int np = nt * K;
+  const int64_t p0 = (int64_t)t0 * K;
+  int st = 0;
+
+  for (int i = tid; i < kLayoutWaves * kMaxExperts; i += kLayoutThreads)
+    (&s_wc[0][0])[i] = 0;
+  for (int r = tid; r < R; r += kLayoutThreads) s_rc[r] = 0;
+  if (tid == 0) s_status = 0;
+
+  // Read the routing once; keep validated ids in LDS.
+  for (int i = tid; i < np; i += kLayoutThreads) {
+    const int64_t v = p.idx[p0 + i];
+    const bool ok = v >= 0 && v < E;
+    if (!ok && v != -1) st |= kStBadExpert;
+    s_ids[i] = ok ? (int16_t)v : (int16_t)-1;
+  }
+  __syncthreads();
+
+  // Per-wave counts over contiguous segments of 64-pair steps.
+  const int seg = (((np + kLayoutWaves - 1) / kLayoutWaves) + 63) & ~63;
+  const int s0 = wave * seg, s1 = min(np, s0 + seg);
+  for (int b = s0; b < s1; b += 64) {
+    const int i = b + lane;
+    const int e = (i < s1) ? s_ids[i] : -1;
+    const uint64_t peers = match_peers((uint32_t)e, e >= 0, p.id_bits);
+    if (is_leader(peers)) s_wc[wave][e] += (uint16_t)__popcll(peers);
+  }
+  __syncthreads();
+
+  // Exclusive prefix over waves for each expert; block totals.
+  for (int e = tid; e < E; e += kLayoutThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kLayoutWaves; ++w) {
+      const int c = s_wc[w][e];
+      s_wc[w][e] = (uint16_t)run;
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+
+  // First slot of each expert.
+  if (kOneBlock) {
+    const int e = tid;  // E <= 1024 = threads
+    const int c = (e < E) ? s_cnt[e] : 0;
+    const int padded = (p.mode == kModeContiguous) ? round_up(c, p.A) : 0;
+    int total = 0;
+    const int excl = block_exclusive_scan(padded, s_wave, &total);
+    if (e < E) {
+      if (p.mode == kModeContiguous) {
+        p.count[e] = c;
+        p.offset[e] = excl;
+        if (e == E - 1) p.offset[E] = total;
+        s_base[e] = excl;
+      } else {
+        const int base = (e * R + p.src) * p.M;
+        p.count[e] = min(c, p.M);
+        if (c > p.M) st |= kStOverflow;
+        if (p.offset) {
+          p.offset[e] = base;
+          if (e == E - 1) p.offset[E] = E * R * p.M;
+        }
+        s_base[e] = base;
+      }
+    }
+    if (E == 0 && tid == 0 && p.mode == kModeContiguous) p.offset[0] = 0;
+  } else {
+    for (int e = tid; e < E; e += kLayoutThreads)
+      p.ws_hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+  }
+  __syncthreads();
+
+  // Stable ranks: walk the same segments again; a wave's running counter per
+  // expert starts at the prefix of the waves before it.
+  for (int b = s0; b < s1; b += 64) {
+    const int i = b + lane;
+    const bool in = i < s1;
+    const int e = in ? s_ids[i] : -1;
+    const uint64_t peers = match_peers((uint32_t)e, e >= 0, p.id_bits);
+    if (in) {
+      int out = -1;
+      if (e >= 0) {
+        const int j = (int)s_wc[wave][e] + below_me(peers);
+        if (kOneBlock) {
+          if (p.mode == kModeContiguous) {
+            out = s_base[e] + j;
+            if (p.row_src) p.row_src[out] = (int32_t)(p0 + i);
+          } else if (j < p.M) {
+            out = s_base[e] + j;
+            if (p.row_src) p.row_src[(int64_t)e * p.M + j] = (int32_t)(p0 + i);
+          } else {
+            st |= kStOverflow;
+          }
+        } else {
+          out = j;
+        }
+      }
+      p.slot[p0 + i] = out;
+    }
+    if (is_leader(peers)) s_wc[wave][e] += (uint16_t)__popcll(peers);
+  }
+
+  // Which ranks each token reaches, and distinct tokens per rank.
+  if (p.in_rank || p.rank_token_count) {
+    const int L = p.L, n = nt * R;
+    for (int b = 0; b < n; b += kLayoutThreads) {
+      const int i = b + tid;
+      bool hit = false;
+      int r = 0;
+      if (i < n) {
+        const int tl = i / R;
+        r = i - tl * R;
+        for (int k = 0; k < K; ++k) {
+          const int e = s_ids[tl * K + k];
+          hit |= (e >= 0) && (e / L == r);
+        }
+        if (p.in_rank) p.in_rank[(int64_t)t0 * R + i] = hit ? 1 : 0;
+      }
+      const uint64_t peers = match_peers((uint32_t)r, hit, p.rank_bits);
+      if (is_leader(peers)) atomicAdd(&s_rc[r], __popcll(peers));
+    }
+  }
+  if (st) atomicOr(&s_status, st);
+  __syncthreads();
+
+  if (p.rank_token_count) {
+    for (int r = tid; r < R; r += kLayoutThreads) {
+      if (kOneBlock)
+        p.rank_token_count[r] = s_rc[r];
+      else
+        p.ws_rcnt[(int64_t)blockIdx.x * R + r] = s_rc[r];
+    }
+  }
+  if (kOneBlock && p.row_src) {
+    if (p.mode == kModeContiguous) {
+      // alignment padding rows carry -1
+      for (int e = tid; e < E; e += kLayoutThreads) {
+        const int lo = s_base[e] + s_cnt[e], hi = s_base[e] + round_up(s_cnt[e], p.A);
+        for (int r = lo; r < hi; ++r) p.row_src[r] = -1;
+      }
+    } else {
+      const int64_t n = (int64_t)E * p.M;
+      for (int64_t i = tid; i < n; i += kLayoutThreads) {
+        const int e = (int)(i / p.M), j = (int)(i - (int64_t)e * p.M);
+        if (j >= s_cnt[e]) p.row_src[i] = -1;
+      }
+    }
+  }
+  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
+}
+
+// Multi-block pass 2 (one workgroup): per-expert exclusive prefix over blocks,
+// aligned scan over experts, block bases, per-rank sums, padding rows.
+__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutParams p) {
+  __shared__ int32_t s_wave[kLayoutWaves];
+  const int tid = threadIdx.x, E = p.E, R = p.R, nb = p.nblocks;
+  const int e = tid;
+  int c = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int b = 0; b < nb; ++b) c += p.ws_hist[(int64_t)b * E + e];
+  }
+  const int padded = (p.mode == kModeContiguous) ? round_up(c, p.A) : 0;
+  int total = 0;
+  const int excl = block_exclusive_scan(padded, s_wave, &total);
+  int st = 0;
+  if (e < E) {
+    int base;
+    if (p.mode == kModeContiguous) {
+      base = excl;
+      p.count[e] = c;
+      p.offset[e] = excl;
+      if (e == E - 1) p.offset[E] = total;
+    } else {
+      base = (e * R + p.src) * p.M;
+      p.count[e] = min(c, p.M);
+      if (c > p.M) st |= kStOverflow;
+      if (p.offset) {
+        p.offset[e] = base;
+        if (e == E - 1) p.offset[E] = E * R * p.M;
+      }
+    }
+    // block b's pairs of expert e start at base + (pairs of e in blocks < b)
+    int run = base;
+#pragma unroll 8
+    for (int b = 0; b < nb; ++b) {
+      const int64_t at = (int64_t)b * E + e;
+      const int h = p.ws_hist[at];
+      p.ws_hist[at] = run;
+      run += h;
+    }
+    if (p.row_src) {
+      if (p.mode == kModeContiguous) {
+        for (int r = base + c; r < base + padded; ++r) p.row_src[r] = -1;
+      } else {
+        for (int j = min(c, p.M); j < p.M; ++j) p.row_src[(int64_t)e * p.M + j] = -1;
+      }
+    }
+  }
+  if (p.rank_token_count) {
+    for (int r = tid; r < R; r += kLayoutThreads) {
+      int s = 0;
+      for (int b = 0; b < nb; ++b) s += p.ws_rcnt[(int64_t)b * R + r];
+      p.rank_token_count[r] = s;
+    }
+  }
+  if (st && p.status) atomicOr(p.status, st);
+}
+
+// Multi-block pass 3: slot = (start of this block's run of the expert) + local rank.
+__global__ __launch_bounds__(256) void layout_fixup_kernel(LayoutParams p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = (int64_t)p.T * p.K;
+  if (i >= n) return;
+  const int64_t v = p.idx[i];
+  if (v < 0 || v >= p.E) return;  // slot already -1
+  const int e = (int)v;
+  const int b = (int)((i / p.K) / p.tokens_per_block);
+  const int s = p.ws_hist[(int64_t)b * p.E + e] + p.slot[i];
+  if (p.mode == kModeContiguous) {
+    p.slot[i] = s;
+    if (p.row_src) p.row_src[s] = (int32_t)i;
+  } else {
+    const int j = s - (e * p.R + p.src) * p.M;
+    if (j < p.M) {
+      p.slot[i] = s;
+      if (p.row_src) p.row_src[(int64_t)e * p.M + j] = (int32_t)i;
+    } else {
+      p.slot[i] = -1;
+      if (p.status) atomicOr(p.status, kStOverflow);
+    }
+  }
+}
+
+// Per-expert load of the batch with one workgroup: LDS histogram fed by one
+// leader lane per (wave, expert) per 64-pair step.
+__global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64_t *idx,
+                                                                     int32_t n, int32_t E,
+                                                                     int32_t bits,
+                                                                     int32_t *load,
+                                                                     int32_t *status) {
+  __shared__ int32_t s_h[kMaxExperts];
+  __shared__ int32_t s_status;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kLayoutThreads) s_h[e] = 0;
+  if (tid == 0) s_status = 0;
+  __syncthreads();
+  int st = 0;
+  for (int b = 0; b < n; b += kLayoutThreads) {
+    const int i = b + tid;
+    int e = -1;
+    if (i < n) {
+      const int64_t v = idx[i];
+      if (v >= 0 && v < E)
+        e = (int)v;
+      else if (v != -1)
+        st |= kStBadExpert;
+    }
+    const uint64_t peers = match_peers((uint32_t)e, e >= 0, bits);
+    if (is_leader(peers)) atomicAdd(&s_h[e], __popcll(peers));
+  }
+  if (st) atomicOr(&s_status, st);
+  __syncthreads();
+  for (int e = tid; e < E; e += kLayoutThreads) load[e] = s_h[e];
+  if (tid == 0 && s_status && status) atomicOr(status, s_status);
+}
+
+}  // namespace
+
+hipError_t launch_layout_one_block(const LayoutParams &p, hipStream_t s) {
+  hipLaunchKernelGGL(layout_block_kernel<true>, dim3(1), dim3(kLayoutThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout_multi_block(const LayoutParams &p, hipStream_t s) {
+  hipLaunchKernelGGL(layout_block_kernel<false>, dim3(p.nblocks), dim3(kLayoutThreads), 0, s, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, s, p);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n = (int64_t)p.T * p.K;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(layout_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_load(const int64_t *idx, int32_t T, int32_t K, int32_t E,
+                              int32_t id_bits, int32_t *load, int32_t *status, hipStream_t s) {
+  hipLaunchKernelGGL(expert_load_kernel, dim3(1), dim3(kLayoutThreads), 0, s, idx, T * K, E,
+                     id_bits, load, status);
+  return hipGetLastError();
+}
+
+}  // namespace moe

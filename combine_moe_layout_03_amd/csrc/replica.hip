@@ -1,0 +1,102 @@
+// Replica planning and routing expansion on gfx950, after the
+// "dots-infra/ultraep architecture" page (Overview: plan replicas from each
+// layer's post-gating routing, then expand the routing before the experts;
+// GPU operations: Placement planning, Routing expansion).
+//
+// Plan: one workgroup, one expert per thread. An expert's place in the order
+// (load descending, id ascending) is the number of experts ahead of it, read
+// from an LDS copy of the loads (broadcast reads); the first C get a second
+// physical replica. Numbering: rank r holds L' = L + C/R physical experts,
+// r*L' + l (l < L) is the primary of logical expert r*L + l, and the i-th
+// hottest expert's replica is (i mod R)*L' + L + i/R, so replicas are dealt
+// round-robin over the ranks.
+// Reroute: one thread per (token, k) pair; the pair uses replica
+// (t mod replica_count[e]) of its expert.
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(kLayoutThreads) void plan_replicas_kernel(
+    int32_t E, int32_t R, int32_t C, const int32_t *__restrict__ load,
+    int32_t *__restrict__ replica_count, int32_t *__restrict__ replica_phys,
+    int32_t *__restrict__ phys_to_logical) {
+  __shared__ int32_t s_load[kMaxExperts];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kLayoutThreads) s_load[e] = load[e];
+  __syncthreads();
+  const int e = tid;
+  if (e >= E) return;
+  const int mine = s_load[e];
+  int ahead = 0;
+  for (int f = 0; f < E; ++f) {
+    const int lf = s_load[f];
+    ahead += (lf > mine) || (lf == mine && f < e);
+  }
+  const int L = E / R, Lp = L + C / R;
+  const int prim = (e / L) * Lp + (e - (e / L) * L);
+  const bool hot = ahead < C;
+  replica_count[e] = hot ? 2 : 1;
+  replica_phys[2 * e] = prim;
+  phys_to_logical[prim] = e;
+  if (hot) {
+    const int rep = (ahead % R) * Lp + L + ahead / R;
+    replica_phys[2 * e + 1] = rep;
+    phys_to_logical[rep] = e;
+  } else {
+    replica_phys[2 * e + 1] = -1;
+  }
+}
+
+__global__ __launch_bounds__(256) void reroute_kernel(int32_t T, int32_t K, int32_t E,
+                                                      const int64_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ replica_count,
+                                                      const int32_t *__restrict__ replica_phys,
+                                                      int32_t E_phys, int64_t *__restrict__ phys,
+                                                      int32_t *status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)T * K) return;
+  const int64_t v = idx[i];
+  int64_t out = -1;
+  int st = 0;
+  if (v >= 0 && v < E) {
+    const int e = (int)v;
+    const int c = replica_count[e];
+    if (c == 1 || c == 2) {
+      const int t = (int)(i / K);
+      const int ph = replica_phys[2 * e + (c == 2 ? (t & 1) : 0)];
+      if (ph >= 0 && ph < E_phys)
+        out = ph;
+      else
+        st |= kStBadReplica;
+    } else {
+      st |= kStBadReplica;
+    }
+  } else if (v != -1) {
+    st |= kStBadExpert;
+  }
+  phys[i] = out;
+  if (st && status) atomicOr(status, st);
+}
+
+}  // namespace
+
+hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
+                                int32_t *replica_count, int32_t *replica_phys,
+                                int32_t *phys_to_logical, hipStream_t s) {
+  hipLaunchKernelGGL(plan_replicas_kernel, dim3(1), dim3(kLayoutThreads), 0, s, E, R, C, load,
+                     replica_count, replica_phys, phys_to_logical);
+  return hipGetLastError();
+}
+
+hipError_t launch_reroute(int32_t T, int32_t K, int32_t E, const int64_t *idx,
+                          const int32_t *replica_count, const int32_t *replica_phys,
+                          int32_t E_phys, int64_t *phys_idx, int32_t *status, hipStream_t s) {
+  const int64_t n = (int64_t)T * K;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(reroute_kernel, dim3(blocks), dim3(256), 0, s, T, K, E, idx, replica_count,
+                     replica_phys, E_phys, phys_idx, status);
+  return hipGetLastError();
+}
+
+}  // namespace moe

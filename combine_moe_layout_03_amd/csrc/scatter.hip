@@ -1,0 +1,196 @@
+// Dispatch scatter and weighted combine on gfx950.
+//
+// Dispatch (NeMo AutoModel page "nemo_automodel.components.moe.uccl_ep.buffer",
+// Buffer.dispatch and Buffer.low_latency_dispatch with bf16 x): every selected
+// (token, k) pair receives a bit copy of the token's hidden row in its slot of
+// the receive buffer.
+// Combine (same page, Buffer.low_latency_combine "reduce with weights"; and
+// Buffer.combine): each token's expert outputs are summed back, times their
+// top-k weights, into a bf16 row.
+//
+// Both are HBM-bound streams with no data reuse, so the design is about
+// bytes in flight: a thread owns one 16-byte vector (8 bf16) of one token row,
+// a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors -- about
+// 115k threads at 128 x 7168, enough to keep every CU busy. Dispatch reads its
+// vector once and issues K 16-byte stores (non-temporal: the receive rows are
+// not re-read by this kernel). Combine issues all K 16-byte loads of a vector
+// before it sums, so K requests per lane are in flight at once, then adds in
+// ascending k in f32 with no fused multiply-add and rounds once to bf16
+// (round to nearest even, NaN -> 0x7FC0).
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even; every NaN becomes 0x7FC0.
+__device__ __forceinline__ uint32_t to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int KT>
+__global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__ x,
+                                                       const int32_t *__restrict__ slot,
+                                                       u32x4 *__restrict__ recv, int32_t T,
+                                                       int32_t Kr, int32_t nvec, int64_t rows,
+                                                       int32_t *status) {
+  const int K = KT ? KT : Kr;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * nvec) return;
+  const int t = i / nvec;
+  const int v = i - t * nvec;
+  const u32x4 val = __builtin_nontemporal_load(x + i);
+  const int32_t *srow = slot + (int64_t)t * K;
+  int st = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int32_t s = srow[k];
+    if (s >= 0 && s < rows) {
+      __builtin_nontemporal_store(val, recv + (int64_t)s * nvec + v);
+    } else if (s != -1) {
+      st |= kStBadSlot;
+    }
+  }
+  if (st && status) atomicOr(status, st);
+}
+
+template <int KT, bool kWeights, bool kF32Out>
+__global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ y, int64_t rows,
+                                                      const int32_t *__restrict__ slot,
+                                                      const float *__restrict__ w,
+                                                      u32x4 *__restrict__ out,
+                                                      f32x4 *__restrict__ out_f32, int32_t T,
+                                                      int32_t Kr, int32_t nvec,
+                                                      int32_t *status) {
+#pragma clang fp contract(off)
+  const int K = KT ? KT : Kr;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * nvec) return;
+  const int t = i / nvec;
+  const int v = i - t * nvec;
+  const int32_t *srow = slot + (int64_t)t * K;
+  const float *wrow = kWeights ? w + (int64_t)t * K : nullptr;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  int st = 0;
+  // Groups of up to 8 pairs: issue the group's loads, then sum in k order.
+  constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
+  for (int k0 = 0; k0 < K; k0 += G) {
+    u32x4 val[G];
+    bool ok[G];
+    float wk[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int k = k0 + g;
+      ok[g] = false;
+      wk[g] = 1.0f;
+      if (k < K) {
+        const int32_t s = srow[k];
+        ok[g] = s >= 0 && s < rows;
+        if (!ok[g] && s != -1) st |= kStBadSlot;
+        if (ok[g]) val[g] = __builtin_nontemporal_load(y + (int64_t)s * nvec + v);
+        if (kWeights) wk[g] = wrow[k];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (!ok[g]) continue;
+      const float a = wk[g];
+      const u32x4 q = val[g];
+      acc[0] = acc[0] + a * bf16_lo(q.x);
+      acc[1] = acc[1] + a * bf16_hi(q.x);
+      acc[2] = acc[2] + a * bf16_lo(q.y);
+      acc[3] = acc[3] + a * bf16_hi(q.y);
+      acc[4] = acc[4] + a * bf16_lo(q.z);
+      acc[5] = acc[5] + a * bf16_hi(q.z);
+      acc[6] = acc[6] + a * bf16_lo(q.w);
+      acc[7] = acc[7] + a * bf16_hi(q.w);
+    }
+  }
+  u32x4 o;
+  o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
+  o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
+  o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
+  o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+  out[i] = o;
+  if (kF32Out) {
+    out_f32[2 * (int64_t)i] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    out_f32[2 * (int64_t)i + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  }
+  if (st && status) atomicOr(status, st);
+}
+
+template <int KT>
+hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
+                      int32_t K, int32_t nvec, int64_t rows, int32_t *status, hipStream_t s) {
+  const int64_t n = (int64_t)T * nvec;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(dispatch_kernel<KT>, dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(x), slot, reinterpret_cast<u32x4 *>(recv),
+                     T, K, nvec, rows, status);
+  return hipGetLastError();
+}
+
+template <int KT, bool kW, bool kF>
+hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
+                      uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
+                      int32_t *status, hipStream_t s) {
+  const int64_t n = (int64_t)T * nvec;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL((combine_kernel<KT, kW, kF>), dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(y), rows, slot, w,
+                     reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
+                     nvec, status);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t combine_k(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
+                     uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
+                     int32_t *status, hipStream_t s) {
+  if (w) {
+    if (out_f32) return combine_k3<KT, true, true>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    return combine_k3<KT, true, false>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+  }
+  if (out_f32) return combine_k3<KT, false, true>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+  return combine_k3<KT, false, false>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
+                           int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s) {
+  const int32_t nvec = H / 8;
+  switch (K) {
+    case 1: return dispatch_k<1>(x, slot, recv, T, K, nvec, rows, status, s);
+    case 2: return dispatch_k<2>(x, slot, recv, T, K, nvec, rows, status, s);
+    case 4: return dispatch_k<4>(x, slot, recv, T, K, nvec, rows, status, s);
+    case 6: return dispatch_k<6>(x, slot, recv, T, K, nvec, rows, status, s);
+    case 8: return dispatch_k<8>(x, slot, recv, T, K, nvec, rows, status, s);
+    default: return dispatch_k<0>(x, slot, recv, T, K, nvec, rows, status, s);
+  }
+}
+
+hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
+                          uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
+                          int32_t *status, hipStream_t s) {
+  const int32_t nvec = H / 8;
+  switch (K) {
+    case 1: return combine_k<1>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    case 2: return combine_k<2>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    case 4: return combine_k<4>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    case 6: return combine_k<6>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    case 8: return combine_k<8>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    default: return combine_k<0>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,149 @@
+"""Allocating convenience layer with the expert-parallel buffer's call names.
+
+The names and return tuples mirror the NeMo AutoModel page
+"nemo_automodel.components.moe.uccl_ep.buffer" (Buffer.get_dispatch_layout,
+Buffer.dispatch, Buffer.combine, Buffer.low_latency_dispatch,
+Buffer.low_latency_combine) reduced to one GPU: the R logical ranks are
+partitions of one HBM receive buffer and nothing crosses a GPU boundary. The
+replica calls mirror the "dots-infra/ultraep architecture" page (Load
+computation, Placement planning, Routing expansion).
+
+This layer only allocates torch tensors and calls the C ABI through ``capi``;
+every step runs in the library's kernels, on the current torch stream, with
+no host synchronisation.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+from . import capi
+
+
+@dataclass
+class Handle:
+    """What dispatch hands on to combine: the shape and the layout arrays."""
+
+    shape: capi.moe_shape
+    layout: capi.LayoutBuffers
+    recv_rows: int
+    ll_M: Optional[int] = None
+    src_rank: int = 0
+
+
+def _workspace(shape: capi.moe_shape, device) -> Optional[torch.Tensor]:
+    n = capi.moe_layout_workspace_bytes(shape)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int,
+                        expert_alignment: int = 1, hidden: int = 8):
+    """Returns (num_tokens_per_rank [R] int32, None, num_tokens_per_expert [E] int32,
+    is_token_in_rank [T, R] bool, handle). The per-RDMA-rank counts are None,
+    as for a single node."""
+    T, K = topk_idx.shape
+    shape = capi.make_shape(T, hidden, num_experts, num_ranks, K, expert_alignment)
+    lay = capi.LayoutBuffers.empty(shape, topk_idx.device)
+    capi.moe_layout(shape, topk_idx.contiguous(), lay, _workspace(shape, topk_idx.device))
+    h = Handle(shape, lay, capi.moe_recv_rows_worst(shape))
+    return (lay.rank_token_count, None, lay.count,
+            lay.is_token_in_rank.view(T, num_ranks).bool(), h)
+
+
+def dispatch(x: torch.Tensor, handle: Handle, recv_x: Optional[torch.Tensor] = None):
+    """Scatter bf16 rows into the contiguous receive buffer, sized for the worst
+    case (T*K + E*(A-1) rows, so no host read of the counts is needed).
+    Rows [offset[e], offset[e] + count[e]) belong to expert e."""
+    T, H = x.shape
+    shape = capi.make_shape(T, H, handle.shape.E, handle.shape.R, handle.shape.K,
+                            handle.shape.A)
+    handle.shape = shape
+    if recv_x is None:
+        recv_x = torch.empty(max(handle.recv_rows, 1), H, dtype=x.dtype, device=x.device)
+    capi.moe_dispatch(shape, x.contiguous(), handle.layout.slot, recv_x, handle.recv_rows,
+                      handle.layout.status)
+    return recv_x
+
+
+def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, out_f32: Optional[torch.Tensor] = None):
+    """Weighted reduce of the expert outputs back to [T, H] bf16 (weights None:
+    plain sum)."""
+    shape = handle.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty(shape.T, H, dtype=torch.bfloat16, device=y.device)
+    w = topk_weights.contiguous() if topk_weights is not None else None
+    capi.moe_combine(shape, y.contiguous(), handle.recv_rows, handle.layout.slot, w, out,
+                     out_f32, handle.layout.status)
+    return out
+
+
+def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
+                         num_max_dispatch_tokens_per_rank: int, num_experts: int,
+                         num_ranks: int, src_rank: int = 0,
+                         recv_x: Optional[torch.Tensor] = None):
+    """Padded low-latency dispatch from source rank ``src_rank``. Returns
+    (recv_x [R, L, R*M, H] -- rank r's receive buffer is recv_x[r] --,
+    recv_count [E] int32, handle). Only the source's stripe is written; rows
+    past recv_count are not valid."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    M = int(num_max_dispatch_tokens_per_rank)
+    E, R = num_experts, num_ranks
+    shape = capi.make_shape(T, H, E, R, K, 1)
+    lay = capi.LayoutBuffers.empty(shape, x.device, ll_M=M)
+    capi.moe_ll_layout(shape, M, src_rank, topk_idx.contiguous(), lay,
+                       _workspace(shape, x.device))
+    rows = capi.moe_ll_recv_rows(E, R, M)
+    if recv_x is None:
+        recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
+    capi.moe_dispatch(shape, x.contiguous(), lay.slot, recv_x, rows, lay.status)
+    h = Handle(shape, lay, rows, ll_M=M, src_rank=src_rank)
+    return recv_x.view(R, E // R, R * M, H), lay.count, h
+
+
+def low_latency_combine(y: torch.Tensor, topk_weights: torch.Tensor, handle: Handle,
+                        out: Optional[torch.Tensor] = None):
+    """Weighted reduce from the padded layout in place (the expert wrote its
+    outputs straight into the padded buffer, as with zero_copy)."""
+    return combine(y.reshape(-1, y.shape[-1]), handle, topk_weights, out)
+
+
+def expert_load(topk_idx: torch.Tensor, num_experts: int,
+                status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, K = topk_idx.shape
+    load = torch.empty(num_experts, dtype=torch.int32, device=topk_idx.device)
+    capi.moe_expert_load(T, K, num_experts, topk_idx.contiguous(), load, status)
+    return load
+
+
+@dataclass
+class ReplicaPlan:
+    replica_count: torch.Tensor    # [E] 1 or 2
+    replica_phys: torch.Tensor     # [E, 2] primary, replica or -1
+    phys_to_logical: torch.Tensor  # [E + C]
+    num_physical: int
+    num_ranks: int
+
+
+def plan_replicas(load: torch.Tensor, num_ranks: int, num_replicas: int) -> ReplicaPlan:
+    E = load.numel()
+    dev = load.device
+    rc = torch.empty(E, dtype=torch.int32, device=dev)
+    rp = torch.empty(E, 2, dtype=torch.int32, device=dev)
+    p2l = torch.empty(E + num_replicas, dtype=torch.int32, device=dev)
+    capi.moe_plan_replicas(E, num_ranks, num_replicas, load.contiguous(), rc, rp, p2l)
+    return ReplicaPlan(rc, rp, p2l, E + num_replicas, num_ranks)
+
+
+def reroute(topk_idx: torch.Tensor, plan: ReplicaPlan,
+            status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    T, K = topk_idx.shape
+    E = plan.replica_count.numel()
+    phys = torch.empty(T, K, dtype=torch.int64, device=topk_idx.device)
+    capi.moe_reroute(T, K, E, topk_idx.contiguous(), plan.replica_count, plan.replica_phys,
+                     plan.num_physical, phys, status)
+    return phys

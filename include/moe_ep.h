@@ -1,0 +1,195 @@
+/*
+ * moe_ep.h -- C ABI of libmoe_ep.so: MoE token dispatch and combine on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the problem statement of the expert-parallel buffer
+ * API documented on the NeMo AutoModel page
+ * "nemo_automodel.components.moe.uccl_ep.buffer" (sections Buffer.get_dispatch_layout,
+ * Buffer.dispatch, Buffer.combine, Buffer.low_latency_dispatch,
+ * Buffer.low_latency_combine, Buffer.get_low_latency_rdma_size_hint) and the
+ * routing expansion of the "dots-infra/ultraep architecture" page (Overview;
+ * GPU operations: Load computation, Placement planning, Routing expansion).
+ * Everything runs on one GPU: the R logical ranks of the expert-parallel group
+ * are partitions of one HBM buffer.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named as device memory are caller-owned device pointers (for
+ *    example a torch tensor's data_ptr()). The library allocates nothing,
+ *    frees nothing and keeps no state between calls beyond a per-device
+ *    architecture check, so calls from several host threads are safe.
+ *  - Every call enqueues its kernels on the caller's stream and returns
+ *    without waiting for them (no host synchronisation, no host-visible
+ *    counts). A NULL stream is the default stream.
+ *  - Return value: MOE_OK (0), or a negative MOE_ERR_* code from a host-side
+ *    check. When a check fails, nothing has been enqueued.
+ *  - Data errors that only the device can see (an expert id outside [-1, E),
+ *    a low-latency expert receiving more than M rows, a slot outside the
+ *    receive buffer) make the kernels skip the offending pair and OR a
+ *    MOE_STATUS_* bit into *status, when the caller passes a status word.
+ *    The caller zeroes it; it can be read after synchronising the stream.
+ *  - T = 0 (an empty batch) is valid: counts and offsets are written as zeros,
+ *    dispatch and combine do nothing.
+ *  - No output needs to be zero-initialised beforehand.
+ *  - Row-major layouts everywhere. bf16 values travel as raw 16-bit patterns
+ *    (uint16_t). Pointers to bf16 rows, f32 rows and the receive buffer must be
+ *    16-byte aligned, and H must be a multiple of 8 (one 16-byte vector is
+ *    8 bf16 values).
+ *  - Limits: 1 <= E <= 1024, 1 <= R, E % R == 0, 1 <= K <= 64,
+ *    0 <= T, T*K + E*(A-1) < 2^31, 8 <= H <= 2^20, 1 <= A <= 2^16.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Host-side return codes. */
+#define MOE_OK 0
+#define MOE_ERR_NULL (-1)      /* a required pointer is NULL */
+#define MOE_ERR_SHAPE (-2)     /* a size is out of range or inconsistent */
+#define MOE_ERR_CAPACITY (-3)  /* receive buffer smaller than the worst case */
+#define MOE_ERR_LL (-4)        /* low latency: T > M, or src_rank not in [0, R) */
+#define MOE_ERR_ALIGN (-5)     /* a row pointer is not 16-byte aligned */
+#define MOE_ERR_WORKSPACE (-6) /* workspace missing or smaller than required */
+#define MOE_ERR_LAUNCH (-7)    /* the HIP runtime refused a kernel launch */
+#define MOE_ERR_ARCH (-8)      /* the current device is not gfx950 */
+#define MOE_ERR_DEVICE (-9)    /* the HIP runtime could not be queried */
+
+/* Device-side status bits (OR-ed into *status). */
+#define MOE_STATUS_BAD_EXPERT 1   /* an id outside [-1, E): the pair is skipped */
+#define MOE_STATUS_LL_OVERFLOW 2  /* low latency: an expert got more than M pairs */
+#define MOE_STATUS_BAD_SLOT 4     /* a slot outside [-1, recv_rows): the pair is skipped */
+#define MOE_STATUS_BAD_REPLICA 8  /* reroute: replica table entry out of range */
+
+/* Problem shape. T tokens, hidden size H, E experts spread evenly over R
+ * logical ranks (L = E/R local experts each, expert e lives on rank e / L),
+ * K selections per token, and expert alignment A (Buffer.dispatch,
+ * expert_alignment: every expert's row count is rounded up to a multiple of A). */
+typedef struct {
+  int32_t T, H, E, R, K, A;
+} moe_shape;
+
+/* Device arrays written by the layout calls; together they are the
+ * communication handle that Buffer.dispatch hands on to Buffer.combine.
+ * Pointers marked "may be NULL" are skipped when NULL. */
+typedef struct {
+  int32_t *count;            /* [E] pairs per expert (num_tokens_per_expert). Low latency:
+                                rows received per expert from this source, min(pairs, M). */
+  int32_t *offset;           /* [E+1] first row of each expert; offset[E] = rows used.
+                                Low latency: stripe base (e*R + src_rank)*M, and E*R*M.
+                                May be NULL in low-latency mode. */
+  int32_t *rank_token_count; /* [R] distinct tokens sent to each rank (num_tokens_per_rank).
+                                May be NULL. */
+  uint8_t *is_token_in_rank; /* [T*R] 1 if token t sends to rank r, else 0. May be NULL. */
+  int32_t *slot;             /* [T*K] receive row of pair (t,k); -1 if not sent. */
+  int32_t *row_src;          /* Contiguous: [moe_recv_rows_worst] pair index t*K+k held by
+                                each row in [0, offset[E]), -1 on alignment padding.
+                                Low latency: [E*M], pair held by stripe row j of expert e at
+                                e*M + j, -1 where empty. May be NULL. */
+  int32_t *status;           /* [1] sticky MOE_STATUS_* bits. May be NULL. */
+} moe_layout_t;
+
+/* ABI version (MOE_ABI_VERSION) of the loaded library. */
+int moe_abi_version(void);
+
+/* Static text for a MOE_OK / MOE_ERR_* code. */
+const char *moe_strerror(int code);
+
+/* Worst-case rows of the contiguous receive buffer: T*K + E*(A-1); -1 for an
+ * invalid shape. Sizing the buffer this way needs no host read of the counts
+ * (Buffer.dispatch, num_worst_tokens: no CPU sync, graph-capturable). */
+int64_t moe_recv_rows_worst(const moe_shape *shape);
+
+/* Rows of the union of the R low-latency receive buffers: each rank holds
+ * [L, R*M, H] (Buffer.low_latency_dispatch, return value; sizing as in
+ * Buffer.get_low_latency_rdma_size_hint), so all of them together are
+ * E*R*M rows. -1 for invalid arguments. */
+int64_t moe_ll_recv_rows(int32_t E, int32_t R, int32_t M);
+
+/* Device workspace bytes that moe_layout / moe_ll_layout need for this shape
+ * (0 when the whole batch fits one workgroup). */
+size_t moe_layout_workspace_bytes(const moe_shape *shape);
+
+/* Contiguous dispatch layout (Buffer.get_dispatch_layout and the layout half of
+ * Buffer.dispatch).
+ *   topk_idx [T*K] int64 device: expert of each pair, -1 = no selection.
+ *   out: count, offset, slot required; the rest may be NULL.
+ *   Result: count[e] = pairs with id e; offset[0] = 0,
+ *   offset[e+1] = offset[e] + ceil(count[e]/A)*A; the j-th pair of expert e in
+ *   pair order t*K+k gets slot offset[e] + j (stable, so the layout is unique);
+ *   alignment padding rows are not written by dispatch.
+ *   ws: device workspace of ws_bytes >= moe_layout_workspace_bytes(shape), may
+ *   be NULL when that is 0. */
+int moe_layout(const moe_shape *shape, const int64_t *topk_idx, const moe_layout_t *out,
+               void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Low-latency padded layout (Buffer.low_latency_dispatch): this GPU is source
+ * rank src_rank with T <= M tokens. The j-th pair of expert e (pair order)
+ * gets slot (e*R + src_rank)*M + j, a row of the [E, R*M, H] union of the R
+ * receive buffers (rank e/L's buffer, local expert e%L, stripe src_rank).
+ * out->count receives the per-expert receive counts min(pairs, M); pairs with
+ * j >= M get slot -1 and set MOE_STATUS_LL_OVERFLOW. shape->A is ignored. */
+int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank, const int64_t *topk_idx,
+                  const moe_layout_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-expert load of the batch (ultraep GPU operations, Load computation):
+ * load[e] = pairs with id e, e in [0, E). Ids outside [-1, E) set
+ * MOE_STATUS_BAD_EXPERT. status may be NULL. */
+int moe_expert_load(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx, int32_t *load,
+                    int32_t *status, hipStream_t stream);
+
+/* Dispatch scatter (Buffer.dispatch / Buffer.low_latency_dispatch with bf16 x):
+ * recv_x[slot[t*K+k]] = x[t] bit for bit, for every pair with slot != -1.
+ *   x [T*H] bf16, slot [T*K] (from moe_layout or moe_ll_layout),
+ *   recv_x [recv_rows*H] bf16. Rows no pair maps to are left untouched.
+ *   status may be NULL. */
+int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *slot,
+                 uint16_t *recv_x, int64_t recv_rows, int32_t *status, hipStream_t stream);
+
+/* Combine (Buffer.low_latency_combine: reduce with weights; Buffer.combine with
+ * topk_weights = NULL is the plain sum):
+ *   out[t] = bf16_rne( sum over k = 0..K-1 with slot != -1 of w[t*K+k] * y[slot[t*K+k]] )
+ * summed in float in ascending k, every product and sum rounded to float
+ * (no fused multiply-add), starting from +0; a token with no valid pair gets +0.
+ *   y [recv_rows*H] bf16 (expert outputs, same row layout as recv_x),
+ *   topk_weights [T*K] f32 or NULL for all ones, out [T*H] bf16,
+ *   out_f32 [T*H] f32 (the unrounded sums) or NULL. status may be NULL. */
+int moe_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                const int32_t *slot, const float *topk_weights, uint16_t *out, float *out_f32,
+                int32_t *status, hipStream_t stream);
+
+/* Replica plan (ultraep GPU operations, Placement planning): the C most loaded
+ * experts (load descending, ties to the lower id) get a second physical
+ * replica. Rank r holds L' = L + C/R physical experts: r*L' + l (l < L) is the
+ * primary of logical expert r*L + l, and the i-th hottest expert's replica is
+ * (i mod R)*L' + L + i/R.
+ *   load [E] int32 (e.g. from moe_expert_load); outputs replica_count [E]
+ *   (1 or 2), replica_phys [E*2] (primary, replica or -1), phys_to_logical [E+C].
+ *   Needs E <= 1024, 0 <= C <= E, C % R == 0. */
+int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
+                      int32_t *replica_count, int32_t *replica_phys, int32_t *phys_to_logical,
+                      hipStream_t stream);
+
+/* Routing expansion (ultraep GPU operations, Routing expansion): logical
+ * routing -> physical routing. The pair (t,k) on expert e uses replica
+ * t mod replica_count[e]: phys_idx[t*K+k] = replica_phys[2e + t mod count];
+ * -1 stays -1. Entries that fall outside [0, E_phys) set MOE_STATUS_BAD_REPLICA
+ * and give -1. phys_idx [T*K] int64 can feed moe_layout with E = E_phys. */
+int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
+                const int32_t *replica_count, const int32_t *replica_phys, int32_t E_phys,
+                int64_t *phys_idx, int32_t *status, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

@@ -1,0 +1,130 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-side checks reject bad arguments before touching a
+device (no kernel is launched here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from combine_moe_layout_03_amd import capi
+
+    return capi
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) == 12, declared
+    assert sorted(lib.EXPORTED) == declared
+    raw = C.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert getattr(raw, name) is not None
+
+
+def test_version_and_strerror(lib):
+    assert lib.moe_abi_version() == 1
+    for code in range(0, -10, -1):
+        assert lib.moe_strerror(code) != "unknown error code"
+    assert lib.moe_strerror(-99) == "unknown error code"
+
+
+def test_size_helpers(lib):
+    s = lib.make_shape(128, 7168, 256, 8, 8, 1)
+    assert lib.moe_recv_rows_worst(s) == 1024
+    s = lib.make_shape(128, 7168, 256, 8, 8, 128)
+    assert lib.moe_recv_rows_worst(s) == 1024 + 256 * 127
+    assert lib.moe_ll_recv_rows(256, 8, 128) == 256 * 8 * 128
+    assert lib.moe_ll_recv_rows(255, 8, 128) == -1
+    assert lib.moe_layout_workspace_bytes(lib.make_shape(128, 7168, 256, 8, 8)) == 0
+    big = lib.make_shape(8192, 7168, 288, 8, 8)
+    n = lib.moe_layout_workspace_bytes(big)
+    assert n >= (64 * 288 + 64 * 8) * 4 and n % 256 == 0
+    assert lib.moe_recv_rows_worst(lib.make_shape(1, 8, 6, 4, 1)) == -1  # E % R != 0
+
+
+def _raw(lib):
+    return lib.lib()
+
+
+BAD_SHAPES = [
+    (-1, 8, 16, 4, 2, 1),  # T < 0
+    (4, 8, 16, 4, 0, 1),  # K < 1
+    (4, 8, 16, 4, 65, 1),  # K > 64
+    (4, 8, 0, 1, 2, 1),  # E < 1
+    (4, 8, 1025, 1, 2, 1),  # E > 1024
+    (4, 8, 16, 3, 2, 1),  # E % R
+    (4, 8, 16, 4, 2, 0),  # A < 1
+    (1 << 30, 8, 16, 4, 2, 1),  # T*K >= 2^31
+]
+
+
+@pytest.mark.parametrize("shp", BAD_SHAPES)
+def test_layout_rejects_bad_shape(lib, shp):
+    s = lib.make_shape(*shp)
+    lt = lib.moe_layout_t()
+    dummy = C.c_void_p(16)
+    lt.count = lt.offset = lt.slot = dummy
+    rc = _raw(lib).moe_layout(C.byref(s), dummy, C.byref(lt), None, 0, None)
+    assert rc == -2
+
+
+def test_null_and_ll_checks(lib):
+    raw = _raw(lib)
+    s = lib.make_shape(4, 8, 16, 4, 2, 1)
+    d = C.c_void_p(256)
+    lt = lib.moe_layout_t()
+    assert raw.moe_layout(None, d, C.byref(lt), None, 0, None) == -1
+    assert raw.moe_layout(C.byref(s), d, C.byref(lt), None, 0, None) == -1  # count/slot NULL
+    lt.count = lt.offset = lt.slot = d
+    assert raw.moe_layout(C.byref(s), None, C.byref(lt), None, 0, None) == -1  # idx NULL, T>0
+    assert raw.moe_ll_layout(C.byref(s), 3, 0, d, C.byref(lt), None, 0, None) == -4  # T > M
+    assert raw.moe_ll_layout(C.byref(s), 4, 4, d, C.byref(lt), None, 0, None) == -4  # src
+    assert raw.moe_ll_layout(C.byref(s), 4, -1, d, C.byref(lt), None, 0, None) == -4
+    big = lib.make_shape(10000, 8, 16, 4, 2, 1)  # needs a workspace
+    assert raw.moe_layout(C.byref(big), d, C.byref(lt), None, 0, None) == -6
+    assert raw.moe_layout(C.byref(big), d, C.byref(lt), d, 16, None) == -6
+
+
+def test_dispatch_combine_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(258)
+    s = lib.make_shape(4, 12, 16, 4, 2, 1)  # H % 8 != 0
+    assert raw.moe_dispatch(C.byref(s), d, d, d, 8, None, None) == -2
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    assert raw.moe_dispatch(C.byref(s), d, d, d, -1, None, None) == -3
+    assert raw.moe_dispatch(C.byref(s), None, d, d, 8, None, None) == -1
+    assert raw.moe_dispatch(C.byref(s), odd, d, d, 8, None, None) == -5
+    assert raw.moe_dispatch(C.byref(s), d, d, odd, 8, None, None) == -5
+    assert raw.moe_combine(C.byref(s), d, 8, d, None, odd, None, None, None) == -5
+    assert raw.moe_combine(C.byref(s), d, 8, d, None, d, odd, None, None) == -5
+    assert raw.moe_combine(C.byref(s), d, 8, None, None, d, None, None, None) == -1
+    # an empty batch is a no-op that needs no device
+    s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
+    assert raw.moe_dispatch(C.byref(s0), None, None, None, 0, None, None) == 0
+    assert raw.moe_combine(C.byref(s0), None, 0, None, None, None, None, None, None) == 0
+
+
+def test_replica_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    assert raw.moe_plan_replicas(256, 8, 30, d, d, d, d, None) == -2  # C % R
+    assert raw.moe_plan_replicas(256, 8, 264, d, d, d, d, None) == -2  # C > E
+    assert raw.moe_plan_replicas(250, 8, 32, d, d, d, d, None) == -2  # E % R
+    assert raw.moe_plan_replicas(256, 8, 32, None, d, d, d, None) == -1
+    assert raw.moe_reroute(4, 0, 16, d, d, d, 20, d, None, None) == -2
+    assert raw.moe_reroute(4, 2, 16, None, d, d, 20, d, None, None) == -1
+    assert raw.moe_reroute(0, 2, 16, None, None, None, 20, None, None, None) == 0
+    assert raw.moe_expert_load(4, 2, 2000, d, d, None, None) == -2

@@ -1,0 +1,346 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, element by element.
+
+Bar: layout arrays, dispatched rows and untouched rows bit-exact; combine within
+1e-2 relative + 1e-3 absolute of the oracle's f64 sum (the stated tolerance),
+and, as a stronger check of the fixed summation order, bit-exact against the
+oracle's f32 ascending-k sum and its bf16 rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from gpu_path import SENTINEL, dev, np16, run_dispatch_combine, run_layout, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def capi():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from combine_moe_layout_03_amd import capi as c
+
+    return c
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def check_layout(got, ref, w, ll=False):
+    assert np.array_equal(got["slot"], ref["slot"]), "slot"
+    if ll:
+        assert np.array_equal(got["count"], ref["recv_count"]), "recv_count"
+    else:
+        assert np.array_equal(got["count"], ref["count"]), "count"
+        assert np.array_equal(got["offset"], ref["offset"]), "offset"
+    if "row_src" in got:
+        assert np.array_equal(got["row_src"], ref["row_src"]), "row_src"
+        assert np.array_equal(got["rank_token_count"], ref["rank_token_count"]), "rank_token_count"
+        assert np.array_equal(got["is_token_in_rank"], ref["is_token_in_rank"]), "in_rank"
+    assert got["status"] == ref["status"], ("status", got["status"], ref["status"])
+
+
+def check_combine(orc, got16, got32, recv_ref, slot, wts, tokens=None):
+    if tokens is not None:
+        slot = slot[tokens]
+        wts = None if wts is None else wts[tokens]
+        got16 = got16[tokens]
+        got32 = None if got32 is None else got32[tokens]
+    r64 = orc.combine(recv_ref, slot, wts, "f64")["out_f64"]
+    r32 = orc.combine(recv_ref, slot, wts, "f32")
+    g16 = mi.bf16_bits_to_f32(got16).astype(np.float64)
+    assert np.all(np.abs(g16 - r64) <= ATOL + RTOL * np.abs(r64)), "bf16 out vs f64 oracle"
+    assert np.array_equal(got16, r32["out_bf16"]), "bf16 out vs f32-order oracle"
+    if got32 is not None:
+        g32 = got32.astype(np.float64)
+        assert np.all(np.abs(g32 - r64) <= ATOL + RTOL * np.abs(r64)), "f32 out vs f64 oracle"
+        assert np.array_equal(got32.view(np.uint32), r32["out_f32"].view(np.uint32)), \
+            "f32 out vs f32-order oracle"
+
+
+def full_case(capi, orc, w, A=None, weights=True):
+    A = w.A if A is None else A
+    got, lay, shape = run_layout(capi, w, A=A)
+    ref = orc.layout(w.topk_idx, w.E, w.R, A)
+    check_layout(got, ref, w)
+    rows = ref["rows"]
+    recv, o16, o32, st = run_dispatch_combine(capi, w, shape, lay, rows, weights=weights)
+    rref, _ = orc.dispatch(w.x, ref["slot"], rows, fill=SENTINEL)
+    assert np.array_equal(recv[:rows], rref), "dispatched rows / untouched padding"
+    check_combine(orc, o16, o32, rref, ref["slot"], w.topk_weights if weights else None)
+    assert st == ref["status"]
+
+
+CASES = {
+    "c1": lambda: mi.config_c1(),
+    "c2": lambda: mi.config_c2(),
+    "rand_ragged_H1000_K6": lambda: mi.random_case(11, 300, 1000, 64, 8, 6, 1, neg_frac=0.1),
+    "rand_H8_K3_dups": lambda: mi.random_case(12, 77, 8, 12, 3, 3, 1, dup_frac=0.4),
+    "rand_K1": lambda: mi.random_case(13, 200, 64, 16, 4, 1, 1),
+    "rand_E1_R1": lambda: mi.random_case(14, 50, 16, 1, 1, 4, 1),
+    "rand_E1024_R64": lambda: mi.random_case(15, 256, 128, 1024, 64, 8, 1),
+    "rand_K64_onefull": lambda: mi.random_case(16, 128, 32, 256, 8, 64, 1),  # 8192 pairs
+    "rand_K64_multi": lambda: mi.random_case(17, 129, 32, 256, 8, 64, 1),  # 8256 pairs
+    "rand_8193pairs": lambda: mi.random_case(18, 8193, 16, 32, 4, 1, 1),
+    "rand_all_neg": lambda: mi.random_case(19, 64, 64, 16, 4, 4, 1, neg_frac=1.0),
+    "rand_bad_ids": lambda: mi.random_case(20, 100, 64, 32, 4, 4, 1, bad_frac=0.1),
+    "rand_T1": lambda: mi.random_case(21, 1, 7168, 256, 8, 8, 1, distinct=True),
+    "rand_hot_expert": lambda: _hot(mi.random_case(22, 3000, 64, 64, 8, 6, 1), 5, 0.9),
+}
+
+
+def _hot(w, e, frac):
+    """Send a fraction of all pairs to one expert (skew far beyond Zipf)."""
+    rng = np.random.default_rng(w.seed)
+    w.topk_idx = np.where(rng.random(w.topk_idx.shape) < frac, e, w.topk_idx)
+    return w
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+@pytest.mark.parametrize("A", [1, 16])
+def test_path_parity(capi, orc, name, A):
+    w = CASES[name]()
+    _announce(f"{name} A={A} T={w.T} H={w.H} E={w.E} R={w.R} K={w.K}")
+    full_case(capi, orc, w, A=A)
+
+
+def test_unweighted_combine(capi, orc):
+    w = mi.config_c2()
+    _announce("c2 unweighted")
+    full_case(capi, orc, w, weights=False)
+
+
+def test_c2_alignment_128(capi, orc):
+    w = mi.config_c2()
+    _announce("c2 A=128")
+    full_case(capi, orc, w, A=128)
+
+
+def test_empty_batch(capi, orc):
+    w = mi.random_case(30, 0, 64, 16, 4, 4, 4)
+    _announce("T=0")
+    got, lay, shape = run_layout(capi, w)
+    assert got["count"].sum() == 0 and np.all(got["offset"] == 0)
+    assert np.all(got["rank_token_count"] == 0) and got["status"] == 0
+    recv, o16, o32, st = run_dispatch_combine(capi, w, shape, lay, 0)
+    assert st == 0
+
+
+def test_c4_skewed_full(capi, orc):
+    w = mi.config_c4()
+    _announce("c4 skewed full size")
+    full_case(capi, orc, w)
+
+
+def _gpu_rows_check(recv_t, x_t, slot, T, K):
+    """On the GPU: every pair's row equals its token's row (bitwise); every
+    other row still holds the sentinel."""
+    v = slot.reshape(-1) >= 0
+    rows_idx = torch.from_numpy(slot.reshape(-1)[v].astype(np.int64)).to(dev())
+    toks = torch.from_numpy(np.repeat(np.arange(T), K)[v]).to(dev())
+    for a in range(0, rows_idx.numel(), 4096):
+        assert torch.equal(recv_t[rows_idx[a:a + 4096]], x_t[toks[a:a + 4096]])
+    written = torch.zeros(recv_t.shape[0], dtype=torch.bool, device=dev())
+    written[rows_idx] = True
+    sent = SENTINEL - 65536 if SENTINEL > 32767 else SENTINEL
+    step = 1 << 16
+    for a in range(0, recv_t.shape[0], step):
+        blk = recv_t[a:a + step][~written[a:a + step]]
+        assert bool((blk == sent).all())
+
+
+def test_c5_replica_path_full(capi, orc):
+    """Replica workload at full size: reroute + layout + dispatch + combine;
+    combine equals the unreplicated path bit for bit."""
+    w = mi.config_c5()
+    _announce("c5 replica full size")
+    C_ = w.replicas
+    d_idx = to_dev(w.topk_idx)
+    load = torch.empty(w.E, dtype=torch.int32, device=dev())
+    status = torch.zeros(1, dtype=torch.int32, device=dev())
+    capi.moe_expert_load(w.T, w.K, w.E, d_idx, load, status)
+    rc = torch.full((w.E,), -7, dtype=torch.int32, device=dev())
+    rp = torch.full((w.E, 2), -7, dtype=torch.int32, device=dev())
+    p2l = torch.full((w.E + C_,), -7, dtype=torch.int32, device=dev())
+    capi.moe_plan_replicas(w.E, w.R, C_, load, rc, rp, p2l)
+    phys = torch.full((w.T, w.K), -7, dtype=torch.int64, device=dev())
+    capi.moe_reroute(w.T, w.K, w.E, d_idx, rc, rp, w.E + C_, phys, status)
+    torch.cuda.synchronize()
+    load_ref, _ = orc.expert_load(w.topk_idx, w.E)
+    assert np.array_equal(load.cpu().numpy(), load_ref)
+    plan = orc.plan_replicas(load_ref, w.R, C_)
+    assert np.array_equal(rc.cpu().numpy(), plan["replica_count"])
+    assert np.array_equal(rp.cpu().numpy(), plan["replica_phys"])
+    assert np.array_equal(p2l.cpu().numpy(), plan["phys_to_logical"])
+    phys_ref, st = orc.reroute(w.topk_idx, w.E, plan["replica_count"], plan["replica_phys"],
+                               plan["E_phys"])
+    assert np.array_equal(phys.cpu().numpy(), phys_ref) and int(status.item()) == 0 == st
+
+    Ep = plan["E_phys"]
+    got, lay, shape = run_layout(capi, w, idx=phys_ref, E=Ep)
+    ref = orc.layout(phys_ref, Ep, w.R, 1)
+    check_layout(got, ref, w)
+    rows = ref["rows"]
+    recv_t = torch.full((rows, w.H), SENTINEL, dtype=torch.int16, device=dev())
+    x_t = to_dev(w.x)
+    capi.moe_dispatch(shape, x_t, lay.slot, recv_t, rows, lay.status)
+    out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
+    o32 = torch.empty(w.T, w.H, dtype=torch.float32, device=dev())
+    wt = to_dev(w.topk_weights)
+    capi.moe_combine(shape, recv_t, rows, lay.slot, wt, out, o32, lay.status)
+    torch.cuda.synchronize()
+    _gpu_rows_check(recv_t, x_t, ref["slot"], w.T, w.K)
+    # sampled tokens against the oracle's own dispatch of the physical layout
+    rref, _ = orc.dispatch(w.x, ref["slot"], rows)
+    rng = np.random.default_rng(0)
+    toks = np.unique(np.concatenate([rng.choice(w.T, 512, replace=False), [0, w.T - 1]]))
+    check_combine(orc, np16(out), o32.cpu().numpy(), rref, ref["slot"], w.topk_weights,
+                  tokens=toks)
+    # the unreplicated path gives the same bits
+    sh2 = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
+    lay2 = capi.LayoutBuffers.empty(sh2, dev())
+    ws = torch.empty(capi.moe_layout_workspace_bytes(sh2), dtype=torch.uint8, device=dev())
+    capi.moe_layout(sh2, d_idx, lay2, ws)
+    rows2 = w.T * w.K
+    recv2 = torch.empty(rows2, w.H, dtype=torch.int16, device=dev())
+    capi.moe_dispatch(sh2, x_t, lay2.slot, recv2, rows2, lay2.status)
+    out2 = torch.empty_like(out)
+    o32b = torch.empty_like(o32)
+    capi.moe_combine(sh2, recv2, rows2, lay2.slot, wt, out2, o32b, lay2.status)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(o32.view(torch.int32), o32b.view(torch.int32))
+    assert int(lay.status.item()) == 0 and int(lay2.status.item()) == 0
+
+
+@pytest.mark.parametrize("M", mi.C3_SWEEP)
+def test_ll_sweep(capi, orc, M):
+    w = mi.config_c3(M)
+    s = 0 if M != 128 else 7
+    _announce(f"c3 LL M={M} src={s}")
+    got, lay, shape = run_layout(capi, w, ll=True, M=M, src=s)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, M, s)
+    check_layout(got, ref, w, ll=True)
+    rows = ref["rows"]
+    x_t = to_dev(w.x)
+    recv_t = torch.full((rows, w.H), SENTINEL, dtype=torch.int16, device=dev())
+    capi.moe_dispatch(shape, x_t, lay.slot, recv_t, rows, lay.status)
+    out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
+    o32 = torch.empty(w.T, w.H, dtype=torch.float32, device=dev())
+    capi.moe_combine(shape, recv_t, rows, lay.slot, to_dev(w.topk_weights), out, o32, lay.status)
+    torch.cuda.synchronize()
+    _gpu_rows_check(recv_t, x_t, ref["slot"], w.T, w.K)
+    # combine: the oracle reads its own padded rows; compact them to the used rows
+    v = ref["slot"] >= 0
+    used = np.unique(ref["slot"][v])
+    remap = np.full(rows, -1, np.int64)
+    remap[used] = np.arange(used.size)
+    slot_c = np.where(v, remap[np.maximum(ref["slot"], 0)], -1).astype(np.int32)
+    rref, _ = orc.dispatch(w.x, slot_c, used.size)
+    check_combine(orc, np16(out), o32.cpu().numpy(), rref, slot_c, w.topk_weights)
+    assert int(lay.status.item()) == 0
+    del recv_t
+    torch.cuda.empty_cache()
+
+
+def test_ll_overflow_and_small_M(capi, orc):
+    w = mi.random_case(40, 30, 64, 16, 4, 4, 1, dup_frac=0.8)
+    _announce("LL overflow by duplicates, M=30")
+    got, lay, shape = run_layout(capi, w, ll=True, M=30, src=2)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, 30, 2)
+    assert ref["status"] & 2
+    check_layout(got, ref, w, ll=True)
+
+
+def test_ll_multiblock(capi, orc):
+    w = mi.random_case(41, 2000, 64, 64, 8, 6, 1, M=2000, neg_frac=0.05)  # 12000 pairs
+    _announce("LL multi-block M=2000")
+    got, lay, shape = run_layout(capi, w, ll=True, M=2000, src=5)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, 2000, 5)
+    check_layout(got, ref, w, ll=True)
+
+
+def test_ll_multiblock_overflow(capi, orc):
+    w = mi.random_case(42, 1500, 16, 8, 2, 8, 1, M=1500, dup_frac=0.7)
+    _announce("LL multi-block overflow")
+    got, lay, shape = run_layout(capi, w, ll=True, M=1500, src=1)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, 1500, 1)
+    assert ref["status"] & 2
+    check_layout(got, ref, w, ll=True)
+
+
+def test_bad_slots_are_skipped(capi, orc):
+    w = mi.random_case(43, 64, 64, 16, 4, 4, 1)
+    _announce("bad slots")
+    shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
+    ref = orc.layout(w.topk_idx, w.E, w.R, 1)
+    slot = ref["slot"].copy()
+    slot[3, 1] = 10_000_000
+    slot[5, 0] = -5
+    rows = ref["rows"]
+    x_t = to_dev(w.x)
+    recv_t = torch.full((rows, w.H), SENTINEL, dtype=torch.int16, device=dev())
+    st = torch.zeros(1, dtype=torch.int32, device=dev())
+    capi.moe_dispatch(shape, x_t, to_dev(slot), recv_t, rows, st)
+    out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
+    st2 = torch.zeros(1, dtype=torch.int32, device=dev())
+    capi.moe_combine(shape, recv_t, rows, to_dev(slot), to_dev(w.topk_weights), out, None, st2)
+    torch.cuda.synchronize()
+    rref, rst = orc.dispatch(w.x, slot, rows, fill=SENTINEL)
+    assert np.array_equal(np16(recv_t), rref) and int(st.item()) == rst == 4
+    cref = orc.combine(rref, slot, w.topk_weights, "f32")
+    assert np.array_equal(np16(out), cref["out_bf16"]) and int(st2.item()) == 4
+
+
+def test_replica_small_and_ties(capi, orc):
+    for seed, (T, E, R, K, C_) in enumerate([(50, 16, 4, 3, 4), (64, 8, 8, 2, 8), (10, 64, 8, 8, 0),
+                                             (300, 256, 8, 8, 32), (5, 1024, 8, 4, 64)]):
+        w = mi.random_case(50 + seed, T, 16, E, R, K, 1, neg_frac=0.1)
+        _announce(f"replica plan T={T} E={E} R={R} C={C_}")
+        d_idx = to_dev(w.topk_idx)
+        load = torch.empty(E, dtype=torch.int32, device=dev())
+        capi.moe_expert_load(T, K, E, d_idx, load)
+        rc = torch.empty(E, dtype=torch.int32, device=dev())
+        rp = torch.empty(E, 2, dtype=torch.int32, device=dev())
+        p2l = torch.empty(E + C_, dtype=torch.int32, device=dev())
+        capi.moe_plan_replicas(E, R, C_, load, rc, rp, p2l)
+        phys = torch.empty(T, K, dtype=torch.int64, device=dev())
+        capi.moe_reroute(T, K, E, d_idx, rc, rp, E + C_, phys)
+        torch.cuda.synchronize()
+        lref, _ = orc.expert_load(w.topk_idx, E)
+        plan = orc.plan_replicas(lref, R, C_)
+        pref, _ = orc.reroute(w.topk_idx, E, plan["replica_count"], plan["replica_phys"],
+                              plan["E_phys"])
+        assert np.array_equal(load.cpu().numpy(), lref)
+        assert np.array_equal(rc.cpu().numpy(), plan["replica_count"])
+        assert np.array_equal(rp.cpu().numpy(), plan["replica_phys"])
+        assert np.array_equal(p2l.cpu().numpy(), plan["phys_to_logical"])
+        assert np.array_equal(phys.cpu().numpy(), pref)
+
+
+def test_expert_load_bad_ids(capi, orc):
+    w = mi.random_case(60, 5000, 8, 64, 8, 6, 1, bad_frac=0.02, neg_frac=0.1)
+    _announce("expert load with bad ids, 30000 pairs")
+    load = torch.empty(w.E, dtype=torch.int32, device=dev())
+    st = torch.zeros(1, dtype=torch.int32, device=dev())
+    capi.moe_expert_load(w.T, w.K, w.E, to_dev(w.topk_idx), load, st)
+    torch.cuda.synchronize()
+    lref, sref = orc.expert_load(w.topk_idx, w.E)
+    assert np.array_equal(load.cpu().numpy(), lref) and int(st.item()) == sref == 1
+
+
+def test_deterministic_runs(capi, orc):
+    """Two runs of the skewed workload give identical bytes (no order depends
+    on atomics)."""
+    w = mi.config_c4()
+    _announce("c4 determinism")
+    outs = []
+    for _ in range(2):
+        got, lay, shape = run_layout(capi, w)
+        recv, o16, o32, st = run_dispatch_combine(capi, w, shape, lay, got["rows"])
+        outs.append((got["slot"].copy(), recv.copy(), o16.copy(), o32.copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
