@@ -60,6 +60,8 @@ def _load():
         "moe_layout_workspace_bytes": (SZ, [P]),
         "moe_layout": (C.c_int, [P, P, P, P, SZ, P]),
         "moe_ll_layout": (C.c_int, [P, I32, I32, P, P, P, SZ, P]),
+        "moe_layout_dispatch": (C.c_int, [P, P, P, P, P, I64, P, SZ, P]),
+        "moe_ll_layout_dispatch": (C.c_int, [P, I32, I32, P, P, P, P, I64, P, SZ, P]),
         "moe_expert_load": (C.c_int, [I32, I32, I32, P, P, P, P]),
         "moe_dispatch": (C.c_int, [P, P, P, P, I64, P, P]),
         "moe_combine": (C.c_int, [P, P, I64, P, P, P, P, P, P]),
@@ -75,7 +77,8 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_recv_rows",
-            "moe_layout_workspace_bytes", "moe_layout", "moe_ll_layout", "moe_expert_load",
+            "moe_layout_workspace_bytes", "moe_layout", "moe_ll_layout", "moe_layout_dispatch",
+            "moe_ll_layout_dispatch", "moe_expert_load",
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute")
 
 
@@ -220,6 +223,33 @@ def moe_ll_layout(shape: moe_shape, M: int, src_rank: int, topk_idx: torch.Tenso
     wsp, wsn = _ws(ws, shape)
     return _check("moe_ll_layout", _lib.moe_ll_layout(C.byref(shape), int(M), int(src_rank), idx,
                                                       C.byref(st), wsp, wsn, _stream(stream)))
+
+
+def moe_layout_dispatch(shape: moe_shape, topk_idx: torch.Tensor, out: LayoutBuffers,
+                        x: torch.Tensor, recv_x: torch.Tensor, recv_rows: int,
+                        ws: Optional[torch.Tensor] = None, stream=None) -> int:
+    T, H, K = shape.T, shape.H, shape.K
+    idx = _dev(topk_idx, "topk_idx", (torch.int64,), T * K)
+    st = out._struct(shape, None)
+    wsp, wsn = _ws(ws, shape)
+    return _check("moe_layout_dispatch", _lib.moe_layout_dispatch(
+        C.byref(shape), idx, C.byref(st), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows), wsp, wsn,
+        _stream(stream)))
+
+
+def moe_ll_layout_dispatch(shape: moe_shape, M: int, src_rank: int, topk_idx: torch.Tensor,
+                           out: LayoutBuffers, x: torch.Tensor, recv_x: torch.Tensor,
+                           recv_rows: int, ws: Optional[torch.Tensor] = None,
+                           stream=None) -> int:
+    T, H, K = shape.T, shape.H, shape.K
+    idx = _dev(topk_idx, "topk_idx", (torch.int64,), T * K)
+    st = out._struct(shape, int(M))
+    wsp, wsn = _ws(ws, shape)
+    return _check("moe_ll_layout_dispatch", _lib.moe_ll_layout_dispatch(
+        C.byref(shape), int(M), int(src_rank), idx, C.byref(st),
+        _dev(x, "x", _BF16_LIKE, T * H), _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H),
+        int(recv_rows), wsp, wsn, _stream(stream)))
 
 
 def moe_expert_load(T: int, K: int, E: int, topk_idx: torch.Tensor, load: torch.Tensor,

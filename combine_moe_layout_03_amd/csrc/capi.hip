@@ -65,11 +65,12 @@ size_t workspace_bytes(const moe_shape *s) {
   return (size_t)((ints * 4 + 255) / 256 * 256);
 }
 
-int layout_common(const moe_shape *s, int mode, int32_t M, int32_t src, const int64_t *idx,
-                  const moe_layout_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+// Checks a layout call's arguments and fills the kernel parameters.
+int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const int64_t *idx,
+                  const moe_layout_t *out, void *ws, size_t ws_bytes, LayoutParams *p) {
   int rc = check_shape(s, false);
   if (rc) return rc;
-  if (!out || !out->count || !out->slot) return MOE_ERR_NULL;
+  if (!out || !out->count || (s->T > 0 && !out->slot)) return MOE_ERR_NULL;
   if (mode == kModeContiguous && !out->offset) return MOE_ERR_NULL;
   if (s->T > 0 && !idx) return MOE_ERR_NULL;
   if (mode == kModeLowLatency) {
@@ -78,41 +79,76 @@ int layout_common(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   }
   const size_t need = workspace_bytes(s);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+
+  std::memset(p, 0, sizeof(*p));
+  p->idx = idx;
+  p->T = s->T;
+  p->K = s->K;
+  p->E = s->E;
+  p->R = s->R;
+  p->L = s->E / s->R;
+  p->A = mode == kModeContiguous ? s->A : 1;
+  p->mode = mode;
+  p->M = M;
+  p->src = src;
+  p->id_bits = bits_for(s->E);
+  p->rank_bits = bits_for(s->R);
+  p->count = out->count;
+  p->offset = out->offset;
+  p->rank_token_count = out->rank_token_count;
+  p->in_rank = out->is_token_in_rank;
+  p->slot = out->slot;
+  p->row_src = out->row_src;
+  p->status = out->status;
+  if (one_block(s)) {
+    p->tokens_per_block = s->T > 0 ? s->T : 1;
+    p->nblocks = 1;
+  } else {
+    p->tokens_per_block = tokens_per_block(s->K);
+    p->nblocks = (s->T + p->tokens_per_block - 1) / p->tokens_per_block;
+    p->ws_hist = static_cast<int32_t *>(ws);
+    p->ws_rcnt = p->ws_hist + (int64_t)p->nblocks * s->E;
+  }
+  return MOE_OK;
+}
+
+hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
+  if (count_layout_fits(p, 0, false)) return launch_count_layout(p, nullptr, nullptr, 0, 0, stream);
+  return p.nblocks == 1 && p.ws_hist == nullptr ? launch_layout_one_block(p, stream)
+                                                 : launch_layout_multi_block(p, stream);
+}
+
+int layout_common(const moe_shape *s, int mode, int32_t M, int32_t src, const int64_t *idx,
+                  const moe_layout_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  LayoutParams p;
+  int rc = layout_params(s, mode, M, src, idx, out, ws, ws_bytes, &p);
+  if (rc) return rc;
   rc = check_device();
   if (rc) return rc;
+  return launch_layout(p, stream) == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
 
+int layout_dispatch_common(const moe_shape *s, int mode, int32_t M, int32_t src,
+                           const int64_t *idx, const moe_layout_t *out, const uint16_t *x,
+                           uint16_t *recv, int64_t rows, void *ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int rc = check_shape(s, true);
+  if (rc) return rc;
   LayoutParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.idx = idx;
-  p.T = s->T;
-  p.K = s->K;
-  p.E = s->E;
-  p.R = s->R;
-  p.L = s->E / s->R;
-  p.A = mode == kModeContiguous ? s->A : 1;
-  p.mode = mode;
-  p.M = M;
-  p.src = src;
-  p.id_bits = bits_for(s->E);
-  p.rank_bits = bits_for(s->R);
-  p.count = out->count;
-  p.offset = out->offset;
-  p.rank_token_count = out->rank_token_count;
-  p.in_rank = out->is_token_in_rank;
-  p.slot = out->slot;
-  p.row_src = out->row_src;
-  p.status = out->status;
+  rc = layout_params(s, mode, M, src, idx, out, ws, ws_bytes, &p);
+  if (rc) return rc;
+  if (rows < 0) return MOE_ERR_CAPACITY;
+  if (s->T > 0 && (!x || (!recv && rows > 0))) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
   hipError_t err;
-  if (one_block(s)) {
-    p.tokens_per_block = s->T > 0 ? s->T : 1;
-    p.nblocks = 1;
-    err = launch_layout_one_block(p, stream);
+  if (count_layout_fits(p, s->H, true)) {
+    err = launch_count_layout(p, x, recv, rows, s->H, stream);
   } else {
-    p.tokens_per_block = tokens_per_block(s->K);
-    p.nblocks = (s->T + p.tokens_per_block - 1) / p.tokens_per_block;
-    p.ws_hist = static_cast<int32_t *>(ws);
-    p.ws_rcnt = p.ws_hist + (int64_t)p.nblocks * s->E;
-    err = launch_layout_multi_block(p, stream);
+    err = launch_layout(p, stream);
+    if (err == hipSuccess && s->T > 0)
+      err = launch_dispatch(x, p.slot, recv, s->T, s->K, s->H, rows, p.status, stream);
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
@@ -161,6 +197,22 @@ MOE_API int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank,
                           const int64_t *topk_idx, const moe_layout_t *out, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
   return layout_common(shape, kModeLowLatency, M, src_rank, topk_idx, out, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx,
+                                const moe_layout_t *out, const uint16_t *x, uint16_t *recv_x,
+                                int64_t recv_rows, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return layout_dispatch_common(shape, kModeContiguous, 0, 0, topk_idx, out, x, recv_x,
+                                recv_rows, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_ll_layout_dispatch(const moe_shape *shape, int32_t M, int32_t src_rank,
+                                   const int64_t *topk_idx, const moe_layout_t *out,
+                                   const uint16_t *x, uint16_t *recv_x, int64_t recv_rows,
+                                   void *ws, size_t ws_bytes, hipStream_t stream) {
+  return layout_dispatch_common(shape, kModeLowLatency, M, src_rank, topk_idx, out, x, recv_x,
+                                recv_rows, ws, ws_bytes, stream);
 }
 
 MOE_API int moe_expert_load(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,

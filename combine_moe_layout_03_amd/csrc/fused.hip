@@ -1,0 +1,391 @@
+// Layout by counting, for small batches, with or without the dispatch copy in
+// the same launch. Same results, bit for bit, as the layout kernels (and the
+// scatter) for alignment 1 and for the low-latency stripes, as the NeMo
+// AutoModel page "nemo_automodel.components.moe.uccl_ep.buffer" describes them
+// for Buffer.get_dispatch_layout, Buffer.dispatch (topk_idx given, no handle)
+// and Buffer.low_latency_dispatch.
+//
+// With alignment 1 the slot of pair (t, k) on expert e is
+//   #(valid pairs with id < e) + #(pairs before token t with id e)
+//   + #(earlier k of token t with id e),
+// and in the low-latency layout it is (e*R + src)*M plus the last two terms.
+// So a workgroup that serves token t needs just two counts per selected expert
+// over the whole routing -- no histogram, no scan, no cross-workgroup step.
+// Each wave reads a few ids per lane (the routing is a few KiB and sits in
+// L2 after the first touch) and turns them into counts with ballot +
+// popcount, accumulated in scalar registers; the waves' partial counts meet
+// in LDS once. The totals the handle also needs (count and offset per expert,
+// tokens per rank, empty low-latency stripe rows) are computed the same way by
+// a few extra "duty" workgroups that copy nothing, so the copying workgroups
+// only derive their own K slots. The id loads are unrolled over a compile-time
+// number of rounds and every count is one compare + ballot + popcount: at this
+// size the kernel is bound by each wave's serial instruction latency, not by
+// memory.
+//
+// With the copy, a workgroup owns up to 8 chunks (1 KiB each) of one token row.
+// It requests the routing first and the row second, derives its K slots while
+// the (cold) row is still in flight, then stores the row K times.
+#include "wave.hpp"
+
+namespace moe {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCountMaxWaves = 8;
+constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * threads
+constexpr int kMaxDuties = 4;       // experts (and ranks) whose totals one workgroup writes
+constexpr int kLayoutOnlyThreads = 256;
+constexpr int kNoId = -2;           // sentinel: matches no expert
+constexpr int kAboveAll = 0x7fffffff;  // sentinel: not below any expert
+
+struct CountParams {
+  LayoutParams lp;
+  const u32x4 *x;  // null: layout only
+  u32x4 *recv;
+  int64_t rows;
+  int32_t nvec, nchunk, chunks_per_wg, wg_per_token;
+  int32_t token_wgs;  // workgroups [0, token_wgs) serve tokens, the rest do duties
+  int32_t duty_wgs;
+};
+
+// v with lane j replaced by the (uniform) value x
+__device__ __forceinline__ int set_lane(int v, int j, int x) { return lane_id() == j ? x : v; }
+
+__device__ __forceinline__ int valid_or_neg(int64_t v, int E, int &st) {
+  const bool ok = v >= 0 && v < E;
+  if (!ok && v != -1) st |= kStBadExpert;
+  return ok ? (int)v : -1;
+}
+
+// The routing as seen by one lane: ids of pairs r*nthreads + tid for
+// r < kRounds, in the three forms the counts compare against (one compare
+// per ballot): any id (sentinel kNoId), ids of pairs before pair `before`
+// (kNoId otherwise), and valid ids for "below" tests (kAboveAll otherwise).
+template <int kRounds>
+struct LaneIds {
+  int64_t raw[kRounds];
+  int any[kRounds], early[kRounds], below[kRounds];
+
+  // request the ids; nothing waits for them here
+  __device__ __forceinline__ void issue(const int64_t *idx, int P, int nthreads) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) raw[r] = idx[min(r * nthreads + (int)threadIdx.x, P - 1)];
+    // every id load stays ahead of whatever the caller issues next (a row load)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // wait for them and build the three forms; pairs [tok, tok + K) are also
+  // written to s_tok (each pair is held by exactly one lane)
+  __device__ __forceinline__ void settle(int P, int E, int nthreads, int before, int tok,
+                                         int K, int32_t *s_tok, int &st) {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * nthreads + (int)threadIdx.x;
+      const int e = i < P ? valid_or_neg(raw[r], E, st) : -1;
+      any[r] = e >= 0 ? e : kNoId;
+      early[r] = (e >= 0 && i < before) ? e : kNoId;
+      below[r] = e >= 0 ? e : kAboveAll;
+      if (s_tok && i >= tok && i < tok + K && i < P) s_tok[i - tok] = e;
+    }
+  }
+  __device__ __forceinline__ void load(const int64_t *idx, int P, int E, int nthreads, int before,
+                                       int &st) {
+    issue(idx, P, nthreads);
+    settle(P, E, nthreads, before, 0, 0, nullptr, st);
+  }
+  // wave-wide counts, as scalars
+  __device__ __forceinline__ int count_equal(int e) const {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(any[r] == e));
+    return n;
+  }
+  __device__ __forceinline__ int count_early_equal(int e) const {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(early[r] == e));
+    return n;
+  }
+  __device__ __forceinline__ int count_below(int e) const {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(below[r] < e));
+    return n;
+  }
+};
+
+// Totals the handle needs besides the slots, one workgroup per group of
+// experts/ranks: count (and first row) of experts d, d+D, ...; distinct tokens
+// of ranks d, d+D, ...; empty low-latency stripe rows.
+template <int kRounds>
+__device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
+  __shared__ int32_t s_c[kCountMaxWaves][kMaxDuties];
+  __shared__ int32_t s_l[kCountMaxWaves][kMaxDuties];
+  __shared__ int32_t s_r[kCountMaxWaves][kMaxDuties];
+  __shared__ uint8_t s_mark[kMaxPairsFused];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+  const int E = p.E, R = p.R, K = p.K, T = p.T, L = p.L, P = T * K;
+  const bool ll = p.mode == kModeLowLatency;
+  LaneIds<kRounds> ids;
+  if (P > 0) {
+    ids.load(p.idx, P, E, nthreads, 0, st);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      ids.any[r] = ids.early[r] = kNoId;
+      ids.below[r] = kAboveAll;
+    }
+  }
+  const int ndx = d < E ? (E - 1 - d) / D + 1 : 0;
+  const int ndr = d < R ? (R - 1 - d) / D + 1 : 0;
+  int cv = 0, lv = 0;  // lane j holds duty j's counts
+  for (int j = 0; j < ndx; ++j) {
+    const int ed = d + j * D;
+    cv = set_lane(cv, j, ids.count_equal(ed));
+    if (!ll) lv = set_lane(lv, j, ids.count_below(ed));
+  }
+  if (lane < ndx) {
+    s_c[wave][lane] = cv;
+    s_l[wave][lane] = lv;
+  }
+  for (int j = 0; j < ndr; ++j) {  // the same trip count for the whole workgroup
+    const int rd = d + j * D;
+    for (int t = tid; t < T; t += nthreads) s_mark[t] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * nthreads + tid;
+      if (ids.any[r] >= 0 && ids.any[r] / L == rd) s_mark[i / K] = 1;
+    }
+    lds_barrier();
+    int n = 0;
+    for (int t0 = 0; t0 < T; t0 += nthreads) {
+      const int t = t0 + tid;
+      n += __popcll(__ballot(t < T && s_mark[t] != 0));
+    }
+    if (lane == 0) s_r[wave][j] = n;
+    lds_barrier();
+  }
+  lds_barrier();
+  if (tid < ndx) {
+    const int ed = d + tid * D;
+    int c = 0, lt = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      c += s_c[w][tid];
+      lt += s_l[w][tid];
+    }
+    if (!ll) {
+      p.count[ed] = c;
+      p.offset[ed] = lt;
+      if (ed == E - 1) p.offset[E] = lt + c;
+    } else {
+      p.count[ed] = min(c, p.M);
+      if (c > p.M) st |= kStOverflow;
+      if (p.offset) {
+        p.offset[ed] = (ed * R + p.src) * p.M;
+        if (ed == E - 1) p.offset[E] = E * R * p.M;
+      }
+    }
+  }
+  if (tid < ndr && p.rank_token_count) {
+    int n = 0;
+    for (int w = 0; w < nwaves; ++w) n += s_r[w][tid];
+    p.rank_token_count[d + tid * D] = n;
+  }
+  if (ll && p.row_src) {
+    // stripe rows past the received count hold no pair
+    for (int j = 0; j < ndx; ++j) {
+      const int ed = d + j * D;
+      int c = 0;
+      for (int w = 0; w < nwaves; ++w) c += s_c[w][j];
+      for (int jj = min(c, p.M) + tid; jj < p.M; jj += nthreads)
+        p.row_src[(int64_t)ed * p.M + jj] = -1;
+    }
+  }
+}
+
+template <bool kCopy, int kRounds>
+__global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
+  __shared__ int32_t s_pre[kCountMaxWaves][64];   // per wave, per k: same id before token
+  __shared__ int32_t s_lt[kCountMaxWaves][64];    // per wave, per k: valid ids below
+  __shared__ int32_t s_tok[64];                   // this token's ids (-1 = none)
+  __shared__ int32_t s_slot[64];
+  __shared__ int32_t s_status;
+
+  const LayoutParams &p = f.lp;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int b = blockIdx.x;
+  int st = 0;
+  if (tid == 0) s_status = 0;
+
+  if (b >= f.token_wgs) {  // uniform per workgroup
+    duty_workgroup<kRounds>(p, b - f.token_wgs, f.duty_wgs, st);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+    const int E = p.E, R = p.R, K = p.K, T = p.T, L = p.L;
+    const int P = T * K;
+    const bool ll = p.mode == kModeLowLatency;
+    const int t = kCopy ? b / f.wg_per_token : b;  // < T
+    const bool token_lead = !kCopy || b % f.wg_per_token == 0;
+    const int pbeg = t * K;
+
+    // 1. the routing first ...
+    LaneIds<kRounds> ids;
+    ids.issue(p.idx, P, nthreads);
+    // 2. ... then the row chunk this wave copies; it stays in flight while
+    //    the slots are worked out. The load is unconditional (address clamped
+    //    into the row): under a branch it would force an early wait.
+    u32x4 val = {0u, 0u, 0u, 0u};
+    int v = 0;
+    bool lane_ok = false;
+    if (kCopy) {
+      const int chunk = (b % f.wg_per_token) * f.chunks_per_wg + wave;
+      v = chunk * 64 + lane;
+      lane_ok = chunk < f.nchunk && v < f.nvec;
+      val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
+    }
+    ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
+    lds_barrier();
+
+    // 3. per selected expert of this token: ids equal to it before the token,
+    //    and valid ids below it. The token's ids sit in lanes 0..K-1 of tokv;
+    //    lane k of prev/ltv collects the counts for its k.
+    const int tokv = lane < K ? s_tok[lane] : -1;
+    int prev = 0, ltv = 0;
+    for (int k = 0; k < K; ++k) {
+      const int ek = __builtin_amdgcn_readlane(tokv, k);
+      if (ek >= 0) {
+        prev = set_lane(prev, k, ids.count_early_equal(ek));
+        if (!ll) ltv = set_lane(ltv, k, ids.count_below(ek));
+      }
+    }
+    if (lane < K) {
+      s_pre[wave][lane] = prev;
+      s_lt[wave][lane] = ltv;
+    }
+    lds_barrier();
+
+    // 4. slots of this token's pairs (wave 0, lane k)
+    if (wave == 0) {
+      const int e = tokv;
+      int dup = 0;
+      for (int k = 0; k < K; ++k) dup += (k < lane && __builtin_amdgcn_readlane(tokv, k) == e);
+      if (lane < K) {
+        int out = -1;
+        if (e >= 0) {
+          int pre = dup, lt = 0;
+          for (int w = 0; w < nwaves; ++w) {
+            pre += s_pre[w][lane];
+            lt += s_lt[w][lane];
+          }
+          if (!ll) {
+            out = lt + pre;
+            if (token_lead && p.row_src) p.row_src[out] = pbeg + lane;
+          } else if (pre < p.M) {
+            out = (e * R + p.src) * p.M + pre;
+            if (token_lead && p.row_src) p.row_src[(int64_t)e * p.M + pre] = pbeg + lane;
+          } else {
+            st |= kStOverflow;
+          }
+        }
+        s_slot[lane] = out;
+        if (token_lead) p.slot[pbeg + lane] = out;
+      }
+      // ranks this token reaches
+      if (token_lead && p.in_rank) {
+        for (int r0 = 0; r0 < R; r0 += 64) {
+          const int r = r0 + lane;
+          bool hit = false;
+          for (int k = 0; k < K; ++k) {
+            const int ek = __builtin_amdgcn_readlane(tokv, k);
+            hit |= ek >= 0 && ek / L == r;
+          }
+          if (r < R) p.in_rank[(int64_t)t * R + r] = hit ? 1 : 0;
+        }
+      }
+    }
+
+    // 5. the row, K times
+    if (kCopy) {
+      lds_barrier();
+      asm volatile("" : "+v"(val));
+      for (int k = 0; k < K; ++k) {
+        const int s = __builtin_amdgcn_readfirstlane(s_slot[k]);
+        if (s >= 0 && s < f.rows) {
+          if (lane_ok) __builtin_nontemporal_store(val, f.recv + (int64_t)s * f.nvec + v);
+        } else if (s != -1) {
+          st |= kStBadSlot;  // receive buffer smaller than the layout needs
+        }
+      }
+    }
+    // every workgroup reads every id; the duty workgroups report bad ones
+    st &= ~kStBadExpert;
+  }
+  if (st) atomicOr(&s_status, st);
+  lds_barrier();
+  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
+}
+
+template <bool kCopy>
+hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const CountParams &f) {
+  if (rounds <= 1)
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1>), grid, block, 0, s, f);
+  else if (rounds <= 2)
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2>), grid, block, 0, s, f);
+  else if (rounds <= 4)
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4>), grid, block, 0, s, f);
+  else
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8>), grid, block, 0, s, f);
+  return hipGetLastError();
+}
+
+int copy_threads(int32_t H) {
+  const int nchunk = (H / 8 + 63) / 64;
+  const int groups = (nchunk + kCountMaxWaves - 1) / kCountMaxWaves;
+  return 64 * ((nchunk + groups - 1) / groups);
+}
+
+}  // namespace
+
+bool count_layout_fits(const LayoutParams &lp, int32_t H, bool copy) {
+  if (lp.mode == kModeContiguous && lp.A != 1) return false;
+  const int64_t P = (int64_t)lp.T * lp.K;
+  if (P > kMaxPairsFused) return false;
+  const int threads = (copy && lp.T > 0) ? copy_threads(H) : kLayoutOnlyThreads;
+  // token and duty workgroups share the block size; the batch must fit 8 rounds
+  return P <= (int64_t)kCountMaxRounds * threads;
+}
+
+hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16_t *recv,
+                               int64_t rows, int32_t H, hipStream_t s) {
+  CountParams f;
+  f.lp = lp;
+  f.x = reinterpret_cast<const u32x4 *>(x);
+  f.recv = reinterpret_cast<u32x4 *>(recv);
+  f.rows = rows;
+  const int need = (lp.E > lp.R ? lp.E : lp.R);
+  f.duty_wgs = (need + kMaxDuties - 1) / kMaxDuties;
+  const int P = lp.T * lp.K;
+  if (x && lp.T > 0) {
+    f.nvec = H / 8;
+    f.nchunk = (f.nvec + 63) / 64;
+    const int threads = copy_threads(H);
+    f.chunks_per_wg = threads / 64;
+    f.wg_per_token = (f.nchunk + f.chunks_per_wg - 1) / f.chunks_per_wg;
+    f.token_wgs = lp.T * f.wg_per_token;
+    // duty workgroups share the block size; their rounds follow from it
+    const int rounds = (P + threads - 1) / threads;
+    return launch_rounds<true>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
+                               dim3(threads), s, f);
+  }
+  f.nvec = f.nchunk = f.chunks_per_wg = f.wg_per_token = 0;
+  f.token_wgs = lp.T;
+  const int rounds = (P + kLayoutOnlyThreads - 1) / kLayoutOnlyThreads;
+  return launch_rounds<false>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
+                              dim3(kLayoutOnlyThreads), s, f);
+}
+
+}  // namespace moe

@@ -16,6 +16,9 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxPairsOneBlock = 8192;
 // Above that, each workgroup of the first layout pass takes about this many pairs.
 constexpr int kPairsPerBlock = 1024;
+// Layout and dispatch share one launch when the batch has at most this many
+// pairs (every dispatch workgroup then re-derives the layout from L2).
+constexpr int kMaxPairsFused = 2048;
 
 enum LayoutMode : int32_t {
   kModeContiguous = 0,  // aligned per-expert partitions of one receive buffer
@@ -53,6 +56,12 @@ hipError_t launch_layout_one_block(const LayoutParams &p, hipStream_t s);
 hipError_t launch_layout_multi_block(const LayoutParams &p, hipStream_t s);
 hipError_t launch_expert_load(const int64_t *idx, int32_t T, int32_t K, int32_t E,
                               int32_t id_bits, int32_t *load, int32_t *status, hipStream_t s);
+
+// Layout by counting (alignment 1 or low latency, at most kMaxPairsFused
+// pairs), optionally with the dispatch copy in the same launch (x != null).
+bool count_layout_fits(const LayoutParams &p, int32_t H, bool copy);
+hipError_t launch_count_layout(const LayoutParams &p, const uint16_t *x, uint16_t *recv,
+                               int64_t rows, int32_t H, hipStream_t s);
 
 hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                            int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s);

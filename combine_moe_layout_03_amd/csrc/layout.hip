@@ -17,58 +17,10 @@
 // pairs is done by one workgroup; larger batches take three launches (per-block
 // counts and local ranks, one-workgroup scan over blocks, per-pair fix-up), with
 // no inter-workgroup waiting.
-#include "kernels.hpp"
+#include "wave.hpp"
 
 namespace moe {
 namespace {
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
-// Lanes of this wave holding the same key (only lanes with valid = true take
-// part). Every lane of the wave must call this (the ballots are wave-wide).
-__device__ __forceinline__ uint64_t match_peers(uint32_t key, bool valid, int bits) {
-  uint64_t m = __ballot(valid);
-  for (int b = 0; b < bits; ++b) {
-    const bool one = (key >> b) & 1u;
-    const uint64_t ones = __ballot(one);
-    m &= one ? ones : ~ones;
-  }
-  return valid ? m : 0ull;
-}
-
-__device__ __forceinline__ bool is_leader(uint64_t peers) {
-  return peers != 0ull && (__ffsll((unsigned long long)peers) - 1) == lane_id();
-}
-
-__device__ __forceinline__ int below_me(uint64_t peers) {
-  const uint64_t lt = (1ull << lane_id()) - 1ull;
-  return __popcll(peers & lt);
-}
-
-// Exclusive scan of one int per thread over the 1024 threads of the block.
-__device__ int block_exclusive_scan(int v, int *s_wave, int *total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kLayoutWaves; ++w) {
-    const int s = s_wave[w];
-    before += (w < wave) ? s : 0;
-    all += s;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
-}
-
-__device__ __forceinline__ int round_up(int c, int a) { return (c + a - 1) / a * a; }
 
 // One workgroup's share of the layout: tokens [t0, t1).
 // kOneBlock: the workgroup holds the whole batch and writes final slots.
@@ -138,7 +90,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     const int c = (e < E) ? s_cnt[e] : 0;
     const int padded = (p.mode == kModeContiguous) ? round_up(c, p.A) : 0;
     int total = 0;
-    const int excl = block_exclusive_scan(padded, s_wave, &total);
+    const int excl = block_exclusive_scan(padded, s_wave, kLayoutWaves, &total);
     if (e < E) {
       if (p.mode == kModeContiguous) {
         p.count[e] = c;
@@ -255,7 +207,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutParam
   }
   const int padded = (p.mode == kModeContiguous) ? round_up(c, p.A) : 0;
   int total = 0;
-  const int excl = block_exclusive_scan(padded, s_wave, &total);
+  const int excl = block_exclusive_scan(padded, s_wave, kLayoutWaves, &total);
   int st = 0;
   if (e < E) {
     int base;

@@ -10,8 +10,8 @@
 //
 // Both are HBM-bound streams with no data reuse, so the design is about
 // bytes in flight: a thread owns one 16-byte vector (8 bf16) of one token row,
-// a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors -- about
-// 115k threads at 128 x 7168, enough to keep every CU busy. Dispatch reads its
+// a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors -- 1792
+// waves at 128 x 7168, seven per CU. Dispatch reads its
 // vector once and issues K 16-byte stores (non-temporal: the receive rows are
 // not re-read by this kernel). Combine issues all K 16-byte loads of a vector
 // before it sums, so K requests per lane are in flight at once, then adds in
@@ -35,30 +35,57 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// A wave owns 64 consecutive 16-byte vectors of one token row, so the token
+// index is wave-uniform: its K slots (and weights) arrive as scalar loads before
+// any vector memory operation, and the row's K stores or loads are issued back
+// to back without waiting on each other. Lanes past the row end (H/8 not a
+// multiple of 64) idle.
+__device__ __forceinline__ int wave_token_chunk(int nchunk, int &t) {
+  const int wid = __builtin_amdgcn_readfirstlane(
+      (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
+  t = wid / nchunk;
+  return (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
+}
+
 template <int KT>
 __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__ x,
                                                        const int32_t *__restrict__ slot,
                                                        u32x4 *__restrict__ recv, int32_t T,
-                                                       int32_t Kr, int32_t nvec, int64_t rows,
-                                                       int32_t *status) {
+                                                       int32_t Kr, int32_t nvec, int32_t nchunk,
+                                                       int64_t rows, int32_t *status) {
   const int K = KT ? KT : Kr;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * nvec) return;
-  const int t = i / nvec;
-  const int v = i - t * nvec;
-  const u32x4 val = __builtin_nontemporal_load(x + i);
+  int t;
+  const int v = wave_token_chunk(nchunk, t);
+  if (t >= T) return;
+  const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
-  int st = 0;
+  constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
+  u32x4 val = {0u, 0u, 0u, 0u};
+  if (lane_ok) val = __builtin_nontemporal_load(x + (int64_t)t * nvec + v);
+  // the first group of slots is requested while the row load is in flight
+  int32_t s[G];
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int32_t s = srow[k];
-    if (s >= 0 && s < rows) {
-      __builtin_nontemporal_store(val, recv + (int64_t)s * nvec + v);
-    } else if (s != -1) {
-      st |= kStBadSlot;
+  for (int g = 0; g < G; ++g) s[g] = (g < K) ? srow[g] : -1;
+  // Settle the row load once here: without this the compiler re-waits on it
+  // before every (conditional) store, and on gfx950 such a wait also drains
+  // the stores already issued, serialising the K copies.
+  asm volatile("" : "+v"(val));
+  int st = 0;
+  for (int k0 = 0; k0 < K; k0 += G) {
+    if (k0 > 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = (k0 + g < K) ? srow[k0 + g] : -1;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (s[g] >= 0 && s[g] < rows) {
+        if (lane_ok) __builtin_nontemporal_store(val, recv + (int64_t)s[g] * nvec + v);
+      } else if (s[g] != -1) {
+        st |= kStBadSlot;
+      }
     }
   }
-  if (st && status) atomicOr(status, st);
+  if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
 template <int KT, bool kWeights, bool kF32Out>
@@ -67,38 +94,38 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
                                                       const float *__restrict__ w,
                                                       u32x4 *__restrict__ out,
                                                       f32x4 *__restrict__ out_f32, int32_t T,
-                                                      int32_t Kr, int32_t nvec,
+                                                      int32_t Kr, int32_t nvec, int32_t nchunk,
                                                       int32_t *status) {
 #pragma clang fp contract(off)
   const int K = KT ? KT : Kr;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * nvec) return;
-  const int t = i / nvec;
-  const int v = i - t * nvec;
+  int t;
+  const int v = wave_token_chunk(nchunk, t);
+  if (t >= T) return;
+  const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
   const float *wrow = kWeights ? w + (int64_t)t * K : nullptr;
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   int st = 0;
-  // Groups of up to 8 pairs: issue the group's loads, then sum in k order.
   constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
   for (int k0 = 0; k0 < K; k0 += G) {
-    u32x4 val[G];
-    bool ok[G];
+    int32_t s[G];
     float wk[G];
+    bool ok[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int k = k0 + g;
-      ok[g] = false;
-      wk[g] = 1.0f;
-      if (k < K) {
-        const int32_t s = srow[k];
-        ok[g] = s >= 0 && s < rows;
-        if (!ok[g] && s != -1) st |= kStBadSlot;
-        if (ok[g]) val[g] = __builtin_nontemporal_load(y + (int64_t)s * nvec + v);
-        if (kWeights) wk[g] = wrow[k];
-      }
+      const bool in = k0 + g < K;
+      s[g] = in ? srow[k0 + g] : -1;
+      wk[g] = (kWeights && in) ? wrow[k0 + g] : 1.0f;
+    }
+    u32x4 val[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      ok[g] = s[g] >= 0 && s[g] < rows;
+      if (!ok[g] && s[g] != -1) st |= kStBadSlot;
+      val[g] = u32x4{0u, 0u, 0u, 0u};
+      if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nvec + v);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -115,27 +142,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
       acc[7] = acc[7] + a * bf16_hi(q.w);
     }
   }
-  u32x4 o;
-  o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
-  o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
-  o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
-  o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
-  out[i] = o;
-  if (kF32Out) {
-    out_f32[2 * (int64_t)i] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-    out_f32[2 * (int64_t)i + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  if (lane_ok) {
+    const int64_t i = (int64_t)t * nvec + v;
+    u32x4 o;
+    o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
+    o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
+    o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
+    o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+    out[i] = o;
+    if (kF32Out) {
+      out_f32[2 * i] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      out_f32[2 * i + 1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
   }
-  if (st && status) atomicOr(status, st);
+  if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
 template <int KT>
 hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                       int32_t K, int32_t nvec, int64_t rows, int32_t *status, hipStream_t s) {
-  const int64_t n = (int64_t)T * nvec;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const int32_t nchunk = (nvec + 63) / 64;
+  const int64_t waves = (int64_t)T * nchunk;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
   hipLaunchKernelGGL(dispatch_kernel<KT>, dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(x), slot, reinterpret_cast<u32x4 *>(recv),
-                     T, K, nvec, rows, status);
+                     T, K, nvec, nchunk, rows, status);
   return hipGetLastError();
 }
 
@@ -143,12 +174,13 @@ template <int KT, bool kW, bool kF>
 hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                       uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
                       int32_t *status, hipStream_t s) {
-  const int64_t n = (int64_t)T * nvec;
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const int32_t nchunk = (nvec + 63) / 64;
+  const int64_t waves = (int64_t)T * nchunk;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
   hipLaunchKernelGGL((combine_kernel<KT, kW, kF>), dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(y), rows, slot, w,
                      reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
-                     nvec, status);
+                     nvec, nchunk, status);
   return hipGetLastError();
 }
 
@@ -168,6 +200,7 @@ hipError_t combine_k(const uint16_t *y, int64_t rows, const int32_t *slot, const
 
 hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                            int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s) {
+  if (T <= 0) return hipSuccess;  // nothing to launch
   const int32_t nvec = H / 8;
   switch (K) {
     case 1: return dispatch_k<1>(x, slot, recv, T, K, nvec, rows, status, s);
@@ -182,6 +215,7 @@ hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *rec
 hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                           uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
                           int32_t *status, hipStream_t s) {
+  if (T <= 0) return hipSuccess;  // nothing to launch
   const int32_t nvec = H / 8;
   switch (K) {
     case 1: return combine_k<1>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);

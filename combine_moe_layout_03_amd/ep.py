@@ -67,6 +67,23 @@ def dispatch(x: torch.Tensor, handle: Handle, recv_x: Optional[torch.Tensor] = N
     return recv_x
 
 
+def dispatch_with_layout(x: torch.Tensor, topk_idx: torch.Tensor, num_experts: int,
+                         num_ranks: int, expert_alignment: int = 1,
+                         recv_x: Optional[torch.Tensor] = None):
+    """Layout and dispatch in one call (Buffer.dispatch given topk_idx and no
+    handle). Returns (recv_x, handle); the handle carries the layout arrays."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    shape = capi.make_shape(T, H, num_experts, num_ranks, K, expert_alignment)
+    lay = capi.LayoutBuffers.empty(shape, x.device)
+    rows = capi.moe_recv_rows_worst(shape)
+    if recv_x is None:
+        recv_x = torch.empty(max(rows, 1), H, dtype=x.dtype, device=x.device)
+    capi.moe_layout_dispatch(shape, topk_idx.contiguous(), lay, x.contiguous(), recv_x, rows,
+                             _workspace(shape, x.device))
+    return recv_x, Handle(shape, lay, rows)
+
+
 def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, out_f32: Optional[torch.Tensor] = None):
     """Weighted reduce of the expert outputs back to [T, H] bf16 (weights None:
@@ -95,12 +112,11 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
     E, R = num_experts, num_ranks
     shape = capi.make_shape(T, H, E, R, K, 1)
     lay = capi.LayoutBuffers.empty(shape, x.device, ll_M=M)
-    capi.moe_ll_layout(shape, M, src_rank, topk_idx.contiguous(), lay,
-                       _workspace(shape, x.device))
     rows = capi.moe_ll_recv_rows(E, R, M)
     if recv_x is None:
         recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
-    capi.moe_dispatch(shape, x.contiguous(), lay.slot, recv_x, rows, lay.status)
+    capi.moe_ll_layout_dispatch(shape, M, src_rank, topk_idx.contiguous(), lay, x.contiguous(),
+                                recv_x, rows, _workspace(shape, x.device))
     h = Handle(shape, lay, rows, ll_M=M, src_rank=src_rank)
     return recv_x.view(R, E // R, R * M, H), lay.count, h
 

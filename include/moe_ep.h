@@ -141,6 +141,25 @@ int moe_layout(const moe_shape *shape, const int64_t *topk_idx, const moe_layout
 int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank, const int64_t *topk_idx,
                   const moe_layout_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Layout and dispatch in one call (Buffer.dispatch given topk_idx and no handle):
+ * the same results as moe_layout followed by moe_dispatch -- every array of out
+ * and every row of recv_x bit for bit -- and the same argument rules as those
+ * two calls (shape->H is used). Batches of at most 2048 pairs run as a single
+ * kernel in which each workgroup re-derives the layout from the routing while
+ * its token rows load; larger batches launch the layout kernels, then the
+ * scatter. A slot at or past recv_rows sets MOE_STATUS_BAD_SLOT and is not
+ * written. */
+int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx, const moe_layout_t *out,
+                        const uint16_t *x, uint16_t *recv_x, int64_t recv_rows, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* Low-latency layout and dispatch in one call: the same results as moe_ll_layout
+ * followed by moe_dispatch (recv_rows is normally moe_ll_recv_rows(E, R, M)). */
+int moe_ll_layout_dispatch(const moe_shape *shape, int32_t M, int32_t src_rank,
+                           const int64_t *topk_idx, const moe_layout_t *out, const uint16_t *x,
+                           uint16_t *recv_x, int64_t recv_rows, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* Per-expert load of the batch (ultraep GPU operations, Load computation):
  * load[e] = pairs with id e, e in [0, E). Ids outside [-1, E) set
  * MOE_STATUS_BAD_EXPERT. status may be NULL. */

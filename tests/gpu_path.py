@@ -80,3 +80,35 @@ def run_dispatch_combine(capi, w, shape, lay, rows, weights=True, f32=True, x=No
     torch.cuda.synchronize()
     return (np16(recv), np16(out), o32.cpu().numpy() if f32 else None,
             int(lay.status.item()))
+
+
+def run_layout_dispatch(capi, w, A=None, ll=False, M=None, src=0, rows=None):
+    """moe_layout_dispatch / moe_ll_layout_dispatch on the GPU into a
+    sentinel-filled receive buffer; returns (layout dict, recv numpy, lay, shape)."""
+    A = w.A if A is None else A
+    shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, A)
+    d_idx = to_dev(w.topk_idx.astype(np.int64))
+    lay = capi.LayoutBuffers.empty(shape, dev(), ll_M=M if ll else None)
+    for t in (lay.count, lay.offset, lay.slot, lay.rank_token_count, lay.row_src):
+        t.fill_(-12345)
+    lay.is_token_in_rank.fill_(7)
+    if rows is None:
+        rows = capi.moe_ll_recv_rows(w.E, w.R, M) if ll else capi.moe_recv_rows_worst(shape)
+    recv = torch.full((max(rows, 1), w.H), SENTINEL, dtype=torch.int16, device=dev())
+    nws = capi.moe_layout_workspace_bytes(shape)
+    ws = torch.full((max(nws, 1),), 0x5A, dtype=torch.uint8, device=dev()) if nws else None
+    x = to_dev(w.x)
+    if ll:
+        capi.moe_ll_layout_dispatch(shape, M, src, d_idx, lay, x, recv, rows, ws)
+    else:
+        capi.moe_layout_dispatch(shape, d_idx, lay, x, recv, rows, ws)
+    torch.cuda.synchronize()
+    E = w.E
+    out = dict(count=lay.count.cpu().numpy(), slot=lay.slot.cpu().numpy().reshape(w.T, w.K),
+               status=int(lay.status.item()), offset=lay.offset.cpu().numpy(),
+               rank_token_count=lay.rank_token_count.cpu().numpy(),
+               is_token_in_rank=lay.is_token_in_rank.cpu().numpy().reshape(w.T, w.R))
+    rs = lay.row_src.cpu().numpy()
+    out["rows"] = E * w.R * M if ll else int(out["offset"][E])
+    out["row_src"] = rs[: E * M] if ll else rs[: out["rows"]]
+    return out, recv, lay, shape

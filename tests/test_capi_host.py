@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 14, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -115,6 +115,22 @@ def test_dispatch_combine_checks(lib):
     s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
     assert raw.moe_dispatch(C.byref(s0), None, None, None, 0, None, None) == 0
     assert raw.moe_combine(C.byref(s0), None, 0, None, None, None, None, None, None) == 0
+
+
+def test_layout_dispatch_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(258)
+    lt = lib.moe_layout_t()
+    lt.count = lt.offset = lt.slot = d
+    s = lib.make_shape(4, 12, 16, 4, 2, 1)  # H % 8
+    assert raw.moe_layout_dispatch(C.byref(s), d, C.byref(lt), d, d, 8, None, 0, None) == -2
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    assert raw.moe_layout_dispatch(C.byref(s), d, C.byref(lt), odd, d, 8, None, 0, None) == -5
+    assert raw.moe_layout_dispatch(C.byref(s), d, C.byref(lt), None, d, 8, None, 0, None) == -1
+    assert raw.moe_layout_dispatch(C.byref(s), d, C.byref(lt), d, d, -1, None, 0, None) == -3
+    assert raw.moe_ll_layout_dispatch(C.byref(s), 3, 0, d, C.byref(lt), d, d, 8, None, 0,
+                                      None) == -4
 
 
 def test_replica_checks(lib):

@@ -247,8 +247,8 @@ def test_ll_sweep(capi, orc, M):
 
 
 def test_ll_overflow_and_small_M(capi, orc):
-    w = mi.random_case(40, 30, 64, 16, 4, 4, 1, dup_frac=0.8)
-    _announce("LL overflow by duplicates, M=30")
+    w = _hot(mi.random_case(40, 30, 64, 16, 4, 4, 1), 5, 0.9)
+    _announce("LL overflow on a hot expert, M=30")
     got, lay, shape = run_layout(capi, w, ll=True, M=30, src=2)
     ref = orc.ll_layout(w.topk_idx, w.E, w.R, 30, 2)
     assert ref["status"] & 2
@@ -264,7 +264,7 @@ def test_ll_multiblock(capi, orc):
 
 
 def test_ll_multiblock_overflow(capi, orc):
-    w = mi.random_case(42, 1500, 16, 8, 2, 8, 1, M=1500, dup_frac=0.7)
+    w = _hot(mi.random_case(42, 1500, 16, 8, 2, 8, 1, M=1500), 3, 0.5)
     _announce("LL multi-block overflow")
     got, lay, shape = run_layout(capi, w, ll=True, M=1500, src=1)
     ref = orc.ll_layout(w.topk_idx, w.E, w.R, 1500, 1)
@@ -344,3 +344,73 @@ def test_deterministic_runs(capi, orc):
         outs.append((got["slot"].copy(), recv.copy(), o16.copy(), o32.copy()))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# -- layout and dispatch in one call -------------------------------------------
+
+from gpu_path import run_layout_dispatch  # noqa: E402
+
+FUSED_CASES = {k: v for k, v in CASES.items()
+               if k not in ("rand_8193pairs", "rand_K64_onefull", "rand_K64_multi")}
+FUSED_CASES["rand_2048pairs"] = lambda: mi.random_case(70, 256, 520, 96, 8, 8, 1, neg_frac=0.05)
+FUSED_CASES["rand_2049pairs"] = lambda: mi.random_case(71, 2049, 64, 32, 4, 1, 1)
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_CASES))
+@pytest.mark.parametrize("A", [1, 16])
+def test_layout_dispatch_parity(capi, orc, name, A):
+    w = FUSED_CASES[name]()
+    _announce(f"layout_dispatch {name} A={A} T={w.T} H={w.H} E={w.E} R={w.R} K={w.K}")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, A=A)
+    ref = orc.layout(w.topk_idx, w.E, w.R, A)
+    check_layout(got, ref, w)
+    rows = ref["rows"]
+    rref, _ = orc.dispatch(w.x, ref["slot"], rows, fill=SENTINEL)
+    recv = np16(recv_t)
+    assert np.array_equal(recv[:rows], rref), "dispatched rows / untouched padding"
+    out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
+    o32 = torch.empty(w.T, w.H, dtype=torch.float32, device=dev())
+    capi.moe_combine(shape, recv_t, recv_t.shape[0], lay.slot, to_dev(w.topk_weights), out, o32,
+                     lay.status)
+    torch.cuda.synchronize()
+    check_combine(orc, np16(out), o32.cpu().numpy(), rref, ref["slot"], w.topk_weights)
+
+
+@pytest.mark.parametrize("M", mi.C3_SWEEP)
+def test_ll_layout_dispatch_sweep(capi, orc, M):
+    w = mi.config_c3(M)
+    s = 3
+    _announce(f"ll_layout_dispatch M={M} src={s}")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, ll=True, M=M, src=s)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, M, s)
+    check_layout(got, ref, w, ll=True)
+    _gpu_rows_check(recv_t, to_dev(w.x), ref["slot"], w.T, w.K)
+    del recv_t
+    torch.cuda.empty_cache()
+
+
+def test_layout_dispatch_empty_and_overflow(capi, orc):
+    w = mi.random_case(72, 0, 64, 16, 4, 4, 2)
+    _announce("layout_dispatch T=0")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w)
+    assert got["count"].sum() == 0 and np.all(got["offset"] == 0) and got["status"] == 0
+    assert np.all(got["rank_token_count"] == 0)
+    w = _hot(mi.random_case(73, 40, 64, 16, 4, 4, 1), 2, 0.9)
+    _announce("ll_layout_dispatch overflow M=40")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, ll=True, M=40, src=1)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, 40, 1)
+    assert ref["status"] & 2
+    check_layout(got, ref, w, ll=True)
+    _gpu_rows_check(recv_t, to_dev(w.x), ref["slot"], w.T, w.K)
+
+
+def test_layout_dispatch_small_receive_buffer(capi, orc):
+    """Rows at or past recv_rows are skipped and flagged, never written."""
+    w = mi.random_case(74, 64, 64, 16, 4, 4, 1)
+    _announce("layout_dispatch with recv_rows = 100 < 256")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, rows=100)
+    ref = orc.layout(w.topk_idx, w.E, w.R, 1)
+    assert np.array_equal(got["slot"], ref["slot"])
+    rref, st = orc.dispatch(w.x, ref["slot"], 100, fill=SENTINEL)
+    assert st == 4 and got["status"] == 4
+    assert np.array_equal(np16(recv_t), rref)
