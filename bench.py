@@ -157,6 +157,137 @@ def cpu_baseline(w, budget_s, gpu_out_bits):
     return reps, el, ok
 
 
+def graph_us_per_step(torch, stream, step_fns, reps):
+    """Capture one HIP graph holding one step per entry of step_fns, replay it
+    `reps` times between events; microseconds per step."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for fn in step_fns:
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            g.replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / (reps * len(step_fns))
+
+
+def row_low_latency(capi, mi, torch, np, dev, stream, n_ev):
+    """Low-latency padded path at 128 tokens per rank: layout + dispatch into
+    the [E, R*M, H] union of the receive buffers, then combine from it. Steps
+    rotate over 4 union buffers x 8 source stripes (> 512 MiB touched)."""
+    M = 128
+    w = mi.config_c3(M)
+    E, R, K, T, H = w.E, w.R, w.K, w.T, w.H
+    rows = capi.moe_ll_recv_rows(E, R, M)
+    shape = capi.make_shape(T, H, E, R, K, 1)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    wt = torch.from_numpy(w.topk_weights).to(dev)
+    unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(4)]
+    sets = []
+    for u in unions:
+        for s in range(R):
+            sets.append(dict(u=u, s=s, x=x.clone(), idx=idx.clone(), w=wt.clone(),
+                             lay=capi.LayoutBuffers.empty(shape, dev, ll_M=M, status=False),
+                             out=torch.empty(T, H, dtype=torch.int16, device=dev)))
+
+    def ld(z):
+        capi.moe_ll_layout_dispatch(shape, M, z["s"], z["idx"], z["lay"], z["x"], z["u"], rows,
+                                    stream=stream)
+
+    def cb(z):
+        capi.moe_combine(shape, z["u"], rows, z["lay"].slot, z["w"], z["out"], None, None,
+                         stream=stream)
+
+    with torch.cuda.stream(stream):
+        for z in sets:
+            ld(z)
+            cb(z)
+    torch.cuda.synchronize()
+    fns = [(lambda z=z: (ld(z), cb(z))) for z in sets]
+    us = graph_us_per_step(torch, stream, fns, 20)
+    with torch.cuda.stream(stream):
+        k_ld = per_launch_event_times(torch, lambda i: ld(sets[i % len(sets)]), n_ev, stream)
+        k_cb = per_launch_event_times(torch, lambda i: cb(sets[i % len(sets)]), n_ev, stream)
+    ab = algo_bytes(T, H, K, E, R, int((w.topk_idx >= 0).sum()))
+    del unions, sets
+    torch.cuda.empty_cache()
+    return {"workload": "low-latency padded: 128 tokens/rank x 7168, 256E top-8, 8 ranks, "
+                        "union receive buffer [256, 8*128, 7168]",
+            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
+            "kernels_us": {"ll_layout_dispatch": round(k_ld["mean_us"], 3),
+                           "combine": round(k_cb["mean_us"], 3)},
+            "algorithmic_bytes_per_step": ab["total"]}
+
+
+def row_replica(capi, mi, torch, np, dev, stream, n_ev):
+    """Replica-expanded routing at full size (8192 tokens x 7168, 256 logical
+    experts top-8 Zipf(1.0), 32 extra replicas): load -> plan -> reroute ->
+    layout + dispatch over 288 physical experts -> combine. Also the large-batch
+    dispatch and combine kernels on their own (their HBM roofline)."""
+    w = mi.config_c5()
+    E, R, K, T, H, C = w.E, w.R, w.K, w.T, w.H, w.replicas
+    Ep = E + C
+    shape = capi.make_shape(T, H, Ep, R, K, 1)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    wt = torch.from_numpy(w.topk_weights).to(dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    load = torch.empty(E, **i32)
+    rc = torch.empty(E, **i32)
+    rp = torch.empty(E, 2, **i32)
+    p2l = torch.empty(Ep, **i32)
+    phys = torch.empty(T, K, dtype=torch.int64, device=dev)
+    lay = capi.LayoutBuffers.empty(shape, dev, status=False)
+    rows = capi.moe_recv_rows_worst(shape)
+    recv = torch.empty(rows, H, dtype=torch.int16, device=dev)
+    out = torch.empty(T, H, dtype=torch.int16, device=dev)
+    ws = torch.empty(max(capi.moe_layout_workspace_bytes(shape), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        capi.moe_expert_load(T, K, E, idx, load, None, stream=stream)
+        capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l, stream=stream)
+        capi.moe_reroute(T, K, E, idx, rc, rp, Ep, phys, None, stream=stream)
+        capi.moe_layout_dispatch(shape, phys, lay, x, recv, rows, ws, stream=stream)
+        capi.moe_combine(shape, recv, rows, lay.slot, wt, out, None, None, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+        step()
+    torch.cuda.synchronize()
+    us = graph_us_per_step(torch, stream, [step], 10)
+    with torch.cuda.stream(stream):
+        k_d = per_launch_event_times(torch, lambda i: capi.moe_dispatch(
+            shape, x, lay.slot, recv, rows, None, stream=stream), n_ev // 4, stream)
+        k_c = per_launch_event_times(torch, lambda i: capi.moe_combine(
+            shape, recv, rows, lay.slot, wt, out, None, None, stream=stream), n_ev // 4, stream)
+    P = T * K
+    ab = algo_bytes(T, H, K, Ep, R, P)
+    reroute_bytes = P * 8 * 3 + E * 4 * 6 + Ep * 4
+    total = ab["total"] + reroute_bytes
+    rd = ab["dispatch"] / (k_d["mean_us"] * 1e-6) / 1e9
+    rcb = ab["combine"] / (k_c["mean_us"] * 1e-6) / 1e9
+    del recv, x, out
+    torch.cuda.empty_cache()
+    return {"workload": "replica-expanded: 8192 tokens x 7168, 256 logical experts top-8 "
+                        "Zipf(1.0) + 32 replicas = 288 physical on 8 ranks",
+            "us_per_step": round(us, 2), "GB_per_s": round(total / us / 1e3, 1),
+            "algorithmic_bytes_per_step": total,
+            "kernels_us": {"dispatch": round(k_d["mean_us"], 2),
+                           "combine": round(k_c["mean_us"], 2)},
+            "roofline_dispatch": {"achieved": round(rd, 1), "frac": round(rd / HBM_PEAK_GBS, 4)},
+            "roofline_combine": {"achieved": round(rcb, 1),
+                                 "frac": round(rcb / HBM_PEAK_GBS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +298,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the low-latency and replica-path measurements")
     ap.add_argument("--profile-pass", action="store_true",
                     help="short fixed run for rocprofv3: warm-up, copy calibration, steps")
     args = ap.parse_args()
@@ -264,19 +397,30 @@ def main():
     def z(i):
         return sets[i % S]
 
-    kern = {
-        "layout_dispatch": ev(lambda i: capi.moe_layout_dispatch(
+    # primary: each kernel alone, one HIP graph of S launches over the rotating
+    # sets, events around the replays (the configuration of the timed steps);
+    # secondary: every launch bracketed by its own event pair (adds the launch
+    # latency of an eager launch)
+    fns = {
+        "layout_dispatch": lambda i: capi.moe_layout_dispatch(
             z(i).shape, z(i).idx, z(i).lay, z(i).x, z(i).recv, z(i).rows, z(i).ws,
-            stream=stream)),
-        "combine": ev(lambda i: capi.moe_combine(
+            stream=stream),
+        "combine": lambda i: capi.moe_combine(
             z(i).shape, z(i).recv, z(i).rows, z(i).lay.slot, z(i).w, z(i).out, None, None,
-            stream=stream)),
+            stream=stream),
         # reference: the same work as two separate kernels
-        "layout": ev(lambda i: capi.moe_layout(z(i).shape, z(i).idx, z(i).lay, z(i).ws,
-                                               stream=stream)),
-        "dispatch": ev(lambda i: capi.moe_dispatch(z(i).shape, z(i).x, z(i).lay.slot, z(i).recv,
-                                                   z(i).rows, None, stream=stream)),
+        "layout": lambda i: capi.moe_layout(z(i).shape, z(i).idx, z(i).lay, z(i).ws,
+                                            stream=stream),
+        "dispatch": lambda i: capi.moe_dispatch(z(i).shape, z(i).x, z(i).lay.slot, z(i).recv,
+                                                z(i).rows, None, stream=stream),
     }
+    kern = {}
+    for name, fn in fns.items():
+        g_us = graph_us_per_step(torch, stream, [(lambda i=i, fn=fn: fn(i)) for i in range(S)],
+                                 max(4, n // S))
+        e = ev(fn)
+        kern[name] = {"mean_us": g_us, "event_mean_us": e["mean_us"],
+                      "event_median_us": e["median_us"]}
     kbytes = {"layout_dispatch": ab["layout"] + ab["dispatch"], "combine": ab["combine"],
               "layout": ab["layout"], "dispatch": ab["dispatch"]}
     dom = max(("layout_dispatch", "combine"), key=lambda k: kern[k]["mean_us"])
@@ -287,6 +431,13 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "algorithmic_bytes": kbytes[dom],
                 "duration_us": round(dur, 3)}
+
+    rows = {}
+    if not args.no_rows:
+        rows["low_latency_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, n)
+        log(f"low-latency row: {rows['low_latency_m128']['us_per_step']} us/step")
+        rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
+        log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
 
     torch.cuda.synchronize()
     out_bits = sets[0].out.cpu().numpy().view(np.uint16)
@@ -324,8 +475,9 @@ def main():
                    "footprint_MiB": round(S * probe.nbytes / 2**20, 1),
                    "algorithmic_bytes_per_step": ab["total"]},
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kern.items()},
-        "kernels_median_us": {k: round(v["median_us"], 3) for k, v in kern.items()},
+        "kernels_eager_event_us": {k: round(v["event_mean_us"], 3) for k, v in kern.items()},
         "roofline": roofline,
+        "rows": rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
