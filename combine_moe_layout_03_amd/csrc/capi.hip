@@ -93,6 +93,7 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   p->src = src;
   p->id_bits = bits_for(s->E);
   p->rank_bits = bits_for(s->R);
+  p->l_magic = ((1ull << 32) + (uint64_t)p->L - 1) / (uint64_t)p->L;
   p->count = out->count;
   p->offset = out->offset;
   p->rank_token_count = out->rank_token_count;

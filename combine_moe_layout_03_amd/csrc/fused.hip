@@ -32,7 +32,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCountMaxWaves = 8;
+constexpr int kCountMaxWaves = 16;
 constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * threads
 constexpr int kMaxDuties = 4;       // experts (and ranks) whose totals one workgroup writes
 constexpr int kLayoutOnlyThreads = 256;
@@ -157,7 +157,7 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int i = r * nthreads + tid;
-      if (ids.any[r] >= 0 && ids.any[r] / L == rd) s_mark[i / K] = 1;
+      if (ids.any[r] >= 0 && rank_of(ids.any[r], p.l_magic) == rd) s_mark[i / K] = 1;
     }
     lds_barrier();
     int n = 0;
@@ -208,10 +208,9 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 
 template <bool kCopy, int kRounds>
 __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
-  __shared__ int32_t s_pre[kCountMaxWaves][64];   // per wave, per k: same id before token
-  __shared__ int32_t s_lt[kCountMaxWaves][64];    // per wave, per k: valid ids below
-  __shared__ int32_t s_tok[64];                   // this token's ids (-1 = none)
-  __shared__ int32_t s_slot[64];
+  __shared__ int32_t s_pre[64];   // per k: pairs with the same id before this token
+  __shared__ int32_t s_lt[64];    // per k: valid ids below it
+  __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
   __shared__ int32_t s_status;
 
   const LayoutParams &p = f.lp;
@@ -224,13 +223,17 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     duty_workgroup<kRounds>(p, b - f.token_wgs, f.duty_wgs, st);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nthreads = blockDim.x, nwaves = nthreads >> 6;
-    const int E = p.E, R = p.R, K = p.K, T = p.T, L = p.L;
+    const int nthreads = blockDim.x;
+    const int E = p.E, R = p.R, K = p.K, T = p.T;
     const int P = T * K;
     const bool ll = p.mode == kModeLowLatency;
     const int t = kCopy ? b / f.wg_per_token : b;  // < T
     const bool token_lead = !kCopy || b % f.wg_per_token == 0;
     const int pbeg = t * K;
+    if (tid < 64) {
+      s_pre[tid] = 0;
+      s_lt[tid] = 0;
+    }
 
     // 1. the routing first ...
     LaneIds<kRounds> ids;
@@ -244,7 +247,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     if (kCopy) {
       const int chunk = (b % f.wg_per_token) * f.chunks_per_wg + wave;
       v = chunk * 64 + lane;
-      lane_ok = chunk < f.nchunk && v < f.nvec;
+      lane_ok = wave < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
       val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
     }
     ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
 
     // 3. per selected expert of this token: ids equal to it before the token,
     //    and valid ids below it. The token's ids sit in lanes 0..K-1 of tokv;
-    //    lane k of prev/ltv collects the counts for its k.
+    //    each wave adds its counts for k into s_pre[k] / s_lt[k].
     const int tokv = lane < K ? s_tok[lane] : -1;
     int prev = 0, ltv = 0;
     for (int k = 0; k < K; ++k) {
@@ -263,61 +266,57 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       }
     }
     if (lane < K) {
-      s_pre[wave][lane] = prev;
-      s_lt[wave][lane] = ltv;
+      atomicAdd(&s_pre[lane], prev);
+      if (!ll) atomicAdd(&s_lt[lane], ltv);
     }
     lds_barrier();
 
-    // 4. slots of this token's pairs (wave 0, lane k)
-    if (wave == 0) {
+    // 4. slots of this token's pairs (lane k of every wave; wave 0 keeps them)
+    int out = -1, j = 0;
+    {
       const int e = tokv;
       int dup = 0;
       for (int k = 0; k < K; ++k) dup += (k < lane && __builtin_amdgcn_readlane(tokv, k) == e);
-      if (lane < K) {
-        int out = -1;
-        if (e >= 0) {
-          int pre = dup, lt = 0;
-          for (int w = 0; w < nwaves; ++w) {
-            pre += s_pre[w][lane];
-            lt += s_lt[w][lane];
-          }
-          if (!ll) {
-            out = lt + pre;
-            if (token_lead && p.row_src) p.row_src[out] = pbeg + lane;
-          } else if (pre < p.M) {
-            out = (e * R + p.src) * p.M + pre;
-            if (token_lead && p.row_src) p.row_src[(int64_t)e * p.M + pre] = pbeg + lane;
-          } else {
-            st |= kStOverflow;
-          }
-        }
-        s_slot[lane] = out;
-        if (token_lead) p.slot[pbeg + lane] = out;
-      }
-      // ranks this token reaches
-      if (token_lead && p.in_rank) {
-        for (int r0 = 0; r0 < R; r0 += 64) {
-          const int r = r0 + lane;
-          bool hit = false;
-          for (int k = 0; k < K; ++k) {
-            const int ek = __builtin_amdgcn_readlane(tokv, k);
-            hit |= ek >= 0 && ek / L == r;
-          }
-          if (r < R) p.in_rank[(int64_t)t * R + r] = hit ? 1 : 0;
+      if (lane < K && e >= 0) {
+        j = s_pre[lane] + dup;
+        if (!ll) {
+          out = s_lt[lane] + j;
+        } else if (j < p.M) {
+          out = (e * R + p.src) * p.M + j;
+        } else if (wave == 0) {
+          st |= kStOverflow;
         }
       }
     }
 
-    // 5. the row, K times
+    // 5. the row, K times (slot k read from lane k)
     if (kCopy) {
-      lds_barrier();
       asm volatile("" : "+v"(val));
       for (int k = 0; k < K; ++k) {
-        const int s = __builtin_amdgcn_readfirstlane(s_slot[k]);
+        const int s = __builtin_amdgcn_readlane(out, k);
         if (s >= 0 && s < f.rows) {
           if (lane_ok) __builtin_nontemporal_store(val, f.recv + (int64_t)s * f.nvec + v);
-        } else if (s != -1) {
+        } else if (s != -1 && wave == 0) {
           st |= kStBadSlot;  // receive buffer smaller than the layout needs
+        }
+      }
+    }
+
+    // 6. this token's handle entries, written after the row so the wait for
+    //    the row load does not also wait for them
+    if (token_lead && wave == 0) {
+      if (lane < K) {
+        p.slot[pbeg + lane] = out;
+        if (out >= 0 && p.row_src)
+          p.row_src[ll ? (int64_t)tokv * p.M + j : (int64_t)out] = pbeg + lane;
+      }
+      if (p.in_rank) {
+        const int rank_v = tokv >= 0 ? rank_of(tokv, p.l_magic) : -1;
+        for (int r0 = 0; r0 < R; r0 += 64) {
+          const int r = r0 + lane;
+          bool hit = false;
+          for (int k = 0; k < K; ++k) hit |= __builtin_amdgcn_readlane(rank_v, k) == r;
+          if (r < R) p.in_rank[(int64_t)t * R + r] = hit ? 1 : 0;
         }
       }
     }
@@ -342,10 +341,20 @@ hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const
   return hipGetLastError();
 }
 
-int copy_threads(int32_t H) {
+// Waves of a copying workgroup: its row chunks (at most kCopyChunks), padded up to
+// kCopyWaves so the routing is read in fewer rounds per wave (extra waves only count).
+constexpr int kCopyChunks = 16;
+constexpr int kCopyWaves = 16;
+
+int copy_chunks(int32_t H) {
   const int nchunk = (H / 8 + 63) / 64;
-  const int groups = (nchunk + kCountMaxWaves - 1) / kCountMaxWaves;
-  return 64 * ((nchunk + groups - 1) / groups);
+  const int groups = (nchunk + kCopyChunks - 1) / kCopyChunks;
+  return (nchunk + groups - 1) / groups;
+}
+
+int copy_threads(int32_t H) {
+  const int c = copy_chunks(H);
+  return 64 * (c > kCopyWaves ? c : kCopyWaves);
 }
 
 }  // namespace
@@ -373,7 +382,7 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
     f.nvec = H / 8;
     f.nchunk = (f.nvec + 63) / 64;
     const int threads = copy_threads(H);
-    f.chunks_per_wg = threads / 64;
+    f.chunks_per_wg = copy_chunks(H);
     f.wg_per_token = (f.nchunk + f.chunks_per_wg - 1) / f.chunks_per_wg;
     f.token_wgs = lp.T * f.wg_per_token;
     // duty workgroups share the block size; their rounds follow from it

@@ -32,6 +32,7 @@ struct LayoutParams {
   int32_t M, src;        // low-latency capacity and source rank
   int32_t id_bits;       // bits needed for an expert id in [0, E)
   int32_t rank_bits;     // bits needed for a rank id in [0, R)
+  uint64_t l_magic;      // ceil(2^32 / L): rank of expert e = (e * l_magic) >> 32
   int32_t tokens_per_block;
   int32_t nblocks;
   int32_t *count;
@@ -44,6 +45,11 @@ struct LayoutParams {
   int32_t *ws_hist;  // [nblocks][E]  multi-block path only
   int32_t *ws_rcnt;  // [nblocks][R]  multi-block path only
 };
+
+// Rank that owns expert e: e / L by a 32.32 reciprocal (exact for e < 2^20, L <= 2^10).
+__device__ __forceinline__ int rank_of(int e, uint64_t l_magic) {
+  return (int)(((uint64_t)(uint32_t)e * l_magic) >> 32);
+}
 
 // Status bits (same values as the MOE_STATUS_* macros of the public header).
 constexpr int32_t kStBadExpert = 1;

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
         r = i - tl * R;
         for (int k = 0; k < K; ++k) {
           const int e = s_ids[tl * K + k];
-          hit |= (e >= 0) && (e / L == r);
+          hit |= (e >= 0) && (rank_of(e, p.l_magic) == r);
         }
         if (p.in_rank) p.in_rank[(int64_t)t0 * R + i] = hit ? 1 : 0;
       }
