@@ -61,7 +61,7 @@ size_t workspace_bytes(const moe_shape *s) {
   if (one_block(s)) return 0;
   const int64_t tpb = tokens_per_block(s->K);
   const int64_t nb = (s->T + tpb - 1) / tpb;
-  const int64_t ints = nb * s->E + nb * s->R;
+  const int64_t ints = nb * s->E + nb * s->R + s->E;
   return (size_t)((ints * 4 + 255) / 256 * 256);
 }
 
@@ -109,6 +109,7 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
     p->nblocks = (s->T + p->tokens_per_block - 1) / p->tokens_per_block;
     p->ws_hist = static_cast<int32_t *>(ws);
     p->ws_rcnt = p->ws_hist + (int64_t)p->nblocks * s->E;
+    p->ws_cnt = p->ws_rcnt + (int64_t)p->nblocks * s->R;
   }
   return MOE_OK;
 }

@@ -33,6 +33,13 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCountMaxWaves = 16;
+// Waves of a copying workgroup that also read the routing and count; the rest
+// only copy. Fewer counting waves share the SIMDs less (the counting is issue
+// bound), at the price of more id rounds each.
+#ifndef MOE_COUNTING_WAVES
+#define MOE_COUNTING_WAVES 8
+#endif
+constexpr int kCountingWaves = MOE_COUNTING_WAVES;
 constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * threads
 constexpr int kMaxDuties = 4;       // experts (and ranks) whose totals one workgroup writes
 constexpr int kLayoutOnlyThreads = 256;
@@ -223,7 +230,9 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     duty_workgroup<kRounds>(p, b - f.token_wgs, f.duty_wgs, st);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int nthreads = blockDim.x;
+    // lanes that read the routing and count (all of them without the copy)
+    const int nthreads = kCopy ? min((int)blockDim.x, kCountingWaves * 64) : (int)blockDim.x;
+    const bool counting = tid < nthreads;
     const int E = p.E, R = p.R, K = p.K, T = p.T;
     const int P = T * K;
     const bool ll = p.mode == kModeLowLatency;
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
 
     // 1. the routing first ...
     LaneIds<kRounds> ids;
-    ids.issue(p.idx, P, nthreads);
+    if (counting) ids.issue(p.idx, P, nthreads);
     // 2. ... then the row chunk this wave copies; it stays in flight while
     //    the slots are worked out. The load is unconditional (address clamped
     //    into the row): under a branch it would force an early wait.
@@ -250,24 +259,27 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       lane_ok = wave < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
       val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
     }
-    ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
+    if (counting) ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
     lds_barrier();
 
     // 3. per selected expert of this token: ids equal to it before the token,
     //    and valid ids below it. The token's ids sit in lanes 0..K-1 of tokv;
     //    each wave adds its counts for k into s_pre[k] / s_lt[k].
+    // (an invalid ek = -1 matches no sentinel-coded id, so it needs no branch;
+    // the below count is simply unused in the low-latency layout)
     const int tokv = lane < K ? s_tok[lane] : -1;
-    int prev = 0, ltv = 0;
-    for (int k = 0; k < K; ++k) {
-      const int ek = __builtin_amdgcn_readlane(tokv, k);
-      if (ek >= 0) {
+    if (counting) {  // uniform per wave
+      int prev = 0, ltv = 0;
+#pragma unroll 2
+      for (int k = 0; k < K; ++k) {
+        const int ek = __builtin_amdgcn_readlane(tokv, k);
         prev = set_lane(prev, k, ids.count_early_equal(ek));
-        if (!ll) ltv = set_lane(ltv, k, ids.count_below(ek));
+        ltv = set_lane(ltv, k, ids.count_below(ek));
       }
-    }
-    if (lane < K) {
-      atomicAdd(&s_pre[lane], prev);
-      if (!ll) atomicAdd(&s_lt[lane], ltv);
+      if (lane < K) {
+        atomicAdd(&s_pre[lane], prev);
+        if (!ll) atomicAdd(&s_lt[lane], ltv);
+      }
     }
     lds_barrier();
 
@@ -363,8 +375,9 @@ bool count_layout_fits(const LayoutParams &lp, int32_t H, bool copy) {
   if (lp.mode == kModeContiguous && lp.A != 1) return false;
   const int64_t P = (int64_t)lp.T * lp.K;
   if (P > kMaxPairsFused) return false;
-  const int threads = (copy && lp.T > 0) ? copy_threads(H) : kLayoutOnlyThreads;
-  // token and duty workgroups share the block size; the batch must fit 8 rounds
+  int threads = (copy && lp.T > 0) ? copy_threads(H) : kLayoutOnlyThreads;
+  if (copy && lp.T > 0 && threads > kCountingWaves * 64) threads = kCountingWaves * 64;
+  // the batch must fit kCountMaxRounds rounds of the counting lanes
   return P <= (int64_t)kCountMaxRounds * threads;
 }
 
@@ -385,8 +398,10 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
     f.chunks_per_wg = copy_chunks(H);
     f.wg_per_token = (f.nchunk + f.chunks_per_wg - 1) / f.chunks_per_wg;
     f.token_wgs = lp.T * f.wg_per_token;
-    // duty workgroups share the block size; their rounds follow from it
-    const int rounds = (P + threads - 1) / threads;
+    // token workgroups count with kCountingWaves waves, duty workgroups with all
+    // of theirs; the rounds template covers the larger need
+    const int counting = threads < kCountingWaves * 64 ? threads : kCountingWaves * 64;
+    const int rounds = (P + counting - 1) / counting;
     return launch_rounds<true>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
                                dim3(threads), s, f);
   }

@@ -42,8 +42,9 @@ struct LayoutParams {
   int32_t *slot;
   int32_t *row_src;
   int32_t *status;
-  int32_t *ws_hist;  // [nblocks][E]  multi-block path only
-  int32_t *ws_rcnt;  // [nblocks][R]  multi-block path only
+  int32_t *ws_hist;  // [E][nblocks]  multi-block path: pairs of e per block, then prefix
+  int32_t *ws_rcnt;  // [R][nblocks]  multi-block path: tokens reaching r per block
+  int32_t *ws_cnt;   // [E]           multi-block path: pairs per expert
 };
 
 // Rank that owns expert e: e / L by a 32.32 reciprocal (exact for e < 2^20, L <= 2^10).

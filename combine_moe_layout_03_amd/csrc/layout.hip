@@ -15,8 +15,9 @@
 // of pairs and a private row of uint16 counters in LDS; a per-expert prefix over
 // the 16 waves then gives every wave its starting rank. A batch of up to 8192
 // pairs is done by one workgroup; larger batches take three launches (per-block
-// counts and local ranks, one-workgroup scan over blocks, per-pair fix-up), with
-// no inter-workgroup waiting.
+// counts and local ranks; one wave per expert for the prefix over blocks; a
+// per-pair fix-up whose workgroups each scan the per-expert totals), with no
+// inter-workgroup waiting.
 #include "wave.hpp"
 
 namespace moe {
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     if (E == 0 && tid == 0 && p.mode == kModeContiguous) p.offset[0] = 0;
   } else {
     for (int e = tid; e < E; e += kLayoutThreads)
-      p.ws_hist[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+      p.ws_hist[(int64_t)e * p.nblocks + blockIdx.x] = s_cnt[e];
   }
   __syncthreads();
 
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
       if (kOneBlock)
         p.rank_token_count[r] = s_rc[r];
       else
-        p.ws_rcnt[(int64_t)blockIdx.x * R + r] = s_rc[r];
+        p.ws_rcnt[(int64_t)r * p.nblocks + blockIdx.x] = s_rc[r];
     }
   }
   if (kOneBlock && p.row_src) {
@@ -194,96 +195,129 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
   if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
 }
 
-// Multi-block pass 2 (one workgroup): per-expert exclusive prefix over blocks,
-// aligned scan over experts, block bases, per-rank sums, padding rows.
-__global__ __launch_bounds__(kLayoutThreads) void layout_scan_kernel(LayoutParams p) {
-  __shared__ int32_t s_wave[kLayoutWaves];
-  const int tid = threadIdx.x, E = p.E, R = p.R, nb = p.nblocks;
-  const int e = tid;
-  int c = 0;
-  if (e < E) {
-#pragma unroll 8
-    for (int b = 0; b < nb; ++b) c += p.ws_hist[(int64_t)b * E + e];
+// Multi-block pass 2: one wave per expert (exclusive prefix of its per-block
+// counts, in place, and its total) and one wave per rank (its token total).
+__global__ __launch_bounds__(64) void layout_prefix_kernel(LayoutParams p) {
+  const int lane = lane_id(), nb = p.nblocks;
+  const int g = blockIdx.x;
+  if (g < p.E) {
+    int32_t *h = p.ws_hist + (int64_t)g * nb;
+    int carry = 0;
+    for (int b0 = 0; b0 < nb; b0 += 64) {
+      const int b = b0 + lane;
+      const int c = b < nb ? h[b] : 0;
+      int x = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+      }
+      if (b < nb) h[b] = carry + x - c;
+      carry += __shfl(x, 63, 64);
+    }
+    if (lane == 0) p.ws_cnt[g] = carry;
+  } else if (p.rank_token_count) {
+    const int r = g - p.E;
+    const int32_t *h = p.ws_rcnt + (int64_t)r * nb;
+    int n = 0;
+    for (int b = lane; b < nb; b += 64) n += h[b];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
+    if (lane == 0) p.rank_token_count[r] = n;
   }
-  const int padded = (p.mode == kModeContiguous) ? round_up(c, p.A) : 0;
+}
+
+// Multi-block pass 3: every workgroup scans the per-expert totals into the
+// first row of each expert (cheap: E <= 1024), workgroup 0 writes the totals,
+// all workgroups share the padding rows, then each thread fixes one pair:
+// slot = first row of its expert + pairs of that expert in earlier blocks +
+// its rank inside its own block.
+constexpr int kFixupThreads = 256;
+
+__global__ __launch_bounds__(kFixupThreads) void layout_fixup_kernel(LayoutParams p) {
+  __shared__ int32_t s_base[kMaxExperts];
+  __shared__ int32_t s_wave[kFixupThreads / 64];
+  const int tid = threadIdx.x, E = p.E, R = p.R;
+  const bool contiguous = p.mode == kModeContiguous;
+  // aligned exclusive scan over experts (E/256 consecutive experts per thread)
+  const int per = (E + kFixupThreads - 1) / kFixupThreads;
+  const int e0 = tid * per;
+  int sum = 0;
+  for (int j = 0; j < per; ++j)
+    if (e0 + j < E) sum += contiguous ? round_up(p.ws_cnt[e0 + j], p.A) : 0;
   int total = 0;
-  const int excl = block_exclusive_scan(padded, s_wave, kLayoutWaves, &total);
+  int run = block_exclusive_scan(sum, s_wave, kFixupThreads / 64, &total);
   int st = 0;
-  if (e < E) {
-    int base;
-    if (p.mode == kModeContiguous) {
-      base = excl;
-      p.count[e] = c;
-      p.offset[e] = excl;
-      if (e == E - 1) p.offset[E] = total;
-    } else {
-      base = (e * R + p.src) * p.M;
-      p.count[e] = min(c, p.M);
-      if (c > p.M) st |= kStOverflow;
-      if (p.offset) {
+  for (int j = 0; j < per; ++j) {
+    const int e = e0 + j;
+    if (e >= E) break;
+    const int c = p.ws_cnt[e];
+    const int base = contiguous ? run : (e * R + p.src) * p.M;
+    s_base[e] = base;
+    if (blockIdx.x == 0) {
+      if (contiguous) {
+        p.count[e] = c;
         p.offset[e] = base;
-        if (e == E - 1) p.offset[E] = E * R * p.M;
-      }
-    }
-    // block b's pairs of expert e start at base + (pairs of e in blocks < b)
-    int run = base;
-#pragma unroll 8
-    for (int b = 0; b < nb; ++b) {
-      const int64_t at = (int64_t)b * E + e;
-      const int h = p.ws_hist[at];
-      p.ws_hist[at] = run;
-      run += h;
-    }
-    if (p.row_src) {
-      if (p.mode == kModeContiguous) {
-        for (int r = base + c; r < base + padded; ++r) p.row_src[r] = -1;
       } else {
-        for (int j = min(c, p.M); j < p.M; ++j) p.row_src[(int64_t)e * p.M + j] = -1;
+        p.count[e] = min(c, p.M);
+        if (c > p.M) st |= kStOverflow;
+        if (p.offset) p.offset[e] = base;
       }
     }
+    // padding rows: expert e's share goes to workgroup e mod gridDim.x
+    if (p.row_src && (int)(e % gridDim.x) == (int)blockIdx.x) {
+      if (contiguous) {
+        for (int r = base + c; r < base + round_up(c, p.A); ++r) p.row_src[r] = -1;
+      } else {
+        for (int j2 = min(c, p.M); j2 < p.M; ++j2) p.row_src[(int64_t)e * p.M + j2] = -1;
+      }
+    }
+    if (contiguous) run += round_up(c, p.A);
   }
-  if (p.rank_token_count) {
-    for (int r = tid; r < R; r += kLayoutThreads) {
-      int s = 0;
-      for (int b = 0; b < nb; ++b) s += p.ws_rcnt[(int64_t)b * R + r];
-      p.rank_token_count[r] = s;
+  if (blockIdx.x == 0 && tid == 0 && p.offset) p.offset[E] = contiguous ? total : E * R * p.M;
+  __syncthreads();
+
+  const int64_t i = (int64_t)blockIdx.x * kFixupThreads + tid;
+  const int64_t n = (int64_t)p.T * p.K;
+  if (i < n) {
+    const int64_t v = p.idx[i];
+    if (v >= 0 && v < E) {  // other pairs already hold slot -1
+      const int e = (int)v;
+      const int b = (int)((i / p.K) / p.tokens_per_block);
+      const int j = p.ws_hist[(int64_t)e * p.nblocks + b] + p.slot[i];
+      if (contiguous) {
+        const int s = s_base[e] + j;
+        p.slot[i] = s;
+        if (p.row_src) p.row_src[s] = (int32_t)i;
+      } else if (j < p.M) {
+        p.slot[i] = s_base[e] + j;
+        if (p.row_src) p.row_src[(int64_t)e * p.M + j] = (int32_t)i;
+      } else {
+        p.slot[i] = -1;
+        st |= kStOverflow;
+      }
     }
   }
   if (st && p.status) atomicOr(p.status, st);
 }
 
-// Multi-block pass 3: slot = (start of this block's run of the expert) + local rank.
-__global__ __launch_bounds__(256) void layout_fixup_kernel(LayoutParams p) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t n = (int64_t)p.T * p.K;
-  if (i >= n) return;
-  const int64_t v = p.idx[i];
-  if (v < 0 || v >= p.E) return;  // slot already -1
-  const int e = (int)v;
-  const int b = (int)((i / p.K) / p.tokens_per_block);
-  const int s = p.ws_hist[(int64_t)b * p.E + e] + p.slot[i];
-  if (p.mode == kModeContiguous) {
-    p.slot[i] = s;
-    if (p.row_src) p.row_src[s] = (int32_t)i;
-  } else {
-    const int j = s - (e * p.R + p.src) * p.M;
-    if (j < p.M) {
-      p.slot[i] = s;
-      if (p.row_src) p.row_src[(int64_t)e * p.M + j] = (int32_t)i;
-    } else {
-      p.slot[i] = -1;
-      if (p.status) atomicOr(p.status, kStOverflow);
-    }
-  }
+// Per-expert load of the batch. Each workgroup histograms its share of the
+// pairs in LDS (one leader lane per (wave, expert) per 64-pair step) and adds
+// its non-zero bins to the output with global atomics; integer sums, so the
+// result does not depend on their order. `zero` first clears the output.
+constexpr int kLoadPairsPerBlock = 4096;
+
+__global__ __launch_bounds__(kLayoutThreads) void load_zero_kernel(int32_t *load, int32_t E) {
+  for (int e = threadIdx.x; e < E; e += kLayoutThreads) load[e] = 0;
 }
 
-// Per-expert load of the batch with one workgroup: LDS histogram fed by one
-// leader lane per (wave, expert) per 64-pair step.
 __global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64_t *idx,
                                                                      int32_t n, int32_t E,
                                                                      int32_t bits,
                                                                      int32_t *load,
-                                                                     int32_t *status) {
+                                                                     int32_t *status,
+                                                                     int32_t per_block,
+                                                                     int32_t accumulate) {
   __shared__ int32_t s_h[kMaxExperts];
   __shared__ int32_t s_status;
   const int tid = threadIdx.x;
@@ -291,10 +325,11 @@ __global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64
   if (tid == 0) s_status = 0;
   __syncthreads();
   int st = 0;
-  for (int b = 0; b < n; b += kLayoutThreads) {
+  const int i0 = blockIdx.x * per_block, i1 = min(n, i0 + per_block);
+  for (int b = i0; b < i1; b += kLayoutThreads) {
     const int i = b + tid;
     int e = -1;
-    if (i < n) {
+    if (i < i1) {
       const int64_t v = idx[i];
       if (v >= 0 && v < E)
         e = (int)v;
@@ -306,7 +341,13 @@ __global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64
   }
   if (st) atomicOr(&s_status, st);
   __syncthreads();
-  for (int e = tid; e < E; e += kLayoutThreads) load[e] = s_h[e];
+  for (int e = tid; e < E; e += kLayoutThreads) {
+    if (accumulate) {
+      if (s_h[e]) atomicAdd(&load[e], s_h[e]);
+    } else {
+      load[e] = s_h[e];
+    }
+  }
   if (tid == 0 && s_status && status) atomicOr(status, s_status);
 }
 
@@ -321,19 +362,29 @@ hipError_t launch_layout_multi_block(const LayoutParams &p, hipStream_t s) {
   hipLaunchKernelGGL(layout_block_kernel<false>, dim3(p.nblocks), dim3(kLayoutThreads), 0, s, p);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(layout_scan_kernel, dim3(1), dim3(kLayoutThreads), 0, s, p);
+  hipLaunchKernelGGL(layout_prefix_kernel, dim3(p.E + p.R), dim3(64), 0, s, p);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int64_t n = (int64_t)p.T * p.K;
-  const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(layout_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  const int64_t blocks = (n + kFixupThreads - 1) / kFixupThreads;
+  hipLaunchKernelGGL(layout_fixup_kernel, dim3((unsigned)blocks), dim3(kFixupThreads), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_load(const int64_t *idx, int32_t T, int32_t K, int32_t E,
                               int32_t id_bits, int32_t *load, int32_t *status, hipStream_t s) {
-  hipLaunchKernelGGL(expert_load_kernel, dim3(1), dim3(kLayoutThreads), 0, s, idx, T * K, E,
-                     id_bits, load, status);
+  const int32_t n = T * K;
+  if (n <= kLoadPairsPerBlock) {  // one workgroup writes the result directly
+    hipLaunchKernelGGL(expert_load_kernel, dim3(1), dim3(kLayoutThreads), 0, s, idx, n, E,
+                       id_bits, load, status, kLoadPairsPerBlock, 0);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(load_zero_kernel, dim3(1), dim3(kLayoutThreads), 0, s, load, E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int blocks = (n + kLoadPairsPerBlock - 1) / kLoadPairsPerBlock;
+  hipLaunchKernelGGL(expert_load_kernel, dim3(blocks), dim3(kLayoutThreads), 0, s, idx, n, E,
+                     id_bits, load, status, kLoadPairsPerBlock, 1);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ __global__ __launch_bounds__(kLayoutThreads) void plan_replicas_kernel(
     int32_t E, int32_t R, int32_t C, const int32_t *__restrict__ load,
     int32_t *__restrict__ replica_count, int32_t *__restrict__ replica_phys,
     int32_t *__restrict__ phys_to_logical) {
-  __shared__ int32_t s_load[kMaxExperts];
+  __shared__ __align__(16) int32_t s_load[kMaxExperts];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kLayoutThreads) s_load[e] = load[e];
   __syncthreads();
@@ -29,7 +29,16 @@ __global__ __launch_bounds__(kLayoutThreads) void plan_replicas_kernel(
   if (e >= E) return;
   const int mine = s_load[e];
   int ahead = 0;
-  for (int f = 0; f < E; ++f) {
+  // 16-byte LDS reads (broadcast: every thread reads the same address)
+  const int E4 = E & ~3;
+  for (int f = 0; f < E4; f += 4) {
+    const int4 q = *reinterpret_cast<const int4 *>(&s_load[f]);
+    ahead += (q.x > mine) || (q.x == mine && f < e);
+    ahead += (q.y > mine) || (q.y == mine && f + 1 < e);
+    ahead += (q.z > mine) || (q.z == mine && f + 2 < e);
+    ahead += (q.w > mine) || (q.w == mine && f + 3 < e);
+  }
+  for (int f = E4; f < E; ++f) {
     const int lf = s_load[f];
     ahead += (lf > mine) || (lf == mine && f < e);
   }

@@ -414,3 +414,47 @@ def test_layout_dispatch_small_receive_buffer(capi, orc):
     rref, st = orc.dispatch(w.x, ref["slot"], 100, fill=SENTINEL)
     assert st == 4 and got["status"] == 4
     assert np.array_equal(np16(recv_t), rref)
+
+
+def test_graph_replays_match_eager(capi, orc):
+    """The standard step captured in a HIP graph: every replay, with eager
+    work and synchronisation between replays, reproduces the eager outputs
+    (layout arrays, receive rows, combine) bit for bit."""
+    w = mi.config_c2()
+    _announce("graph capture of layout_dispatch + combine, 4 replays")
+    shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
+    idx, x, wt = to_dev(w.topk_idx), to_dev(w.x), to_dev(w.topk_weights)
+    lay = capi.LayoutBuffers.empty(shape, dev())
+    rows = capi.moe_recv_rows_worst(shape)
+    recv = torch.zeros(rows, w.H, dtype=torch.int16, device=dev())
+    out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
+    stream = torch.cuda.Stream()
+
+    def step():
+        capi.moe_layout_dispatch(shape, idx, lay, x, recv, rows, stream=stream)
+        capi.moe_combine(shape, recv, rows, lay.slot, wt, out, None, lay.status, stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (lay.count, lay.offset, lay.slot, lay.row_src, lay.rank_token_count,
+                               lay.is_token_in_rank, recv, out)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for rep in range(4):
+        for t in (lay.count, lay.offset, lay.slot, out):
+            t.fill_(-3)
+        recv.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (lay.count, lay.offset, lay.slot, lay.row_src, lay.rank_token_count,
+               lay.is_token_in_rank, recv, out)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        junk = torch.randn(1 << 20, device=dev()).sum()  # eager work between replays
+        assert torch.isfinite(junk)
+    ref_lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+    assert np.array_equal(lay.slot.cpu().numpy().reshape(w.T, w.K), ref_lay["slot"])
+    assert int(lay.status.item()) == 0
