@@ -28,11 +28,15 @@ ST_LL_OVERFLOW = 2
 ST_BAD_SLOT = 4
 ST_BAD_REPLICA = 8
 
+FP8_ROUND_SCALE = 1
+FP8_UE8M0 = 2
+FP8_GROUP = 128
+
 
 def build(out: str = LIB, mutant: Optional[int] = None) -> str:
     """Compile oracle.c into a shared library (optionally with a planted mutant)."""
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-Werror", "-o", out + ".tmp", SRC]
+           "-Wall", "-Wextra", "-Werror", "-o", out + ".tmp", SRC, "-lm"]
     if mutant is not None:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     subprocess.run(cmd, check=True)
@@ -70,6 +74,14 @@ class Oracle:
         lib.oracle_combine_f32.argtypes = [_I64, _I32, _I32, _P, _I64, _P, _P, _P, _P, _P]
         lib.oracle_plan_replicas.argtypes = [_I32, _I32, _I32, _P, _P, _P, _P]
         lib.oracle_reroute.argtypes = [_I64, _I32, _I32, _P, _P, _P, _I32, _P, _P]
+        lib.oracle_e4m3_value.argtypes = [C.c_uint8]
+        lib.oracle_e4m3_value.restype = C.c_double
+        lib.oracle_e4m3_from_f32.argtypes = [_P, _P, _I64]
+        lib.oracle_quantize_fp8.argtypes = [_I64, _I32, _P, _I32, _P, _P, _P]
+        lib.oracle_ll_dispatch_fp8.argtypes = [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
+                                               _P, _P, _P, _P, _P, _P]
+        lib.oracle_quantize_fp8.restype = C.c_int
+        lib.oracle_ll_dispatch_fp8.restype = C.c_int
         for f in ("oracle_layout", "oracle_ll_layout", "oracle_expert_load", "oracle_dispatch",
                   "oracle_combine_f64", "oracle_combine_f32", "oracle_plan_replicas",
                   "oracle_reroute"):
@@ -171,6 +183,68 @@ class Oracle:
                                         _ptr(o16), _ptr(status))
             return dict(out_f32=o32, out_bf16=o16, status=int(status[0]))
         raise ValueError(acc)
+
+    # -- FP8 ----------------------------------------------------------------
+    def e4m3_value(self, codes: np.ndarray) -> np.ndarray:
+        """Values (float64) of E4M3 codes; NaN for the two NaN codes."""
+        codes = np.asarray(codes, dtype=np.uint8)
+        return np.array([self.lib.oracle_e4m3_value(int(c)) for c in codes.ravel()],
+                        np.float64).reshape(codes.shape)
+
+    def e4m3_from_f32(self, v: np.ndarray) -> np.ndarray:
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        out = np.empty(v.shape, np.uint8)
+        self.lib.oracle_e4m3_from_f32(_ptr(v), _ptr(out), v.size)
+        return out
+
+    def quantize_fp8(self, x: np.ndarray, flags: int = 0) -> dict:
+        """Per-token E4M3 cast with one scale per 128 channels (see oracle.c)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        T, H = x.shape
+        G = H // FP8_GROUP
+        q = np.empty((T, H), np.uint8)
+        scale = np.empty((T, G), np.float32)
+        ue = np.empty((T, max(G // 4, 1)), np.int32) if flags & FP8_UE8M0 else None
+        rc = self.lib.oracle_quantize_fp8(T, H, _ptr(x), flags, _ptr(q), _ptr(scale), _ptr(ue))
+        if rc != 0:
+            raise ValueError(f"oracle_quantize_fp8 rejected its arguments ({rc})")
+        return dict(q=q, scale=scale, ue8m0=ue)
+
+    def ll_dispatch_fp8(self, qz: dict, slot: np.ndarray, E: int, R: int, M: int, flags: int = 0,
+                        fill_q: int = 0, fill_scale: float = 0.0, fill_ue: int = 0) -> dict:
+        """Scatter quantized rows and their column-major scales to the
+        low-latency padded layout; untouched entries keep the fill values."""
+        q, scale, ue = qz["q"], qz["scale"], qz["ue8m0"]
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        T, H = q.shape
+        K = slot.shape[1]
+        G = H // FP8_GROUP
+        rows = E * R * M
+        recv_q = np.full((rows, H), fill_q, np.uint8)
+        recv_s = np.full((E, G, R * M), fill_scale, np.float32)
+        recv_u = np.full((E, max(G // 4, 1), R * M), fill_ue, np.int32) \
+            if flags & FP8_UE8M0 else None
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_ll_dispatch_fp8(T, H, K, E, R, M, flags, _ptr(slot), _ptr(q),
+                                             _ptr(scale), _ptr(ue), _ptr(recv_q), _ptr(recv_s),
+                                             _ptr(recv_u), _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle_ll_dispatch_fp8 rejected its arguments ({rc})")
+        return dict(recv_q=recv_q, recv_scale=recv_s, recv_ue8m0=recv_u, status=int(status[0]))
+
+    def dispatch_fp8_tuple(self, q: np.ndarray, scale: np.ndarray, slot: np.ndarray, rows: int,
+                           fill16: int = 0) -> tuple:
+        """Buffer.dispatch with x = (E4M3 rows, float scales): both members of
+        the tuple are copied row by row to the pair's slot -- the plain row
+        copy, applied to the code bytes and to the scale words (viewed as
+        16-bit units). Untouched rows hold the 16-bit pattern fill16."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        T, H = q.shape
+        G = scale.shape[1]
+        rq, st1 = self.dispatch(q.view(np.uint16), slot, rows, fill=fill16)
+        rs, st2 = self.dispatch(scale.view(np.uint16), slot, rows, fill=fill16)
+        return rq.view(np.uint8).reshape(rows, H), rs.view(np.float32).reshape(rows, G), st1 | st2
 
     # -- replicas -----------------------------------------------------------
     def plan_replicas(self, load: np.ndarray, R: int, C_: int) -> dict:

@@ -27,7 +27,11 @@
  *   - low-latency row of the j-th pair of expert e sent by rank s is
  *     (e*R + s)*M + j; pairs with j >= M are dropped and set status bit 2;
  *   - replica plan: the C most loaded experts (ties -> lower id) get one extra
- *     physical replica; a pair of token t uses replica (t mod count).
+ *     physical replica; a pair of token t uses replica (t mod count);
+ *   - FP8: one scale per 128 channels, max(amax, 1e-4) / 448; codes are the
+ *     nearest E4M3 of x / scale (ties to even, saturating at 448, sign kept);
+ *     round_scale rounds the scale up to a power of two; UE8M0 packs group
+ *     4w+b into byte b of word w; low-latency scales are stored [E][G][R*M].
  *
  * Arithmetic: combine is provided twice -- in double (the exact definition up
  * to rounding of a K-term sum), and in float with every product and every sum
@@ -38,6 +42,7 @@
  * suite uses those builds to show that its pins catch each of them. A normal
  * build has ORACLE_MUTANT undefined.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -419,6 +424,193 @@ int oracle_reroute(int64_t T, int32_t K, int32_t E, const int64_t *idx,
                 continue;
             }
             phys_idx[p] = ph;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP8 rows with per-128-channel scales ([P1] Buffer.low_latency_dispatch: */
+/* use_fp8, round_scale, use_ue8m0, and the returned scale tensors;     */
+/* Buffer.dispatch: x given as an (e4m3 rows, float scales) tuple)     */
+/* ------------------------------------------------------------------ */
+
+#define FP8_GROUP 128       /* channels per scale ([P1]: hidden // 128 scales) */
+#define FP8_ROUND_SCALE 1   /* scales rounded up to a power of two */
+#define FP8_UE8M0 2         /* scales also emitted as packed exponent bytes */
+#define FP8_AMAX_FLOOR 1e-4f /* reading: a group's amax is taken as at least this */
+
+/* Value of an E4M3 ("fn" variant) code, from the format's definition (OCP 8-bit
+ * floating point specification, E4M3): 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6; the two
+ * codes S.1111.111 are NaN and there is no infinity, so 448 is the largest
+ * finite magnitude. */
+double oracle_e4m3_value(uint8_t c) {
+    int s = c >> 7, ef = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ef == 15 && m == 7) return NAN;
+    if (ef == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, ef - 7);
+    return s ? -v : v;
+}
+
+/* Magnitudes of codes 0x00 .. 0x7E; the codes are ordered by magnitude. */
+static double g_e4m3_mag[127];
+static int g_e4m3_ready;
+static void e4m3_table(void) {
+    if (g_e4m3_ready) return;
+    for (int c = 0; c < 127; ++c) g_e4m3_mag[c] = oracle_e4m3_value((uint8_t)c);
+    g_e4m3_ready = 1;
+}
+
+/* Nearest E4M3 code to a finite float, ties to the even code (even mantissa),
+ * magnitudes of 448 and above saturate to 448 (reading: the format has no
+ * infinity). The sign is kept, also for results that round to zero. */
+static uint8_t e4m3_from_f32(float v) {
+    e4m3_table();
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    /* lo = largest code whose magnitude is <= a (binary search) */
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (g_e4m3_mag[mid] <= a) lo = mid; else hi = mid - 1;
+    }
+    if (g_e4m3_mag[lo] == a) return sign | (uint8_t)lo;
+    double dlo = a - g_e4m3_mag[lo], dhi = g_e4m3_mag[lo + 1] - a;
+    int c;
+    if (dlo < dhi)
+        c = lo;
+    else if (dhi < dlo)
+        c = lo + 1;
+    else
+#if ORACLE_MUTANT == 10
+        c = lo + 1; /* mutant: ties away from zero */
+#else
+        c = (lo & 1) ? lo + 1 : lo;
+#endif
+    return sign | (uint8_t)c;
+}
+
+void oracle_e4m3_from_f32(const float *in, uint8_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_from_f32(in[i]);
+}
+
+/* Smallest power of two >= s, for a positive normal float s (round_scale). */
+static float pow2_ceil(float s) {
+    int e;
+    float m = frexpf(s, &e); /* s = m * 2^e, m in [0.5, 1) */
+#if ORACLE_MUTANT == 12
+    (void)m;
+    return ldexpf(1.0f, e - 1); /* mutant: rounds the scale down */
+#else
+    return m == 0.5f ? s : ldexpf(1.0f, e);
+#endif
+}
+
+/* Per-token cast of bf16 rows to E4M3 with one float scale per 128 channels:
+ *   amax  = max |x| over the group (at least FP8_AMAX_FLOOR),
+ *   scale = amax / 448 in float (FP8_ROUND_SCALE: then rounded up to a power
+ *           of two),
+ *   code  = nearest E4M3 (ties to even) of x / scale, divided in float,
+ * so the group's largest magnitude maps to the largest finite code and
+ * x ~= value(code) * scale. q is [T, H], scale [T, H/128] row-major. With
+ * FP8_UE8M0 (needs FP8_ROUND_SCALE and H % 512 == 0) ue8m0 [T, H/512] also
+ * receives the scales' biased exponents (scale = 2^(byte - 127)), four groups
+ * per int32, group 4w + b in byte b (bits 8b .. 8b+7) of word w. */
+int oracle_quantize_fp8(int64_t T, int32_t H, const uint16_t *x, int32_t flags, uint8_t *q,
+                        float *scale, int32_t *ue8m0) {
+    if (T < 0 || H < FP8_GROUP || H % FP8_GROUP != 0) return -2;
+    if ((flags & FP8_UE8M0) && (!(flags & FP8_ROUND_SCALE) || H % (4 * FP8_GROUP) != 0 || !ue8m0))
+        return -2;
+    const int32_t G = H / FP8_GROUP;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *xr = x + t * (int64_t)H;
+#if ORACLE_MUTANT == 15
+        float row_amax = 0.0f; /* mutant: one amax for the whole row */
+        for (int32_t h = 0; h < H; ++h) {
+            float a = fabsf(bf16_to_f32(xr[h]));
+            if (a > row_amax) row_amax = a;
+        }
+#endif
+        for (int32_t g = 0; g < G; ++g) {
+            float amax = 0.0f;
+            for (int32_t c = 0; c < FP8_GROUP; ++c) {
+                float a = fabsf(bf16_to_f32(xr[g * FP8_GROUP + c]));
+                if (a > amax) amax = a;
+            }
+#if ORACLE_MUTANT == 15
+            amax = row_amax;
+#endif
+            if (amax < FP8_AMAX_FLOOR) amax = FP8_AMAX_FLOOR;
+#if ORACLE_MUTANT == 11
+            float s = amax / 240.0f; /* mutant: the other FP8 variant's maximum */
+#else
+            float s = amax / 448.0f;
+#endif
+            if (flags & FP8_ROUND_SCALE) s = pow2_ceil(s);
+            scale[t * G + g] = s;
+            for (int32_t c = 0; c < FP8_GROUP; ++c) {
+                float v = bf16_to_f32(xr[g * FP8_GROUP + c]) / s;
+                q[t * (int64_t)H + g * FP8_GROUP + c] = e4m3_from_f32(v);
+            }
+            if (flags & FP8_UE8M0) {
+                int e;
+                (void)frexpf(s, &e); /* s = 0.5 * 2^e exactly */
+                uint32_t byte = (uint32_t)(e - 1 + 127);
+                int32_t w = g / 4;
+#if ORACLE_MUTANT == 14
+                int32_t b = 3 - g % 4; /* mutant: bytes packed high to low */
+#else
+                int32_t b = g % 4;
+#endif
+                uint32_t *word = (uint32_t *)&ue8m0[t * (G / 4) + w];
+                if (g % 4 == 0) *word = 0;
+                *word |= byte << (8 * b);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Low-latency dispatch with the FP8 cast ([P1] Buffer.low_latency_dispatch,
+ * use_fp8): every valid pair's row of codes goes to its padded row
+ * slot = (e*R + s)*M + j of recv_q [E*R*M, H], and the token's scales go to
+ * the same row of the scale tensor, whose last two dimensions are
+ * column-major ([P1] returns): recv_scale is stored as [E][H/128][R*M], so
+ * the scale of group g for row i of expert e's R*M rows sits at
+ * (e*(H/128) + g)*(R*M) + i; with FP8_UE8M0 the packed words go to
+ * recv_ue8m0 stored as [E][H/512][R*M] the same way. Rows no pair maps to
+ * are left untouched. */
+int oracle_ll_dispatch_fp8(int64_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t M,
+                           int32_t flags, const int32_t *slot, const uint8_t *q,
+                           const float *scale, const int32_t *ue8m0, uint8_t *recv_q,
+                           float *recv_scale, int32_t *recv_ue8m0, int32_t *status) {
+    if (T < 0 || H % FP8_GROUP != 0 || E < 1 || R < 1 || M < 1) return -2;
+    const int32_t G = H / FP8_GROUP, W = G / 4;
+    const int64_t RM = (int64_t)R * M, rows = (int64_t)E * RM;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int32_t r = slot[t * K + k];
+            if (r == -1) continue;
+            if (r < -1 || r >= rows) {
+                if (status) *status |= ST_BAD_SLOT;
+                continue;
+            }
+            int64_t e = r / RM, i = r % RM;
+            memcpy(recv_q + (int64_t)r * H, q + t * (int64_t)H, (size_t)H);
+            for (int32_t g = 0; g < G; ++g) {
+#if ORACLE_MUTANT == 13
+                recv_scale[(int64_t)r * G + g] = scale[t * G + g]; /* mutant: row-major */
+#else
+                recv_scale[(e * G + g) * RM + i] = scale[t * G + g];
+#endif
+            }
+            if ((flags & FP8_UE8M0) && recv_ue8m0)
+                for (int32_t w = 0; w < W; ++w) recv_ue8m0[(e * W + w) * RM + i] = ue8m0[t * W + w];
         }
     }
     return 0;

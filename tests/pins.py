@@ -12,7 +12,10 @@ mistake) and raises ``AssertionError`` when the oracle disagrees with
   softmax weights give x back after bf16 rounding, K=1 is a permutation
   round trip),
 * the float error bound between the f32 and f64 combine sums,
-* torch's CPU float->bf16 cast,
+* torch's CPU float->bf16 cast, and its float->float8_e4m3fn cast and
+  float8 values,
+* the hand-worked FP8 example in ``golden/fp8_hand_worked.json`` and the
+  E4M3 rounding error bound of the per-128-channel cast,
 * invariants (counts sum to the valid pairs; every pair has exactly one row;
   rows inside an expert increase with the pair index; offsets are multiples
   of the alignment; the replica tables are a bijection onto physical slots;
@@ -320,6 +323,234 @@ def check_ll_matches_contiguous(orc, w):
     assert np.all(j < ll["recv_count"][e])
 
 
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3 rows, one scale per 128 channels)
+# ---------------------------------------------------------------------------
+FP8_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                          "fp8_hand_worked.json")
+ROUND, UE8M0 = 1, 2
+
+
+def _fp8_golden_x(g):
+    x = np.zeros((1, g["H"]), np.float32)
+    for c, v in g["x"]:
+        x[0, c] = v
+    xb = mi.to_bf16_bits(x)
+    # every listed value is exactly representable in bf16
+    assert np.array_equal(mi.bf16_bits_to_f32(xb), x)
+    return xb
+
+
+def check_fp8_golden(orc):
+    with open(FP8_GOLDEN) as f:
+        g = json.load(f)
+    xb = _fp8_golden_x(g)
+    H = g["H"]
+    for name, flags in (("plain", 0), ("round_scale", ROUND), ("round_scale", ROUND | UE8M0)):
+        qz = orc.quantize_fp8(xb, flags)
+        want = np.zeros(H, np.uint8)
+        for c, code in g["codes"][name]:
+            want[c] = code
+        assert qz["q"][0].tolist() == want.tolist(), (name, np.nonzero(qz["q"][0] != want))
+        sc = qz["scale"][0]
+        if name == "plain":
+            for gi, v in g["scale_exact"]["plain"].items():
+                assert float(sc[int(gi)]) == v
+            for gi, v in g["scale_approx"]["plain"].items():
+                assert abs(float(sc[int(gi)]) - v) <= 1e-6 * v
+        else:
+            assert sc.tolist() == g["scale_exact"]["round_scale"]
+        if flags & UE8M0:
+            assert int(qz["ue8m0"][0, 0]) == g["ue8m0_word"]
+    ll = g["ll"]
+    idx = np.array(ll["topk_idx"], np.int64)
+    lay = orc.ll_layout(idx, ll["E"], ll["R"], ll["M"], ll["src"])
+    assert lay["slot"].tolist() == ll["slot"]
+    qz = orc.quantize_fp8(xb, ROUND | UE8M0)
+    out = orc.ll_dispatch_fp8(qz, lay["slot"], ll["E"], ll["R"], ll["M"], ROUND | UE8M0,
+                              fill_q=0xAB, fill_scale=-1.0, fill_ue=-1)
+    flat_s = out["recv_scale"].ravel()
+    flat_u = out["recv_ue8m0"].ravel()
+    touched_s, touched_u = set(), set()
+    for row, sidx in ll["scale_index"].items():
+        assert out["recv_q"][int(row)].tolist() == qz["q"][0].tolist()
+        assert flat_s[sidx].tolist() == qz["scale"][0].tolist()
+        assert int(flat_u[ll["ue8m0_index"][row]]) == g["ue8m0_word"]
+        touched_s.update(sidx)
+        touched_u.add(ll["ue8m0_index"][row])
+    others = [i for i in range(flat_s.size) if i not in touched_s]
+    assert np.all(flat_s[others] == -1.0)
+    assert np.all(np.delete(flat_u, sorted(touched_u)) == -1)
+    rows_used = {int(r) for r in ll["scale_index"]}
+    for r in range(out["recv_q"].shape[0]):
+        if r not in rows_used:
+            assert np.all(out["recv_q"][r] == 0xAB)
+
+
+def _torch_e4m3(v: np.ndarray) -> np.ndarray:
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values() -> np.ndarray:
+    import torch
+
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(
+        torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+
+
+def check_e4m3_values_vs_torch(orc):
+    """Code -> value for all 256 codes, against torch's float8_e4m3fn."""
+    mine = orc.e4m3_value(np.arange(256, dtype=np.uint8))
+    ref = _torch_e4m3_values()
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def check_e4m3_vs_torch(orc, n: int = 1 << 20, seed: int = 7):
+    """float -> E4M3 against torch's cast (round to nearest even) wherever the
+    two readings agree (|v| <= 464: torch turns larger magnitudes into NaN,
+    the reading here saturates them to 448, checked as a closed form)."""
+    rng = np.random.default_rng(seed)
+    vals = _torch_e4m3_values()
+    fin = np.sort(np.unique(np.abs(vals[~np.isnan(vals)])))
+    mids = (fin[:-1] + fin[1:]) / 2  # exact ties, as float32 (all representable)
+    pats = np.arange(1 << 16, dtype=np.uint32) << 16
+    allbf = pats.view(np.float32)
+    allbf = allbf[np.isfinite(allbf) & (np.abs(allbf) <= 464)]
+    mags = np.exp2(rng.uniform(-14, 9, n)).astype(np.float32)
+    sgn = np.where(rng.random(n) < 0.5, -1, 1).astype(np.float32)
+    rnd = mags * sgn
+    rnd = rnd[np.abs(rnd) <= 464]
+    near = np.concatenate([mids, -mids]).astype(np.float32)
+    near = np.concatenate([near, np.nextafter(near, np.float32(np.inf)),
+                           np.nextafter(near, np.float32(-np.inf))])
+    v = np.concatenate([allbf, rnd, near, np.array([0.0, -0.0, 448, -448, 464, -464],
+                                                    np.float32)])
+    v = v[np.abs(v) <= 464]
+    got = orc.e4m3_from_f32(v)
+    ref = _torch_e4m3(v)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (v[bad[:5]], got[bad[:5]], ref[bad[:5]])
+    big = np.array([464.5, 480, 1e4, 3e38, -465, -1e30], np.float32)
+    want = np.where(np.signbit(big), 0xFE, 0x7E).astype(np.uint8)
+    assert orc.e4m3_from_f32(big).tolist() == want.tolist()
+
+
+def _e4m3_half_ulp(a: np.ndarray) -> np.ndarray:
+    """Half the E4M3 spacing at magnitude a (2^-10 in the subnormal range,
+    2^(floor(log2 a) - 4) among normals)."""
+    a = np.maximum(np.abs(a), 2.0 ** -6)
+    return np.exp2(np.floor(np.log2(a)) - 4)
+
+
+def check_quantize_properties(orc, xb: np.ndarray, flags: int):
+    """Closed-form properties of the per-128-channel cast:
+    * the scale is amax/448 to float rounding (round_scale: the smallest power
+      of two >= that value), with amax floored at 1e-4;
+    * without round_scale the group's largest magnitude gets the code for 448;
+    * every code is within half an E4M3 spacing of x/scale (plus the float
+      rounding of the division);
+    * UE8M0 bytes are the scales' exponents, group 4w+b in byte b of word w."""
+    qz = orc.quantize_fp8(xb, flags)
+    T, H = xb.shape
+    G = H // 128
+    x = mi.bf16_bits_to_f32(xb).astype(np.float64).reshape(T, G, 128)
+    s = qz["scale"].astype(np.float64)
+    amax = np.maximum(np.abs(x).max(axis=2), np.float64(np.float32(1e-4)))
+    ideal = amax / 448.0
+    if flags & ROUND:
+        m, e = np.frexp(s)
+        assert np.all(m == 0.5), "round_scale scales must be powers of two"
+        lo = ideal * (1 - 2.0 ** -23)
+        assert np.all(s >= lo) and np.all(s / 2 < ideal * (1 + 2.0 ** -23))
+    else:
+        assert np.all(np.abs(s - ideal) <= ideal * 2.0 ** -24 * 1.0001)
+    vals = orc.e4m3_value(np.arange(256, dtype=np.uint8))
+    q = qz["q"].reshape(T, G, 128)
+    dq = vals[q]
+    assert not np.any(np.isnan(dq))
+    r = x / s[:, :, None]
+    tol = _e4m3_half_ulp(r) + np.abs(r) * 2.0 ** -23
+    err = np.abs(dq - r)
+    assert np.all(err <= tol), float((err - tol).max())
+    # signs are kept, zeros included
+    assert np.array_equal(np.signbit(dq), np.signbit(x))
+    mag = np.abs(dq).max(axis=2)
+    nonzero = np.abs(x).max(axis=2) >= np.float32(1e-4)
+    if not (flags & ROUND):
+        assert np.all(mag[nonzero] == 448.0)
+    else:
+        assert np.all((mag[nonzero] >= 224.0) & (mag[nonzero] <= 448.0))
+    if flags & UE8M0:
+        words = qz["ue8m0"].astype(np.int64) & 0xFFFFFFFF
+        for b in range(4):
+            byte = (words >> (8 * b)) & 0xFF
+            assert np.array_equal(np.exp2(byte.astype(np.float64) - 127), s[:, b::4])
+
+
+def check_fp8_cast_on_inputs(orc, n: int = 6, seed: int = 8):
+    """check_quantize_properties on random bf16 rows with a wide dynamic range,
+    all-zero groups and tiny groups."""
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        T, H = int(rng.integers(1, 9)), 512 * int(rng.integers(1, 4))
+        x = rng.standard_normal((T, H)).astype(np.float32)
+        x *= np.exp2(rng.integers(-20, 12, (T, H // 128, 1))).astype(np.float32).repeat(
+            128, axis=2).reshape(T, H)
+        x[:, 128:256] = 0.0
+        if H >= 512:
+            x[:, 384:512] *= np.float32(1e-7)
+        xb = mi.to_bf16_bits(x)
+        for flags in (0, ROUND, ROUND | UE8M0):
+            check_quantize_properties(orc, xb, flags)
+
+
+def check_ll_fp8_dispatch(orc, n: int = 8, seed: int = 9):
+    """Low-latency FP8 placement against numpy: every valid pair's row of codes
+    is the token's codes, and reading the scale tensor as [E, R*M, G] (numpy
+    transpose of the column-major storage) gives the token's scales on that
+    row; everything else keeps its fill."""
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        R = int(rng.choice([1, 2, 4]))
+        E = R * int(rng.integers(1, 5))
+        K = int(rng.integers(1, 5))
+        M = int(rng.integers(1, 9))
+        T = int(rng.integers(0, M + 1))
+        w = mi.random_case(500 + i, T, 512, E, R, K, neg_frac=0.2, dup_frac=0.2)
+        src = int(rng.integers(0, R))
+        lay = orc.ll_layout(w.topk_idx, E, R, M, src)
+        for flags in (0, ROUND | UE8M0):
+            qz = orc.quantize_fp8(w.x, flags)
+            out = orc.ll_dispatch_fp8(qz, lay["slot"], E, R, M, flags, fill_q=0xCD,
+                                      fill_scale=7.0, fill_ue=5)
+            rows = E * R * M
+            rs = out["recv_scale"].transpose(0, 2, 1).reshape(rows, 4)
+            ru = out["recv_ue8m0"].transpose(0, 2, 1).reshape(rows, 1) if flags & UE8M0 \
+                else None
+            used = np.zeros(rows, bool)
+            for t in range(T):
+                for k in range(K):
+                    r = lay["slot"][t, k]
+                    if r < 0:
+                        continue
+                    used[r] = True
+                    assert np.array_equal(out["recv_q"][r], qz["q"][t])
+                    assert np.array_equal(rs[r], qz["scale"][t])
+                    if ru is not None:
+                        assert np.array_equal(ru[r], qz["ue8m0"][t])
+            assert np.all(out["recv_q"][~used] == 0xCD)
+            assert np.all(rs[~used] == 7.0)
+            if ru is not None:
+                assert np.all(ru[~used] == 5)
+
+
 ALL_SMALL_CHECKS = (
     check_golden,
     check_layout_vs_bruteforce,
@@ -328,4 +559,9 @@ ALL_SMALL_CHECKS = (
     check_combine_dense,
     check_combine_closed_forms,
     check_combine_f32_bound,
+    check_fp8_golden,
+    check_e4m3_values_vs_torch,
+    lambda o: check_e4m3_vs_torch(o, n=1 << 14),
+    lambda o: check_fp8_cast_on_inputs(o, n=2),
+    lambda o: check_ll_fp8_dispatch(o, n=3),
 )

@@ -17,6 +17,12 @@ MUTANTS = {
     7: "replicas planned for the coldest experts",
     8: "replica chosen by k instead of by token",
     9: "bf16 rounding ties away from even",
+    10: "E4M3 rounding ties away from zero",
+    11: "FP8 scale from the FNUZ maximum 240",
+    12: "round_scale rounds the scale down",
+    13: "low-latency FP8 scales stored row-major",
+    14: "UE8M0 bytes packed high to low",
+    15: "FP8 amax over the whole row",
 }
 
 

@@ -88,3 +88,48 @@ def test_empty_batch(orc):
     lay = orc.layout(idx, 256, 8, 4)
     assert lay["rows"] == 0 and lay["count"].sum() == 0 and lay["offset"].sum() == 0
     assert lay["rank_token_count"].sum() == 0
+
+
+def test_fp8_golden_hand_worked(orc):
+    pins.check_fp8_golden(orc)
+
+
+def test_e4m3_values_match_torch(orc):
+    pins.check_e4m3_values_vs_torch(orc)
+
+
+def test_e4m3_rounding_matches_torch(orc):
+    pins.check_e4m3_vs_torch(orc)
+
+
+def test_fp8_cast_closed_forms(orc):
+    pins.check_fp8_cast_on_inputs(orc, n=8)
+
+
+@pytest.mark.parametrize("flags", [0, 1, 3])
+def test_fp8_cast_at_low_latency_config(orc, flags):
+    w = mi.config_c3(128)
+    pins.check_quantize_properties(orc, w.x, flags)
+
+
+def test_ll_fp8_dispatch_placement(orc):
+    pins.check_ll_fp8_dispatch(orc, n=12)
+
+
+def test_fp8_tuple_dispatch_is_row_copy(orc):
+    """Buffer.dispatch with an (E4M3, scales) tuple: codes and scales land on
+    the pair's row, bit for bit, by numpy indexing."""
+    w = mi.config_c1()
+    qz = orc.quantize_fp8(np.repeat(w.x, 1, axis=1)[:, :256], 0)
+    lay = orc.layout(w.topk_idx, w.E, w.R, 4)
+    rq, rs, st = orc.dispatch_fp8_tuple(qz["q"], qz["scale"], lay["slot"], lay["rows"],
+                                        fill16=0x7E57)
+    assert st == 0
+    used = np.zeros(lay["rows"], bool)
+    for t in range(w.T):
+        for k in range(w.K):
+            r = lay["slot"][t, k]
+            used[r] = True
+            assert np.array_equal(rq[r], qz["q"][t]) and np.array_equal(rs[r], qz["scale"][t])
+    assert np.all(rq[~used] == 0x57) or np.all(rq[~used].view(np.uint16) == 0x7E57)
+    assert np.all(rs[~used].view(np.uint32) == 0x7E577E57)
