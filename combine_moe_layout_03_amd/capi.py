@@ -20,10 +20,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
 
+MOE_ABI_VERSION = 2  # the version the binding is written against
+
 MOE_STATUS_BAD_EXPERT = 1
 MOE_STATUS_LL_OVERFLOW = 2
 MOE_STATUS_BAD_SLOT = 4
 MOE_STATUS_BAD_REPLICA = 8
+
+MOE_FP8_ROUND_SCALE = 1
+MOE_FP8_UE8M0 = 2
+FP8_GROUP = 128
 
 
 class MoeError(RuntimeError):
@@ -67,6 +73,11 @@ def _load():
         "moe_combine": (C.c_int, [P, P, I64, P, P, P, P, P, P]),
         "moe_plan_replicas": (C.c_int, [I32, I32, I32, P, P, P, P, P]),
         "moe_reroute": (C.c_int, [I32, I32, I32, P, P, P, I32, P, P, P]),
+        "moe_quantize_fp8": (C.c_int, [I32, I32, P, P, P, I32, P]),
+        "moe_ll_layout_dispatch_fp8": (C.c_int, [P, I32, I32, P, P, P, P, P, I64, I32, P, SZ,
+                                                 P]),
+        "moe_ll_dispatch_fp8": (C.c_int, [P, I32, P, P, P, P, I64, I32, P, P]),
+        "moe_dispatch_fp8": (C.c_int, [P, P, P, P, P, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -79,7 +90,9 @@ _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_recv_rows",
             "moe_layout_workspace_bytes", "moe_layout", "moe_ll_layout", "moe_layout_dispatch",
             "moe_ll_layout_dispatch", "moe_expert_load",
-            "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute")
+            "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
+            "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
+            "moe_dispatch_fp8")
 
 
 def lib():
@@ -89,6 +102,16 @@ def lib():
 # -- marshalling helpers -----------------------------------------------------
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8_CODES = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+
+
+def fp8_scale_cols(H: int, flags: int) -> int:
+    """Scale entries per row: one float per 128 channels, or one UE8M0 word per 512."""
+    return H // (4 * FP8_GROUP) if flags & MOE_FP8_UE8M0 else H // FP8_GROUP
+
+
+def _fp8_scale_dtypes(flags: int):
+    return (torch.int32,) if flags & MOE_FP8_UE8M0 else (torch.float32,)
 
 
 def _dev(t: Optional[torch.Tensor], name: str, dtypes, min_numel: int = 0, optional=False):
@@ -303,3 +326,56 @@ def moe_reroute(T: int, K: int, E: int, topk_idx: torch.Tensor, replica_count: t
         _dev(replica_phys, "replica_phys", i32, 2 * E), int(E_phys),
         _dev(phys_idx, "phys_idx", (torch.int64,), T * K),
         _dev(status, "status", i32, 1, optional=True), _stream(stream)))
+
+
+def moe_quantize_fp8(T: int, H: int, x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                     flags: int = 0, stream=None) -> int:
+    return _check("moe_quantize_fp8", _lib.moe_quantize_fp8(
+        int(T), int(H), _dev(x, "x", _BF16_LIKE, T * H), _dev(q, "q", _FP8_CODES, T * H),
+        _dev(scale, "scale", _fp8_scale_dtypes(flags), T * fp8_scale_cols(H, flags)),
+        int(flags), _stream(stream)))
+
+
+def moe_ll_layout_dispatch_fp8(shape: moe_shape, M: int, src_rank: int, topk_idx: torch.Tensor,
+                               out: LayoutBuffers, x: torch.Tensor, recv_q: torch.Tensor,
+                               recv_scale: torch.Tensor, recv_rows: int, flags: int = 0,
+                               ws: Optional[torch.Tensor] = None, stream=None) -> int:
+    T, H, K, E, R = shape.T, shape.H, shape.K, shape.E, shape.R
+    idx = _dev(topk_idx, "topk_idx", (torch.int64,), T * K)
+    st = out._struct(shape, int(M))
+    wsp, wsn = _ws(ws, shape)
+    return _check("moe_ll_layout_dispatch_fp8", _lib.moe_ll_layout_dispatch_fp8(
+        C.byref(shape), int(M), int(src_rank), idx, C.byref(st), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
+        _dev(recv_scale, "recv_scale", _fp8_scale_dtypes(flags),
+             E * fp8_scale_cols(H, flags) * R * int(M) if recv_rows else 0),
+        int(recv_rows), int(flags), wsp, wsn, _stream(stream)))
+
+
+def moe_ll_dispatch_fp8(shape: moe_shape, M: int, x: torch.Tensor, slot: torch.Tensor,
+                        recv_q: torch.Tensor, recv_scale: torch.Tensor, recv_rows: int,
+                        flags: int = 0, status: Optional[torch.Tensor] = None,
+                        stream=None) -> int:
+    T, H, K, E, R = shape.T, shape.H, shape.K, shape.E, shape.R
+    return _check("moe_ll_dispatch_fp8", _lib.moe_ll_dispatch_fp8(
+        C.byref(shape), int(M), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(slot, "slot", (torch.int32,), T * K),
+        _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
+        _dev(recv_scale, "recv_scale", _fp8_scale_dtypes(flags),
+             E * fp8_scale_cols(H, flags) * R * int(M) if recv_rows else 0),
+        int(recv_rows), int(flags), _dev(status, "status", (torch.int32,), 1, optional=True),
+        _stream(stream)))
+
+
+def moe_dispatch_fp8(shape: moe_shape, x_q: torch.Tensor, x_scale: torch.Tensor,
+                     slot: torch.Tensor, recv_q: torch.Tensor, recv_scale: torch.Tensor,
+                     recv_rows: int, status: Optional[torch.Tensor] = None, stream=None) -> int:
+    T, H, K = shape.T, shape.H, shape.K
+    G = H // FP8_GROUP
+    return _check("moe_dispatch_fp8", _lib.moe_dispatch_fp8(
+        C.byref(shape), _dev(x_q, "x_q", _FP8_CODES, T * H),
+        _dev(x_scale, "x_scale", (torch.float32,), T * G),
+        _dev(slot, "slot", (torch.int32,), T * K),
+        _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
+        _dev(recv_scale, "recv_scale", (torch.float32,), int(recv_rows) * G), int(recv_rows),
+        _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstring>
 
+#include "fp8.hpp"
 #include "kernels.hpp"
 #include "moe_ep.h"
 
@@ -12,6 +13,12 @@
 namespace {
 
 using namespace moe;
+
+static_assert(MOE_FP8_ROUND_SCALE == kFp8RoundScale && MOE_FP8_UE8M0 == kFp8Ue8m0,
+              "FP8 flag values of the header and the kernels differ");
+static_assert(MOE_STATUS_BAD_EXPERT == kStBadExpert && MOE_STATUS_LL_OVERFLOW == kStOverflow &&
+                  MOE_STATUS_BAD_SLOT == kStBadSlot && MOE_STATUS_BAD_REPLICA == kStBadReplica,
+              "status bits of the header and the kernels differ");
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];  // 0 = not checked yet, 1 = gfx950, 2 = other
@@ -37,6 +44,17 @@ int bits_for(int n) {  // bits needed to tell apart the values 0 .. n-1
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// FP8 flag set and the hidden sizes it needs: scales cover 128 channels, and
+// UE8M0 words pack four of them (and require power-of-two scales).
+int check_fp8(int32_t H, int32_t flags) {
+  if (flags != 0 && flags != MOE_FP8_ROUND_SCALE && flags != (MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0))
+    return MOE_ERR_FLAGS;
+  if (H % kFp8Group != 0) return MOE_ERR_SHAPE;
+  if ((flags & MOE_FP8_UE8M0) && H % (4 * kFp8Group) != 0) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
 
 // Shape checks shared by every call that takes a moe_shape.
 int check_shape(const moe_shape *s, bool need_h) {
@@ -115,7 +133,8 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
 }
 
 hipError_t launch_layout(const LayoutParams &p, hipStream_t stream) {
-  if (count_layout_fits(p, 0, false)) return launch_count_layout(p, nullptr, nullptr, 0, 0, stream);
+  if (count_layout_fits(p, 0, false))
+    return launch_count_layout(p, nullptr, nullptr, 0, 0, nullptr, stream);
   return p.nblocks == 1 && p.ws_hist == nullptr ? launch_layout_one_block(p, stream)
                                                  : launch_layout_multi_block(p, stream);
 }
@@ -130,27 +149,40 @@ int layout_common(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   return launch_layout(p, stream) == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
+// Layout + dispatch: bf16 rows into recv, or (fp8 != null, low latency) the
+// E4M3 cast into fp8->q / fp8->scale.
 int layout_dispatch_common(const moe_shape *s, int mode, int32_t M, int32_t src,
                            const int64_t *idx, const moe_layout_t *out, const uint16_t *x,
-                           uint16_t *recv, int64_t rows, void *ws, size_t ws_bytes,
-                           hipStream_t stream) {
+                           uint16_t *recv, int64_t rows, const Fp8Out *fp8, void *ws,
+                           size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(s, true);
   if (rc) return rc;
   LayoutParams p;
   rc = layout_params(s, mode, M, src, idx, out, ws, ws_bytes, &p);
   if (rc) return rc;
   if (rows < 0) return MOE_ERR_CAPACITY;
-  if (s->T > 0 && (!x || (!recv && rows > 0))) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(recv)) return MOE_ERR_ALIGN;
+  if (fp8) {
+    rc = check_fp8(s->H, fp8->flags);
+    if (rc) return rc;
+    if (rows > (int64_t)s->E * s->R * M) return MOE_ERR_CAPACITY;
+    if (s->T > 0 && (!x || (rows > 0 && (!fp8->q || !fp8->scale)))) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(fp8->q) || !aligned4(fp8->scale)) return MOE_ERR_ALIGN;
+  } else {
+    if (s->T > 0 && (!x || (!recv && rows > 0))) return MOE_ERR_NULL;
+    if (!aligned16(x) || !aligned16(recv)) return MOE_ERR_ALIGN;
+  }
   rc = check_device();
   if (rc) return rc;
   hipError_t err;
   if (count_layout_fits(p, s->H, true)) {
-    err = launch_count_layout(p, x, recv, rows, s->H, stream);
+    err = launch_count_layout(p, x, recv, rows, s->H, fp8, stream);
   } else {
     err = launch_layout(p, stream);
-    if (err == hipSuccess && s->T > 0)
-      err = launch_dispatch(x, p.slot, recv, s->T, s->K, s->H, rows, p.status, stream);
+    if (err == hipSuccess && s->T > 0) {
+      err = fp8 ? launch_ll_quant_dispatch(x, p.slot, *fp8, s->T, s->K, s->H, rows, p.status,
+                                           stream)
+                : launch_dispatch(x, p.slot, recv, s->T, s->K, s->H, rows, p.status, stream);
+    }
   }
   return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
@@ -171,6 +203,7 @@ MOE_API const char *moe_strerror(int code) {
     case MOE_ERR_LAUNCH: return "kernel launch failed";
     case MOE_ERR_ARCH: return "current device is not gfx950";
     case MOE_ERR_DEVICE: return "HIP runtime query failed";
+    case MOE_ERR_FLAGS: return "unsupported FP8 flag combination";
     default: return "unknown error code";
   }
 }
@@ -206,7 +239,7 @@ MOE_API int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx,
                                 int64_t recv_rows, void *ws, size_t ws_bytes,
                                 hipStream_t stream) {
   return layout_dispatch_common(shape, kModeContiguous, 0, 0, topk_idx, out, x, recv_x,
-                                recv_rows, ws, ws_bytes, stream);
+                                recv_rows, nullptr, ws, ws_bytes, stream);
 }
 
 MOE_API int moe_ll_layout_dispatch(const moe_shape *shape, int32_t M, int32_t src_rank,
@@ -214,7 +247,77 @@ MOE_API int moe_ll_layout_dispatch(const moe_shape *shape, int32_t M, int32_t sr
                                    const uint16_t *x, uint16_t *recv_x, int64_t recv_rows,
                                    void *ws, size_t ws_bytes, hipStream_t stream) {
   return layout_dispatch_common(shape, kModeLowLatency, M, src_rank, topk_idx, out, x, recv_x,
-                                recv_rows, ws, ws_bytes, stream);
+                                recv_rows, nullptr, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_ll_layout_dispatch_fp8(const moe_shape *shape, int32_t M, int32_t src_rank,
+                                       const int64_t *topk_idx, const moe_layout_t *out,
+                                       const uint16_t *x, uint8_t *recv_q, void *recv_scale,
+                                       int64_t recv_rows, int32_t flags, void *ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  if (!shape) return MOE_ERR_NULL;
+  // R*M is validated (E*R*M < 2^31) by the layout checks before any use
+  const int64_t rm = (int64_t)shape->R * (M > 0 ? M : 0);
+  Fp8Out o{flags, recv_q, recv_scale, (int32_t)(rm < (1ll << 31) ? rm : 0)};
+  return layout_dispatch_common(shape, kModeLowLatency, M, src_rank, topk_idx, out, x, nullptr,
+                                recv_rows, &o, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_ll_dispatch_fp8(const moe_shape *shape, int32_t M, const uint16_t *x,
+                                const int32_t *slot, uint8_t *recv_q, void *recv_scale,
+                                int64_t recv_rows, int32_t flags, int32_t *status,
+                                hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  rc = check_fp8(shape->H, flags);
+  if (rc) return rc;
+  if (M < 1 || (int64_t)shape->E * shape->R * M >= ((int64_t)1 << 31)) return MOE_ERR_LL;
+  if (recv_rows < 0 || recv_rows > (int64_t)shape->E * shape->R * M) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!x || !slot || (recv_rows > 0 && (!recv_q || !recv_scale))) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_q) || !aligned4(recv_scale)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const Fp8Out o{flags, recv_q, recv_scale, shape->R * M};
+  return launch_ll_quant_dispatch(x, slot, o, shape->T, shape->K, shape->H, recv_rows, status,
+                                  stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_dispatch_fp8(const moe_shape *shape, const uint8_t *x_q, const float *x_scale,
+                             const int32_t *slot, uint8_t *recv_q, float *recv_scale,
+                             int64_t recv_rows, int32_t *status, hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (shape->H % kFp8Group != 0) return MOE_ERR_SHAPE;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!x_q || !x_scale || !slot || (recv_rows > 0 && (!recv_q || !recv_scale)))
+    return MOE_ERR_NULL;
+  if (!aligned16(x_q) || !aligned16(recv_q) || !aligned4(x_scale) || !aligned4(recv_scale))
+    return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_fp8_copy_dispatch(x_q, x_scale, slot, recv_q, recv_scale, shape->T, shape->K,
+                                  shape->H, recv_rows, status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, void *scale,
+                             int32_t flags, hipStream_t stream) {
+  if (T < 0 || H < kFp8Group || H > (1 << 20)) return MOE_ERR_SHAPE;
+  if ((int64_t)T * (H / 8) >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  int rc = check_fp8(H, flags);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  if (!x || !q || !scale) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(q) || !aligned4(scale)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_quantize_fp8(x, q, scale, flags, T, H, stream) == hipSuccess ? MOE_OK
+                                                                              : MOE_ERR_LAUNCH;
 }
 
 MOE_API int moe_expert_load(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,

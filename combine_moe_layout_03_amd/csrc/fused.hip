@@ -22,15 +22,19 @@
 // size the kernel is bound by each wave's serial instruction latency, not by
 // memory.
 //
-// With the copy, a workgroup owns up to 8 chunks (1 KiB each) of one token row.
-// It requests the routing first and the row second, derives its K slots while
-// the (cold) row is still in flight, then stores the row K times.
+// With the copy, a workgroup owns up to 16 chunks (1 KiB each) of one token
+// row. It requests the routing first and the row second, derives its K slots
+// while the (cold) row is still in flight, then stores the row K times -- as
+// bf16, or (low-latency FP8 dispatch) cast once to E4M3 with per-128-channel
+// scales (fp8.hpp) and stored as codes plus column-major scales.
+#include "fp8.hpp"
 #include "wave.hpp"
 
 namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kCountMaxWaves = 16;
 // Waves of a copying workgroup that also read the routing and count; the rest
@@ -54,6 +58,11 @@ struct CountParams {
   int32_t nvec, nchunk, chunks_per_wg, wg_per_token;
   int32_t token_wgs;  // workgroups [0, token_wgs) serve tokens, the rest do duties
   int32_t duty_wgs;
+  // FP8 output (kFp8 >= 0): codes, scales, rows per expert, scale groups per row
+  u32x2 *q;
+  float *scale;
+  uint32_t *ue;
+  int32_t RM, G;
 };
 
 // v with lane j replaced by the (uniform) value x
@@ -213,7 +222,8 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
   }
 }
 
-template <bool kCopy, int kRounds>
+// kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast.
+template <bool kCopy, int kRounds, int kFp8>
 __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
   __shared__ int32_t s_pre[64];   // per k: pairs with the same id before this token
   __shared__ int32_t s_lt[64];    // per k: valid ids below it
@@ -251,10 +261,10 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     //    the slots are worked out. The load is unconditional (address clamped
     //    into the row): under a branch it would force an early wait.
     u32x4 val = {0u, 0u, 0u, 0u};
-    int v = 0;
+    int v = 0, chunk = 0;
     bool lane_ok = false;
     if (kCopy) {
-      const int chunk = (b % f.wg_per_token) * f.chunks_per_wg + wave;
+      chunk = (b % f.wg_per_token) * f.chunks_per_wg + wave;
       v = chunk * 64 + lane;
       lane_ok = wave < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
       val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
@@ -302,7 +312,30 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     }
 
     // 5. the row, K times (slot k read from lane k)
-    if (kCopy) {
+    if (kCopy && kFp8 >= 0) {
+      asm volatile("" : "+v"(val));
+      // H % 128 == 0: a 16-lane scale group is inside the row or wholly past it
+      const Fp8Lane q = fp8_cast_lane<(kFp8 < 0 ? 0 : kFp8)>(val);
+      const u32x2 codes = {q.lo, q.hi};
+      const int grp = chunk * 4 + (lane >> 4);
+      uint32_t word = 0;
+      if (kFp8 & kFp8Ue8m0) word = ue8m0_word(q.scale);
+      for (int k = 0; k < K; ++k) {
+        const int s = __builtin_amdgcn_readlane(out, k);
+        if (s >= 0 && s < f.rows) {
+          const int e = __builtin_amdgcn_readlane(tokv, k);
+          const int i = s - e * f.RM;  // row within the expert's R*M rows
+          if (lane_ok) __builtin_nontemporal_store(codes, f.q + (int64_t)s * f.nvec + v);
+          if (kFp8 & kFp8Ue8m0) {
+            if (lane == 0 && lane_ok) f.ue[((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
+          } else if ((lane & 15) == 0 && lane_ok) {
+            f.scale[((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
+          }
+        } else if (s != -1 && wave == 0) {
+          st |= kStBadSlot;  // receive buffer smaller than the layout needs
+        }
+      }
+    } else if (kCopy) {
       asm volatile("" : "+v"(val));
       for (int k = 0; k < K; ++k) {
         const int s = __builtin_amdgcn_readlane(out, k);
@@ -340,16 +373,16 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
   if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
 }
 
-template <bool kCopy>
+template <bool kCopy, int kFp8>
 hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const CountParams &f) {
   if (rounds <= 1)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8>), grid, block, 0, s, f);
   else if (rounds <= 2)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2, kFp8>), grid, block, 0, s, f);
   else if (rounds <= 4)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4, kFp8>), grid, block, 0, s, f);
   else
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8, kFp8>), grid, block, 0, s, f);
   return hipGetLastError();
 }
 
@@ -382,12 +415,17 @@ bool count_layout_fits(const LayoutParams &lp, int32_t H, bool copy) {
 }
 
 hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16_t *recv,
-                               int64_t rows, int32_t H, hipStream_t s) {
+                               int64_t rows, int32_t H, const Fp8Out *fp8, hipStream_t s) {
   CountParams f;
   f.lp = lp;
   f.x = reinterpret_cast<const u32x4 *>(x);
   f.recv = reinterpret_cast<u32x4 *>(recv);
   f.rows = rows;
+  f.q = fp8 ? reinterpret_cast<u32x2 *>(fp8->q) : nullptr;
+  f.scale = fp8 ? static_cast<float *>(fp8->scale) : nullptr;
+  f.ue = fp8 ? static_cast<uint32_t *>(fp8->scale) : nullptr;
+  f.RM = fp8 ? fp8->rows_per_expert : 0;
+  f.G = H / kFp8Group;
   const int need = (lp.E > lp.R ? lp.E : lp.R);
   f.duty_wgs = (need + kMaxDuties - 1) / kMaxDuties;
   const int P = lp.T * lp.K;
@@ -402,14 +440,19 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
     // of theirs; the rounds template covers the larger need
     const int counting = threads < kCountingWaves * 64 ? threads : kCountingWaves * 64;
     const int rounds = (P + counting - 1) / counting;
-    return launch_rounds<true>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
-                               dim3(threads), s, f);
+    const dim3 grid((unsigned)(f.token_wgs + f.duty_wgs)), block(threads);
+    if (!fp8) return launch_rounds<true, -1>(rounds, grid, block, s, f);
+    switch (fp8->flags) {
+      case 0: return launch_rounds<true, 0>(rounds, grid, block, s, f);
+      case kFp8RoundScale: return launch_rounds<true, kFp8RoundScale>(rounds, grid, block, s, f);
+      default: return launch_rounds<true, kFp8RoundScale | kFp8Ue8m0>(rounds, grid, block, s, f);
+    }
   }
   f.nvec = f.nchunk = f.chunks_per_wg = f.wg_per_token = 0;
   f.token_wgs = lp.T;
   const int rounds = (P + kLayoutOnlyThreads - 1) / kLayoutOnlyThreads;
-  return launch_rounds<false>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
-                              dim3(kLayoutOnlyThreads), s, f);
+  return launch_rounds<false, -1>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
+                                  dim3(kLayoutOnlyThreads), s, f);
 }
 
 }  // namespace moe

@@ -64,11 +64,32 @@ hipError_t launch_layout_multi_block(const LayoutParams &p, hipStream_t s);
 hipError_t launch_expert_load(const int64_t *idx, int32_t T, int32_t K, int32_t E,
                               int32_t id_bits, int32_t *load, int32_t *status, hipStream_t s);
 
+// FP8 form of a low-latency receive buffer: E4M3 codes [rows, H] and the
+// per-128-channel scales, stored [E][H/128][rows_per_expert] as floats, or
+// [E][H/512][rows_per_expert] as packed UE8M0 words (flags has kFp8Ue8m0).
+struct Fp8Out {
+  int32_t flags;            // kFp8RoundScale | kFp8Ue8m0 bits (fp8.hpp)
+  uint8_t *q;
+  void *scale;
+  int32_t rows_per_expert;  // R*M
+};
+
 // Layout by counting (alignment 1 or low latency, at most kMaxPairsFused
-// pairs), optionally with the dispatch copy in the same launch (x != null).
+// pairs), optionally with the dispatch copy in the same launch (x != null):
+// bf16 rows into recv, or, with fp8 != null (low latency only), the E4M3 cast.
 bool count_layout_fits(const LayoutParams &p, int32_t H, bool copy);
 hipError_t launch_count_layout(const LayoutParams &p, const uint16_t *x, uint16_t *recv,
-                               int64_t rows, int32_t H, hipStream_t s);
+                               int64_t rows, int32_t H, const Fp8Out *fp8, hipStream_t s);
+
+// FP8 kernels (fp8.hip).
+hipError_t launch_ll_quant_dispatch(const uint16_t *x, const int32_t *slot, const Fp8Out &o,
+                                    int32_t T, int32_t K, int32_t H, int64_t rows,
+                                    int32_t *status, hipStream_t s);
+hipError_t launch_fp8_copy_dispatch(const uint8_t *xq, const float *xs, const int32_t *slot,
+                                    uint8_t *rq, float *rs, int32_t T, int32_t K, int32_t H,
+                                    int64_t rows, int32_t *status, hipStream_t s);
+hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, void *scale, int32_t flags,
+                               int32_t T, int32_t H, hipStream_t s);
 
 hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                            int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s);

@@ -17,7 +17,7 @@
 // before it sums, so K requests per lane are in flight at once, then adds in
 // ascending k in f32 with no fused multiply-add and rounds once to bf16
 // (round to nearest even, NaN -> 0x7FC0).
-#include "kernels.hpp"
+#include "wave.hpp"
 
 namespace moe {
 namespace {
@@ -33,18 +33,6 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// A wave owns 64 consecutive 16-byte vectors of one token row, so the token
-// index is wave-uniform: its K slots (and weights) arrive as scalar loads before
-// any vector memory operation, and the row's K stores or loads are issued back
-// to back without waiting on each other. Lanes past the row end (H/8 not a
-// multiple of 64) idle.
-__device__ __forceinline__ int wave_token_chunk(int nchunk, int &t) {
-  const int wid = __builtin_amdgcn_readfirstlane(
-      (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
-  t = wid / nchunk;
-  return (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
 }
 
 template <int KT>

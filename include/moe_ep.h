@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Host-side return codes. */
 #define MOE_OK 0
@@ -63,6 +63,12 @@ extern "C" {
 #define MOE_ERR_LAUNCH (-7)    /* the HIP runtime refused a kernel launch */
 #define MOE_ERR_ARCH (-8)      /* the current device is not gfx950 */
 #define MOE_ERR_DEVICE (-9)    /* the HIP runtime could not be queried */
+#define MOE_ERR_FLAGS (-10)    /* an unsupported FP8 flag combination */
+
+/* FP8 cast options (Buffer.low_latency_dispatch: round_scale, use_ue8m0). */
+#define MOE_FP8_ROUND_SCALE 1 /* scales rounded up to powers of two */
+#define MOE_FP8_UE8M0 2       /* scales stored as packed exponent bytes; needs
+                                 MOE_FP8_ROUND_SCALE and H % 512 == 0 */
 
 /* Device-side status bits (OR-ed into *status). */
 #define MOE_STATUS_BAD_EXPERT 1   /* an id outside [-1, E): the pair is skipped */
@@ -206,6 +212,67 @@ int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
 int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
                 const int32_t *replica_count, const int32_t *replica_phys, int32_t E_phys,
                 int64_t *phys_idx, int32_t *status, hipStream_t stream);
+
+/* ---------------------------------------------------------------------
+ * FP8 dispatch (Buffer.low_latency_dispatch with use_fp8, round_scale and
+ * use_ue8m0, and its returns; Buffer.dispatch with x given as a tuple of
+ * float8_e4m3fn rows and float scales).
+ *
+ * The cast, per token row and per group of 128 channels:
+ *   amax  = the group's largest |x|, taken as at least 1e-4;
+ *   scale = amax / 448 (float, correctly rounded; 448 is the largest finite
+ *           E4M3 value); with MOE_FP8_ROUND_SCALE rounded up to the next
+ *           power of two;
+ *   code  = E4M3 (OCP "fn" encoding: no infinity) nearest to x / scale
+ *           (float division, ties to even, saturating at 448; the sign is
+ *           kept, so -0 gives 0x80);
+ * so x ~= value(code) * scale. With MOE_FP8_UE8M0 a power-of-two scale is
+ * stored as its biased exponent byte (scale = 2^(byte - 127)), groups
+ * 4w..4w+3 in bytes 0..3 (low to high) of int32 word w. x must be finite:
+ * a NaN or infinity gives unspecified codes and scale for its group.
+ * H must be a multiple of 128 (of 512 with MOE_FP8_UE8M0); flags is 0,
+ * MOE_FP8_ROUND_SCALE or MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0, anything else
+ * returns MOE_ERR_FLAGS. Code and bf16 row pointers must be 16-byte aligned,
+ * scale pointers 4-byte aligned.
+ * ------------------------------------------------------------------- */
+
+/* The cast alone, row-major: q [T*H] E4M3 codes; scale [T*H/128] float, or
+ * with MOE_FP8_UE8M0 [T*H/512] int32 words. Produces the (codes, scales)
+ * tuple that moe_dispatch_fp8 takes. */
+int moe_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, void *scale,
+                     int32_t flags, hipStream_t stream);
+
+/* Low-latency layout and FP8 dispatch in one call (Buffer.low_latency_dispatch,
+ * use_fp8 = True): the layout arrays exactly as moe_ll_layout, and for every
+ * pair with a slot, the token's codes in row slot of recv_q [recv_rows*H] and
+ * its scales in the column-major scale tensor of the page's return value:
+ * recv_scale is [E][H/128][R*M] float -- the scale of group g for row i of
+ * expert e's R*M rows (slot = e*R*M + i) is at (e*(H/128) + g)*R*M + i -- or,
+ * with MOE_FP8_UE8M0, [E][H/512][R*M] int32 words placed the same way.
+ * recv_rows <= E*R*M (normally moe_ll_recv_rows(E, R, M)). Entries no pair
+ * maps to are left untouched. */
+int moe_ll_layout_dispatch_fp8(const moe_shape *shape, int32_t M, int32_t src_rank,
+                               const int64_t *topk_idx, const moe_layout_t *out,
+                               const uint16_t *x, uint8_t *recv_q, void *recv_scale,
+                               int64_t recv_rows, int32_t flags, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* The FP8 low-latency scatter given the slots of moe_ll_layout (same output
+ * layout as moe_ll_layout_dispatch_fp8; M is the per-rank capacity the slots
+ * were made with). A slot outside [-1, recv_rows) sets MOE_STATUS_BAD_SLOT
+ * and is skipped. status may be NULL. */
+int moe_ll_dispatch_fp8(const moe_shape *shape, int32_t M, const uint16_t *x,
+                        const int32_t *slot, uint8_t *recv_q, void *recv_scale,
+                        int64_t recv_rows, int32_t flags, int32_t *status, hipStream_t stream);
+
+/* Dispatch of an already cast tuple (Buffer.dispatch, x = (E4M3 [T, H],
+ * float [T, H/128])): for every pair with slot != -1, row slot of
+ * recv_q [recv_rows*H] receives the token's codes and row slot of
+ * recv_scale [recv_rows*H/128] its scales, bit for bit (row-major, like the
+ * input). Rows no pair maps to are left untouched. status may be NULL. */
+int moe_dispatch_fp8(const moe_shape *shape, const uint8_t *x_q, const float *x_scale,
+                     const int32_t *slot, uint8_t *recv_q, float *recv_scale,
+                     int64_t recv_rows, int32_t *status, hipStream_t stream);
 
 #ifdef __cplusplus
 }

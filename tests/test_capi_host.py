@@ -21,12 +21,12 @@ def lib():
 def header_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 14, declared
+    assert len(declared) == 18, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -34,8 +34,8 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.moe_abi_version() == 1
-    for code in range(0, -10, -1):
+    assert lib.moe_abi_version() == lib.MOE_ABI_VERSION
+    for code in range(0, -11, -1):
         assert lib.moe_strerror(code) != "unknown error code"
     assert lib.moe_strerror(-99) == "unknown error code"
 
@@ -144,3 +144,54 @@ def test_replica_checks(lib):
     assert raw.moe_reroute(4, 2, 16, None, d, d, 20, d, None, None) == -1
     assert raw.moe_reroute(0, 2, 16, None, None, None, 20, None, None, None) == 0
     assert raw.moe_expert_load(4, 2, 2000, d, d, None, None) == -2
+
+
+def test_fp8_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd16 = C.c_void_p(264)  # 8-byte aligned, not 16
+    odd4 = C.c_void_p(258)
+    lt = lib.moe_layout_t()
+    lt.count = lt.offset = lt.slot = d
+    # flags: only 0, ROUND, ROUND|UE8M0
+    for bad in (2, 4, -1, 7):
+        assert raw.moe_quantize_fp8(4, 512, d, d, d, bad, None) == -10
+        assert raw.moe_ll_dispatch_fp8(C.byref(lib.make_shape(4, 512, 16, 4, 2, 1)), 4, d, d, d,
+                                       d, 64, bad, None, None) == -10
+    # H must be a multiple of 128 (512 with UE8M0)
+    assert raw.moe_quantize_fp8(4, 136, d, d, d, 0, None) == -2
+    assert raw.moe_quantize_fp8(4, 384, d, d, d, 3, None) == -2
+    s = lib.make_shape(4, 384, 16, 4, 2, 1)
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 4, 0, d, C.byref(lt), d, d, d, 64, 3,
+                                          None, 0, None) == -2
+    assert raw.moe_ll_dispatch_fp8(C.byref(s), 4, d, d, d, d, 64, 3, None, None) == -2
+    s = lib.make_shape(4, 136, 16, 4, 2, 1)
+    assert raw.moe_dispatch_fp8(C.byref(s), d, d, d, d, d, 8, None, None) == -2
+    s = lib.make_shape(4, 512, 16, 4, 2, 1)
+    # recv_rows beyond the E*R*M rows the column-major scales describe
+    assert raw.moe_ll_dispatch_fp8(C.byref(s), 4, d, d, d, d, 16 * 4 * 4 + 1, 0, None,
+                                   None) == -3
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 4, 0, d, C.byref(lt), d, d, d,
+                                          16 * 4 * 4 + 1, 0, None, 0, None) == -3
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 3, 0, d, C.byref(lt), d, d, d, 48, 0,
+                                          None, 0, None) == -4  # T > M
+    # null and alignment
+    assert raw.moe_quantize_fp8(4, 512, None, d, d, 0, None) == -1
+    assert raw.moe_quantize_fp8(4, 512, d, odd16, d, 0, None) == -5
+    assert raw.moe_quantize_fp8(4, 512, d, d, odd4, 0, None) == -5
+    assert raw.moe_ll_dispatch_fp8(C.byref(s), 4, d, None, d, d, 64, 0, None, None) == -1
+    assert raw.moe_ll_dispatch_fp8(C.byref(s), 4, d, d, d, odd4, 64, 0, None, None) == -5
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 4, 0, d, C.byref(lt), d, None, d, 64, 0,
+                                          None, 0, None) == -1
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 4, 0, d, C.byref(lt), d, odd16, d, 64, 0,
+                                          None, 0, None) == -5
+    assert raw.moe_dispatch_fp8(C.byref(s), d, None, d, d, d, 8, None, None) == -1
+    assert raw.moe_dispatch_fp8(C.byref(s), odd16, d, d, d, d, 8, None, None) == -5
+    assert raw.moe_dispatch_fp8(C.byref(s), d, odd4, d, d, d, 8, None, None) == -5
+    assert raw.moe_dispatch_fp8(C.byref(s), d, d, d, d, d, -1, None, None) == -3
+    # empty batches need no device
+    s0 = lib.make_shape(0, 512, 16, 4, 2, 1)
+    assert raw.moe_quantize_fp8(0, 512, None, None, None, 3, None) == 0
+    assert raw.moe_ll_dispatch_fp8(C.byref(s0), 4, None, None, None, None, 0, 0, None,
+                                   None) == 0
+    assert raw.moe_dispatch_fp8(C.byref(s0), None, None, None, None, None, 0, None, None) == 0
