@@ -45,10 +45,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algo_bytes(T, H, K, E, R, P_valid):
-    """Bytes the method must move (not what a kernel happens to move)."""
+def algo_bytes(T, H, K, E, R, P_valid, fp8_flags=None):
+    """Bytes the method must move (not what a kernel happens to move). With
+    fp8_flags, dispatch writes E4M3 rows (H bytes) plus one 4-byte scale per
+    128 channels (one 4-byte UE8M0 word per 512 with MOE_FP8_UE8M0)."""
     row = 2 * H
     dispatch = P_valid * (row + 4) + T * row
+    if fp8_flags is not None:
+        scale_bytes = 4 * (H // 512 if fp8_flags & 2 else H // 128)
+        dispatch = P_valid * (H + scale_bytes + 4) + T * row
     combine = P_valid * (row + 8) + T * row
     layout = T * K * 8 + P_valid * 4 + P_valid * 4 + E * 4 * 2 + 4 + R * 4 + T * R
     return dict(layout=layout, dispatch=dispatch, combine=combine,
@@ -178,10 +183,13 @@ def graph_us_per_step(torch, stream, step_fns, reps):
     return start.elapsed_time(end) * 1e3 / (reps * len(step_fns))
 
 
-def row_low_latency(capi, mi, torch, np, dev, stream, n_ev):
+def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     """Low-latency padded path at 128 tokens per rank: layout + dispatch into
     the [E, R*M, H] union of the receive buffers, then combine from it. Steps
-    rotate over 4 union buffers x 8 source stripes (> 512 MiB touched)."""
+    rotate over 4 union buffers x 8 source stripes (> 512 MiB touched).
+    With fp8_flags, dispatch casts to E4M3 + per-128-channel scales
+    (moe_ll_layout_dispatch_fp8) and combine reads a bf16 expert-output union
+    of the same layout (filled once by a bf16 dispatch of the same batch)."""
     M = 128
     w = mi.config_c3(M)
     E, R, K, T, H = w.E, w.R, w.K, w.T, w.H
@@ -190,17 +198,30 @@ def row_low_latency(capi, mi, torch, np, dev, stream, n_ev):
     x = torch.from_numpy(w.x.view(np.int16)).to(dev)
     idx = torch.from_numpy(w.topk_idx).to(dev)
     wt = torch.from_numpy(w.topk_weights).to(dev)
+    fp8 = fp8_flags is not None
     unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(4)]
+    if fp8:
+        cols = capi.fp8_scale_cols(H, fp8_flags)
+        sdt = torch.int32 if fp8_flags & capi.MOE_FP8_UE8M0 else torch.float32
+        qunions = [torch.empty(rows, H, dtype=torch.uint8, device=dev) for _ in range(4)]
+        sunions = [torch.empty(E, cols, R * M, dtype=sdt, device=dev) for _ in range(4)]
     sets = []
-    for u in unions:
+    for ui, u in enumerate(unions):
         for s in range(R):
-            sets.append(dict(u=u, s=s, x=x.clone(), idx=idx.clone(), w=wt.clone(),
-                             lay=capi.LayoutBuffers.empty(shape, dev, ll_M=M, status=False),
-                             out=torch.empty(T, H, dtype=torch.int16, device=dev)))
+            z = dict(u=u, s=s, x=x.clone(), idx=idx.clone(), w=wt.clone(),
+                     lay=capi.LayoutBuffers.empty(shape, dev, ll_M=M, status=False),
+                     out=torch.empty(T, H, dtype=torch.int16, device=dev))
+            if fp8:
+                z.update(q=qunions[ui], sc=sunions[ui])
+            sets.append(z)
 
     def ld(z):
-        capi.moe_ll_layout_dispatch(shape, M, z["s"], z["idx"], z["lay"], z["x"], z["u"], rows,
-                                    stream=stream)
+        if fp8:
+            capi.moe_ll_layout_dispatch_fp8(shape, M, z["s"], z["idx"], z["lay"], z["x"], z["q"],
+                                            z["sc"], rows, fp8_flags, stream=stream)
+        else:
+            capi.moe_ll_layout_dispatch(shape, M, z["s"], z["idx"], z["lay"], z["x"], z["u"],
+                                        rows, stream=stream)
 
     def cb(z):
         capi.moe_combine(shape, z["u"], rows, z["lay"].slot, z["w"], z["out"], None, None,
@@ -208,23 +229,33 @@ def row_low_latency(capi, mi, torch, np, dev, stream, n_ev):
 
     with torch.cuda.stream(stream):
         for z in sets:
+            if fp8:  # expert output: the bf16 rows of the same layout
+                capi.moe_ll_layout_dispatch(shape, M, z["s"], z["idx"], z["lay"], z["x"], z["u"],
+                                            rows, stream=stream)
             ld(z)
             cb(z)
     torch.cuda.synchronize()
     fns = [(lambda z=z: (ld(z), cb(z))) for z in sets]
     us = graph_us_per_step(torch, stream, fns, 20)
-    with torch.cuda.stream(stream):
-        k_ld = per_launch_event_times(torch, lambda i: ld(sets[i % len(sets)]), n_ev, stream)
-        k_cb = per_launch_event_times(torch, lambda i: cb(sets[i % len(sets)]), n_ev, stream)
-    ab = algo_bytes(T, H, K, E, R, int((w.topk_idx >= 0).sum()))
+    k_ld = graph_us_per_step(torch, stream, [(lambda z=z: ld(z)) for z in sets], 20)
+    k_cb = graph_us_per_step(torch, stream, [(lambda z=z: cb(z)) for z in sets], 20)
+    P = int((w.topk_idx >= 0).sum())
+    ab = algo_bytes(T, H, K, E, R, P, fp8_flags)
     del unions, sets
+    if fp8:
+        del qunions, sunions
     torch.cuda.empty_cache()
-    return {"workload": "low-latency padded: 128 tokens/rank x 7168, 256E top-8, 8 ranks, "
-                        "union receive buffer [256, 8*128, 7168]",
-            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
-            "kernels_us": {"ll_layout_dispatch": round(k_ld["mean_us"], 3),
-                           "combine": round(k_cb["mean_us"], 3)},
-            "algorithmic_bytes_per_step": ab["total"]}
+    name = "low-latency padded" + (f" FP8 (flags {fp8_flags})" if fp8 else "")
+    res = {"workload": name + ": 128 tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
+                              "buffer [256, 8*128, 7168]",
+           "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
+           "kernels_us": {"ll_layout_dispatch" + ("_fp8" if fp8 else ""): round(k_ld, 3),
+                          "combine": round(k_cb, 3)},
+           "algorithmic_bytes_per_step": ab["total"]}
+    res["roofline_dispatch"] = {"achieved": round((ab["layout"] + ab["dispatch"]) / k_ld / 1e3, 1),
+                                "frac": round((ab["layout"] + ab["dispatch"]) / k_ld / 1e3
+                                              / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def row_replica(capi, mi, torch, np, dev, stream, n_ev):
@@ -434,8 +465,10 @@ def main():
 
     rows = {}
     if not args.no_rows:
-        rows["low_latency_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, n)
+        rows["low_latency_m128"] = row_low_latency(capi, mi, torch, np, dev, stream)
         log(f"low-latency row: {rows['low_latency_m128']['us_per_step']} us/step")
+        rows["low_latency_fp8_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, 0)
+        log(f"low-latency FP8 row: {rows['low_latency_fp8_m128']['us_per_step']} us/step")
         rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
         log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
 

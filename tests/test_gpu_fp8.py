@@ -101,6 +101,50 @@ def test_quantize_crafted_ties_and_subnormals(capi, orc, flags):
     check_quantize(capi, orc, xb, flags)
 
 
+def _near_tie_rows():
+    """Groups with non-power-of-two scales (every bf16 group maximum in [1, 2),
+    and a few others) whose other channels are every bf16 x below the maximum
+    for which x / scale lies within 4 float ulps of a midpoint between
+    adjacent E4M3 values (about 1500 of them, both signs): the codes there
+    depend on the quotient being the correctly rounded float, so they test the
+    kernels' division and the conversion's tie handling together. Packed into
+    rows of 2048 channels."""
+    import torch as _t
+
+    vals = _t.arange(127, dtype=_t.int32).to(_t.uint8).view(_t.float8_e4m3fn).to(
+        _t.float32).numpy().astype(np.float64)
+    mids = (vals[:-1] + vals[1:]) / 2
+    pats = (np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16).view(np.float32)  # positive normals
+    amaxs = list((np.arange(0x3F80, 0x4000, dtype=np.uint32) << 16).view(np.float32))
+    amaxs += [np.float32(v) for v in (0.01226806640625, 77.5, 0.005035400390625, 250.0)]
+    groups = []
+    for amax in amaxs:
+        s = np.float32(amax) / np.float32(448.0)
+        xs = pats[(pats > 0) & (pats < np.float32(amax))].astype(np.float64)
+        q = xs / np.float64(s)
+        j = np.clip(np.searchsorted(mids, q), 1, mids.size - 1)
+        d = np.minimum(np.abs(q - mids[j]), np.abs(q - mids[j - 1]))
+        ulp = np.spacing(q.astype(np.float32)).astype(np.float64)
+        near = xs[d <= 4 * ulp].astype(np.float32)
+        sel = np.concatenate([near, -near])
+        for c in range(0, max(sel.size, 1), 127):
+            g = np.zeros(128, np.float32)
+            g[0] = amax
+            part = sel[c:c + 127]
+            g[1:1 + part.size] = part
+            groups.append(g)
+    while len(groups) % 16:
+        groups.append(np.zeros(128, np.float32))
+    return mi.to_bf16_bits(np.concatenate(groups).reshape(-1, 2048))
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_quantize_near_ties_with_inexact_scales(capi, orc, flags):
+    xb = _near_tie_rows()
+    _announce(f"quantize near-tie quotients H={xb.shape[1]} flags={flags}")
+    check_quantize(capi, orc, xb, flags)
+
+
 @pytest.mark.parametrize("flags", FLAGS)
 def test_quantize_wide_range_and_zero_groups(capi, orc, flags):
     rng = np.random.default_rng(11)
