@@ -30,6 +30,7 @@ ST_BAD_REPLICA = 8
 
 FP8_ROUND_SCALE = 1
 FP8_UE8M0 = 2
+FP8_SCALE_ROWS = 4
 FP8_GROUP = 128
 
 
@@ -212,8 +213,9 @@ class Oracle:
 
     def ll_dispatch_fp8(self, qz: dict, slot: np.ndarray, E: int, R: int, M: int, flags: int = 0,
                         fill_q: int = 0, fill_scale: float = 0.0, fill_ue: int = 0) -> dict:
-        """Scatter quantized rows and their column-major scales to the
-        low-latency padded layout; untouched entries keep the fill values."""
+        """Scatter quantized rows and their scales (column-major [E, G, R*M], or
+        row-major [rows, G] with FP8_SCALE_ROWS) to the low-latency padded
+        layout; untouched entries keep the fill values."""
         q, scale, ue = qz["q"], qz["scale"], qz["ue8m0"]
         slot = np.ascontiguousarray(slot, dtype=np.int32)
         T, H = q.shape
@@ -221,9 +223,14 @@ class Oracle:
         G = H // FP8_GROUP
         rows = E * R * M
         recv_q = np.full((rows, H), fill_q, np.uint8)
-        recv_s = np.full((E, G, R * M), fill_scale, np.float32)
-        recv_u = np.full((E, max(G // 4, 1), R * M), fill_ue, np.int32) \
-            if flags & FP8_UE8M0 else None
+        if flags & FP8_SCALE_ROWS:  # row-major option: [rows, G] / [rows, G/4]
+            recv_s = np.full((rows, G), fill_scale, np.float32)
+            recv_u = np.full((rows, max(G // 4, 1)), fill_ue, np.int32) \
+                if flags & FP8_UE8M0 else None
+        else:  # the page's column-major last two dimensions
+            recv_s = np.full((E, G, R * M), fill_scale, np.float32)
+            recv_u = np.full((E, max(G // 4, 1), R * M), fill_ue, np.int32) \
+                if flags & FP8_UE8M0 else None
         status = np.zeros(1, np.int32)
         rc = self.lib.oracle_ll_dispatch_fp8(T, H, K, E, R, M, flags, _ptr(slot), _ptr(q),
                                              _ptr(scale), _ptr(ue), _ptr(recv_q), _ptr(recv_s),

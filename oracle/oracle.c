@@ -438,6 +438,7 @@ int oracle_reroute(int64_t T, int32_t K, int32_t E, const int64_t *idx,
 #define FP8_GROUP 128       /* channels per scale ([P1]: hidden // 128 scales) */
 #define FP8_ROUND_SCALE 1   /* scales rounded up to a power of two */
 #define FP8_UE8M0 2         /* scales also emitted as packed exponent bytes */
+#define FP8_SCALE_ROWS 4    /* receive-side scales row-major instead of column-major */
 #define FP8_AMAX_FLOOR 1e-4f /* reading: a group's amax is taken as at least this */
 
 /* Value of an E4M3 ("fn" variant) code, from the format's definition (OCP 8-bit
@@ -583,8 +584,10 @@ int oracle_quantize_fp8(int64_t T, int32_t H, const uint16_t *x, int32_t flags, 
  * column-major ([P1] returns): recv_scale is stored as [E][H/128][R*M], so
  * the scale of group g for row i of expert e's R*M rows sits at
  * (e*(H/128) + g)*(R*M) + i; with FP8_UE8M0 the packed words go to
- * recv_ue8m0 stored as [E][H/512][R*M] the same way. Rows no pair maps to
- * are left untouched. */
+ * recv_ue8m0 stored as [E][H/512][R*M] the same way. With FP8_SCALE_ROWS
+ * (an option of this implementation, not of the page) both are row-major
+ * instead: the scales of receive row r at r*(H/128) + g (UE8M0 words at
+ * r*(H/512) + w). Rows no pair maps to are left untouched. */
 int oracle_ll_dispatch_fp8(int64_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t M,
                            int32_t flags, const int32_t *slot, const uint8_t *q,
                            const float *scale, const int32_t *ue8m0, uint8_t *recv_q,
@@ -603,14 +606,20 @@ int oracle_ll_dispatch_fp8(int64_t T, int32_t H, int32_t K, int32_t E, int32_t R
             int64_t e = r / RM, i = r % RM;
             memcpy(recv_q + (int64_t)r * H, q + t * (int64_t)H, (size_t)H);
             for (int32_t g = 0; g < G; ++g) {
+                int64_t at = (flags & FP8_SCALE_ROWS) ? (int64_t)r * G + g : (e * G + g) * RM + i;
 #if ORACLE_MUTANT == 13
-                recv_scale[(int64_t)r * G + g] = scale[t * G + g]; /* mutant: row-major */
-#else
-                recv_scale[(e * G + g) * RM + i] = scale[t * G + g];
+                at = (int64_t)r * G + g; /* mutant: always row-major */
 #endif
+                recv_scale[at] = scale[t * G + g];
             }
             if ((flags & FP8_UE8M0) && recv_ue8m0)
-                for (int32_t w = 0; w < W; ++w) recv_ue8m0[(e * W + w) * RM + i] = ue8m0[t * W + w];
+                for (int32_t w = 0; w < W; ++w) {
+                    int64_t at = (flags & FP8_SCALE_ROWS) ? (int64_t)r * W + w : (e * W + w) * RM + i;
+#if ORACLE_MUTANT == 16
+                    at = (flags & FP8_SCALE_ROWS) ? (int64_t)w * rows + r : at; /* mutant: rows transposed */
+#endif
+                    recv_ue8m0[at] = ue8m0[t * W + w];
+                }
         }
     }
     return 0;

@@ -329,7 +329,7 @@ def check_ll_matches_contiguous(orc, w):
 # ---------------------------------------------------------------------------
 FP8_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
                           "fp8_hand_worked.json")
-ROUND, UE8M0 = 1, 2
+ROUND, UE8M0, SCALE_ROWS = 1, 2, 4
 
 
 def _fp8_golden_x(g):
@@ -523,7 +523,7 @@ def check_ll_fp8_dispatch(orc, n: int = 8, seed: int = 9):
         K = int(rng.integers(1, 5))
         M = int(rng.integers(1, 9))
         T = int(rng.integers(0, M + 1))
-        w = mi.random_case(500 + i, T, 512, E, R, K, neg_frac=0.2, dup_frac=0.2)
+        w = mi.random_case(500 + i, T, 1024, E, R, K, neg_frac=0.2, dup_frac=0.2)
         src = int(rng.integers(0, R))
         lay = orc.ll_layout(w.topk_idx, E, R, M, src)
         for flags in (0, ROUND | UE8M0):
@@ -531,8 +531,8 @@ def check_ll_fp8_dispatch(orc, n: int = 8, seed: int = 9):
             out = orc.ll_dispatch_fp8(qz, lay["slot"], E, R, M, flags, fill_q=0xCD,
                                       fill_scale=7.0, fill_ue=5)
             rows = E * R * M
-            rs = out["recv_scale"].transpose(0, 2, 1).reshape(rows, 4)
-            ru = out["recv_ue8m0"].transpose(0, 2, 1).reshape(rows, 1) if flags & UE8M0 \
+            rs = out["recv_scale"].transpose(0, 2, 1).reshape(rows, 8)
+            ru = out["recv_ue8m0"].transpose(0, 2, 1).reshape(rows, 2) if flags & UE8M0 \
                 else None
             used = np.zeros(rows, bool)
             for t in range(T):
@@ -549,6 +549,15 @@ def check_ll_fp8_dispatch(orc, n: int = 8, seed: int = 9):
             assert np.all(rs[~used] == 7.0)
             if ru is not None:
                 assert np.all(ru[~used] == 5)
+            # the row-major option: the scale tensors read directly as rows,
+            # holding the same entries as the column-major ones
+            rowm = orc.ll_dispatch_fp8(qz, lay["slot"], E, R, M, flags | SCALE_ROWS, fill_q=0xCD,
+                                       fill_scale=7.0, fill_ue=5)
+            assert np.array_equal(rowm["recv_q"], out["recv_q"])
+            assert rowm["recv_scale"].shape == (rows, 8)
+            assert np.array_equal(rowm["recv_scale"], rs)
+            if ru is not None:
+                assert np.array_equal(rowm["recv_ue8m0"], ru)
 
 
 ALL_SMALL_CHECKS = (

@@ -23,6 +23,7 @@ MUTANTS = {
     13: "low-latency FP8 scales stored row-major",
     14: "UE8M0 bytes packed high to low",
     15: "FP8 amax over the whole row",
+    16: "row-major UE8M0 scales stored transposed",
 }
 
 
