@@ -204,7 +204,8 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
         cols = capi.fp8_scale_cols(H, fp8_flags)
         sdt = torch.int32 if fp8_flags & capi.MOE_FP8_UE8M0 else torch.float32
         qunions = [torch.empty(rows, H, dtype=torch.uint8, device=dev) for _ in range(4)]
-        sunions = [torch.empty(E, cols, R * M, dtype=sdt, device=dev) for _ in range(4)]
+        sshape = (rows, cols) if fp8_flags & capi.MOE_FP8_SCALE_ROWS else (E, cols, R * M)
+        sunions = [torch.empty(sshape, dtype=sdt, device=dev) for _ in range(4)]
     sets = []
     for ui, u in enumerate(unions):
         for s in range(R):
@@ -245,7 +246,9 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     if fp8:
         del qunions, sunions
     torch.cuda.empty_cache()
-    name = "low-latency padded" + (f" FP8 (flags {fp8_flags})" if fp8 else "")
+    name = "low-latency padded" + (f" FP8 (flags {fp8_flags}: "
+                                   + ("row-major" if fp8_flags & 4 else "column-major")
+                                   + " scales)" if fp8 else "")
     res = {"workload": name + ": 128 tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
                               "buffer [256, 8*128, 7168]",
            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
@@ -469,6 +472,10 @@ def main():
         log(f"low-latency row: {rows['low_latency_m128']['us_per_step']} us/step")
         rows["low_latency_fp8_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, 0)
         log(f"low-latency FP8 row: {rows['low_latency_fp8_m128']['us_per_step']} us/step")
+        rows["low_latency_fp8_rowscales_m128"] = row_low_latency(
+            capi, mi, torch, np, dev, stream, capi.MOE_FP8_SCALE_ROWS)
+        log(f"low-latency FP8 row-major scales: "
+            f"{rows['low_latency_fp8_rowscales_m128']['us_per_step']} us/step")
         rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
         log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
 

@@ -29,6 +29,7 @@ MOE_STATUS_BAD_REPLICA = 8
 
 MOE_FP8_ROUND_SCALE = 1
 MOE_FP8_UE8M0 = 2
+MOE_FP8_SCALE_ROWS = 4
 FP8_GROUP = 128
 
 
@@ -108,6 +109,15 @@ _FP8_CODES = (torch.uint8, torch.int8, torch.float8_e4m3fn)
 def fp8_scale_cols(H: int, flags: int) -> int:
     """Scale entries per row: one float per 128 channels, or one UE8M0 word per 512."""
     return H // (4 * FP8_GROUP) if flags & MOE_FP8_UE8M0 else H // FP8_GROUP
+
+
+def _ll_scale_numel(E: int, R: int, M: int, H: int, recv_rows: int, flags: int) -> int:
+    """Scale entries the low-latency FP8 calls may write: [E][cols][R*M]
+    column-major, or [recv_rows][cols] with MOE_FP8_SCALE_ROWS."""
+    if not recv_rows:
+        return 0
+    cols = fp8_scale_cols(H, flags)
+    return int(recv_rows) * cols if flags & MOE_FP8_SCALE_ROWS else E * cols * R * int(M)
 
 
 def _fp8_scale_dtypes(flags: int):
@@ -348,7 +358,7 @@ def moe_ll_layout_dispatch_fp8(shape: moe_shape, M: int, src_rank: int, topk_idx
         C.byref(shape), int(M), int(src_rank), idx, C.byref(st), _dev(x, "x", _BF16_LIKE, T * H),
         _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
         _dev(recv_scale, "recv_scale", _fp8_scale_dtypes(flags),
-             E * fp8_scale_cols(H, flags) * R * int(M) if recv_rows else 0),
+             _ll_scale_numel(E, R, M, H, recv_rows, flags)),
         int(recv_rows), int(flags), wsp, wsn, _stream(stream)))
 
 
@@ -362,7 +372,7 @@ def moe_ll_dispatch_fp8(shape: moe_shape, M: int, x: torch.Tensor, slot: torch.T
         _dev(slot, "slot", (torch.int32,), T * K),
         _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
         _dev(recv_scale, "recv_scale", _fp8_scale_dtypes(flags),
-             E * fp8_scale_cols(H, flags) * R * int(M) if recv_rows else 0),
+             _ll_scale_numel(E, R, M, H, recv_rows, flags)),
         int(recv_rows), int(flags), _dev(status, "status", (torch.int32,), 1, optional=True),
         _stream(stream)))
 

@@ -14,7 +14,8 @@ namespace {
 
 using namespace moe;
 
-static_assert(MOE_FP8_ROUND_SCALE == kFp8RoundScale && MOE_FP8_UE8M0 == kFp8Ue8m0,
+static_assert(MOE_FP8_ROUND_SCALE == kFp8RoundScale && MOE_FP8_UE8M0 == kFp8Ue8m0 &&
+                  MOE_FP8_SCALE_ROWS == kFp8ScaleRows,
               "FP8 flag values of the header and the kernels differ");
 static_assert(MOE_STATUS_BAD_EXPERT == kStBadExpert && MOE_STATUS_LL_OVERFLOW == kStOverflow &&
                   MOE_STATUS_BAD_SLOT == kStBadSlot && MOE_STATUS_BAD_REPLICA == kStBadReplica,
@@ -49,7 +50,9 @@ bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // FP8 flag set and the hidden sizes it needs: scales cover 128 channels, and
 // UE8M0 words pack four of them (and require power-of-two scales).
 int check_fp8(int32_t H, int32_t flags) {
-  if (flags != 0 && flags != MOE_FP8_ROUND_SCALE && flags != (MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0))
+  const int cast = flags & ~MOE_FP8_SCALE_ROWS;
+  if (flags < 0 || (flags & ~(MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0 | MOE_FP8_SCALE_ROWS)) ||
+      (cast != 0 && cast != MOE_FP8_ROUND_SCALE && cast != (MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0)))
     return MOE_ERR_FLAGS;
   if (H % kFp8Group != 0) return MOE_ERR_SHAPE;
   if ((flags & MOE_FP8_UE8M0) && H % (4 * kFp8Group) != 0) return MOE_ERR_SHAPE;

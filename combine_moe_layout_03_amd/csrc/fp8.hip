@@ -7,6 +7,10 @@
 //    [E][H/512][R*M] packed UE8M0 words;
 //  - Buffer.dispatch with x given as an (E4M3 [T, H], float [T, H/128]) tuple:
 //    both members are copied to the pair's row;
+//  - optionally (kFp8ScaleRows) the low-latency scales row-major, [rows][H/128]
+//    or [rows][H/512]: each pair's scales then fill contiguous bytes of its
+//    own row instead of one 4-byte entry in each of H/128 lines shared with
+//    the expert's other tokens;
 //  - the cast alone (the tuple that Buffer.dispatch takes), row-major scales.
 //
 // The decomposition is the bf16 scatter's: a wave owns 64 consecutive 16-byte
@@ -66,9 +70,12 @@ __global__ __launch_bounds__(256) void ll_quant_dispatch_kernel(
         const int i = r - e * RM;
         if (lane_ok) __builtin_nontemporal_store(codes, recv_q + (int64_t)r * nvec + v);
         if (kFlags & kFp8Ue8m0) {
-          if (lane == 0) recv_ue[((int64_t)e * nchunk + chunk) * RM + i] = word;
+          if (lane == 0)
+            recv_ue[(kFlags & kFp8ScaleRows) ? (int64_t)r * nchunk + chunk
+                                             : ((int64_t)e * nchunk + chunk) * RM + i] = word;
         } else if ((lane & 15) == 0 && lane_ok) {
-          recv_scale[((int64_t)e * G + grp) * RM + i] = q.scale;
+          recv_scale[(kFlags & kFp8ScaleRows) ? (int64_t)r * G + grp
+                                              : ((int64_t)e * G + grp) * RM + i] = q.scale;
         }
       } else if (r != -1) {
         st |= kStBadSlot;
@@ -167,11 +174,14 @@ hipError_t ll_quant_k(const uint16_t *x, const int32_t *slot, const Fp8Out &o, i
 template <int KT>
 hipError_t ll_quant_flags(const uint16_t *x, const int32_t *slot, const Fp8Out &o, int32_t T,
                           int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s) {
+  constexpr int R1 = kFp8RoundScale, U = kFp8Ue8m0, SR = kFp8ScaleRows;
   switch (o.flags) {
     case 0: return ll_quant_k<KT, 0>(x, slot, o, T, K, H, rows, status, s);
-    case kFp8RoundScale: return ll_quant_k<KT, kFp8RoundScale>(x, slot, o, T, K, H, rows, status, s);
-    default:
-      return ll_quant_k<KT, kFp8RoundScale | kFp8Ue8m0>(x, slot, o, T, K, H, rows, status, s);
+    case R1: return ll_quant_k<KT, R1>(x, slot, o, T, K, H, rows, status, s);
+    case R1 | U: return ll_quant_k<KT, R1 | U>(x, slot, o, T, K, H, rows, status, s);
+    case SR: return ll_quant_k<KT, SR>(x, slot, o, T, K, H, rows, status, s);
+    case SR | R1: return ll_quant_k<KT, SR | R1>(x, slot, o, T, K, H, rows, status, s);
+    default: return ll_quant_k<KT, SR | R1 | U>(x, slot, o, T, K, H, rows, status, s);
   }
 }
 
@@ -230,7 +240,7 @@ hipError_t launch_fp8_copy_dispatch(const uint8_t *xq, const float *xs, const in
 hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, void *scale, int32_t flags,
                                int32_t T, int32_t H, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  switch (flags) {
+  switch (flags & (kFp8RoundScale | kFp8Ue8m0)) {  // the cast alone is always row-major
     case 0: return quantize_k<0>(x, q, scale, T, H, s);
     case kFp8RoundScale: return quantize_k<kFp8RoundScale>(x, q, scale, T, H, s);
     default: return quantize_k<kFp8RoundScale | kFp8Ue8m0>(x, q, scale, T, H, s);

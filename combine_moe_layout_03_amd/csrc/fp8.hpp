@@ -28,6 +28,7 @@ namespace moe {
 
 constexpr int kFp8RoundScale = 1;  // scales rounded up to powers of two
 constexpr int kFp8Ue8m0 = 2;       // scales stored as packed exponent bytes
+constexpr int kFp8ScaleRows = 4;   // receive-side scales row-major [rows][...]
 constexpr int kFp8Group = 128;     // channels per scale
 
 typedef uint32_t fp8_u32x4 __attribute__((ext_vector_type(4)));
@@ -70,6 +71,7 @@ struct Fp8Lane {
 // Cast one lane's 8 bf16 values; the lane's DPP row is the 128-channel group.
 template <int kFlags>
 __device__ __forceinline__ Fp8Lane fp8_cast_lane(fp8_u32x4 v) {
+  // (kFp8ScaleRows only changes where the caller stores the scales)
   // |x| as bf16 bit patterns: for finite values the integer order is the
   // magnitude order
   uint32_t m = umax32(umax32(v.x & 0x7fffu, v.x >> 16 & 0x7fffu),

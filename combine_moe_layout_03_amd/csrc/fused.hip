@@ -327,9 +327,12 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           const int i = s - e * f.RM;  // row within the expert's R*M rows
           if (lane_ok) __builtin_nontemporal_store(codes, f.q + (int64_t)s * f.nvec + v);
           if (kFp8 & kFp8Ue8m0) {
-            if (lane == 0 && lane_ok) f.ue[((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
+            if (lane == 0 && lane_ok)
+              f.ue[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.nchunk + chunk
+                                          : ((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
           } else if ((lane & 15) == 0 && lane_ok) {
-            f.scale[((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
+            f.scale[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.G + grp
+                                           : ((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
           }
         } else if (s != -1 && wave == 0) {
           st |= kStBadSlot;  // receive buffer smaller than the layout needs
@@ -442,10 +445,14 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
     const int rounds = (P + counting - 1) / counting;
     const dim3 grid((unsigned)(f.token_wgs + f.duty_wgs)), block(threads);
     if (!fp8) return launch_rounds<true, -1>(rounds, grid, block, s, f);
+    constexpr int R1 = kFp8RoundScale, U = kFp8Ue8m0, SR = kFp8ScaleRows;
     switch (fp8->flags) {
       case 0: return launch_rounds<true, 0>(rounds, grid, block, s, f);
-      case kFp8RoundScale: return launch_rounds<true, kFp8RoundScale>(rounds, grid, block, s, f);
-      default: return launch_rounds<true, kFp8RoundScale | kFp8Ue8m0>(rounds, grid, block, s, f);
+      case R1: return launch_rounds<true, R1>(rounds, grid, block, s, f);
+      case R1 | U: return launch_rounds<true, R1 | U>(rounds, grid, block, s, f);
+      case SR: return launch_rounds<true, SR>(rounds, grid, block, s, f);
+      case SR | R1: return launch_rounds<true, SR | R1>(rounds, grid, block, s, f);
+      default: return launch_rounds<true, SR | R1 | U>(rounds, grid, block, s, f);
     }
   }
   f.nvec = f.nchunk = f.chunks_per_wg = f.wg_per_token = 0;

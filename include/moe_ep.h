@@ -69,6 +69,7 @@ extern "C" {
 #define MOE_FP8_ROUND_SCALE 1 /* scales rounded up to powers of two */
 #define MOE_FP8_UE8M0 2       /* scales stored as packed exponent bytes; needs
                                  MOE_FP8_ROUND_SCALE and H % 512 == 0 */
+#define MOE_FP8_SCALE_ROWS 4  /* low-latency scales row-major (see below) */
 
 /* Device-side status bits (OR-ed into *status). */
 #define MOE_STATUS_BAD_EXPERT 1   /* an id outside [-1, E): the pair is skipped */
@@ -231,14 +232,14 @@ int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
  * 4w..4w+3 in bytes 0..3 (low to high) of int32 word w. x must be finite:
  * a NaN or infinity gives unspecified codes and scale for its group.
  * H must be a multiple of 128 (of 512 with MOE_FP8_UE8M0); flags is 0,
- * MOE_FP8_ROUND_SCALE or MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0, anything else
- * returns MOE_ERR_FLAGS. Code and bf16 row pointers must be 16-byte aligned,
+ * MOE_FP8_ROUND_SCALE or MOE_FP8_ROUND_SCALE | MOE_FP8_UE8M0, optionally
+ * OR MOE_FP8_SCALE_ROWS; anything else returns MOE_ERR_FLAGS. Code and bf16 row pointers must be 16-byte aligned,
  * scale pointers 4-byte aligned.
  * ------------------------------------------------------------------- */
 
 /* The cast alone, row-major: q [T*H] E4M3 codes; scale [T*H/128] float, or
- * with MOE_FP8_UE8M0 [T*H/512] int32 words. Produces the (codes, scales)
- * tuple that moe_dispatch_fp8 takes. */
+ * with MOE_FP8_UE8M0 [T*H/512] int32 words (MOE_FP8_SCALE_ROWS has no effect
+ * here). Produces the (codes, scales) tuple that moe_dispatch_fp8 takes. */
 int moe_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, void *scale,
                      int32_t flags, hipStream_t stream);
 
@@ -249,8 +250,13 @@ int moe_quantize_fp8(int32_t T, int32_t H, const uint16_t *x, uint8_t *q, void *
  * recv_scale is [E][H/128][R*M] float -- the scale of group g for row i of
  * expert e's R*M rows (slot = e*R*M + i) is at (e*(H/128) + g)*R*M + i -- or,
  * with MOE_FP8_UE8M0, [E][H/512][R*M] int32 words placed the same way.
- * recv_rows <= E*R*M (normally moe_ll_recv_rows(E, R, M)). Entries no pair
- * maps to are left untouched. */
+ * recv_rows <= E*R*M (normally moe_ll_recv_rows(E, R, M)). With
+ * MOE_FP8_SCALE_ROWS (an option of this library, not of the page) the scales
+ * are row-major instead: [recv_rows][H/128] floats or [recv_rows][H/512]
+ * words, the scales of row slot at slot*(H/128) + g. The column-major format
+ * spreads each pair's scales over H/128 cache lines shared with the expert's
+ * other tokens; the row-major one keeps them in contiguous bytes of the row,
+ * which is cheaper to write. Entries no pair maps to are left untouched. */
 int moe_ll_layout_dispatch_fp8(const moe_shape *shape, int32_t M, int32_t src_rank,
                                const int64_t *topk_idx, const moe_layout_t *out,
                                const uint16_t *x, uint8_t *recv_q, void *recv_scale,

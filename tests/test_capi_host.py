@@ -153,14 +153,15 @@ def test_fp8_checks(lib):
     odd4 = C.c_void_p(258)
     lt = lib.moe_layout_t()
     lt.count = lt.offset = lt.slot = d
-    # flags: only 0, ROUND, ROUND|UE8M0
-    for bad in (2, 4, -1, 7):
+    # flags: 0, ROUND or ROUND|UE8M0, optionally with SCALE_ROWS (4)
+    for bad in (2, 6, 8, -1, 10):
         assert raw.moe_quantize_fp8(4, 512, d, d, d, bad, None) == -10
         assert raw.moe_ll_dispatch_fp8(C.byref(lib.make_shape(4, 512, 16, 4, 2, 1)), 4, d, d, d,
                                        d, 64, bad, None, None) == -10
     # H must be a multiple of 128 (512 with UE8M0)
     assert raw.moe_quantize_fp8(4, 136, d, d, d, 0, None) == -2
     assert raw.moe_quantize_fp8(4, 384, d, d, d, 3, None) == -2
+    assert raw.moe_quantize_fp8(4, 384, d, d, d, 7, None) == -2
     s = lib.make_shape(4, 384, 16, 4, 2, 1)
     assert raw.moe_ll_layout_dispatch_fp8(C.byref(s), 4, 0, d, C.byref(lt), d, d, d, 64, 3,
                                           None, 0, None) == -2

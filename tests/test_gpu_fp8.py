@@ -16,6 +16,8 @@ from gpu_path import dev, to_dev
 pytestmark = pytest.mark.gpu
 
 FLAGS = [0, 1, 3]  # plain, round_scale, round_scale + UE8M0
+ROWS = 4  # MOE_FP8_SCALE_ROWS: receive-side scales row-major
+LL_FLAGS = [0, 1, 3, 4, 5, 7]
 Q_SENT = 0x57  # code byte pre-filled into receive rows
 S_SENT = 0x7FC01234  # scale word pre-filled (a NaN: no real scale has it)
 
@@ -173,8 +175,8 @@ def run_ll_fp8(capi, w, M, src, flags, fused=True, rows=None):
     rows = full if rows is None else rows
     cols = capi.fp8_scale_cols(w.H, flags)
     rq = torch.full((full, w.H), Q_SENT, dtype=torch.uint8, device=dev())
-    rs = torch.empty((w.E, cols, w.R * M), dtype=torch.int32, device=dev()).fill_(
-        S_SENT)
+    sshape = (full, cols) if flags & ROWS else (w.E, cols, w.R * M)
+    rs = torch.empty(sshape, dtype=torch.int32, device=dev()).fill_(S_SENT)
     rs_arg = rs if flags & 2 else rs.view(torch.float32)
     idx = to_dev(w.topk_idx.astype(np.int64))
     nws = capi.moe_layout_workspace_bytes(shape)
@@ -215,7 +217,7 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", SMALL)
-@pytest.mark.parametrize("flags", FLAGS)
+@pytest.mark.parametrize("flags", LL_FLAGS)
 @pytest.mark.parametrize("fused", [True, False])
 def test_ll_fp8_small_full(capi, orc, case, flags, fused):
     seed, T, H, E, R, K, M, src, neg, dup = case
@@ -254,8 +256,11 @@ def gpu_check_ll_fp8(rq, rs, qz, slot, w, M, flags):
     s_ref = torch.from_numpy(np.ascontiguousarray(_ref_scale_bits(qz, flags)).view(np.int32)).to(
         dev())
     full = rq.shape[0]
-    cols = rs.shape[1]
-    rs_rows = rs.permute(0, 2, 1).reshape(full, cols)  # [E, R*M, cols] -> rows
+    if flags & ROWS:
+        rs_rows = rs  # already [rows, cols]
+    else:
+        cols = rs.shape[1]
+        rs_rows = rs.permute(0, 2, 1).reshape(full, cols)  # [E, R*M, cols] -> rows
     for a in range(0, rows_t.numel(), 4096):
         r, t = rows_t[a:a + 4096], toks_t[a:a + 4096]
         assert torch.equal(rq[r], q_ref[t]), "codes"
@@ -270,7 +275,7 @@ def gpu_check_ll_fp8(rq, rs, qz, slot, w, M, flags):
 
 
 @pytest.mark.parametrize("M", mi.C3_SWEEP)
-@pytest.mark.parametrize("flags", [0, 3])
+@pytest.mark.parametrize("flags", [0, 3, 4, 7])
 def test_ll_fp8_sweep(capi, orc, M, flags):
     w = mi.config_c3(M)
     src = 5
@@ -295,10 +300,11 @@ def test_ll_fp8_overflow(capi, orc):
     assert ref["status"] & 2
     qz = orc.quantize_fp8(w.x, 3)
     for fused in (True, False):
-        _announce(f"ll fp8 overflow M={M} fused={fused}")
-        got, rq, rs, _ = run_ll_fp8(capi, w, M, 1, 3, fused)
-        check_ll_layout(got, ref)
-        gpu_check_ll_fp8(rq, rs, qz, ref["slot"], w, M, 3)
+        for flags in (3, 7):
+            _announce(f"ll fp8 overflow M={M} fused={fused} flags={flags}")
+            got, rq, rs, _ = run_ll_fp8(capi, w, M, 1, flags, fused)
+            check_ll_layout(got, ref)
+            gpu_check_ll_fp8(rq, rs, qz, ref["slot"], w, M, flags)
 
 
 def test_ll_fp8_bad_slots(capi, orc):
