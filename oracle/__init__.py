@@ -82,6 +82,10 @@ class Oracle:
         lib.oracle_ll_dispatch_fp8.argtypes = [_I64, _I32, _I32, _I32, _I32, _I32, _I32, _P, _P,
                                                _P, _P, _P, _P, _P, _P]
         lib.oracle_quantize_fp8.restype = C.c_int
+        lib.oracle_combine_masked_f32.argtypes = [_I64, _I32, _I32, _P, _I64, _P, _P, _I32, _I32,
+                                                  _P, _P, _P, _P, _P]
+        lib.oracle_combine_masked_f32.restype = C.c_int
+        lib.oracle_accumulate_recv_stats.argtypes = [_I32, _P, _P]
         lib.oracle_ll_dispatch_fp8.restype = C.c_int
         for f in ("oracle_layout", "oracle_ll_layout", "oracle_expert_load", "oracle_dispatch",
                   "oracle_combine_f64", "oracle_combine_f32", "oracle_plan_replicas",
@@ -252,6 +256,34 @@ class Oracle:
         rq, st1 = self.dispatch(q.view(np.uint16), slot, rows, fill=fill16)
         rs, st2 = self.dispatch(scale.view(np.uint16), slot, rows, fill=fill16)
         return rq.view(np.uint8).reshape(rows, H), rs.view(np.float32).reshape(rows, G), st1 | st2
+
+    def combine_masked(self, y: np.ndarray, slot: np.ndarray, idx: np.ndarray, E: int, R: int,
+                       mask: np.ndarray, w: Optional[np.ndarray]) -> dict:
+        """Combine (float, ascending k) skipping pairs whose expert's rank is masked."""
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        slot = np.ascontiguousarray(slot, dtype=np.int32)
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        mask = np.ascontiguousarray(mask, dtype=np.int32)
+        T, K = slot.shape
+        rows, H = y.shape
+        if w is not None:
+            w = np.ascontiguousarray(w, dtype=np.float32)
+        o32 = np.empty((T, H), np.float32)
+        o16 = np.empty((T, H), np.uint16)
+        status = np.zeros(1, np.int32)
+        rc = self.lib.oracle_combine_masked_f32(T, H, K, _ptr(y), rows, _ptr(slot), _ptr(idx), E,
+                                                R, _ptr(mask), _ptr(w), _ptr(o32), _ptr(o16),
+                                                _ptr(status))
+        if rc != 0:
+            raise ValueError(rc)
+        return dict(out_f32=o32, out_bf16=o16, status=int(status[0]))
+
+    def accumulate_recv_stats(self, recv_count: np.ndarray, stats: np.ndarray) -> np.ndarray:
+        """stats += recv_count (cumulative_local_expert_recv_stats); returns stats."""
+        rc_ = np.ascontiguousarray(recv_count, dtype=np.int32)
+        st = np.ascontiguousarray(stats, dtype=np.int32).copy()
+        self.lib.oracle_accumulate_recv_stats(rc_.size, _ptr(rc_), _ptr(st))
+        return st
 
     # -- replicas -----------------------------------------------------------
     def plan_replicas(self, load: np.ndarray, R: int, C_: int) -> dict:

@@ -337,6 +337,40 @@ int oracle_combine_f32(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64
     return 0;
 }
 
+/* Combine with an active-rank mask ([P1] Buffer.low_latency_combine on a
+ * buffer whose ranks can be masked; the combine checks each destination
+ * rank's mask entry, as the NIXL EP notes describe for the combine loops).
+ * A pair whose expert lives on a masked rank (mask[e / L] != 0, L = E / R)
+ * contributes nothing, as if its expert output never arrived; otherwise the
+ * sum is oracle_combine_f32's (ascending k, float, no fused multiply-add). */
+int oracle_combine_masked_f32(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64_t rows,
+                              const int32_t *slot, const int64_t *idx, int32_t E, int32_t R,
+                              const int32_t *mask, const float *w, float *out_f32,
+                              uint16_t *out_bf16, int32_t *status) {
+    if (E < 1 || R < 1 || E % R != 0) return -2;
+    const int32_t L = E / R;
+    int32_t *s2 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(T * K > 0 ? T * K : 1));
+    for (int64_t p = 0; p < T * K; ++p) {
+        int64_t e = idx[p];
+        int masked = valid_id(e, E) && mask[e / L] != 0;
+#if ORACLE_MUTANT == 17
+        masked = valid_id(e, E) && mask[e % R] != 0; /* mutant: rank taken as e mod R */
+#endif
+        s2[p] = masked ? -1 : slot[p];
+    }
+    int rc = oracle_combine_f32(T, H, K, y, rows, s2, w, out_f32, out_bf16, status);
+    free(s2);
+    return rc;
+}
+
+/* [P1] Buffer.low_latency_dispatch, cumulative_local_expert_recv_stats: a
+ * running per-expert count of received tokens, stats[e] += recv_count[e]
+ * for every dispatch (the union of the ranks' [L] tensors: rank r's local
+ * expert l is entry r*L + l). */
+void oracle_accumulate_recv_stats(int32_t E, const int32_t *recv_count, int32_t *stats) {
+    for (int32_t e = 0; e < E; ++e) stats[e] += recv_count[e];
+}
+
 /* ------------------------------------------------------------------ */
 /* Replica plan and routing expansion ([P3] Overview; GPU operations:  */
 /* Placement planning, Routing expansion)                              */

@@ -560,6 +560,60 @@ def check_ll_fp8_dispatch(orc, n: int = 8, seed: int = 9):
                 assert np.array_equal(rowm["recv_ue8m0"], ru)
 
 
+def check_combine_masked(orc, n: int = 30, seed: int = 10):
+    """Masked combine against a dense formulation (numpy, f64): the weight of a
+    pair on a masked rank is zeroed in W before W @ Y; the float sum is within
+    the K-term float bound of it. Closed forms: no rank masked gives the plain
+    combine bit for bit; every rank masked gives +0 everywhere."""
+    rng = np.random.default_rng(seed)
+    for i in range(n):
+        R = int(rng.choice([1, 2, 4, 8]))
+        E = R * int(rng.integers(1, 5))
+        K = int(rng.integers(1, 7))
+        T = int(rng.integers(1, 30))
+        w = mi.random_case(800 + i, T, 16, E, R, K, neg_frac=0.2, dup_frac=0.2)
+        lay = orc.layout(w.topk_idx, E, R, 1)
+        y = mi.to_bf16_bits(rng.standard_normal((max(lay["rows"], 1), 16)).astype(np.float32))
+        mask = (rng.random(R) < 0.4).astype(np.int32)
+        got = orc.combine_masked(y, lay["slot"], w.topk_idx, E, R, mask, w.topk_weights)
+        L = E // R
+        W = np.zeros((T, y.shape[0]))
+        absW = np.zeros((T, y.shape[0]))
+        for t in range(T):
+            for k in range(K):
+                e, s_ = w.topk_idx[t, k], lay["slot"][t, k]
+                if s_ < 0 or mask[e // L]:
+                    continue
+                W[t, s_] += w.topk_weights[t, k]
+                absW[t, s_] += abs(float(w.topk_weights[t, k]))
+        yf = mi.bf16_bits_to_f32(y).astype(np.float64)
+        ref = W @ yf
+        bound = (K + 1) * 2.0 ** -24 * (absW @ np.abs(yf)) + 1e-30
+        assert np.all(np.abs(got["out_f32"].astype(np.float64) - ref) <= bound)
+        none = orc.combine_masked(y, lay["slot"], w.topk_idx, E, R, np.zeros(R, np.int32),
+                                  w.topk_weights)
+        plain = orc.combine(y, lay["slot"], w.topk_weights, "f32")
+        assert np.array_equal(none["out_f32"].view(np.uint32), plain["out_f32"].view(np.uint32))
+        allm = orc.combine_masked(y, lay["slot"], w.topk_idx, E, R, np.ones(R, np.int32),
+                                  w.topk_weights)
+        assert np.all(allm["out_f32"].view(np.uint32) == 0)
+
+
+def check_recv_stats(orc, seed: int = 11):
+    """Cumulative receive counts: after n dispatches of the same batch the
+    stats hold n times the per-expert receive counts (numpy bincount of the
+    valid ids, capped at M for the low-latency layout)."""
+    w = mi.random_case(900, 40, 16, 32, 4, 4, neg_frac=0.1, dup_frac=0.1)
+    M = 40
+    ll = orc.ll_layout(w.topk_idx, 32, 4, M, 1)
+    ids = w.topk_idx[(w.topk_idx >= 0) & (w.topk_idx < 32)]
+    want = np.minimum(np.bincount(ids, minlength=32), M)
+    st = np.full(32, 5, np.int32)
+    for n in range(1, 4):
+        st = orc.accumulate_recv_stats(ll["recv_count"], st)
+        assert np.array_equal(st, 5 + n * want)
+
+
 ALL_SMALL_CHECKS = (
     check_golden,
     check_layout_vs_bruteforce,
@@ -573,4 +627,6 @@ ALL_SMALL_CHECKS = (
     lambda o: check_e4m3_vs_torch(o, n=1 << 14),
     lambda o: check_fp8_cast_on_inputs(o, n=2),
     lambda o: check_ll_fp8_dispatch(o, n=3),
+    lambda o: check_combine_masked(o, n=8),
+    check_recv_stats,
 )

@@ -24,6 +24,7 @@ MUTANTS = {
     14: "UE8M0 bytes packed high to low",
     15: "FP8 amax over the whole row",
     16: "row-major UE8M0 scales stored transposed",
+    17: "masked combine takes the rank as e mod R",
 }
 
 

@@ -133,3 +133,11 @@ def test_fp8_tuple_dispatch_is_row_copy(orc):
             assert np.array_equal(rq[r], qz["q"][t]) and np.array_equal(rs[r], qz["scale"][t])
     assert np.all(rq[~used] == 0x57) or np.all(rq[~used].view(np.uint16) == 0x7E57)
     assert np.all(rs[~used].view(np.uint32) == 0x7E577E57)
+
+
+def test_masked_combine_vs_dense_and_closed_forms(orc):
+    pins.check_combine_masked(orc, n=40)
+
+
+def test_recv_stats_accumulate(orc):
+    pins.check_recv_stats(orc)
