@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
 
-MOE_ABI_VERSION = 2  # the version the binding is written against
+MOE_ABI_VERSION = 3  # the version the binding is written against
 
 MOE_STATUS_BAD_EXPERT = 1
 MOE_STATUS_LL_OVERFLOW = 2
@@ -50,7 +50,8 @@ class moe_shape(C.Structure):
 
 class moe_layout_t(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("count", "offset", "rank_token_count",
-                                          "is_token_in_rank", "slot", "row_src", "status")]
+                                          "is_token_in_rank", "slot", "row_src", "status",
+                                          "recv_stats")]
 
 
 def _load():
@@ -79,6 +80,7 @@ def _load():
                                                  P]),
         "moe_ll_dispatch_fp8": (C.c_int, [P, I32, P, P, P, P, I64, I32, P, P]),
         "moe_dispatch_fp8": (C.c_int, [P, P, P, P, P, P, I64, P, P]),
+        "moe_combine_masked": (C.c_int, [P, P, I64, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -93,7 +95,7 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_re
             "moe_ll_layout_dispatch", "moe_expert_load",
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
             "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
-            "moe_dispatch_fp8")
+            "moe_dispatch_fp8", "moe_combine_masked")
 
 
 def lib():
@@ -169,6 +171,7 @@ class LayoutBuffers:
     is_token_in_rank: Optional[torch.Tensor] = None
     row_src: Optional[torch.Tensor] = None
     status: Optional[torch.Tensor] = None
+    recv_stats: Optional[torch.Tensor] = None  # [E] int32, cumulative (+= count)
 
     @staticmethod
     def empty(shape: moe_shape, device, ll_M: Optional[int] = None, extras: bool = True,
@@ -203,6 +206,7 @@ class LayoutBuffers:
             _dev(self.slot, "slot", i32, T * K),
             _dev(self.row_src, "row_src", i32, rs_need, optional=True),
             _dev(self.status, "status", i32, 1, optional=True),
+            _dev(self.recv_stats, "recv_stats", i32, E, optional=True),
         )
 
 
@@ -311,6 +315,23 @@ def moe_combine(shape: moe_shape, y: torch.Tensor, recv_rows: int, slot: torch.T
         C.byref(shape), _dev(y, "y", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
         _dev(slot, "slot", (torch.int32,), T * K),
         _dev(topk_weights, "topk_weights", (torch.float32,), T * K, optional=True),
+        _dev(out, "out", _BF16_LIKE, T * H),
+        _dev(out_f32, "out_f32", (torch.float32,), T * H, optional=True),
+        _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
+
+
+def moe_combine_masked(shape: moe_shape, y: torch.Tensor, recv_rows: int, slot: torch.Tensor,
+                       topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                       rank_mask: torch.Tensor, out: torch.Tensor,
+                       out_f32: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None, stream=None) -> int:
+    T, H, K = shape.T, shape.H, shape.K
+    return _check("moe_combine_masked", _lib.moe_combine_masked(
+        C.byref(shape), _dev(y, "y", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
+        _dev(slot, "slot", (torch.int32,), T * K),
+        _dev(topk_idx, "topk_idx", (torch.int64,), T * K),
+        _dev(topk_weights, "topk_weights", (torch.float32,), T * K, optional=True),
+        _dev(rank_mask, "rank_mask", (torch.int32,), shape.R),
         _dev(out, "out", _BF16_LIKE, T * H),
         _dev(out_f32, "out_f32", (torch.float32,), T * H, optional=True),
         _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))

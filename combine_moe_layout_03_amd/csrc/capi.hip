@@ -122,6 +122,7 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   p->slot = out->slot;
   p->row_src = out->row_src;
   p->status = out->status;
+  p->recv_stats = out->recv_stats;
   if (one_block(s)) {
     p->tokens_per_block = s->T > 0 ? s->T : 1;
     p->nblocks = 1;
@@ -364,7 +365,28 @@ MOE_API int moe_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_
   rc = check_device();
   if (rc) return rc;
   return launch_combine(y, recv_rows, slot, topk_weights, out, out_f32, shape->T, shape->K,
-                        shape->H, status, stream) == hipSuccess
+                        shape->H, nullptr, status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_combine_masked(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                               const int32_t *slot, const int64_t *topk_idx,
+                               const float *topk_weights, const int32_t *rank_mask,
+                               uint16_t *out, float *out_f32, int32_t *status,
+                               hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!slot || !out || !topk_idx || !rank_mask || (!y && recv_rows > 0)) return MOE_ERR_NULL;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  const uint64_t L = (uint64_t)(shape->E / shape->R);
+  const CombineMask cm{topk_idx, rank_mask, shape->E, ((1ull << 32) + L - 1) / L};
+  return launch_combine(y, recv_rows, slot, topk_weights, out, out_f32, shape->T, shape->K,
+                        shape->H, &cm, status, stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_LAUNCH;
 }

@@ -194,10 +194,12 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
     }
     if (!ll) {
       p.count[ed] = c;
+      if (p.recv_stats) p.recv_stats[ed] += c;
       p.offset[ed] = lt;
       if (ed == E - 1) p.offset[E] = lt + c;
     } else {
       p.count[ed] = min(c, p.M);
+      if (p.recv_stats) p.recv_stats[ed] += min(c, p.M);
       if (c > p.M) st |= kStOverflow;
       if (p.offset) {
         p.offset[ed] = (ed * R + p.src) * p.M;

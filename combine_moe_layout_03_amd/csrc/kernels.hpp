@@ -42,6 +42,7 @@ struct LayoutParams {
   int32_t *slot;
   int32_t *row_src;
   int32_t *status;
+  int32_t *recv_stats;  // [E] cumulative receive counts (+= count), may be null
   int32_t *ws_hist;  // [E][nblocks]  multi-block path: pairs of e per block, then prefix
   int32_t *ws_rcnt;  // [R][nblocks]  multi-block path: tokens reaching r per block
   int32_t *ws_cnt;   // [E]           multi-block path: pairs per expert
@@ -93,9 +94,17 @@ hipError_t launch_quantize_fp8(const uint16_t *x, uint8_t *q, void *scale, int32
 
 hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                            int32_t K, int32_t H, int64_t rows, int32_t *status, hipStream_t s);
+// Active-rank mask of a combine: pairs whose expert e lives on a rank r with
+// mask[r] != 0 are left out of the sum.
+struct CombineMask {
+  const int64_t *idx;   // [T*K] expert ids
+  const int32_t *mask;  // [R]
+  int32_t E;
+  uint64_t l_magic;     // rank of e = (e * l_magic) >> 32
+};
 hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                           uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
-                          int32_t *status, hipStream_t s);
+                          const CombineMask *mask, int32_t *status, hipStream_t s);
 
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,

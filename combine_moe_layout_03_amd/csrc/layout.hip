@@ -95,12 +95,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     if (e < E) {
       if (p.mode == kModeContiguous) {
         p.count[e] = c;
+        if (p.recv_stats) p.recv_stats[e] += c;
         p.offset[e] = excl;
         if (e == E - 1) p.offset[E] = total;
         s_base[e] = excl;
       } else {
         const int base = (e * R + p.src) * p.M;
         p.count[e] = min(c, p.M);
+        if (p.recv_stats) p.recv_stats[e] += min(c, p.M);
         if (c > p.M) st |= kStOverflow;
         if (p.offset) {
           p.offset[e] = base;
@@ -257,9 +259,11 @@ __global__ __launch_bounds__(kFixupThreads) void layout_fixup_kernel(LayoutParam
     if (blockIdx.x == 0) {
       if (contiguous) {
         p.count[e] = c;
+        if (p.recv_stats) p.recv_stats[e] += c;
         p.offset[e] = base;
       } else {
         p.count[e] = min(c, p.M);
+        if (p.recv_stats) p.recv_stats[e] += min(c, p.M);
         if (c > p.M) st |= kStOverflow;
         if (p.offset) p.offset[e] = base;
       }

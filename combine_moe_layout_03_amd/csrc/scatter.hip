@@ -6,7 +6,12 @@
 // the receive buffer.
 // Combine (same page, Buffer.low_latency_combine "reduce with weights"; and
 // Buffer.combine): each token's expert outputs are summed back, times their
-// top-k weights, into a bf16 row.
+// top-k weights, into a bf16 row. Optionally with an active-rank mask (the
+// NIXL EP notes: the combine loops check each rank's mask entry): pairs whose
+// expert lives on a masked rank are left out. The row loads do not wait for
+// the mask -- they are issued from the slots as usual, and the (scalar) id and
+// mask reads complete while the rows are in flight; the mask only gates the
+// sum.
 //
 // Both are HBM-bound streams with no data reuse, so the design is about
 // bytes in flight: a thread owns one 16-byte vector (8 bf16) of one token row,
@@ -76,14 +81,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
-template <int KT, bool kWeights, bool kF32Out>
+template <int KT, bool kWeights, bool kF32Out, bool kMask>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ y, int64_t rows,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ w,
                                                       u32x4 *__restrict__ out,
                                                       f32x4 *__restrict__ out_f32, int32_t T,
                                                       int32_t Kr, int32_t nvec, int32_t nchunk,
-                                                      int32_t *status) {
+                                                      CombineMask cm, int32_t *status) {
 #pragma clang fp contract(off)
   const int K = KT ? KT : Kr;
   int t;
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
   for (int k0 = 0; k0 < K; k0 += G) {
     int32_t s[G];
     float wk[G];
-    bool ok[G];
+    bool ok[G], off[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const bool in = k0 + g < K;
@@ -111,13 +116,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       ok[g] = s[g] >= 0 && s[g] < rows;
-      if (!ok[g] && s[g] != -1) st |= kStBadSlot;
       val[g] = u32x4{0u, 0u, 0u, 0u};
       if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nvec + v);
     }
 #pragma unroll
+    for (int g = 0; g < G; ++g) {  // masked ranks (scalar reads, rows already in flight)
+      off[g] = false;
+      if (kMask && k0 + g < K) {
+        const int64_t e = cm.idx[(int64_t)t * K + k0 + g];
+        off[g] = e >= 0 && e < cm.E && cm.mask[rank_of((int)e, cm.l_magic)] != 0;
+      }
+      if (!ok[g] && s[g] != -1 && !off[g]) st |= kStBadSlot;
+    }
+#pragma unroll
     for (int g = 0; g < G; ++g) {
-      if (!ok[g]) continue;
+      if (!ok[g] || off[g]) continue;
       const float a = wk[g];
       const u32x4 q = val[g];
       acc[0] = acc[0] + a * bf16_lo(q.x);
@@ -158,30 +171,41 @@ hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, in
   return hipGetLastError();
 }
 
-template <int KT, bool kW, bool kF>
+template <int KT, bool kW, bool kF, bool kM>
 hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                       uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
-                      int32_t *status, hipStream_t s) {
+                      const CombineMask &cm, int32_t *status, hipStream_t s) {
   const int32_t nchunk = (nvec + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
   const unsigned blocks = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((combine_kernel<KT, kW, kF>), dim3(blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM>), dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(y), rows, slot, w,
                      reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
-                     nvec, nchunk, status);
+                     nvec, nchunk, cm, status);
   return hipGetLastError();
+}
+
+template <int KT, bool kM>
+hipError_t combine_km(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
+                      uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
+                      const CombineMask &cm, int32_t *status, hipStream_t s) {
+  if (w) {
+    if (out_f32)
+      return combine_k3<KT, true, true, kM>(y, rows, slot, w, out, out_f32, T, K, nvec, cm, status, s);
+    return combine_k3<KT, true, false, kM>(y, rows, slot, w, out, out_f32, T, K, nvec, cm, status, s);
+  }
+  if (out_f32)
+    return combine_k3<KT, false, true, kM>(y, rows, slot, w, out, out_f32, T, K, nvec, cm, status, s);
+  return combine_k3<KT, false, false, kM>(y, rows, slot, w, out, out_f32, T, K, nvec, cm, status, s);
 }
 
 template <int KT>
 hipError_t combine_k(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                      uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t nvec,
-                     int32_t *status, hipStream_t s) {
-  if (w) {
-    if (out_f32) return combine_k3<KT, true, true>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    return combine_k3<KT, true, false>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-  }
-  if (out_f32) return combine_k3<KT, false, true>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-  return combine_k3<KT, false, false>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+                     const CombineMask *mask, int32_t *status, hipStream_t s) {
+  if (mask) return combine_km<KT, true>(y, rows, slot, w, out, out_f32, T, K, nvec, *mask, status, s);
+  const CombineMask none{nullptr, nullptr, 0, 0};
+  return combine_km<KT, false>(y, rows, slot, w, out, out_f32, T, K, nvec, none, status, s);
 }
 
 }  // namespace
@@ -202,16 +226,16 @@ hipError_t launch_dispatch(const uint16_t *x, const int32_t *slot, uint16_t *rec
 
 hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, const float *w,
                           uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
-                          int32_t *status, hipStream_t s) {
+                          const CombineMask *mask, int32_t *status, hipStream_t s) {
   if (T <= 0) return hipSuccess;  // nothing to launch
   const int32_t nvec = H / 8;
   switch (K) {
-    case 1: return combine_k<1>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    case 2: return combine_k<2>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    case 4: return combine_k<4>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    case 6: return combine_k<6>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    case 8: return combine_k<8>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
-    default: return combine_k<0>(y, rows, slot, w, out, out_f32, T, K, nvec, status, s);
+    case 1: return combine_k<1>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+    case 2: return combine_k<2>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+    case 4: return combine_k<4>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+    case 6: return combine_k<6>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+    case 8: return combine_k<8>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+    default: return combine_k<0>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
   }
 }
 

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Host-side return codes. */
 #define MOE_OK 0
@@ -103,6 +103,10 @@ typedef struct {
                                 Low latency: [E*M], pair held by stripe row j of expert e at
                                 e*M + j, -1 where empty. May be NULL. */
   int32_t *status;           /* [1] sticky MOE_STATUS_* bits. May be NULL. */
+  int32_t *recv_stats;       /* [E] cumulative receive counts (Buffer.low_latency_dispatch,
+                                cumulative_local_expert_recv_stats; rank r's local expert l
+                                is entry r*L + l): every layout call adds count[e] to entry e.
+                                The caller initialises it. May be NULL. */
 } moe_layout_t;
 
 /* ABI version (MOE_ABI_VERSION) of the loaded library. */
@@ -192,6 +196,20 @@ int moe_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *slot,
 int moe_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
                 const int32_t *slot, const float *topk_weights, uint16_t *out, float *out_f32,
                 int32_t *status, hipStream_t stream);
+
+/* Combine with an active-rank mask (the NIXL EP change notes, "Combine active
+ * rank mask optimization": the combine loops check each destination rank's
+ * mask entry). As moe_combine, except that a pair whose expert e lives on a
+ * masked rank -- rank_mask[e / L] != 0, L = E/R -- contributes nothing (and a
+ * bad slot on such a pair is not reported): the masked rank's expert output is
+ * treated as absent.
+ *   topk_idx [T*K] int64: the routing the slots were made from;
+ *   rank_mask [R] int32: nonzero = masked. Both device memory, read with
+ *   plain loads (the mask is data written before the launch). */
+int moe_combine_masked(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                       const int32_t *slot, const int64_t *topk_idx, const float *topk_weights,
+                       const int32_t *rank_mask, uint16_t *out, float *out_f32, int32_t *status,
+                       hipStream_t stream);
 
 /* Replica plan (ultraep GPU operations, Placement planning): the C most loaded
  * experts (load descending, ties to the lower id) get a second physical

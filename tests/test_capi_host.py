@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 18, declared
+    assert len(declared) == 19, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -196,3 +196,23 @@ def test_fp8_checks(lib):
     assert raw.moe_ll_dispatch_fp8(C.byref(s0), 4, None, None, None, None, 0, 0, None,
                                    None) == 0
     assert raw.moe_dispatch_fp8(C.byref(s0), None, None, None, None, None, 0, None, None) == 0
+
+
+def test_combine_masked_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(258)
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    args = lambda **kw: [kw.get(n, d) for n in ("y", "slot", "idx", "w", "mask", "out")]
+    y, slot, idx, w, mask, out = args()
+    assert raw.moe_combine_masked(C.byref(s), y, 8, slot, None, w, mask, out, None, None,
+                                  None) == -1
+    assert raw.moe_combine_masked(C.byref(s), y, 8, slot, idx, w, None, out, None, None,
+                                  None) == -1
+    assert raw.moe_combine_masked(C.byref(s), y, -1, slot, idx, w, mask, out, None, None,
+                                  None) == -3
+    assert raw.moe_combine_masked(C.byref(s), y, 8, slot, idx, w, mask, odd, None, None,
+                                  None) == -5
+    s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
+    assert raw.moe_combine_masked(C.byref(s0), None, 0, None, None, None, None, None, None,
+                                  None, None) == 0
