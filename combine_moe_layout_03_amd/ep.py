@@ -15,7 +15,7 @@ no host synchronisation.
 from __future__ import annotations
 
 from dataclasses import dataclass
-from typing import Optional, Tuple
+from typing import Optional, Tuple, Union
 
 import torch
 
@@ -31,6 +31,7 @@ class Handle:
     recv_rows: int
     ll_M: Optional[int] = None
     src_rank: int = 0
+    topk_idx: Optional[torch.Tensor] = None  # kept for a masked combine
 
 
 def _workspace(shape: capi.moe_shape, device) -> Optional[torch.Tensor]:
@@ -52,10 +53,26 @@ def get_dispatch_layout(topk_idx: torch.Tensor, num_experts: int, num_ranks: int
             lay.is_token_in_rank.view(T, num_ranks).bool(), h)
 
 
-def dispatch(x: torch.Tensor, handle: Handle, recv_x: Optional[torch.Tensor] = None):
-    """Scatter bf16 rows into the contiguous receive buffer, sized for the worst
+def dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]], handle: Handle,
+             recv_x: Optional[torch.Tensor] = None):
+    """Scatter rows into the contiguous receive buffer, sized for the worst
     case (T*K + E*(A-1) rows, so no host read of the counts is needed).
-    Rows [offset[e], offset[e] + count[e]) belong to expert e."""
+    Rows [offset[e], offset[e] + count[e]) belong to expert e. x is bf16
+    [T, H], or (as on the page) a tuple of E4M3 codes [T, H] and float scales
+    [T, H/128], in which case the result is the tuple (codes, scales) of the
+    receive rows."""
+    if isinstance(x, tuple):
+        xq, xs = x
+        T, H = xq.shape
+        shape = capi.make_shape(T, H, handle.shape.E, handle.shape.R, handle.shape.K,
+                                handle.shape.A)
+        handle.shape = shape
+        rows = max(handle.recv_rows, 1)
+        rq = torch.empty(rows, H, dtype=xq.dtype, device=xq.device)
+        rs = torch.empty(rows, H // capi.FP8_GROUP, dtype=torch.float32, device=xq.device)
+        capi.moe_dispatch_fp8(shape, xq.contiguous(), xs.contiguous(), handle.layout.slot,
+                              rq.view(torch.uint8), rs, handle.recv_rows, handle.layout.status)
+        return rq, rs
     T, H = x.shape
     shape = capi.make_shape(T, H, handle.shape.E, handle.shape.R, handle.shape.K,
                             handle.shape.A)
@@ -101,31 +118,72 @@ def combine(y: torch.Tensor, handle: Handle, topk_weights: Optional[torch.Tensor
 def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
                          num_max_dispatch_tokens_per_rank: int, num_experts: int,
                          num_ranks: int, src_rank: int = 0,
+                         cumulative_local_expert_recv_stats: Optional[torch.Tensor] = None,
+                         use_fp8: bool = False, round_scale: bool = False,
+                         use_ue8m0: bool = False, scale_rows: bool = False,
                          recv_x: Optional[torch.Tensor] = None):
     """Padded low-latency dispatch from source rank ``src_rank``. Returns
     (recv_x [R, L, R*M, H] -- rank r's receive buffer is recv_x[r] --,
     recv_count [E] int32, handle). Only the source's stripe is written; rows
-    past recv_count are not valid."""
+    past recv_count are not valid.
+
+    use_fp8: recv_x is the tuple (E4M3 codes [R, L, R*M, H], scales), the
+    scales as on the page: float [R, L, R*M, H/128] (UE8M0: int32
+    [R, L, R*M, H/512]) whose last two dimensions are column-major; with
+    scale_rows (an option of this library) they are row-major instead.
+    cumulative_local_expert_recv_stats: an [E] int32 tensor (the R ranks'
+    [L] tensors end to end) to which the receive counts are added."""
     T, H = x.shape
     K = topk_idx.shape[1]
     M = int(num_max_dispatch_tokens_per_rank)
     E, R = num_experts, num_ranks
+    L = E // R
     shape = capi.make_shape(T, H, E, R, K, 1)
     lay = capi.LayoutBuffers.empty(shape, x.device, ll_M=M)
+    lay.recv_stats = cumulative_local_expert_recv_stats
     rows = capi.moe_ll_recv_rows(E, R, M)
+    ws = _workspace(shape, x.device)
+    idx = topk_idx.contiguous()
+    h = Handle(shape, lay, rows, ll_M=M, src_rank=src_rank, topk_idx=idx)
+    if use_fp8:
+        flags = ((capi.MOE_FP8_ROUND_SCALE if round_scale or use_ue8m0 else 0)
+                 | (capi.MOE_FP8_UE8M0 if use_ue8m0 else 0)
+                 | (capi.MOE_FP8_SCALE_ROWS if scale_rows else 0))
+        cols = capi.fp8_scale_cols(H, flags)
+        sdt = torch.int32 if use_ue8m0 else torch.float32
+        q = torch.empty(rows, H, dtype=torch.float8_e4m3fn, device=x.device)
+        if scale_rows:
+            sc = torch.empty(rows, cols, dtype=sdt, device=x.device)
+            sc_view = sc.view(R, L, R * M, cols)
+        else:
+            sc = torch.empty(E, cols, R * M, dtype=sdt, device=x.device)
+            sc_view = sc.view(R, L, cols, R * M).transpose(2, 3)
+        capi.moe_ll_layout_dispatch_fp8(shape, M, src_rank, idx, lay, x.contiguous(),
+                                        q.view(torch.uint8), sc, rows, flags, ws)
+        return (q.view(R, L, R * M, H), sc_view), lay.count, h
     if recv_x is None:
         recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
-    capi.moe_ll_layout_dispatch(shape, M, src_rank, topk_idx.contiguous(), lay, x.contiguous(),
-                                recv_x, rows, _workspace(shape, x.device))
-    h = Handle(shape, lay, rows, ll_M=M, src_rank=src_rank)
-    return recv_x.view(R, E // R, R * M, H), lay.count, h
+    capi.moe_ll_layout_dispatch(shape, M, src_rank, idx, lay, x.contiguous(), recv_x, rows, ws)
+    return recv_x.view(R, L, R * M, H), lay.count, h
 
 
 def low_latency_combine(y: torch.Tensor, topk_weights: torch.Tensor, handle: Handle,
-                        out: Optional[torch.Tensor] = None):
+                        out: Optional[torch.Tensor] = None,
+                        rank_mask: Optional[torch.Tensor] = None):
     """Weighted reduce from the padded layout in place (the expert wrote its
-    outputs straight into the padded buffer, as with zero_copy)."""
-    return combine(y.reshape(-1, y.shape[-1]), handle, topk_weights, out)
+    outputs straight into the padded buffer, as with zero_copy). rank_mask
+    ([R] int32, nonzero = masked): pairs whose expert lives on a masked rank
+    are left out (the combine's active-rank mask)."""
+    if rank_mask is None:
+        return combine(y.reshape(-1, y.shape[-1]), handle, topk_weights, out)
+    shape = handle.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty(shape.T, H, dtype=torch.bfloat16, device=y.device)
+    capi.moe_combine_masked(shape, y.reshape(-1, H).contiguous(), handle.recv_rows,
+                            handle.layout.slot, handle.topk_idx, topk_weights.contiguous(),
+                            rank_mask.contiguous(), out, None, handle.layout.status)
+    return out
 
 
 def expert_load(topk_idx: torch.Tensor, num_experts: int,
