@@ -86,6 +86,10 @@ class Oracle:
                                                   _P, _P, _P, _P, _P]
         lib.oracle_combine_masked_f32.restype = C.c_int
         lib.oracle_accumulate_recv_stats.argtypes = [_I32, _P, _P]
+        lib.oracle_rank_layout.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P,
+                                           _P, _P, _P]
+        lib.oracle_rank_layout.restype = C.c_int
+        lib.oracle_combine_rank_weights.argtypes = [_I64, _I32, _I32, _P, _P, _I64, _P, _P]
         lib.oracle_ll_dispatch_fp8.restype = C.c_int
         for f in ("oracle_layout", "oracle_ll_layout", "oracle_expert_load", "oracle_dispatch",
                   "oracle_combine_f64", "oracle_combine_f32", "oracle_plan_replicas",
@@ -284,6 +288,43 @@ class Oracle:
         st = np.ascontiguousarray(stats, dtype=np.int32).copy()
         self.lib.oracle_accumulate_recv_stats(rc_.size, _ptr(rc_), _ptr(st))
         return st
+
+    # -- normal mode: one row per (token, rank) ----------------------------
+    def rank_layout(self, idx: np.ndarray, E: int, R: int, A: int = 1,
+                    w: Optional[np.ndarray] = None) -> dict:
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        T, K = idx.shape
+        worst = max(T * min(K, R), 1)
+        rank_slot = np.empty((T, R), np.int32)
+        rank_offset = np.empty(R + 1, np.int32)
+        recv_src = np.empty(worst, np.int32)
+        recv_idx = np.empty((worst, K), np.int64)
+        recv_w = np.empty((worst, K), np.float32)
+        rec = np.empty(E, np.int32)
+        status = np.zeros(1, np.int32)
+        if w is not None:
+            w = np.ascontiguousarray(w, dtype=np.float32)
+        rc = self.lib.oracle_rank_layout(T, K, E, R, A, _ptr(idx), _ptr(w), _ptr(rank_slot),
+                                         _ptr(rank_offset), _ptr(recv_src), _ptr(recv_idx),
+                                         _ptr(recv_w), _ptr(rec), _ptr(status))
+        if rc != 0:
+            raise ValueError(f"oracle_rank_layout rejected its arguments ({rc})")
+        rows = int(rank_offset[R])
+        return dict(rank_slot=rank_slot, rank_offset=rank_offset, recv_src=recv_src[:rows].copy(),
+                    recv_topk_idx=recv_idx[:rows].copy(),
+                    recv_topk_weights=recv_w[:rows].copy() if w is not None else None,
+                    recv_expert_count=rec, rows=rows, status=int(status[0]))
+
+    def combine_rank_weights(self, rank_slot: np.ndarray, recv_w: np.ndarray) -> tuple:
+        rank_slot = np.ascontiguousarray(rank_slot, dtype=np.int32)
+        recv_w = np.ascontiguousarray(recv_w, dtype=np.float32)
+        T, R = rank_slot.shape
+        rows, K = recv_w.shape
+        out = np.empty((T, K), np.float32)
+        status = np.zeros(1, np.int32)
+        self.lib.oracle_combine_rank_weights(T, K, R, _ptr(rank_slot), _ptr(recv_w), rows,
+                                             _ptr(out), _ptr(status))
+        return out, int(status[0])
 
     # -- replicas -----------------------------------------------------------
     def plan_replicas(self, load: np.ndarray, R: int, C_: int) -> dict:

@@ -28,6 +28,8 @@
  *     (e*R + s)*M + j; pairs with j >= M are dropped and set status bit 2;
  *   - replica plan: the C most loaded experts (ties -> lower id) get one extra
  *     physical replica; a pair of token t uses replica (t mod count);
+ *   - normal mode sends one row per (token, rank), tokens ascending within a
+ *     rank; received expert ids are rank-local (-1 for other ranks' experts);
  *   - FP8: one scale per 128 channels, max(amax, 1e-4) / 448; codes are the
  *     nearest E4M3 of x / scale (ties to even, saturating at 448, sign kept);
  *     round_scale rounds the scale up to a power of two; UE8M0 packs group
@@ -236,6 +238,90 @@ int oracle_expert_load(int64_t T, int32_t K, int32_t E, const int64_t *idx, int3
         }
         load[e] += 1;
     }
+    return 0;
+}
+
+/* Normal-mode layout, one row per (token, rank) ([P1] Buffer.dispatch:
+ * num_tokens_per_rank, is_token_in_rank, topk_idx, topk_weights,
+ * expert_alignment; its returns recv_topk_idx, recv_topk_weights and the
+ * per-expert receive counts; Buffer.combine adds the rows back without
+ * weights). Each token is sent once to every rank that hosts one of its
+ * experts. The R ranks' receive buffers are one buffer: rank r owns rows
+ * [rank_offset[r], rank_offset[r+1]), its tokens in ascending t. For the row of
+ * (t, r): rank_slot[t*R + r] = row (-1 if t does not reach r),
+ * recv_src[row] = t, recv_idx[row*K + k] = the rank-local id e - r*L of the
+ * k-th expert if it lives on r, else -1, and recv_w[row*K + k] = w[t,k] there,
+ * else 0 (w may be NULL: then recv_w is not written). recv_expert_count[e] =
+ * ceil(count[e] / A) * A, the receive count of expert e aligned to A. */
+int oracle_rank_layout(int64_t T, int32_t K, int32_t E, int32_t R, int32_t A, const int64_t *idx,
+                       const float *w, int32_t *rank_slot, int32_t *rank_offset,
+                       int32_t *recv_src, int64_t *recv_idx, float *recv_w,
+                       int32_t *recv_expert_count, int32_t *status) {
+    if (T < 0 || K < 1 || E < 1 || R < 1 || E % R != 0 || A < 1) return -2;
+    const int32_t L = E / R;
+    int32_t *count = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    int32_t *rtc = (int32_t *)calloc((size_t)R, sizeof(int32_t));
+    uint8_t *in_rank = (uint8_t *)calloc((size_t)(T * R > 0 ? T * R : 1), 1);
+    count_pairs(T, K, E, R, idx, count, NULL, in_rank, status);
+    for (int32_t r = 0; r < R; ++r)
+        for (int64_t t = 0; t < T; ++t) rtc[r] += in_rank[t * R + r];
+    rank_offset[0] = 0;
+    for (int32_t r = 0; r < R; ++r) rank_offset[r + 1] = rank_offset[r] + rtc[r];
+    int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (size_t)R);
+    for (int32_t r = 0; r < R; ++r) cursor[r] = rank_offset[r];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t r = 0; r < R; ++r) {
+            if (!in_rank[t * R + r]) {
+                rank_slot[t * R + r] = -1;
+                continue;
+            }
+#if ORACLE_MUTANT == 18
+            int32_t row = rank_offset[r + 1] - 1 - (cursor[r]++ - rank_offset[r]); /* mutant: tokens descending */
+#else
+            int32_t row = cursor[r]++;
+#endif
+            rank_slot[t * R + r] = row;
+            recv_src[row] = (int32_t)t;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t e = idx[t * K + k];
+                int local = valid_id(e, E) && e / L == r;
+#if ORACLE_MUTANT == 19
+                recv_idx[(int64_t)row * K + k] = local ? e : -1; /* mutant: global id */
+#else
+                recv_idx[(int64_t)row * K + k] = local ? e - (int64_t)r * L : -1;
+#endif
+                if (w) recv_w[(int64_t)row * K + k] = local ? w[t * K + k] : 0.0f;
+            }
+        }
+    }
+    for (int32_t e = 0; e < E; ++e) recv_expert_count[e] = (count[e] + A - 1) / A * A;
+    free(cursor);
+    free(in_rank);
+    free(rtc);
+    free(count);
+    return 0;
+}
+
+/* Buffer.combine's weight output: the received top-k weights summed back per
+ * token over the ranks it reached, ascending r, in float:
+ * out_w[t,k] = sum_r recv_w[rank_slot[t,r]*K + k]. */
+int oracle_combine_rank_weights(int64_t T, int32_t K, int32_t R, const int32_t *rank_slot,
+                                const float *recv_w, int64_t rows, float *out_w,
+                                int32_t *status) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t k = 0; k < K; ++k) {
+            float acc = 0.0f;
+            for (int32_t r = 0; r < R; ++r) {
+                int32_t row = rank_slot[t * R + r];
+                if (row == -1) continue;
+                if (row < -1 || row >= rows) {
+                    if (status) *status |= ST_BAD_SLOT;
+                    continue;
+                }
+                acc = acc + recv_w[(int64_t)row * K + k];
+            }
+            out_w[t * K + k] = acc;
+        }
     return 0;
 }
 

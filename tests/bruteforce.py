@@ -70,3 +70,31 @@ def dense_combine(y_f32: np.ndarray, slot: np.ndarray, w) -> np.ndarray:
             if r >= 0:
                 W[t, r] += 1.0 if w is None else float(w[t, k])
     return W @ y_f32.astype(np.float64)
+
+
+def rank_layout(idx, E: int, R: int, A: int, w=None):
+    """Normal-mode layout by sorting: the distinct (rank, token) keys of the
+    valid pairs, sorted, take consecutive rows; per row the rank-local ids."""
+    idx = np.asarray(idx)
+    T, K = idx.shape
+    L = E // R
+    keys = sorted({(int(e) // L, t) for t in range(T) for e in idx[t] if 0 <= e < E})
+    rank_slot = -np.ones((T, R), np.int64)
+    recv_src, recv_idx, recv_w = [], [], []
+    for row, (r, t) in enumerate(keys):
+        rank_slot[t, r] = row
+        recv_src.append(t)
+        recv_idx.append([int(e) - r * L if 0 <= e < E and int(e) // L == r else -1
+                         for e in idx[t]])
+        if w is not None:
+            recv_w.append([float(w[t, k]) if 0 <= idx[t, k] < E and int(idx[t, k]) // L == r
+                           else 0.0 for k in range(K)])
+    counts = np.array([sum(1 for (r, _) in keys if r == q) for q in range(R)], np.int64)
+    rank_offset = np.concatenate([[0], np.cumsum(counts)])
+    ids = idx[(idx >= 0) & (idx < E)]
+    cnt = np.bincount(ids, minlength=E)
+    return dict(rank_slot=rank_slot, rank_offset=rank_offset, recv_src=np.array(recv_src),
+                recv_topk_idx=np.array(recv_idx, np.int64).reshape(-1, K),
+                recv_topk_weights=np.array(recv_w, np.float32).reshape(-1, K)
+                if w is not None else None,
+                recv_expert_count=(cnt + A - 1) // A * A)

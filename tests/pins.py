@@ -614,6 +614,52 @@ def check_recv_stats(orc, seed: int = 11):
         assert np.array_equal(st, 5 + n * want)
 
 
+def check_rank_golden(orc):
+    g = _golden()
+    ex = g["expected"]["ranks"]
+    rl = orc.rank_layout(g["idx"], g["E"], g["R"], g["A"], g["w"])
+    for key in ("rank_offset", "rank_slot", "recv_src", "recv_topk_idx", "recv_topk_weights",
+                "recv_expert_count"):
+        assert rl[key].tolist() == ex[key], (key, rl[key].tolist())
+    recv, _ = orc.dispatch(g["xb"], rl["rank_slot"], rl["rows"], fill=0)
+    out = orc.combine(recv, rl["rank_slot"], None, "f64")["out_f64"]
+    assert out.tolist() == ex["combine_identity"]
+    cw, st = orc.combine_rank_weights(rl["rank_slot"], rl["recv_topk_weights"])
+    assert cw.tolist() == ex["combined_weights"] and st == 0
+
+
+def check_rank_layout_vs_bruteforce(orc, n: int = 100, seed: int = 12):
+    for w in tiny_cases(n, seed):
+        got = orc.rank_layout(w.topk_idx, w.E, w.R, w.A, w.topk_weights)
+        ref = bf.rank_layout(w.topk_idx, w.E, w.R, w.A, w.topk_weights)
+        for key in ("rank_slot", "rank_offset", "recv_src", "recv_topk_idx",
+                    "recv_expert_count"):
+            assert np.array_equal(np.asarray(got[key]), np.asarray(ref[key])), key
+        assert np.array_equal(got["recv_topk_weights"].view(np.uint32),
+                              ref["recv_topk_weights"].view(np.uint32))
+
+
+def check_rank_closed_forms(orc, w, A: int = 1):
+    """Identity expert, no weights: a token's combined row is (ranks it
+    reaches) x its row, exactly (small integer times a bf16 value); the
+    weights summed back over ranks are the original ones (0 for -1 ids); the
+    rank partitions hold the contiguous layout's distinct tokens per rank; the
+    expert receive counts are numpy's bincount aligned to A."""
+    rl = orc.rank_layout(w.topk_idx, w.E, w.R, A, w.topk_weights)
+    lay = orc.layout(w.topk_idx, w.E, w.R, 1)
+    assert np.array_equal(np.diff(rl["rank_offset"]), lay["rank_token_count"])
+    ids = w.topk_idx[(w.topk_idx >= 0) & (w.topk_idx < w.E)]
+    cnt = np.bincount(ids, minlength=w.E)
+    assert np.array_equal(rl["recv_expert_count"], (cnt + A - 1) // A * A)
+    recv, _ = orc.dispatch(w.x, rl["rank_slot"], max(rl["rows"], 1), fill=0)
+    out = orc.combine(recv, rl["rank_slot"], None, "f32")["out_f32"]
+    n = (rl["rank_slot"] >= 0).sum(axis=1).astype(np.float32)
+    assert np.array_equal(out, n[:, None] * mi.bf16_bits_to_f32(w.x))
+    cw, _ = orc.combine_rank_weights(rl["rank_slot"], rl["recv_topk_weights"])
+    valid = (w.topk_idx >= 0) & (w.topk_idx < w.E)
+    assert np.array_equal(cw, np.where(valid, w.topk_weights, 0.0).astype(np.float32))
+
+
 ALL_SMALL_CHECKS = (
     check_golden,
     check_layout_vs_bruteforce,
@@ -629,4 +675,6 @@ ALL_SMALL_CHECKS = (
     lambda o: check_ll_fp8_dispatch(o, n=3),
     lambda o: check_combine_masked(o, n=8),
     check_recv_stats,
+    check_rank_golden,
+    lambda o: check_rank_layout_vs_bruteforce(o, n=30),
 )

@@ -25,6 +25,8 @@ MUTANTS = {
     15: "FP8 amax over the whole row",
     16: "row-major UE8M0 scales stored transposed",
     17: "masked combine takes the rank as e mod R",
+    18: "normal-mode rows in descending token order",
+    19: "normal-mode received ids global instead of rank-local",
 }
 
 

@@ -141,3 +141,19 @@ def test_masked_combine_vs_dense_and_closed_forms(orc):
 
 def test_recv_stats_accumulate(orc):
     pins.check_recv_stats(orc)
+
+
+def test_rank_layout_golden(orc):
+    pins.check_rank_golden(orc)
+
+
+def test_rank_layout_vs_bruteforce(orc):
+    pins.check_rank_layout_vs_bruteforce(orc, n=200)
+
+
+@pytest.mark.parametrize("name,A", [("c1", 1), ("c2", 1), ("c2", 32), ("c4", 1), ("c5", 16)])
+def test_rank_layout_closed_forms(orc, name, A):
+    w = mi.by_name(name)
+    if name == "c5":  # the replica workload's routing, at reduced width
+        w = mi.config_c5(T=2048, H=64)
+    pins.check_rank_closed_forms(orc, w, A)
