@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ep.so")
-SOURCES = ["capi.hip", "layout.hip", "fused.hip", "scatter.hip", "fp8.hip", "replica.hip"]
+SOURCES = ["capi.hip", "layout.hip", "fused.hip", "scatter.hip", "fp8.hip", "ranks.hip",
+           "replica.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

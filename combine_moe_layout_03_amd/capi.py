@@ -81,6 +81,10 @@ def _load():
         "moe_ll_dispatch_fp8": (C.c_int, [P, I32, P, P, P, P, I64, I32, P, P]),
         "moe_dispatch_fp8": (C.c_int, [P, P, P, P, P, P, I64, P, P]),
         "moe_combine_masked": (C.c_int, [P, P, I64, P, P, P, P, P, P, P, P]),
+        "moe_rank_recv_rows_worst": (I64, [P]),
+        "moe_rank_layout": (C.c_int, [P, P, P, P, I64, P]),
+        "moe_rank_dispatch": (C.c_int, [P, P, P, P, I64, P, P]),
+        "moe_rank_combine": (C.c_int, [P, P, I64, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -95,7 +99,8 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_re
             "moe_ll_layout_dispatch", "moe_expert_load",
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
             "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
-            "moe_dispatch_fp8", "moe_combine_masked")
+            "moe_dispatch_fp8", "moe_combine_masked", "moe_rank_recv_rows_worst",
+            "moe_rank_layout", "moe_rank_dispatch", "moe_rank_combine")
 
 
 def lib():
@@ -208,6 +213,53 @@ class LayoutBuffers:
             _dev(self.status, "status", i32, 1, optional=True),
             _dev(self.recv_stats, "recv_stats", i32, E, optional=True),
         )
+
+
+class moe_rank_layout_t(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("rank_slot", "rank_offset", "recv_src",
+                                          "recv_topk_idx", "recv_topk_weights",
+                                          "recv_expert_count", "status")]
+
+
+@dataclass
+class RankLayoutBuffers:
+    """Device arrays of a normal-mode layout (one row per (token, rank))."""
+
+    rank_slot: torch.Tensor
+    rank_offset: torch.Tensor
+    recv_src: Optional[torch.Tensor] = None
+    recv_topk_idx: Optional[torch.Tensor] = None
+    recv_topk_weights: Optional[torch.Tensor] = None
+    recv_expert_count: Optional[torch.Tensor] = None
+    status: Optional[torch.Tensor] = None
+    cap: int = 0
+
+    @staticmethod
+    def empty(shape: "moe_shape", device, weights: bool = True, cap: Optional[int] = None):
+        T, E, R, K = shape.T, shape.E, shape.R, shape.K
+        cap = int(moe_rank_recv_rows_worst(shape)) if cap is None else int(cap)
+        n = max(cap, 1)
+        i32 = dict(dtype=torch.int32, device=device)
+        return RankLayoutBuffers(
+            rank_slot=torch.empty(T * R, **i32), rank_offset=torch.empty(R + 1, **i32),
+            recv_src=torch.empty(n, **i32),
+            recv_topk_idx=torch.empty(n * K, dtype=torch.int64, device=device),
+            recv_topk_weights=torch.empty(n * K, dtype=torch.float32, device=device)
+            if weights else None,
+            recv_expert_count=torch.empty(E, **i32), status=torch.zeros(1, **i32), cap=cap)
+
+    def _struct(self, shape: "moe_shape") -> moe_rank_layout_t:
+        T, E, R, K = shape.T, shape.E, shape.R, shape.K
+        i32 = (torch.int32,)
+        return moe_rank_layout_t(
+            _dev(self.rank_slot, "rank_slot", i32, T * R),
+            _dev(self.rank_offset, "rank_offset", i32, R + 1),
+            _dev(self.recv_src, "recv_src", i32, self.cap, optional=True),
+            _dev(self.recv_topk_idx, "recv_topk_idx", (torch.int64,), self.cap * K, optional=True),
+            _dev(self.recv_topk_weights, "recv_topk_weights", (torch.float32,), self.cap * K,
+                 optional=True),
+            _dev(self.recv_expert_count, "recv_expert_count", i32, E, optional=True),
+            _dev(self.status, "status", i32, 1, optional=True))
 
 
 # -- entry points (same names as the C ABI) -----------------------------------
@@ -334,6 +386,49 @@ def moe_combine_masked(shape: moe_shape, y: torch.Tensor, recv_rows: int, slot: 
         _dev(rank_mask, "rank_mask", (torch.int32,), shape.R),
         _dev(out, "out", _BF16_LIKE, T * H),
         _dev(out_f32, "out_f32", (torch.float32,), T * H, optional=True),
+        _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
+
+
+def moe_rank_recv_rows_worst(shape: moe_shape) -> int:
+    return int(_lib.moe_rank_recv_rows_worst(C.byref(shape)))
+
+
+def moe_rank_layout(shape: moe_shape, topk_idx: torch.Tensor,
+                    topk_weights: Optional[torch.Tensor], out: RankLayoutBuffers,
+                    stream=None) -> int:
+    T, K = shape.T, shape.K
+    st = out._struct(shape)
+    return _check("moe_rank_layout", _lib.moe_rank_layout(
+        C.byref(shape), _dev(topk_idx, "topk_idx", (torch.int64,), T * K),
+        _dev(topk_weights, "topk_weights", (torch.float32,), T * K, optional=True),
+        C.byref(st), int(out.cap), _stream(stream)))
+
+
+def moe_rank_dispatch(shape: moe_shape, x: torch.Tensor, rank_slot: torch.Tensor,
+                      recv_x: torch.Tensor, recv_rows: int, status: Optional[torch.Tensor] = None,
+                      stream=None) -> int:
+    T, H, R = shape.T, shape.H, shape.R
+    return _check("moe_rank_dispatch", _lib.moe_rank_dispatch(
+        C.byref(shape), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(rank_slot, "rank_slot", (torch.int32,), T * R),
+        _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
+        _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
+
+
+def moe_rank_combine(shape: moe_shape, y: torch.Tensor, recv_rows: int, rank_slot: torch.Tensor,
+                     recv_topk_weights: Optional[torch.Tensor], out: torch.Tensor,
+                     out_f32: Optional[torch.Tensor] = None,
+                     out_topk_weights: Optional[torch.Tensor] = None,
+                     status: Optional[torch.Tensor] = None, stream=None) -> int:
+    T, H, R, K = shape.T, shape.H, shape.R, shape.K
+    return _check("moe_rank_combine", _lib.moe_rank_combine(
+        C.byref(shape), _dev(y, "y", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
+        _dev(rank_slot, "rank_slot", (torch.int32,), T * R),
+        _dev(recv_topk_weights, "recv_topk_weights", (torch.float32,), int(recv_rows) * K,
+             optional=True),
+        _dev(out, "out", _BF16_LIKE, T * H),
+        _dev(out_f32, "out_f32", (torch.float32,), T * H, optional=True),
+        _dev(out_topk_weights, "out_topk_weights", (torch.float32,), T * K, optional=True),
         _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
 
 

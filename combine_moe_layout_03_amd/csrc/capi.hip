@@ -22,6 +22,7 @@ static_assert(MOE_STATUS_BAD_EXPERT == kStBadExpert && MOE_STATUS_LL_OVERFLOW ==
               "status bits of the header and the kernels differ");
 
 constexpr int kMaxDevices = 64;
+constexpr int kMaxRanksNormal = 64;  // a token's set of ranks is one 64-bit mask
 std::atomic<int> g_arch[kMaxDevices];  // 0 = not checked yet, 1 = gfx950, 2 = other
 
 // The kernels are compiled for gfx950 only; refuse any other current device.
@@ -389,6 +390,73 @@ MOE_API int moe_combine_masked(const moe_shape *shape, const uint16_t *y, int64_
                         shape->H, &cm, status, stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_LAUNCH;
+}
+
+MOE_API int64_t moe_rank_recv_rows_worst(const moe_shape *shape) {
+  if (check_shape(shape, false)) return -1;
+  return (int64_t)shape->T * (shape->K < shape->R ? shape->K : shape->R);
+}
+
+MOE_API int moe_rank_layout(const moe_shape *shape, const int64_t *topk_idx,
+                            const float *topk_weights, const moe_rank_layout_t *out,
+                            int64_t recv_cap, hipStream_t stream) {
+  int rc = check_shape(shape, false);
+  if (rc) return rc;
+  if (shape->R > kMaxRanksNormal) return MOE_ERR_SHAPE;
+  if (!out || !out->rank_offset || (shape->T > 0 && !out->rank_slot)) return MOE_ERR_NULL;
+  if (shape->T > 0 && !topk_idx) return MOE_ERR_NULL;
+  if (out->recv_topk_weights && !topk_weights && shape->T > 0) return MOE_ERR_NULL;
+  if (recv_cap < 0) return MOE_ERR_CAPACITY;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_rank_layout(topk_idx, topk_weights, shape->T, shape->K, shape->E, shape->R,
+                            shape->A, out->rank_slot, out->rank_offset, out->recv_src,
+                            out->recv_topk_idx, out->recv_topk_weights, out->recv_expert_count,
+                            recv_cap, out->status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_rank_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *rank_slot,
+                              uint16_t *recv_x, int64_t recv_rows, int32_t *status,
+                              hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (shape->R > kMaxRanksNormal) return MOE_ERR_SHAPE;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!x || !rank_slot || (!recv_x && recv_rows > 0)) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_x)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  // one row copy per (token, rank): the pair scatter over the [T, R] table
+  return launch_dispatch(x, rank_slot, recv_x, shape->T, shape->R, shape->H, recv_rows, status,
+                         stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_rank_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                             const int32_t *rank_slot, const float *recv_topk_weights,
+                             uint16_t *out, float *out_f32, float *out_topk_weights,
+                             int32_t *status, hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (shape->R > kMaxRanksNormal) return MOE_ERR_SHAPE;
+  if (recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T == 0) return MOE_OK;
+  if (!rank_slot || !out || (!y && recv_rows > 0)) return MOE_ERR_NULL;
+  if (out_topk_weights && !recv_topk_weights) return MOE_ERR_NULL;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  // the unweighted row sum over the [T, R] table
+  hipError_t err = launch_combine(y, recv_rows, rank_slot, nullptr, out, out_f32, shape->T,
+                                  shape->R, shape->H, nullptr, status, stream);
+  if (err == hipSuccess && out_topk_weights)
+    err = launch_rank_weights(shape->T, shape->K, shape->R, rank_slot, recv_topk_weights,
+                              recv_rows, out_topk_weights, status, stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 MOE_API int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,

@@ -106,6 +106,16 @@ hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, 
                           uint16_t *out, float *out_f32, int32_t T, int32_t K, int32_t H,
                           const CombineMask *mask, int32_t *status, hipStream_t s);
 
+// Normal-mode layout, one row per (token, rank) (ranks.hip); R <= 64.
+hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int32_t K,
+                              int32_t E, int32_t R, int32_t A, int32_t *rank_slot,
+                              int32_t *rank_offset, int32_t *recv_src, int64_t *recv_idx,
+                              float *recv_w, int32_t *recv_count, int64_t cap, int32_t *status,
+                              hipStream_t s);
+hipError_t launch_rank_weights(int32_t T, int32_t K, int32_t R, const int32_t *rank_slot,
+                               const float *recv_w, int64_t rows, float *out_w, int32_t *status,
+                               hipStream_t s);
+
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,
                                 int32_t *phys_to_logical, hipStream_t s);

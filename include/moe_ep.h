@@ -211,6 +211,54 @@ int moe_combine_masked(const moe_shape *shape, const uint16_t *y, int64_t recv_r
                        const int32_t *rank_mask, uint16_t *out, float *out_f32, int32_t *status,
                        hipStream_t stream);
 
+/* ---------------------------------------------------------------------
+ * Normal-mode dispatch: one receive row per (token, rank reached)
+ * (Buffer.dispatch with is_token_in_rank / num_tokens_per_rank, returning
+ * recv_topk_idx, recv_topk_weights and the per-expert receive counts;
+ * Buffer.combine, which adds the rows back without weights). The R ranks'
+ * receive buffers are one buffer: rank r owns rows
+ * [rank_offset[r], rank_offset[r+1]), its tokens in ascending order.
+ * Needs R <= 64.
+ * ------------------------------------------------------------------- */
+typedef struct {
+  int32_t *rank_slot;         /* [T*R] row of (t, r), -1 if token t reaches no expert on r */
+  int32_t *rank_offset;       /* [R+1] first row of each rank; rank_offset[R] = rows used */
+  int32_t *recv_src;          /* [recv_cap] token held by each row. May be NULL. */
+  int64_t *recv_topk_idx;     /* [recv_cap*K] per row: the rank-local id e - r*L of each
+                                 selected expert that lives on the row's rank, -1 otherwise.
+                                 May be NULL. */
+  float *recv_topk_weights;   /* [recv_cap*K] the weight where the id is local, else 0.
+                                 May be NULL (needs topk_weights when set). */
+  int32_t *recv_expert_count; /* [E] pairs per expert rounded up to shape->A (the receive
+                                 count of each local expert). May be NULL. */
+  int32_t *status;            /* [1] sticky MOE_STATUS_* bits. May be NULL. */
+} moe_rank_layout_t;
+
+/* Worst-case rows of the normal-mode receive buffer: T * min(K, R). */
+int64_t moe_rank_recv_rows_worst(const moe_shape *shape);
+
+/* Normal-mode layout. topk_idx [T*K] int64; topk_weights [T*K] f32 or NULL.
+ * recv_cap = rows the recv_* arrays hold (normally moe_rank_recv_rows_worst);
+ * a row at or past it sets MOE_STATUS_BAD_SLOT and gets rank_slot -1. */
+int moe_rank_layout(const moe_shape *shape, const int64_t *topk_idx, const float *topk_weights,
+                    const moe_rank_layout_t *out, int64_t recv_cap, hipStream_t stream);
+
+/* Normal-mode dispatch: recv_x[rank_slot[t*R + r]] = x[t] for every row,
+ * bit for bit; rows no token maps to are left untouched. */
+int moe_rank_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *rank_slot,
+                      uint16_t *recv_x, int64_t recv_rows, int32_t *status, hipStream_t stream);
+
+/* Normal-mode combine (Buffer.combine, addition without weights):
+ *   out[t] = bf16_rne( sum over r = 0..R-1 with rank_slot[t*R + r] != -1 of y[row] )
+ * in float, ascending r, from +0 (out_f32 [T*H] receives the float sums, or
+ * NULL). With out_topk_weights [T*K] (and recv_topk_weights [recv_rows*K]),
+ * also out_topk_weights[t*K + k] = sum over the same rows of
+ * recv_topk_weights[row*K + k], ascending r: the original weights come back. */
+int moe_rank_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
+                     const int32_t *rank_slot, const float *recv_topk_weights, uint16_t *out,
+                     float *out_f32, float *out_topk_weights, int32_t *status,
+                     hipStream_t stream);
+
 /* Replica plan (ultraep GPU operations, Placement planning): the C most loaded
  * experts (load descending, ties to the lower id) get a second physical
  * replica. Rank r holds L' = L + C/R physical experts: r*L' + l (l < L) is the

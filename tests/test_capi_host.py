@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 23, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -216,3 +216,29 @@ def test_combine_masked_checks(lib):
     s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
     assert raw.moe_combine_masked(C.byref(s0), None, 0, None, None, None, None, None, None,
                                   None, None) == 0
+
+
+def test_rank_mode_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(258)
+    assert lib.moe_rank_recv_rows_worst(lib.make_shape(128, 7168, 256, 8, 8)) == 128 * 8
+    assert lib.moe_rank_recv_rows_worst(lib.make_shape(10, 8, 16, 4, 2)) == 20
+    rl = lib.moe_rank_layout_t()
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    assert raw.moe_rank_layout(C.byref(s), d, None, C.byref(rl), 8, None) == -1  # slot NULL
+    rl.rank_slot = rl.rank_offset = d
+    assert raw.moe_rank_layout(C.byref(s), None, None, C.byref(rl), 8, None) == -1
+    assert raw.moe_rank_layout(C.byref(s), d, None, C.byref(rl), -1, None) == -3
+    rl.recv_topk_weights = d
+    assert raw.moe_rank_layout(C.byref(s), d, None, C.byref(rl), 8, None) == -1  # weights
+    big = lib.make_shape(4, 16, 128, 128, 2, 1)  # R > 64
+    assert raw.moe_rank_layout(C.byref(big), d, d, C.byref(rl), 8, None) == -2
+    assert raw.moe_rank_dispatch(C.byref(big), d, d, d, 8, None, None) == -2
+    assert raw.moe_rank_dispatch(C.byref(s), odd, d, d, 8, None, None) == -5
+    assert raw.moe_rank_combine(C.byref(s), d, 8, d, None, d, None, d, None, None) == -1
+    assert raw.moe_rank_combine(C.byref(s), d, 8, None, None, d, None, None, None, None) == -1
+    s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
+    assert raw.moe_rank_dispatch(C.byref(s0), None, None, None, 0, None, None) == 0
+    assert raw.moe_rank_combine(C.byref(s0), None, 0, None, None, None, None, None, None,
+                                None) == 0
