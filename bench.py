@@ -261,6 +261,63 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     return res
 
 
+def row_normal(capi, mi, torch, np, dev, stream):
+    """Normal-mode path on the standard batch (128 tokens x 7168, 256 experts
+    top-8 on 8 ranks): one receive row per (token, rank reached), then the
+    unweighted row sum and the weight reduce. 30 rotating buffer sets."""
+    w = mi.config_c2()
+    E, R, K, T, H = w.E, w.R, w.K, w.T, w.H
+    shape = capi.make_shape(T, H, E, R, K, 1)
+    cap = capi.moe_rank_recv_rows_worst(shape)
+    x = torch.from_numpy(w.x.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    wt = torch.from_numpy(w.topk_weights).to(dev)
+    sets = []
+    for _ in range(30):
+        sets.append(dict(x=x.clone(), idx=idx.clone(), w=wt.clone(),
+                         lay=capi.RankLayoutBuffers.empty(shape, dev),
+                         recv=torch.empty(cap, H, dtype=torch.int16, device=dev),
+                         out=torch.empty(T, H, dtype=torch.int16, device=dev),
+                         ow=torch.empty(T, K, dtype=torch.float32, device=dev)))
+
+    def lay(z):
+        capi.moe_rank_layout(shape, z["idx"], z["w"], z["lay"], stream=stream)
+
+    def dsp(z):
+        capi.moe_rank_dispatch(shape, z["x"], z["lay"].rank_slot, z["recv"], cap, None,
+                               stream=stream)
+
+    def cmb(z):
+        capi.moe_rank_combine(shape, z["recv"], cap, z["lay"].rank_slot,
+                              z["lay"].recv_topk_weights, z["out"], None, z["ow"], None,
+                              stream=stream)
+
+    with torch.cuda.stream(stream):
+        for z in sets:
+            lay(z)
+            dsp(z)
+            cmb(z)
+    torch.cuda.synchronize()
+    rows = int(sets[0]["lay"].rank_offset[R].item())
+    us = graph_us_per_step(torch, stream, [(lambda z=z: (lay(z), dsp(z), cmb(z))) for z in sets], 20)
+    k = {n: graph_us_per_step(torch, stream, [(lambda z=z, f=f: f(z)) for z in sets], 20)
+         for n, f in (("rank_layout", lay), ("rank_dispatch", dsp), ("rank_combine", cmb))}
+    b_layout = T * K * 12 + T * R * 4 + (R + 1) * 4 + rows * (4 + K * 12) + E * 4
+    b_dispatch = T * 2 * H + rows * 2 * H + T * R * 4
+    b_combine = rows * 2 * H + T * 2 * H + T * R * 4 + rows * K * 4 + T * K * 4
+    total = b_layout + b_dispatch + b_combine
+    del sets
+    torch.cuda.empty_cache()
+    return {"workload": "normal mode: 128 tokens x 7168, 256E top-8 on 8 ranks, one row per "
+                        "(token, rank): %d rows for %d pairs" % (rows, int((w.topk_idx >= 0).sum())),
+            "us_per_step": round(us, 3), "GB_per_s": round(total / us / 1e3, 1),
+            "kernels_us": {n: round(v, 3) for n, v in k.items()},
+            "algorithmic_bytes_per_step": total,
+            "roofline_dispatch": {"achieved": round(b_dispatch / k["rank_dispatch"] / 1e3, 1),
+                                  "frac": round(b_dispatch / k["rank_dispatch"] / 1e3
+                                                / HBM_PEAK_GBS, 4)}}
+
+
 def row_replica(capi, mi, torch, np, dev, stream, n_ev):
     """Replica-expanded routing at full size (8192 tokens x 7168, 256 logical
     experts top-8 Zipf(1.0), 32 extra replicas): load -> plan -> reroute ->
@@ -476,6 +533,8 @@ def main():
             capi, mi, torch, np, dev, stream, capi.MOE_FP8_SCALE_ROWS)
         log(f"low-latency FP8 row-major scales: "
             f"{rows['low_latency_fp8_rowscales_m128']['us_per_step']} us/step")
+        rows["normal_mode_128x7168"] = row_normal(capi, mi, torch, np, dev, stream)
+        log(f"normal-mode row: {rows['normal_mode_128x7168']['us_per_step']} us/step")
         rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
         log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
 

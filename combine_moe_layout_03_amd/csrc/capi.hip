@@ -450,13 +450,13 @@ MOE_API int moe_rank_combine(const moe_shape *shape, const uint16_t *y, int64_t 
   if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
-  // the unweighted row sum over the [T, R] table
-  hipError_t err = launch_combine(y, recv_rows, rank_slot, nullptr, out, out_f32, shape->T,
-                                  shape->R, shape->H, nullptr, status, stream);
-  if (err == hipSuccess && out_topk_weights)
-    err = launch_rank_weights(shape->T, shape->K, shape->R, rank_slot, recv_topk_weights,
-                              recv_rows, out_topk_weights, status, stream);
-  return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+  // the unweighted row sum over the [T, R] table, with the weights summed back
+  const RowWeightSum ws{out_topk_weights ? recv_topk_weights : nullptr, out_topk_weights,
+                        shape->K};
+  return launch_rank_combine(y, recv_rows, rank_slot, out, out_f32, shape->T, shape->R,
+                             shape->H, ws, status, stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
 }
 
 MOE_API int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,

@@ -112,9 +112,16 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
                               int32_t *rank_offset, int32_t *recv_src, int64_t *recv_idx,
                               float *recv_w, int32_t *recv_count, int64_t cap, int32_t *status,
                               hipStream_t s);
-hipError_t launch_rank_weights(int32_t T, int32_t K, int32_t R, const int32_t *rank_slot,
-                               const float *recv_w, int64_t rows, float *out_w, int32_t *status,
-                               hipStream_t s);
+// Normal-mode combine: the unweighted row sum over the [T, R] rank table, and
+// (ws.in != null) the rows' top-k weights summed back per token.
+struct RowWeightSum {
+  const float *in;  // [rows*Kw]
+  float *out;       // [T*Kw]
+  int32_t Kw;
+};
+hipError_t launch_rank_combine(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
+                               uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t H,
+                               const RowWeightSum &ws, int32_t *status, hipStream_t s);
 
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,

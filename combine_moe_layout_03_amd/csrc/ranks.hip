@@ -36,17 +36,120 @@ struct RankParams {
   int32_t *status;
 };
 
-// Ranks reached by token t (bit r), from its K ids; bad ids set *st.
-__device__ __forceinline__ uint64_t token_ranks(const RankParams &p, int t, int &st) {
-  uint64_t m = 0;
-  for (int k = 0; k < p.K; ++k) {
-    const int64_t e = p.idx[(int64_t)t * p.K + k];
-    if (e >= 0 && e < p.E)
-      m |= 1ull << rank_of((int)e, p.l_magic);
-    else if (e != -1)
-      st |= kStBadExpert;
+// A token's ids, 8 at a time: the 8 loads are issued together (addresses
+// clamped into the row, so none waits behind a branch), then examined.
+struct IdChunk {
+  int64_t e[8];
+  __device__ __forceinline__ void load(const RankParams &p, int t, int k0) {
+    const int64_t *row = p.idx + (int64_t)t * p.K;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = row[min(k0 + j, p.K - 1)];
   }
+};
+
+// Ranks reached by token t (bit r), the pairs of t whose expert lives on rank
+// r (bit k), and, with s_cnt, one count per such pair into its local expert.
+__device__ __forceinline__ uint64_t token_ranks(const RankParams &p, int t, int r, int &st,
+                                                uint64_t *local, int32_t *s_cnt) {
+  uint64_t m = 0, loc = 0;
+  for (int k0 = 0; k0 < p.K; k0 += 8) {
+    IdChunk c;
+    c.load(p, t, k0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t e = c.e[j];
+      if (k0 + j >= p.K) break;
+      if (e >= 0 && e < p.E) {
+        const int rr = rank_of((int)e, p.l_magic);
+        m |= 1ull << rr;
+        if (rr == r) {
+          loc |= 1ull << (k0 + j);
+          if (s_cnt) atomicAdd(&s_cnt[(int)e - r * p.L], 1);
+        }
+      } else if (e != -1) {
+        st |= kStBadExpert;
+      }
+    }
+  }
+  if (local) *local = loc;
   return m;
+}
+
+// One pass for a batch of at most kRankThreads tokens and K <= 8: every
+// thread loads its token's ids and weights once, up front (one memory
+// latency), and keeps them in registers for both scans.
+__global__ __launch_bounds__(kRankThreads) void rank_layout_small_kernel(RankParams p) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_wave[kRankWaves];
+  __shared__ int32_t s_status;
+  const int tid = threadIdx.x, r = blockIdx.x;
+  const uint64_t below = (1ull << r) - 1ull;  // r < 64
+  const int t = tid;
+  const bool live = t < p.T;
+  const int tc = live ? t : 0;
+  int st = 0;
+  IdChunk c;
+  float wk[8];
+  if (p.T > 0) {
+    c.load(p, tc, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wk[j] = p.w ? p.w[(int64_t)tc * p.K + min(j, p.K - 1)] : 0.0f;
+  }
+  if (tid == 0) s_status = 0;
+  for (int l = tid; l < p.L; l += kRankThreads) s_cnt[l] = 0;
+  __syncthreads();
+  uint64_t m = 0, loc = 0;
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t e = c.e[j];
+      if (j >= p.K) break;
+      if (e >= 0 && e < p.E) {
+        const int rr = rank_of((int)e, p.l_magic);
+        m |= 1ull << rr;
+        if (rr == r) {
+          loc |= 1ull << j;
+          atomicAdd(&s_cnt[(int)e - r * p.L], 1);
+        }
+      } else if (e != -1) {
+        st |= kStBadExpert;
+      }
+    }
+  }
+  int before = 0;
+  block_exclusive_scan(__popcll(m & below), s_wave, kRankWaves, &before);
+  const int hit = (int)((m >> r) & 1ull);
+  int total = 0;
+  const int pos = block_exclusive_scan(hit, s_wave, kRankWaves, &total);
+  if (p.recv_count)
+    for (int l = tid; l < p.L; l += kRankThreads)
+      p.recv_count[r * p.L + l] = round_up(s_cnt[l], p.A);
+  if (live) {
+    int row = hit ? before + pos : -1;
+    if (row >= p.cap) {
+      st |= kStBadSlot;
+      row = -1;
+    }
+    p.rank_slot[(int64_t)t * p.R + r] = row;
+    if (row >= 0) {
+      if (p.recv_src) p.recv_src[row] = t;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j >= p.K) break;
+        const bool l = (loc >> j) & 1ull;
+        if (p.recv_idx) p.recv_idx[(int64_t)row * p.K + j] = l ? c.e[j] - (int64_t)r * p.L : -1;
+        if (p.recv_w && p.w) p.recv_w[(int64_t)row * p.K + j] = l ? wk[j] : 0.0f;
+      }
+    }
+  }
+  if (tid == 0) {
+    p.rank_offset[r] = before;
+    if (r == p.R - 1) p.rank_offset[p.R] = before + total;
+  }
+  if (r != 0) st &= ~kStBadExpert;
+  if (st) atomicOr(&s_status, st);
+  __syncthreads();
+  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
 }
 
 __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p) {
@@ -65,15 +168,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
   for (int t0 = 0; t0 < p.T; t0 += kRankThreads) {
     const int t = t0 + tid;
     int n = 0;
-    if (t < p.T) {
-      const uint64_t m = token_ranks(p, t, st);
-      n = __popcll(m & below);
-      for (int k = 0; k < p.K; ++k) {
-        const int64_t e = p.idx[(int64_t)t * p.K + k];
-        if (e >= 0 && e < p.E && rank_of((int)e, p.l_magic) == r)
-          atomicAdd(&s_cnt[(int)e - r * p.L], 1);
-      }
-    }
+    if (t < p.T) n = __popcll(token_ranks(p, t, r, st, nullptr, s_cnt) & below);
     int total = 0;
     block_exclusive_scan(n, s_wave, kRankWaves, &total);
     before += total;
@@ -88,7 +183,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
   for (int t0 = 0; t0 < p.T; t0 += kRankThreads) {
     const int t = t0 + tid;
     int hit = 0;
-    if (t < p.T) hit = (int)((token_ranks(p, t, st) >> r) & 1ull);
+    uint64_t local = 0;
+    if (t < p.T) hit = (int)((token_ranks(p, t, r, st, &local, nullptr) >> r) & 1ull);
     int total = 0;
     const int pos = block_exclusive_scan(hit, s_wave, kRankWaves, &total);
     if (t < p.T) {
@@ -100,11 +196,21 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
       p.rank_slot[(int64_t)t * p.R + r] = row;
       if (row >= 0) {
         if (p.recv_src) p.recv_src[row] = t;
-        for (int k = 0; k < p.K; ++k) {
-          const int64_t e = p.idx[(int64_t)t * p.K + k];
-          const bool local = e >= 0 && e < p.E && rank_of((int)e, p.l_magic) == r;
-          if (p.recv_idx) p.recv_idx[(int64_t)row * p.K + k] = local ? e - (int64_t)r * p.L : -1;
-          if (p.recv_w && p.w) p.recv_w[(int64_t)row * p.K + k] = local ? p.w[(int64_t)t * p.K + k] : 0.0f;
+        for (int k0 = 0; k0 < p.K; k0 += 8) {
+          IdChunk c;
+          c.load(p, t, k0);
+          float wk[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            wk[j] = p.w ? p.w[(int64_t)t * p.K + min(k0 + j, p.K - 1)] : 0.0f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int k = k0 + j;
+            if (k >= p.K) break;
+            const bool loc = (local >> k) & 1ull;
+            if (p.recv_idx) p.recv_idx[(int64_t)row * p.K + k] = loc ? c.e[j] - (int64_t)r * p.L : -1;
+            if (p.recv_w && p.w) p.recv_w[(int64_t)row * p.K + k] = loc ? wk[j] : 0.0f;
+          }
         }
       }
     }
@@ -118,33 +224,6 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
   if (st) atomicOr(&s_status, st);
   __syncthreads();
   if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
-}
-
-// Combined weights: out_w[t,k] = sum over r ascending of
-// recv_w[rank_slot[t,r]*K + k], in float.
-__global__ __launch_bounds__(256) void rank_weights_kernel(int32_t T, int32_t K, int32_t R,
-                                                           const int32_t *__restrict__ rank_slot,
-                                                           const float *__restrict__ recv_w,
-                                                           int64_t rows, float *__restrict__ out_w,
-                                                           int32_t *status) {
-#pragma clang fp contract(off)
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * K) return;
-  const int64_t t = i / K;
-  const int k = (int)(i - t * K);
-  float acc = 0.0f;
-  int st = 0;
-  for (int r = 0; r < R; ++r) {
-    const int row = rank_slot[t * R + r];
-    if (row == -1) continue;
-    if (row < -1 || row >= rows) {
-      st |= kStBadSlot;
-      continue;
-    }
-    acc = acc + recv_w[(int64_t)row * K + k];
-  }
-  out_w[i] = acc;
-  if (st && status) atomicOr(status, st);
 }
 
 }  // namespace
@@ -172,17 +251,10 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
   p.recv_count = recv_count;
   p.cap = cap;
   p.status = status;
-  hipLaunchKernelGGL(rank_layout_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_rank_weights(int32_t T, int32_t K, int32_t R, const int32_t *rank_slot,
-                               const float *recv_w, int64_t rows, float *out_w, int32_t *status,
-                               hipStream_t s) {
-  const int64_t n = (int64_t)T * K;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rank_weights_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, T,
-                     K, R, rank_slot, recv_w, rows, out_w, status);
+  if (T <= kRankThreads && K <= 8)
+    hipLaunchKernelGGL(rank_layout_small_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(rank_layout_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -11,7 +11,9 @@
 // expert lives on a masked rank are left out. The row loads do not wait for
 // the mask -- they are issued from the slots as usual, and the (scalar) id and
 // mask reads complete while the rows are in flight; the mask only gates the
-// sum.
+// sum. In normal mode (one row per token and rank, slots = the [T, R] rank
+// table) the first wave of each token also sums the received top-k weights of
+// its rows back, lanes 0..Kw-1, loaded alongside the rows.
 //
 // Both are HBM-bound streams with no data reuse, so the design is about
 // bytes in flight: a thread owns one 16-byte vector (8 bf16) of one token row,
@@ -81,14 +83,15 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
-template <int KT, bool kWeights, bool kF32Out, bool kMask>
+template <int KT, bool kWeights, bool kF32Out, bool kMask, bool kWsum>
 __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ y, int64_t rows,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ w,
                                                       u32x4 *__restrict__ out,
                                                       f32x4 *__restrict__ out_f32, int32_t T,
                                                       int32_t Kr, int32_t nvec, int32_t nchunk,
-                                                      CombineMask cm, int32_t *status) {
+                                                      CombineMask cm, RowWeightSum ws,
+                                                      int32_t *status) {
 #pragma clang fp contract(off)
   const int K = KT ? KT : Kr;
   int t;
@@ -101,6 +104,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
   int st = 0;
+  // normal mode: the first wave of the token, lanes < Kw, sum the rows' weights
+  const bool wsum_lane = kWsum && v < 64 && (int)(threadIdx.x & 63) < ws.Kw;
+  const int wl = kWsum ? min((int)(threadIdx.x & 63), ws.Kw - 1) : 0;
+  float wacc = 0.0f;
   constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
   for (int k0 = 0; k0 < K; k0 += G) {
     int32_t s[G];
@@ -113,11 +120,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
       wk[g] = (kWeights && in) ? wrow[k0 + g] : 1.0f;
     }
     u32x4 val[G];
+    float rw[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       ok[g] = s[g] >= 0 && s[g] < rows;
       val[g] = u32x4{0u, 0u, 0u, 0u};
       if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nvec + v);
+      rw[g] = 0.0f;
+      if (kWsum && ok[g] && wsum_lane) rw[g] = ws.in[(int64_t)s[g] * ws.Kw + wl];
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {  // masked ranks (scalar reads, rows already in flight)
@@ -131,6 +141,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (!ok[g] || off[g]) continue;
+      if (kWsum) wacc = wacc + rw[g];
       const float a = wk[g];
       const u32x4 q = val[g];
       acc[0] = acc[0] + a * bf16_lo(q.x);
@@ -143,6 +154,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
       acc[7] = acc[7] + a * bf16_hi(q.w);
     }
   }
+  if (kWsum && wsum_lane) ws.out[(int64_t)t * ws.Kw + wl] = wacc;
   if (lane_ok) {
     const int64_t i = (int64_t)t * nvec + v;
     u32x4 o;
@@ -178,11 +190,39 @@ hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, cons
   const int32_t nchunk = (nvec + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
   const unsigned blocks = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM>), dim3(blocks), dim3(256), 0, s,
+  const RowWeightSum none{nullptr, nullptr, 0};
+  hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM, false>), dim3(blocks), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(y), rows, slot, w,
                      reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
-                     nvec, nchunk, cm, status);
+                     nvec, nchunk, cm, none, status);
   return hipGetLastError();
+}
+
+template <int KT, bool kF, bool kWs>
+hipError_t rank_combine_k(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
+                          uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t nvec,
+                          const RowWeightSum &ws, int32_t *status, hipStream_t s) {
+  const int32_t nchunk = (nvec + 63) / 64;
+  const int64_t waves = (int64_t)T * nchunk;
+  const unsigned blocks = (unsigned)((waves + 3) / 4);
+  const CombineMask none{nullptr, nullptr, 0, 0};
+  hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs>), dim3(blocks), dim3(256), 0, s,
+                     reinterpret_cast<const u32x4 *>(y), rows, rank_slot, nullptr,
+                     reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, R,
+                     nvec, nchunk, none, ws, status);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t rank_combine_kt(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
+                           uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t nvec,
+                           const RowWeightSum &ws, int32_t *status, hipStream_t s) {
+  if (ws.in) {
+    if (out_f32) return rank_combine_k<KT, true, true>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
+    return rank_combine_k<KT, false, true>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
+  }
+  if (out_f32) return rank_combine_k<KT, true, false>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
+  return rank_combine_k<KT, false, false>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
 }
 
 template <int KT, bool kM>
@@ -236,6 +276,18 @@ hipError_t launch_combine(const uint16_t *y, int64_t rows, const int32_t *slot, 
     case 6: return combine_k<6>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
     case 8: return combine_k<8>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
     default: return combine_k<0>(y, rows, slot, w, out, out_f32, T, K, nvec, mask, status, s);
+  }
+}
+
+hipError_t launch_rank_combine(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
+                               uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t H,
+                               const RowWeightSum &ws, int32_t *status, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int32_t nvec = H / 8;
+  switch (R) {
+    case 4: return rank_combine_kt<4>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
+    case 8: return rank_combine_kt<8>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
+    default: return rank_combine_kt<0>(y, rows, rank_slot, out, out_f32, T, R, nvec, ws, status, s);
   }
 }
 

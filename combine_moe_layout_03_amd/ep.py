@@ -186,6 +186,59 @@ def low_latency_combine(y: torch.Tensor, topk_weights: torch.Tensor, handle: Han
     return out
 
 
+@dataclass
+class RankHandle:
+    """What normal-mode dispatch hands on to combine."""
+
+    shape: capi.moe_shape
+    layout: capi.RankLayoutBuffers
+    recv_rows: int
+
+
+def normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
+                    topk_weights: Optional[torch.Tensor], num_experts: int, num_ranks: int,
+                    expert_alignment: int = 1):
+    """Buffer.dispatch in normal mode: each token is sent once to every rank
+    hosting one of its experts. Returns (recv_x [rows, H], recv_topk_idx
+    [rows, K] rank-local ids or -1, recv_topk_weights [rows, K] or None,
+    num_recv_tokens_per_expert [E] int32 aligned to expert_alignment,
+    rank_offset [R+1] int32, handle). The receive buffers of the R ranks are
+    one buffer sized for the worst case, T * min(K, R) rows; rank r's tokens
+    are rows [rank_offset[r], rank_offset[r+1]) (device values, no host
+    read)."""
+    T, H = x.shape
+    K = topk_idx.shape[1]
+    shape = capi.make_shape(T, H, num_experts, num_ranks, K, expert_alignment)
+    lay = capi.RankLayoutBuffers.empty(shape, x.device, weights=topk_weights is not None)
+    capi.moe_rank_layout(shape, topk_idx.contiguous(),
+                         topk_weights.contiguous() if topk_weights is not None else None, lay)
+    rows = max(lay.cap, 1)
+    recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
+    capi.moe_rank_dispatch(shape, x.contiguous(), lay.rank_slot, recv_x, lay.cap, lay.status)
+    w = lay.recv_topk_weights.view(rows, K) if lay.recv_topk_weights is not None else None
+    return (recv_x, lay.recv_topk_idx.view(rows, K), w, lay.recv_expert_count,
+            lay.rank_offset, RankHandle(shape, lay, lay.cap))
+
+
+def normal_combine(y: torch.Tensor, handle: RankHandle,
+                   topk_weights: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None):
+    """Buffer.combine in normal mode: adds each token's rows back from the
+    ranks it reached, without weights. Returns (combined_x [T, H] bf16,
+    combined_topk_weights [T, K] or None -- the received weights summed back)."""
+    shape = handle.shape
+    H = y.shape[-1]
+    if out is None:
+        out = torch.empty(shape.T, H, dtype=torch.bfloat16, device=y.device)
+    ow = None
+    if topk_weights is not None:
+        ow = torch.empty(shape.T, shape.K, dtype=torch.float32, device=y.device)
+    capi.moe_rank_combine(shape, y.contiguous(), handle.recv_rows, handle.layout.rank_slot,
+                          topk_weights.contiguous() if topk_weights is not None else None, out,
+                          None, ow, handle.layout.status)
+    return out, ow
+
+
 def expert_load(topk_idx: torch.Tensor, num_experts: int,
                 status: Optional[torch.Tensor] = None) -> torch.Tensor:
     T, K = topk_idx.shape

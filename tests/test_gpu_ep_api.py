@@ -108,3 +108,23 @@ def test_low_latency_dispatch_and_masked_combine(ep, orc, use_fp8, round_scale, 
     out2 = ep.low_latency_combine(recv, to_dev(w.topk_weights), h)
     assert np.array_equal(_bits(out2), orc.combine(y, ll["slot"], w.topk_weights,
                                                    "f32")["out_bf16"])
+
+
+def test_normal_dispatch_and_combine(ep, orc):
+    w = mi.config_c2()
+    x = to_dev(w.x).view(torch.bfloat16)
+    recv, ridx, rw, rcount, roff, h = ep.normal_dispatch(x, to_dev(w.topk_idx),
+                                                         to_dev(w.topk_weights), w.E, w.R, 4)
+    ref = orc.rank_layout(w.topk_idx, w.E, w.R, 4, w.topk_weights)
+    rows = ref["rows"]
+    assert np.array_equal(roff.cpu().numpy(), ref["rank_offset"])
+    assert np.array_equal(rcount.cpu().numpy(), ref["recv_expert_count"])
+    assert np.array_equal(ridx.cpu().numpy()[:rows], ref["recv_topk_idx"])
+    assert np.array_equal(rw.cpu().numpy()[:rows], ref["recv_topk_weights"])
+    assert np.array_equal(_bits(recv)[:rows], w.x[ref["recv_src"]])
+    out, cw = ep.normal_combine(recv, h, rw)
+    rref, _ = orc.dispatch(w.x, ref["rank_slot"], max(w.T * min(w.K, w.R), 1), fill=0)
+    assert np.array_equal(_bits(out), orc.combine(rref, ref["rank_slot"], None,
+                                                  "f32")["out_bf16"])
+    want, _ = orc.combine_rank_weights(ref["rank_slot"], ref["recv_topk_weights"])
+    assert np.array_equal(cw.cpu().numpy(), want)

@@ -98,6 +98,7 @@ CASES = [
     (4, 2000, 64, 32, 1, 4, 0.2, 0.0, 0.0),
     (5, 1500, 512, 256, 8, 8, 0.0, 0.0, 0.02),
     (6, 77, 1032, 96, 32, 6, 0.3, 0.3, 0.0),
+    (7, 50, 64, 16, 4, 12, 0.1, 0.3, 0.0),  # K > 8: the general two-pass kernel
 ]
 
 
