@@ -90,6 +90,8 @@ class Oracle:
                                            _P, _P, _P]
         lib.oracle_rank_layout.restype = C.c_int
         lib.oracle_combine_rank_weights.argtypes = [_I64, _I32, _I32, _P, _P, _I64, _P, _P]
+        lib.oracle_replica_weight_sync.argtypes = [_I32, _I64, _P, _P, _I32, _P]
+        lib.oracle_replica_grad_reduce.argtypes = [_I32, _I64, _P, _P, _I32, _P]
         lib.oracle_ll_dispatch_fp8.restype = C.c_int
         for f in ("oracle_layout", "oracle_ll_layout", "oracle_expert_load", "oracle_dispatch",
                   "oracle_combine_f64", "oracle_combine_f32", "oracle_plan_replicas",
@@ -338,6 +340,30 @@ class Oracle:
             raise ValueError(f"oracle_plan_replicas rejected its arguments ({rc})")
         return dict(replica_count=rc_, replica_phys=rp, phys_to_logical=p2l, E_phys=E + C_,
                     L_phys=E // R + C_ // R)
+
+    def replica_weight_sync(self, w: np.ndarray, replica_count: np.ndarray,
+                            replica_phys: np.ndarray) -> np.ndarray:
+        """Copy of w [E_phys, S] (bf16 bits) after the replica weight sync."""
+        w = np.ascontiguousarray(w, dtype=np.uint16).copy()
+        rc = np.ascontiguousarray(replica_count, np.int32)
+        rp = np.ascontiguousarray(replica_phys, np.int32)
+        res = self.lib.oracle_replica_weight_sync(rc.size, w.shape[1], _ptr(rc), _ptr(rp),
+                                                  w.shape[0], _ptr(w))
+        if res != 0:
+            raise ValueError(res)
+        return w
+
+    def replica_grad_reduce(self, g: np.ndarray, replica_count: np.ndarray,
+                            replica_phys: np.ndarray) -> np.ndarray:
+        """Copy of g [E_phys, S] (f32) after the replica gradient reduction."""
+        g = np.ascontiguousarray(g, dtype=np.float32).copy()
+        rc = np.ascontiguousarray(replica_count, np.int32)
+        rp = np.ascontiguousarray(replica_phys, np.int32)
+        res = self.lib.oracle_replica_grad_reduce(rc.size, g.shape[1], _ptr(rc), _ptr(rp),
+                                                  g.shape[0], _ptr(g))
+        if res != 0:
+            raise ValueError(res)
+        return g
 
     def reroute(self, idx: np.ndarray, E: int, replica_count: np.ndarray,
                 replica_phys: np.ndarray, E_phys: int) -> tuple:

@@ -508,6 +508,46 @@ int oracle_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
     return 0;
 }
 
+/* Replica weight sync ([P3] Overview: replicas get synchronized weights
+ * before expert execution; GPU operations: Replica weight sync). The physical
+ * expert buffer w [E_phys][S] holds every logical expert's master weights in
+ * its primary slot; each expert with a second replica gets a bit copy of them
+ * in the replica slot: w[replica_phys[2e+1]] = w[replica_phys[2e]]. */
+int oracle_replica_weight_sync(int32_t E, int64_t S, const int32_t *replica_count,
+                               const int32_t *replica_phys, int32_t E_phys, uint16_t *w) {
+    for (int32_t e = 0; e < E; ++e) {
+        if (replica_count[e] != 2) continue;
+        int32_t prim = replica_phys[2 * e], rep = replica_phys[2 * e + 1];
+        if (prim < 0 || prim >= E_phys || rep < 0 || rep >= E_phys) return -3;
+        memcpy(w + (int64_t)rep * S, w + (int64_t)prim * S, sizeof(uint16_t) * (size_t)S);
+    }
+    return 0;
+}
+
+/* Replica gradient reduction ([P3] Overview: replica gradients are reduced
+ * during backward; GPU operations: Replica gradient reduction). g [E_phys][S]
+ * f32 holds one gradient per physical expert; each replicated expert's master
+ * gradient, kept in its primary slot, becomes primary + replica, one float add
+ * per element: g[prim] = g[prim] + g[rep]. */
+int oracle_replica_grad_reduce(int32_t E, int64_t S, const int32_t *replica_count,
+                               const int32_t *replica_phys, int32_t E_phys, float *g) {
+    for (int32_t e = 0; e < E; ++e) {
+        if (replica_count[e] != 2) continue;
+        int32_t prim = replica_phys[2 * e], rep = replica_phys[2 * e + 1];
+        if (prim < 0 || prim >= E_phys || rep < 0 || rep >= E_phys) return -3;
+        float *gp = g + (int64_t)prim * S;
+        const float *gr = g + (int64_t)rep * S;
+        for (int64_t i = 0; i < S; ++i) {
+#if ORACLE_MUTANT == 20
+            gp[i] = gr[i]; /* mutant: the replica gradient replaces the master */
+#else
+            gp[i] = gp[i] + gr[i];
+#endif
+        }
+    }
+    return 0;
+}
+
 /* Expand logical routing to physical routing: the pair (t, k) on logical
  * expert e goes to replica (t mod replica_count[e]) of e; -1 stays -1. */
 int oracle_reroute(int64_t T, int32_t K, int32_t E, const int64_t *idx,

@@ -660,6 +660,39 @@ def check_rank_closed_forms(orc, w, A: int = 1):
     assert np.array_equal(cw, np.where(valid, w.topk_weights, 0.0).astype(np.float32))
 
 
+def check_replica_sync_and_reduce(orc, seed: int = 13):
+    """Weight sync and gradient reduction against numpy, through the other
+    table of the plan (phys_to_logical): after the sync every physical slot
+    holds its logical expert's master weights (numpy fancy indexing); the
+    master gradient of expert e is numpy's float32 sum of the gradients of all
+    physical slots that map to e (at most two terms: one rounding, so equal
+    bit for bit); replicas of cold experts and all other slots are untouched."""
+    rng = np.random.default_rng(seed)
+    for E, R, C, S in ((16, 4, 4, 40), (64, 8, 16, 7), (8, 2, 0, 5), (32, 8, 32, 3)):
+        load = rng.integers(0, 100, E).astype(np.int32)
+        plan = orc.plan_replicas(load, R, C)
+        Ep = plan["E_phys"]
+        p2l = plan["phys_to_logical"]
+        w = rng.integers(0, 1 << 16, (Ep, S)).astype(np.uint16)
+        prim = plan["replica_phys"][:, 0]
+        master = w[prim]  # the masters sit in the primary slots
+        ws = orc.replica_weight_sync(w, plan["replica_count"], plan["replica_phys"])
+        assert np.array_equal(ws, master[p2l])
+        g = rng.standard_normal((Ep, S)).astype(np.float32)
+        gr = orc.replica_grad_reduce(g, plan["replica_count"], plan["replica_phys"])
+        want = np.zeros((E, S), np.float32)
+        for e in range(E):
+            terms = [g[p] for p in range(Ep) if p2l[p] == e]
+            acc = terms[0]
+            for tm in terms[1:]:
+                acc = (acc + tm).astype(np.float32)
+            want[e] = acc
+        assert np.array_equal(gr[prim].view(np.uint32), want.view(np.uint32))
+        others = np.ones(Ep, bool)
+        others[prim] = False
+        assert np.array_equal(gr[others].view(np.uint32), g[others].view(np.uint32))
+
+
 ALL_SMALL_CHECKS = (
     check_golden,
     check_layout_vs_bruteforce,
@@ -677,4 +710,5 @@ ALL_SMALL_CHECKS = (
     check_recv_stats,
     check_rank_golden,
     lambda o: check_rank_layout_vs_bruteforce(o, n=30),
+    check_replica_sync_and_reduce,
 )

@@ -27,6 +27,7 @@ MUTANTS = {
     17: "masked combine takes the rank as e mod R",
     18: "normal-mode rows in descending token order",
     19: "normal-mode received ids global instead of rank-local",
+    20: "replica gradient replaces the master gradient",
 }
 
 

@@ -157,3 +157,7 @@ def test_rank_layout_closed_forms(orc, name, A):
     if name == "c5":  # the replica workload's routing, at reduced width
         w = mi.config_c5(T=2048, H=64)
     pins.check_rank_closed_forms(orc, w, A)
+
+
+def test_replica_weight_sync_and_grad_reduce(orc):
+    pins.check_replica_sync_and_reduce(orc)
