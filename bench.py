@@ -318,6 +318,55 @@ def row_normal(capi, mi, torch, np, dev, stream):
                                                 / HBM_PEAK_GBS, 4)}}
 
 
+def row_replica_train(capi, mi, torch, np, dev, stream):
+    """Replica weight sync and replica gradient reduction for the replica
+    workload's plan (256 logical experts, 32 replicas on 8 ranks), with one
+    7168 x 2048 matrix per expert (a stand-in: the pages give no expert size):
+    bf16 weights, f32 gradients, 288 physical experts."""
+    w5 = mi.config_c5(T=8192, H=8)
+    E, R, C = w5.E, w5.R, w5.replicas
+    Ep = E + C
+    S = 7168 * 2048
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.from_numpy(w5.topk_idx).to(dev)
+    load = torch.empty(E, **i32)
+    rc = torch.empty(E, **i32)
+    rp = torch.empty(E, 2, **i32)
+    p2l = torch.empty(Ep, **i32)
+    capi.moe_expert_load(w5.T, w5.K, E, idx, load)
+    capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l)
+    w = torch.zeros(Ep * S, dtype=torch.int16, device=dev)
+    g = torch.zeros(Ep * S, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def timed(fn, n=5):
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    t_sync = timed(lambda: capi.moe_replica_weight_sync(E, Ep, S, rc, rp, w, stream=stream))
+    t_red = timed(lambda: capi.moe_replica_grad_reduce(E, Ep, S, rc, rp, g, stream=stream))
+    b_sync = 2 * C * S * 2
+    b_red = 3 * C * S * 4
+    del w, g
+    torch.cuda.empty_cache()
+    return {"workload": "replica weight sync (bf16) and gradient reduction (f32), 256 experts + 32 "
+                        "replicas, one 7168x2048 matrix per expert",
+            "weight_sync_us": round(t_sync, 1), "grad_reduce_us": round(t_red, 1),
+            "weight_sync_GB_per_s": round(b_sync / t_sync / 1e3, 1),
+            "grad_reduce_GB_per_s": round(b_red / t_red / 1e3, 1),
+            "frac_weight_sync": round(b_sync / t_sync / 1e3 / HBM_PEAK_GBS, 4),
+            "frac_grad_reduce": round(b_red / t_red / 1e3 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": {"weight_sync": b_sync, "grad_reduce": b_red}}
+
+
 def row_replica(capi, mi, torch, np, dev, stream, n_ev):
     """Replica-expanded routing at full size (8192 tokens x 7168, 256 logical
     experts top-8 Zipf(1.0), 32 extra replicas): load -> plan -> reroute ->
@@ -537,6 +586,9 @@ def main():
         log(f"normal-mode row: {rows['normal_mode_128x7168']['us_per_step']} us/step")
         rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
         log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
+        rows["replica_train"] = row_replica_train(capi, mi, torch, np, dev, stream)
+        log(f"replica sync/reduce row: {rows['replica_train']['weight_sync_us']} / "
+            f"{rows['replica_train']['grad_reduce_us']} us")
 
     torch.cuda.synchronize()
     out_bits = sets[0].out.cpu().numpy().view(np.uint16)

@@ -85,6 +85,8 @@ def _load():
         "moe_rank_layout": (C.c_int, [P, P, P, P, I64, P]),
         "moe_rank_dispatch": (C.c_int, [P, P, P, P, I64, P, P]),
         "moe_rank_combine": (C.c_int, [P, P, I64, P, P, P, P, P, P, P]),
+        "moe_replica_weight_sync": (C.c_int, [I32, I32, I64, P, P, P, P, P]),
+        "moe_replica_grad_reduce": (C.c_int, [I32, I32, I64, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -100,7 +102,8 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_re
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
             "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
             "moe_dispatch_fp8", "moe_combine_masked", "moe_rank_recv_rows_worst",
-            "moe_rank_layout", "moe_rank_dispatch", "moe_rank_combine")
+            "moe_rank_layout", "moe_rank_dispatch", "moe_rank_combine",
+            "moe_replica_weight_sync", "moe_replica_grad_reduce")
 
 
 def lib():
@@ -505,3 +508,24 @@ def moe_dispatch_fp8(shape: moe_shape, x_q: torch.Tensor, x_scale: torch.Tensor,
         _dev(recv_q, "recv_q", _FP8_CODES, int(recv_rows) * H),
         _dev(recv_scale, "recv_scale", (torch.float32,), int(recv_rows) * G), int(recv_rows),
         _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
+
+
+def moe_replica_weight_sync(E: int, E_phys: int, S: int, replica_count: torch.Tensor,
+                            replica_phys: torch.Tensor, w: torch.Tensor,
+                            status: Optional[torch.Tensor] = None, stream=None) -> int:
+    i32 = (torch.int32,)
+    return _check("moe_replica_weight_sync", _lib.moe_replica_weight_sync(
+        int(E), int(E_phys), int(S), _dev(replica_count, "replica_count", i32, E),
+        _dev(replica_phys, "replica_phys", i32, 2 * E), _dev(w, "w", _BF16_LIKE, E_phys * S),
+        _dev(status, "status", i32, 1, optional=True), _stream(stream)))
+
+
+def moe_replica_grad_reduce(E: int, E_phys: int, S: int, replica_count: torch.Tensor,
+                            replica_phys: torch.Tensor, g: torch.Tensor,
+                            status: Optional[torch.Tensor] = None, stream=None) -> int:
+    i32 = (torch.int32,)
+    return _check("moe_replica_grad_reduce", _lib.moe_replica_grad_reduce(
+        int(E), int(E_phys), int(S), _dev(replica_count, "replica_count", i32, E),
+        _dev(replica_phys, "replica_phys", i32, 2 * E),
+        _dev(g, "g", (torch.float32,), E_phys * S),
+        _dev(status, "status", i32, 1, optional=True), _stream(stream)))

@@ -473,6 +473,45 @@ MOE_API int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *lo
              : MOE_ERR_LAUNCH;
 }
 
+namespace {
+int replica_move_checks(int32_t E, int32_t E_phys, int64_t S, const int32_t *replica_count,
+                        const int32_t *replica_phys, const void *buf) {
+  if (E < 1 || E > 65535 || E_phys < E || S < 0 || S % 8 != 0) return MOE_ERR_SHAPE;
+  if (S > 0 && (int64_t)E_phys * S / 4 >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (!replica_count || !replica_phys || (S > 0 && !buf)) return MOE_ERR_NULL;
+  if (!aligned16(buf)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+}  // namespace
+
+MOE_API int moe_replica_weight_sync(int32_t E, int32_t E_phys, int64_t S,
+                                    const int32_t *replica_count, const int32_t *replica_phys,
+                                    uint16_t *w, int32_t *status, hipStream_t stream) {
+  int rc = replica_move_checks(E, E_phys, S, replica_count, replica_phys, w);
+  if (rc) return rc;
+  if (S == 0) return MOE_OK;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_replica_weight_sync(E, E_phys, S, replica_count, replica_phys, w, status,
+                                    stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
+MOE_API int moe_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S,
+                                    const int32_t *replica_count, const int32_t *replica_phys,
+                                    float *g, int32_t *status, hipStream_t stream) {
+  int rc = replica_move_checks(E, E_phys, S, replica_count, replica_phys, g);
+  if (rc) return rc;
+  if (S == 0) return MOE_OK;
+  rc = check_device();
+  if (rc) return rc;
+  return launch_replica_grad_reduce(E, E_phys, S, replica_count, replica_phys, g, status,
+                                    stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_LAUNCH;
+}
+
 MOE_API int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
                         const int32_t *replica_count, const int32_t *replica_phys,
                         int32_t E_phys, int64_t *phys_idx, int32_t *status, hipStream_t stream) {

@@ -123,6 +123,12 @@ hipError_t launch_rank_combine(const uint16_t *y, int64_t rows, const int32_t *r
                                uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t H,
                                const RowWeightSum &ws, int32_t *status, hipStream_t s);
 
+hipError_t launch_replica_weight_sync(int32_t E, int32_t E_phys, int64_t S,
+                                      const int32_t *replica_count, const int32_t *replica_phys,
+                                      uint16_t *w, int32_t *status, hipStream_t s);
+hipError_t launch_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S,
+                                      const int32_t *replica_count, const int32_t *replica_phys,
+                                      float *g, int32_t *status, hipStream_t s);
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,
                                 int32_t *phys_to_logical, hipStream_t s);

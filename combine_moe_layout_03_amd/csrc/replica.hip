@@ -12,6 +12,13 @@
 // round-robin over the ranks.
 // Reroute: one thread per (token, k) pair; the pair uses replica
 // (t mod replica_count[e]) of its expert.
+// Weight sync and gradient reduction (GPU operations: Replica weight sync,
+// Replica gradient reduction): the physical expert buffer keeps each expert's
+// master copy in its primary slot; the sync copies it into the replica slot,
+// the reduction adds the replica's f32 gradient into the primary's. Grid: one
+// row of workgroups per logical expert (the ones without a replica exit at
+// once), each streaming its share of the S elements as 16-byte vectors, four
+// in flight per thread.
 #include "kernels.hpp"
 
 namespace moe {
@@ -88,7 +95,82 @@ __global__ __launch_bounds__(256) void reroute_kernel(int32_t T, int32_t K, int3
   if (st && status) atomicOr(status, st);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kReplicaUnroll = 4;
+
+template <bool kReduce>
+__global__ __launch_bounds__(256) void replica_move_kernel(const int32_t *__restrict__ replica_count,
+                                                           const int32_t *__restrict__ replica_phys,
+                                                           int32_t E_phys, int64_t nvec,
+                                                           void *buf, int32_t *status) {
+  const int e = blockIdx.y;
+  if (replica_count[e] != 2) return;  // wave-uniform
+  const int prim = replica_phys[2 * e], rep = replica_phys[2 * e + 1];
+  if (prim < 0 || prim >= E_phys || rep < 0 || rep >= E_phys) {
+    if (status && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, kStBadReplica);
+    return;
+  }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (!kReduce) {
+    const u32x4 *src = static_cast<const u32x4 *>(buf) + (int64_t)prim * nvec;
+    u32x4 *dst = static_cast<u32x4 *>(buf) + (int64_t)rep * nvec;
+    for (; v + (kReplicaUnroll - 1) * stride < nvec; v += kReplicaUnroll * stride) {
+      u32x4 a[kReplicaUnroll];
+#pragma unroll
+      for (int j = 0; j < kReplicaUnroll; ++j) a[j] = __builtin_nontemporal_load(src + v + j * stride);
+#pragma unroll
+      for (int j = 0; j < kReplicaUnroll; ++j) __builtin_nontemporal_store(a[j], dst + v + j * stride);
+    }
+    for (; v < nvec; v += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+  } else {
+#pragma clang fp contract(off)
+    f32x4 *gp = static_cast<f32x4 *>(buf) + (int64_t)prim * nvec;
+    const f32x4 *gr = static_cast<const f32x4 *>(buf) + (int64_t)rep * nvec;
+    for (; v + (kReplicaUnroll - 1) * stride < nvec; v += kReplicaUnroll * stride) {
+      f32x4 a[kReplicaUnroll], b[kReplicaUnroll];
+#pragma unroll
+      for (int j = 0; j < kReplicaUnroll; ++j) {
+        a[j] = __builtin_nontemporal_load(gp + v + j * stride);
+        b[j] = __builtin_nontemporal_load(gr + v + j * stride);
+      }
+#pragma unroll
+      for (int j = 0; j < kReplicaUnroll; ++j) __builtin_nontemporal_store(a[j] + b[j], gp + v + j * stride);
+    }
+    for (; v < nvec; v += stride)
+      __builtin_nontemporal_store(__builtin_nontemporal_load(gp + v) + __builtin_nontemporal_load(gr + v), gp + v);
+  }
+}
+
+// Workgroups per expert: enough for ~8 vectors per thread, at most 1024.
+unsigned replica_wgs(int64_t nvec) {
+  const int64_t per = 256LL * kReplicaUnroll * 2;
+  int64_t n = (nvec + per - 1) / per;
+  return (unsigned)(n < 1 ? 1 : (n > 1024 ? 1024 : n));
+}
+
 }  // namespace
+
+hipError_t launch_replica_weight_sync(int32_t E, int32_t E_phys, int64_t S,
+                                      const int32_t *replica_count, const int32_t *replica_phys,
+                                      uint16_t *w, int32_t *status, hipStream_t s) {
+  const int64_t nvec = S / 8;  // bf16, 8 per vector
+  hipLaunchKernelGGL(replica_move_kernel<false>, dim3(replica_wgs(nvec), (unsigned)E), dim3(256),
+                     0, s, replica_count, replica_phys, E_phys, nvec, static_cast<void *>(w),
+                     status);
+  return hipGetLastError();
+}
+
+hipError_t launch_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S,
+                                      const int32_t *replica_count, const int32_t *replica_phys,
+                                      float *g, int32_t *status, hipStream_t s) {
+  const int64_t nvec = S / 4;  // f32, 4 per vector
+  hipLaunchKernelGGL(replica_move_kernel<true>, dim3(replica_wgs(nvec), (unsigned)E), dim3(256),
+                     0, s, replica_count, replica_phys, E_phys, nvec, static_cast<void *>(g),
+                     status);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,

@@ -346,6 +346,29 @@ int moe_dispatch_fp8(const moe_shape *shape, const uint8_t *x_q, const float *x_
                      const int32_t *slot, uint8_t *recv_q, float *recv_scale,
                      int64_t recv_rows, int32_t *status, hipStream_t stream);
 
+/* Replica weight sync (ultraep Overview: replicas get synchronized weights
+ * before expert execution; GPU operations: Replica weight sync). w [E_phys*S]
+ * bf16 is the physical expert buffer, expert p's S parameters at p*S; each
+ * logical expert's master weights sit in its primary slot. For every expert e
+ * with replica_count[e] == 2, the replica slot replica_phys[2e+1] receives a
+ * bit copy of the primary slot replica_phys[2e]. S % 8 == 0; w 16-byte
+ * aligned. Table entries outside [0, E_phys) set MOE_STATUS_BAD_REPLICA and
+ * that expert is skipped. (Restoring the weights after backward needs no data
+ * movement: the replica slots are scratch.) */
+int moe_replica_weight_sync(int32_t E, int32_t E_phys, int64_t S, const int32_t *replica_count,
+                            const int32_t *replica_phys, uint16_t *w, int32_t *status,
+                            hipStream_t stream);
+
+/* Replica gradient reduction (ultraep Overview: replica gradients are reduced
+ * during backward; GPU operations: Replica gradient reduction). g [E_phys*S]
+ * f32: for every expert e with a second replica,
+ * g[prim*S + i] = g[prim*S + i] + g[rep*S + i] (one float add), leaving the
+ * master gradient in the primary slot. Same argument rules as
+ * moe_replica_weight_sync. */
+int moe_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S, const int32_t *replica_count,
+                            const int32_t *replica_phys, float *g, int32_t *status,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 23, declared
+    assert len(declared) == 25, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -242,3 +242,16 @@ def test_rank_mode_checks(lib):
     assert raw.moe_rank_dispatch(C.byref(s0), None, None, None, 0, None, None) == 0
     assert raw.moe_rank_combine(C.byref(s0), None, 0, None, None, None, None, None, None,
                                 None) == 0
+
+
+def test_replica_move_checks(lib):
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(264)
+    for f in (raw.moe_replica_weight_sync, raw.moe_replica_grad_reduce):
+        assert f(16, 20, 12, d, d, d, None, None) == -2  # S % 8
+        assert f(16, 12, 8, d, d, d, None, None) == -2  # E_phys < E
+        assert f(16, 20, 8, None, d, d, None, None) == -1
+        assert f(16, 20, 8, d, d, None, None, None) == -1
+        assert f(16, 20, 8, d, d, odd, None, None) == -5
+        assert f(16, 20, 0, d, d, None, None, None) == 0  # nothing to move
