@@ -36,6 +36,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "dispatch+combine µs & HBM GB/s (% of peak), 128 tok×7168 hidden, 256E top-8"
 KERNEL_SOURCES = ("combine_moe_layout_03_amd/csrc/scatter.hip",
                   "combine_moe_layout_03_amd/csrc/fused.hip",
+                  "combine_moe_layout_03_amd/csrc/fp8.hpp",
                   "combine_moe_layout_03_amd/csrc/layout.hip",
                   "combine_moe_layout_03_amd/csrc/wave.hpp",
                   "combine_moe_layout_03_amd/csrc/kernels.hpp")
