@@ -515,7 +515,7 @@ MOE_API int moe_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S,
 MOE_API int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
                         const int32_t *replica_count, const int32_t *replica_phys,
                         int32_t E_phys, int64_t *phys_idx, int32_t *status, hipStream_t stream) {
-  if (T < 0 || K < 1 || K > 64 || E < 1 || E_phys < 1) return MOE_ERR_SHAPE;
+  if (T < 0 || K < 1 || K > 64 || E < 1 || E > kMaxExperts || E_phys < 1) return MOE_ERR_SHAPE;
   if ((int64_t)T * K >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!topk_idx || !replica_count || !replica_phys || !phys_idx) return MOE_ERR_NULL;

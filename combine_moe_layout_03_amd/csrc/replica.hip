@@ -36,16 +36,23 @@ __global__ __launch_bounds__(kLayoutThreads) void plan_replicas_kernel(
   if (e >= E) return;
   const int mine = s_load[e];
   int ahead = 0;
-  // 16-byte LDS reads (broadcast: every thread reads the same address)
-  const int E4 = E & ~3;
-  for (int f = 0; f < E4; f += 4) {
-    const int4 q = *reinterpret_cast<const int4 *>(&s_load[f]);
-    ahead += (q.x > mine) || (q.x == mine && f < e);
-    ahead += (q.y > mine) || (q.y == mine && f + 1 < e);
-    ahead += (q.z > mine) || (q.z == mine && f + 2 < e);
-    ahead += (q.w > mine) || (q.w == mine && f + 3 < e);
+  // 16-byte LDS reads (broadcast: every thread reads the same address), eight
+  // in flight per wait, so the LDS latency is paid once per 32 experts
+  const int E32 = E & ~31;
+  for (int f0 = 0; f0 < E32; f0 += 32) {
+    int4 q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = *reinterpret_cast<const int4 *>(&s_load[f0 + 4 * j]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = f0 + 4 * j;
+      ahead += (q[j].x > mine) || (q[j].x == mine && f < e);
+      ahead += (q[j].y > mine) || (q[j].y == mine && f + 1 < e);
+      ahead += (q[j].z > mine) || (q[j].z == mine && f + 2 < e);
+      ahead += (q[j].w > mine) || (q[j].w == mine && f + 3 < e);
+    }
   }
-  for (int f = E4; f < E; ++f) {
+  for (int f = E32; f < E; ++f) {
     const int lf = s_load[f];
     ahead += (lf > mine) || (lf == mine && f < e);
   }
@@ -70,17 +77,28 @@ __global__ __launch_bounds__(256) void reroute_kernel(int32_t T, int32_t K, int3
                                                       const int32_t *__restrict__ replica_phys,
                                                       int32_t E_phys, int64_t *__restrict__ phys,
                                                       int32_t *status) {
+  // The plan's tables go to LDS while the ids load, so each pair costs one
+  // global read instead of three dependent ones.
+  __shared__ int32_t s_count[kMaxExperts];
+  __shared__ int32_t s_phys[2 * kMaxExperts];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)T * K) return;
-  const int64_t v = idx[i];
+  const bool live = i < (int64_t)T * K;
+  const int64_t v = live ? idx[i] : -1;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_count[e] = replica_count[e];
+    s_phys[2 * e] = replica_phys[2 * e];
+    s_phys[2 * e + 1] = replica_phys[2 * e + 1];
+  }
+  __syncthreads();
+  if (!live) return;
   int64_t out = -1;
   int st = 0;
   if (v >= 0 && v < E) {
     const int e = (int)v;
-    const int c = replica_count[e];
+    const int c = s_count[e];
     if (c == 1 || c == 2) {
       const int t = (int)(i / K);
-      const int ph = replica_phys[2 * e + (c == 2 ? (t & 1) : 0)];
+      const int ph = s_phys[2 * e + (c == 2 ? (t & 1) : 0)];
       if (ph >= 0 && ph < E_phys)
         out = ph;
       else

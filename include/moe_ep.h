@@ -275,7 +275,8 @@ int moe_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
  * routing -> physical routing. The pair (t,k) on expert e uses replica
  * t mod replica_count[e]: phys_idx[t*K+k] = replica_phys[2e + t mod count];
  * -1 stays -1. Entries that fall outside [0, E_phys) set MOE_STATUS_BAD_REPLICA
- * and give -1. phys_idx [T*K] int64 can feed moe_layout with E = E_phys. */
+ * and give -1. phys_idx [T*K] int64 can feed moe_layout with E = E_phys.
+ * Needs 1 <= E <= 1024. */
 int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx,
                 const int32_t *replica_count, const int32_t *replica_phys, int32_t E_phys,
                 int64_t *phys_idx, int32_t *status, hipStream_t stream);

@@ -141,6 +141,7 @@ def test_replica_checks(lib):
     assert raw.moe_plan_replicas(250, 8, 32, d, d, d, d, None) == -2  # E % R
     assert raw.moe_plan_replicas(256, 8, 32, None, d, d, d, None) == -1
     assert raw.moe_reroute(4, 0, 16, d, d, d, 20, d, None, None) == -2
+    assert raw.moe_reroute(4, 2, 1025, d, d, d, 2000, d, None, None) == -2
     assert raw.moe_reroute(4, 2, 16, None, d, d, 20, d, None, None) == -1
     assert raw.moe_reroute(0, 2, 16, None, None, None, 20, None, None, None) == 0
     assert raw.moe_expert_load(4, 2, 2000, d, d, None, None) == -2
