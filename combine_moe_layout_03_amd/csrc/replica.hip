@@ -3,10 +3,10 @@
 // layer's post-gating routing, then expand the routing before the experts;
 // GPU operations: Placement planning, Routing expansion).
 //
-// Plan: one workgroup, one expert per thread. An expert's place in the order
-// (load descending, id ascending) is the number of experts ahead of it, read
-// from an LDS copy of the loads (broadcast reads); the first C get a second
-// physical replica. Numbering: rank r holds L' = L + C/R physical experts,
+// Plan: one workgroup per expert. An expert's place in the order (load
+// descending, id ascending) is the number of experts ahead of it, counted by
+// the workgroup's threads over the E loads and summed; the first C get a
+// second physical replica. Numbering: rank r holds L' = L + C/R physical experts,
 // r*L' + l (l < L) is the primary of logical expert r*L + l, and the i-th
 // hottest expert's replica is (i mod R)*L' + L + i/R, so replicas are dealt
 // round-robin over the ranks.
@@ -19,51 +19,37 @@
 // row of workgroups per logical expert (the ones without a replica exit at
 // once), each streaming its share of the S elements as 16-byte vectors, four
 // in flight per thread.
-#include "kernels.hpp"
+#include "wave.hpp"
 
 namespace moe {
 namespace {
 
-__global__ __launch_bounds__(kLayoutThreads) void plan_replicas_kernel(
+// One workgroup per expert e: its threads compare e against a share of the E
+// loads and the counts meet in one block sum, so the E^2 comparisons are
+// spread over E CUs instead of queuing on one.
+__global__ __launch_bounds__(256) void plan_replicas_kernel(
     int32_t E, int32_t R, int32_t C, const int32_t *__restrict__ load,
     int32_t *__restrict__ replica_count, int32_t *__restrict__ replica_phys,
     int32_t *__restrict__ phys_to_logical) {
-  __shared__ __align__(16) int32_t s_load[kMaxExperts];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kLayoutThreads) s_load[e] = load[e];
-  __syncthreads();
-  const int e = tid;
-  if (e >= E) return;
-  const int mine = s_load[e];
+  __shared__ int32_t s_wave[4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int mine = load[e];
   int ahead = 0;
-  // 16-byte LDS reads (broadcast: every thread reads the same address), eight
-  // in flight per wait, so the LDS latency is paid once per 32 experts
-  const int E32 = E & ~31;
-  for (int f0 = 0; f0 < E32; f0 += 32) {
-    int4 q[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = *reinterpret_cast<const int4 *>(&s_load[f0 + 4 * j]);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int f = f0 + 4 * j;
-      ahead += (q[j].x > mine) || (q[j].x == mine && f < e);
-      ahead += (q[j].y > mine) || (q[j].y == mine && f + 1 < e);
-      ahead += (q[j].z > mine) || (q[j].z == mine && f + 2 < e);
-      ahead += (q[j].w > mine) || (q[j].w == mine && f + 3 < e);
-    }
-  }
-  for (int f = E32; f < E; ++f) {
-    const int lf = s_load[f];
+  for (int f = tid; f < E; f += 256) {
+    const int lf = load[f];
     ahead += (lf > mine) || (lf == mine && f < e);
   }
+  int total = 0;
+  block_exclusive_scan(ahead, s_wave, 4, &total);
+  if (tid != 0) return;
   const int L = E / R, Lp = L + C / R;
   const int prim = (e / L) * Lp + (e - (e / L) * L);
-  const bool hot = ahead < C;
+  const bool hot = total < C;
   replica_count[e] = hot ? 2 : 1;
   replica_phys[2 * e] = prim;
   phys_to_logical[prim] = e;
   if (hot) {
-    const int rep = (ahead % R) * Lp + L + ahead / R;
+    const int rep = (total % R) * Lp + L + total / R;
     replica_phys[2 * e + 1] = rep;
     phys_to_logical[rep] = e;
   } else {
@@ -193,7 +179,7 @@ hipError_t launch_replica_grad_reduce(int32_t E, int32_t E_phys, int64_t S,
 hipError_t launch_plan_replicas(int32_t E, int32_t R, int32_t C, const int32_t *load,
                                 int32_t *replica_count, int32_t *replica_phys,
                                 int32_t *phys_to_logical, hipStream_t s) {
-  hipLaunchKernelGGL(plan_replicas_kernel, dim3(1), dim3(kLayoutThreads), 0, s, E, R, C, load,
+  hipLaunchKernelGGL(plan_replicas_kernel, dim3((unsigned)E), dim3(256), 0, s, E, R, C, load,
                      replica_count, replica_phys, phys_to_logical);
   return hipGetLastError();
 }
