@@ -458,3 +458,33 @@ def test_graph_replays_match_eager(capi, orc):
     ref_lay = orc.layout(w.topk_idx, w.E, w.R, 1)
     assert np.array_equal(lay.slot.cpu().numpy().reshape(w.T, w.K), ref_lay["slot"])
     assert int(lay.status.item()) == 0
+
+
+def test_special_values_bit_patterns(capi, orc):
+    """Rows of arbitrary bf16 bit patterns (NaN, infinities, -0, subnormals
+    included) and weights of any sign and size: dispatch copies the bits,
+    combine matches the oracle's float ascending-k path bit for bit (NaN
+    results as 0x7FC0; subnormal products kept, not flushed)."""
+    rng = np.random.default_rng(99)
+    w = mi.random_case(99, 200, 264, 32, 4, 6, 1, neg_frac=0.1, dup_frac=0.2)
+    x = rng.integers(0, 1 << 16, (w.T, w.H)).astype(np.uint16)
+    x[:, :8] = np.array([0x7F80, 0xFF80, 0x7FC1, 0x8000, 0x0001, 0x807F, 0x0080, 0x7F7F],
+                        np.uint16)
+    wts = (rng.standard_normal((w.T, w.K)) * np.exp2(rng.integers(-130, 20, (w.T, w.K)))
+           ).astype(np.float32)
+    wts[0, :] = 0.0
+    wts[1, 0] = -0.0
+    w.topk_weights = wts
+    _announce("special bit patterns: dispatch + weighted combine")
+    got, lay, shape = run_layout(capi, w)
+    ref = orc.layout(w.topk_idx, w.E, w.R, 1)
+    check_layout(got, ref, w)
+    recv, out16, out32, st = run_dispatch_combine(capi, w, shape, lay, got["rows"], x=x)
+    rref, _ = orc.dispatch(x, ref["slot"], got["rows"], fill=SENTINEL)
+    assert np.array_equal(recv[:got["rows"]], rref), "dispatch bits"
+    r32 = orc.combine(rref, ref["slot"], wts, "f32")
+    assert np.array_equal(out16, r32["out_bf16"]), "combine bf16 bits"
+    g, r = out32.view(np.uint32), r32["out_f32"].view(np.uint32)
+    nan = np.isnan(r32["out_f32"])
+    assert np.array_equal(np.isnan(out32), nan)
+    assert np.array_equal(g[~nan], r[~nan]), "combine f32 bits"
