@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ep.so")
 SOURCES = ["capi.hip", "layout.hip", "fused.hip", "scatter.hip", "fp8.hip", "ranks.hip",
-           "replica.hip"]
+           "rank_fused.hip", "replica.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
 
-MOE_ABI_VERSION = 3  # the version the binding is written against
+MOE_ABI_VERSION = 4  # the version the binding is written against
 
 MOE_STATUS_BAD_EXPERT = 1
 MOE_STATUS_LL_OVERFLOW = 2
@@ -84,6 +84,7 @@ def _load():
         "moe_rank_recv_rows_worst": (I64, [P]),
         "moe_rank_layout": (C.c_int, [P, P, P, P, I64, P]),
         "moe_rank_dispatch": (C.c_int, [P, P, P, P, I64, P, P]),
+        "moe_rank_layout_dispatch": (C.c_int, [P, P, P, P, I64, P, P, I64, P]),
         "moe_rank_combine": (C.c_int, [P, P, I64, P, P, P, P, P, P, P]),
         "moe_replica_weight_sync": (C.c_int, [I32, I32, I64, P, P, P, P, P]),
         "moe_replica_grad_reduce": (C.c_int, [I32, I32, I64, P, P, P, P, P]),
@@ -102,7 +103,8 @@ EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_re
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
             "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
             "moe_dispatch_fp8", "moe_combine_masked", "moe_rank_recv_rows_worst",
-            "moe_rank_layout", "moe_rank_dispatch", "moe_rank_combine",
+            "moe_rank_layout", "moe_rank_dispatch", "moe_rank_layout_dispatch",
+            "moe_rank_combine",
             "moe_replica_weight_sync", "moe_replica_grad_reduce")
 
 
@@ -416,6 +418,20 @@ def moe_rank_dispatch(shape: moe_shape, x: torch.Tensor, rank_slot: torch.Tensor
         _dev(rank_slot, "rank_slot", (torch.int32,), T * R),
         _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
         _dev(status, "status", (torch.int32,), 1, optional=True), _stream(stream)))
+
+
+def moe_rank_layout_dispatch(shape: moe_shape, topk_idx: torch.Tensor,
+                             topk_weights: Optional[torch.Tensor], out: RankLayoutBuffers,
+                             x: torch.Tensor, recv_x: torch.Tensor, recv_rows: int,
+                             stream=None) -> int:
+    T, K, H = shape.T, shape.K, shape.H
+    st = out._struct(shape)
+    return _check("moe_rank_layout_dispatch", _lib.moe_rank_layout_dispatch(
+        C.byref(shape), _dev(topk_idx, "topk_idx", (torch.int64,), T * K),
+        _dev(topk_weights, "topk_weights", (torch.float32,), T * K, optional=True),
+        C.byref(st), int(out.cap), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
+        _stream(stream)))
 
 
 def moe_rank_combine(shape: moe_shape, y: torch.Tensor, recv_rows: int, rank_slot: torch.Tensor,

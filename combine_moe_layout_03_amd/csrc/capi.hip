@@ -436,6 +436,40 @@ MOE_API int moe_rank_dispatch(const moe_shape *shape, const uint16_t *x, const i
              : MOE_ERR_LAUNCH;
 }
 
+MOE_API int moe_rank_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx,
+                                     const float *topk_weights, const moe_rank_layout_t *out,
+                                     int64_t recv_cap, const uint16_t *x, uint16_t *recv_x,
+                                     int64_t recv_rows, hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  if (shape->R > kMaxRanksNormal) return MOE_ERR_SHAPE;
+  if (!out || !out->rank_offset || (shape->T > 0 && !out->rank_slot)) return MOE_ERR_NULL;
+  if (shape->T > 0 && !topk_idx) return MOE_ERR_NULL;
+  if (out->recv_topk_weights && !topk_weights && shape->T > 0) return MOE_ERR_NULL;
+  if (recv_cap < 0 || recv_rows < 0) return MOE_ERR_CAPACITY;
+  if (shape->T > 0 && (!x || (!recv_x && recv_rows > 0))) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(recv_x)) return MOE_ERR_ALIGN;
+  rc = check_device();
+  if (rc) return rc;
+  hipError_t e;
+  if (rank_layout_dispatch_fits(shape->T, shape->K, shape->R)) {
+    e = launch_rank_layout_dispatch(topk_idx, topk_weights, shape->T, shape->K, shape->E,
+                                    shape->R, shape->A, out->rank_slot, out->rank_offset,
+                                    out->recv_src, out->recv_topk_idx, out->recv_topk_weights,
+                                    out->recv_expert_count, recv_cap, out->status, x, recv_x,
+                                    recv_rows, shape->H, stream);
+  } else {
+    e = launch_rank_layout(topk_idx, topk_weights, shape->T, shape->K, shape->E, shape->R,
+                           shape->A, out->rank_slot, out->rank_offset, out->recv_src,
+                           out->recv_topk_idx, out->recv_topk_weights, out->recv_expert_count,
+                           recv_cap, out->status, stream);
+    if (e == hipSuccess && shape->T > 0)
+      e = launch_dispatch(x, out->rank_slot, recv_x, shape->T, shape->R, shape->H, recv_rows,
+                          out->status, stream);
+  }
+  return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
 MOE_API int moe_rank_combine(const moe_shape *shape, const uint16_t *y, int64_t recv_rows,
                              const int32_t *rank_slot, const float *recv_topk_weights,
                              uint16_t *out, float *out_f32, float *out_topk_weights,

@@ -112,6 +112,16 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
                               int32_t *rank_offset, int32_t *recv_src, int64_t *recv_idx,
                               float *recv_w, int32_t *recv_count, int64_t cap, int32_t *status,
                               hipStream_t s);
+// Normal-mode layout and dispatch in one launch (rank_fused.hip), for
+// T <= 1024, K <= 8, R <= 64: the results of launch_rank_layout followed by
+// the rank scatter.
+bool rank_layout_dispatch_fits(int32_t T, int32_t K, int32_t R);
+hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32_t T, int32_t K,
+                                       int32_t E, int32_t R, int32_t A, int32_t *rank_slot,
+                                       int32_t *rank_offset, int32_t *recv_src,
+                                       int64_t *recv_idx, float *recv_w, int32_t *recv_count,
+                                       int64_t cap, int32_t *status, const uint16_t *x,
+                                       uint16_t *recv, int64_t rows, int32_t H, hipStream_t s);
 // Normal-mode combine: the unweighted row sum over the [T, R] rank table, and
 // (ws.in != null) the rows' top-k weights summed back per token.
 struct RowWeightSum {

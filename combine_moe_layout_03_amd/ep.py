@@ -210,11 +210,13 @@ def normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
     K = topk_idx.shape[1]
     shape = capi.make_shape(T, H, num_experts, num_ranks, K, expert_alignment)
     lay = capi.RankLayoutBuffers.empty(shape, x.device, weights=topk_weights is not None)
-    capi.moe_rank_layout(shape, topk_idx.contiguous(),
-                         topk_weights.contiguous() if topk_weights is not None else None, lay)
     rows = max(lay.cap, 1)
     recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
-    capi.moe_rank_dispatch(shape, x.contiguous(), lay.rank_slot, recv_x, lay.cap, lay.status)
+    # layout and row copies in one call (one launch for batches of up to 1024 tokens)
+    capi.moe_rank_layout_dispatch(
+        shape, topk_idx.contiguous(),
+        topk_weights.contiguous() if topk_weights is not None else None, lay, x.contiguous(),
+        recv_x, lay.cap)
     w = lay.recv_topk_weights.view(rows, K) if lay.recv_topk_weights is not None else None
     return (recv_x, lay.recv_topk_idx.view(rows, K), w, lay.recv_expert_count,
             lay.rank_offset, RankHandle(shape, lay, lay.cap))

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Host-side return codes. */
 #define MOE_OK 0
@@ -247,6 +247,17 @@ int moe_rank_layout(const moe_shape *shape, const int64_t *topk_idx, const float
  * bit for bit; rows no token maps to are left untouched. */
 int moe_rank_dispatch(const moe_shape *shape, const uint16_t *x, const int32_t *rank_slot,
                       uint16_t *recv_x, int64_t recv_rows, int32_t *status, hipStream_t stream);
+
+/* Normal-mode layout and dispatch in one call (Buffer.dispatch in normal
+ * mode): the results of moe_rank_layout followed by moe_rank_dispatch, bit for
+ * bit, including the status bits (out->status). Batches of at most 1024
+ * tokens with K <= 8 take one launch that derives each token's rows while its
+ * row is loaded; larger ones take the two launches. x [T*H] bf16 and recv_x
+ * [recv_rows*H] are 16-byte aligned. */
+int moe_rank_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx,
+                             const float *topk_weights, const moe_rank_layout_t *out,
+                             int64_t recv_cap, const uint16_t *x, uint16_t *recv_x,
+                             int64_t recv_rows, hipStream_t stream);
 
 /* Normal-mode combine (Buffer.combine, addition without weights):
  *   out[t] = bf16_rne( sum over r = 0..R-1 with rank_slot[t*R + r] != -1 of y[row] )

@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 25, declared
+    assert len(declared) == 26, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -239,6 +239,21 @@ def test_rank_mode_checks(lib):
     assert raw.moe_rank_dispatch(C.byref(s), odd, d, d, 8, None, None) == -5
     assert raw.moe_rank_combine(C.byref(s), d, 8, d, None, d, None, d, None, None) == -1
     assert raw.moe_rank_combine(C.byref(s), d, 8, None, None, d, None, None, None, None) == -1
+    # the one-call layout + dispatch checks the arguments of both
+    rl2 = lib.moe_rank_layout_t()
+    rld = raw.moe_rank_layout_dispatch
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, d, d, 8, None) == -1  # slot NULL
+    rl2.rank_slot = rl2.rank_offset = d
+    assert rld(C.byref(s), None, None, C.byref(rl2), 8, d, d, 8, None) == -1  # ids
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, None, d, 8, None) == -1  # x
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, d, None, 8, None) == -1  # recv_x
+    assert rld(C.byref(s), d, None, C.byref(rl2), -1, d, d, 8, None) == -3
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, d, d, -1, None) == -3
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, odd, d, 8, None) == -5
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, d, odd, 8, None) == -5
+    assert rld(C.byref(big), d, d, C.byref(rl2), 8, d, d, 8, None) == -2
+    rl2.recv_topk_weights = d
+    assert rld(C.byref(s), d, None, C.byref(rl2), 8, d, d, 8, None) == -1  # weights
     s0 = lib.make_shape(0, 16, 16, 4, 2, 1)
     assert raw.moe_rank_dispatch(C.byref(s0), None, None, None, 0, None, None) == 0
     assert raw.moe_rank_combine(C.byref(s0), None, 0, None, None, None, None, None, None,

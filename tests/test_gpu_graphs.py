@@ -42,7 +42,9 @@ def replay_check(step, outputs, poison, reps=3):
         g.replay()
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(zip(outputs, ref)):
-            assert torch.equal(a, b), f"replay {rep}: output {i} differs"
+            # bit patterns: rows a call leaves untouched may hold NaN
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                f"replay {rep}: output {i} differs"
         junk = torch.randn(1 << 20, device=dev()).sum()
         assert torch.isfinite(junk)
     return ref
@@ -76,7 +78,8 @@ def test_graph_low_latency_fp8(capi, orc, flags):
     assert np.array_equal(lay.slot.cpu().numpy().reshape(T, K), ll["slot"])
 
 
-def test_graph_normal_mode(capi, orc):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+def test_graph_normal_mode(capi, orc, fused):
     w = mi.config_c2()
     shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
     idx, x, wt = to_dev(w.topk_idx), to_dev(w.x), to_dev(w.topk_weights)
@@ -84,11 +87,14 @@ def test_graph_normal_mode(capi, orc):
     recv = torch.zeros(max(lay.cap, 1), w.H, dtype=torch.int16, device=dev())
     out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev())
     ow = torch.empty(w.T, w.K, dtype=torch.float32, device=dev())
-    _announce("graph: normal-mode layout + dispatch + combine")
+    _announce(f"graph: normal-mode layout + dispatch + combine, fused={fused}")
 
     def step(s):
-        capi.moe_rank_layout(shape, idx, wt, lay, stream=s)
-        capi.moe_rank_dispatch(shape, x, lay.rank_slot, recv, lay.cap, lay.status, stream=s)
+        if fused:
+            capi.moe_rank_layout_dispatch(shape, idx, wt, lay, x, recv, lay.cap, stream=s)
+        else:
+            capi.moe_rank_layout(shape, idx, wt, lay, stream=s)
+            capi.moe_rank_dispatch(shape, x, lay.rank_slot, recv, lay.cap, lay.status, stream=s)
         capi.moe_rank_combine(shape, recv, lay.cap, lay.rank_slot, lay.recv_topk_weights, out,
                               None, ow, lay.status, stream=s)
 

@@ -30,7 +30,10 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None):
+def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None, fused=False, recv_rows=None):
+    """fused: moe_rank_layout_dispatch instead of moe_rank_layout followed by
+    moe_rank_dispatch (same results); recv_rows: rows the receive buffer
+    passes (default: the layout's capacity)."""
     shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, A)
     lay = capi.RankLayoutBuffers.empty(shape, dev(), weights=weights, cap=cap)
     for t in (lay.rank_slot, lay.rank_offset, lay.recv_src, lay.recv_expert_count):
@@ -40,18 +43,21 @@ def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None):
         lay.recv_topk_weights.fill_(float("nan"))
     idx = to_dev(w.topk_idx.astype(np.int64))
     wt = to_dev(w.topk_weights) if weights else None
-    capi.moe_rank_layout(shape, idx, wt, lay)
+    nrecv = lay.cap if recv_rows is None else recv_rows
+    recv = torch.full((max(nrecv, 1), w.H), SENTINEL, dtype=torch.int16, device=dev())
+    if fused:
+        capi.moe_rank_layout_dispatch(shape, idx, wt, lay, to_dev(w.x), recv, nrecv)
+    else:
+        capi.moe_rank_layout(shape, idx, wt, lay)
+        capi.moe_rank_dispatch(shape, to_dev(w.x), lay.rank_slot, recv, nrecv, lay.status)
     torch.cuda.synchronize()
     rows = int(lay.rank_offset[w.R].item())
-    cap_rows = max(lay.cap, 1)
-    recv = torch.full((cap_rows, w.H), SENTINEL, dtype=torch.int16, device=dev())
-    capi.moe_rank_dispatch(shape, to_dev(w.x), lay.rank_slot, recv, lay.cap, lay.status)
     src = recv if y is None else to_dev(y)
     out = torch.full((w.T, w.H), 0x1234, dtype=torch.int16, device=dev())
     o32 = torch.full((w.T, w.H), float("nan"), dtype=torch.float32, device=dev())
     ow = torch.full((w.T, w.K), float("nan"), dtype=torch.float32, device=dev()) \
         if weights else None
-    capi.moe_rank_combine(shape, src, lay.cap, lay.rank_slot, lay.recv_topk_weights, out, o32,
+    capi.moe_rank_combine(shape, src, nrecv, lay.rank_slot, lay.recv_topk_weights, out, o32,
                           ow, lay.status)
     torch.cuda.synchronize()
     K = w.K
@@ -67,8 +73,8 @@ def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None):
     return got
 
 
-def check_rank_path(capi, orc, w, A=1, weights=True):
-    got = run_rank_path(capi, w, A, weights=weights)
+def check_rank_path(capi, orc, w, A=1, weights=True, fused=False):
+    got = run_rank_path(capi, w, A, weights=weights, fused=fused)
     ref = orc.rank_layout(w.topk_idx, w.E, w.R, A, w.topk_weights if weights else None)
     for key in ("rank_slot", "rank_offset", "recv_src", "recv_topk_idx", "recv_expert_count"):
         assert np.array_equal(got[key], ref[key]), key
@@ -99,46 +105,73 @@ CASES = [
     (5, 1500, 512, 256, 8, 8, 0.0, 0.0, 0.02),
     (6, 77, 1032, 96, 32, 6, 0.3, 0.3, 0.0),
     (7, 50, 64, 16, 4, 12, 0.1, 0.3, 0.0),  # K > 8: the general two-pass kernel
+    # one-launch layout + dispatch with two tokens per lane (T > 512)
+    (8, 1024, 256, 64, 16, 8, 0.05, 0.1, 0.01),
+    (9, 513, 7168, 256, 8, 8, 0.0, 0.0, 0.0),
+    (10, 700, 1032, 128, 64, 5, 0.2, 0.2, 0.0),
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("case", CASES)
 @pytest.mark.parametrize("A", [1, 32])
-def test_rank_path_random(capi, orc, case, A):
+def test_rank_path_random(capi, orc, case, A, fused):
     seed, T, H, E, R, K, neg, dup, bad = case
     w = mi.random_case(1300 + seed, T, H, E, R, K, A, neg_frac=neg, dup_frac=dup, bad_frac=bad)
-    _announce(f"rank path seed={seed} T={T} H={H} E={E} R={R} K={K} A={A}")
-    check_rank_path(capi, orc, w, A)
+    _announce(f"rank path seed={seed} T={T} H={H} E={E} R={R} K={K} A={A} fused={fused}")
+    check_rank_path(capi, orc, w, A, fused=fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
 @pytest.mark.parametrize("name", ["c1", "c2", "c4"])
-def test_rank_path_workloads(capi, orc, name):
+def test_rank_path_workloads(capi, orc, name, fused):
     w = mi.by_name(name)
-    _announce(f"rank path {name} T={w.T} H={w.H}")
-    check_rank_path(capi, orc, w)
+    _announce(f"rank path {name} T={w.T} H={w.H} fused={fused}")
+    check_rank_path(capi, orc, w, fused=fused)
 
 
-def test_rank_path_without_weights(capi, orc):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+def test_rank_path_without_weights(capi, orc, fused):
     w = mi.random_case(1320, 50, 64, 16, 4, 4, 1, neg_frac=0.1)
-    _announce("rank path, no weights")
-    check_rank_path(capi, orc, w, weights=False)
+    _announce(f"rank path, no weights, fused={fused}")
+    check_rank_path(capi, orc, w, weights=False, fused=fused)
 
 
-def test_rank_layout_small_capacity(capi, orc):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+def test_rank_layout_small_capacity(capi, orc, fused):
     """Rows at or past the capacity get rank_slot -1 and flag a bad slot."""
     w = mi.random_case(1321, 30, 64, 16, 4, 4, 1)
     ref = orc.rank_layout(w.topk_idx, 16, 4, 1, w.topk_weights)
     cap = ref["rows"] - 5
-    _announce(f"rank layout with capacity {cap} < {ref['rows']}")
-    got = run_rank_path(capi, w, cap=cap)
+    _announce(f"rank layout with capacity {cap} < {ref['rows']}, fused={fused}")
+    got = run_rank_path(capi, w, cap=cap, fused=fused)
     want = np.where(ref["rank_slot"] >= cap, -1, ref["rank_slot"])
     assert np.array_equal(got["rank_slot"], want)
+    rref, _ = orc.dispatch(w.x, want, cap, fill=SENTINEL)
+    assert np.array_equal(got["recv"][:cap], rref), "rows below the capacity"
     assert got["status"] & 4
 
 
-def test_rank_path_empty(capi, orc):
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+def test_rank_dispatch_small_receive_buffer(capi, orc, fused):
+    """A receive buffer shorter than the layout: rows past it are not written
+    and flag a bad slot; the layout itself is complete."""
+    w = mi.random_case(1323, 60, 136, 32, 8, 6, 1, neg_frac=0.1)
+    ref = orc.rank_layout(w.topk_idx, 32, 8, 1, w.topk_weights)
+    n = ref["rows"] - 7
+    _announce(f"rank dispatch into {n} < {ref['rows']} rows, fused={fused}")
+    got = run_rank_path(capi, w, fused=fused, recv_rows=n)
+    assert np.array_equal(got["rank_slot"], ref["rank_slot"])
+    rref, st = orc.dispatch(w.x, ref["rank_slot"], n, fill=SENTINEL)
+    assert st & 4
+    assert np.array_equal(got["recv"], rref), "rows"
+    assert got["status"] & 4
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+def test_rank_path_empty(capi, orc, fused):
     w = mi.random_case(1322, 0, 64, 16, 4, 4, 1)
-    _announce("rank path T=0")
-    got = run_rank_path(capi, w)
+    _announce(f"rank path T=0, fused={fused}")
+    got = run_rank_path(capi, w, fused=fused)
     assert np.all(got["rank_offset"] == 0) and np.all(got["recv_expert_count"] == 0)
     assert got["status"] == 0
