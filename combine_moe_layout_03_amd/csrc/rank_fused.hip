@@ -14,8 +14,9 @@
 // low-latency counting kernel (fused.hip), a row is split over workgroups of
 // 8 waves (two for a 7168-wide row): each requests the routing, then its row
 // chunk, counts while the chunk is in flight and stores it once per rank the
-// token reaches. A few duty workgroups write the totals: the aligned receive
-// count of each expert, and the rank offsets.
+// token reaches. Each workgroup also counts the pairs of one or a few experts
+// (the aligned receive counts; duty workgroups with no token take the rest
+// when there are few tokens), and one more workgroup writes the rank offsets.
 #include "wave.hpp"
 
 namespace moe {
@@ -28,7 +29,7 @@ constexpr int kRfWaves = kRfThreads / 64;
 constexpr int kRfChunks = 8;     // row chunks of 64 x 16 bytes per workgroup, at most
 constexpr int kRfMaxK = 8;
 constexpr int kRfMaxTokens = 2 * kRfThreads;  // two tokens per lane
-constexpr int kRfDuties = 4;     // experts whose receive counts one duty workgroup writes
+constexpr int kRfDuties = 4;     // experts whose pairs one workgroup counts, at most
 
 struct RankFusedParams {
   const int64_t *idx;  // [T*K]
@@ -47,9 +48,10 @@ struct RankFusedParams {
   u32x4 *recv;     // [rows, nvec]
   int64_t rows;
   int32_t nvec, nchunk, chunks_per_wg, wg_per_token;
-  int32_t token_wgs;   // [0, token_wgs) serve tokens
-  int32_t expert_wgs;  // then expert_wgs duty workgroups for the receive counts, then one
-                       // for the rank offsets
+  int32_t token_wgs;  // [0, token_wgs) serve tokens
+  int32_t count_wgs;  // [0, count_wgs) also count experts b, b + count_wgs, ... (at most
+                      // kRfDuties each); workgroups [token_wgs, count_wgs) only do that;
+                      // workgroup count_wgs writes the rank offsets
 };
 
 __device__ __forceinline__ int set_lane(int v, int j, int x) { return lane_id() == j ? x : v; }
@@ -101,103 +103,159 @@ struct LaneTokens {
   }
 };
 
-// Inclusive sum over the lanes of a wave (every lane must call it).
+// Inclusive prefix sum over the lanes of a wave (every lane must call it):
+// a Hillis-Steele scan inside each 16-lane DPP row (row_shr by 1, 2, 4, 8),
+// then row 1 and 3 add the last lane of the row before (row_bcast:15) and
+// rows 2 and 3 the last lane of row 1 (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
   return x;
 }
 
+// Sum over the 64 lanes of a wave, wave-uniform (every lane must call it):
+// rotations inside each 16-lane row (by 8, 4, 2, 1) give every lane its row's
+// sum, then the four row sums are added.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 32) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+}
+
+// Bits 0..3 of x to bits 0, 8, 16, 24: four one-byte counters that a sum over
+// a wave's lanes (at most 2 * 64 per byte here) cannot carry out of.
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return (x * 0x00204081u) & 0x01010101u; }
+
+// This wave's pairs on experts b, b + G, ... (lane j: the j-th of them; at
+// most kRfDuties), for the aligned receive counts. Every lane of the wave must
+// call it.
 template <int kRounds>
-__device__ void token_workgroup(const RankFusedParams &p, int b, int &st) {
-  __shared__ int32_t s_cnt[64];       // per rank below the token's highest: tokens reaching it
-  __shared__ int32_t s_pos[kRfMaxK];  // per rank of the token: tokens before t reaching it
+__device__ __forceinline__ int count_experts(const RankFusedParams &p,
+                                             const LaneTokens<kRounds> &rt, int b, int G,
+                                             int &ne) {
+  ne = b < p.E ? (p.E - 1 - b) / G + 1 : 0;
+  int cv = 0;
+  for (int j = 0; j < ne; ++j) {
+    const int e = b + j * G;
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i)
+#pragma unroll
+      for (int k = 0; k < kRfMaxK; ++k) n += __popcll(__ballot(rt.id[i][k] == e));
+    cv = set_lane(cv, j, n);
+  }
+  return cv;
+}
+
+template <int kRounds>
+__device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp) {
+  __shared__ int32_t s_cnt[64];  // per rank: tokens reaching it
+  __shared__ int32_t s_pos[64];  // per rank: tokens before t reaching it
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = b / p.wg_per_token;  // < T
   const bool lead = b % p.wg_per_token == 0;
   const int K = p.K;
-  if (tid < 64) s_cnt[tid] = 0;
-  if (tid < kRfMaxK) s_pos[tid] = 0;
+  if (tid < 64) {
+    s_cnt[tid] = 0;
+    s_pos[tid] = 0;
+  }
 
-  // 1. the routing, and this token's ids and weights (lane k holds pair k) ...
+  // 1. pair (t, lane mod K) and its weight (lanes 0..K-1 hold the token's K
+  //    pairs; without weights the load reads id bits, unused: no branch
+  //    around it) ...
+  const int kl = lane % K;
+  const int64_t *trow = p.idx + (int64_t)t * K;
+  const int64_t te = trow[kl];
+  const float *wsrc = p.w ? p.w : reinterpret_cast<const float *>(p.idx);
+  const float tw = wsrc[(int64_t)t * K + kl];
+  // 2. ... the routing ...
   LaneTokens<kRounds> rt;
   rt.issue(p);
-  const int kk = min(lane, K - 1);
-  const int64_t te = p.idx[(int64_t)t * K + kk];
-  // (without weights the load reads id bits, unused: no branch around it)
-  const float *wsrc = p.w ? p.w : reinterpret_cast<const float *>(p.idx);
-  const float tw = wsrc[(int64_t)t * K + kk];
-  // 2. ... then the row chunk this wave copies, unconditionally (address
+  // 3. ... then the row chunk this wave copies, unconditionally (address
   //    clamped into the row), so it stays in flight while the rows are derived
   const int chunk = (b % p.wg_per_token) * p.chunks_per_wg + wave;
   const int v = chunk * 64 + lane;
   const bool lane_ok = wave < p.chunks_per_wg && chunk < p.nchunk && v < p.nvec;
   u32x4 val = __builtin_nontemporal_load(p.x + (int64_t)t * p.nvec + min(v, p.nvec - 1));
-  lds_barrier();  // the LDS counters are zero
-  rt.settle(p, st);
+  __builtin_amdgcn_sched_barrier(0);  // nothing below waits before the row load is issued
 
-  // 3. the token's set of ranks (uniform), and the masks of earlier tokens
-  const bool tk = lane < K && te >= 0 && te < p.E;
-  const int tr = tk ? rank_of((int)te, p.l_magic) : -1;  // rank of pair `lane`
+  // 4. the token's set of ranks (uniform)
+  const bool tok = te >= 0 && te < p.E;
+  const int tr = tok ? rank_of((int)te, p.l_magic) : -1;  // rank of pair `lane` (lane < K)
   uint64_t mt = 0;
   for (int k = 0; k < K; ++k) {
     const int rk = __builtin_amdgcn_readlane(tr, k);
     if (rk >= 0) mt |= 1ull << rk;
   }
-  uint64_t early[kRounds];
-#pragma unroll
-  for (int i = 0; i < kRounds; ++i) early[i] = (i * kRfThreads + tid < t) ? rt.ranks[i] : 0ull;
-  const int nj = __popcll(mt);
-  const int rhi = mt ? 63 - __builtin_clzll(mt) : 0;  // ranks below the highest reached
+  const int rhi = mt ? 63 - __builtin_clzll(mt) : 0;  // highest rank reached
+  const int nc = (rhi >> 3) + 1;                       // 8-rank groups up to it
+  lds_barrier();  // the LDS counters are zero
+  rt.settle(p, st);
 
-  // 4. this wave's share of n(r') for r' < rhi (lane r'), and of the tokens
-  //    before t on the token's j-th rank (lane j)
-  int cv = 0;
-  for (int r = 0; r < rhi; ++r) {
-    int n = 0;
+  // 5. per rank r of the first nc groups, this wave's tokens reaching r and
+  //    its tokens before t reaching r: one byte counter per rank, summed over
+  //    the wave by DPP; lane r takes rank r's counts. Waves that hold no token
+  //    add nothing.
+  if (wave * 64 < p.T) {  // uniform
+    int cv = 0, pv = 0;
+    for (int c = 0; c < nc; ++c) {
+      uint32_t alo = 0, ahi = 0, elo = 0, ehi = 0;
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) n += __popcll(__ballot((rt.ranks[i] >> r) & 1ull));
-    cv = set_lane(cv, r, n);
-  }
-  int pv = 0, rjv = 0;
-  uint64_t rest = mt;
-  for (int j = 0; j < nj; ++j) {
-    const int rj = __ffsll((unsigned long long)rest) - 1;
-    rest &= rest - 1ull;
-    int n = 0;
-#pragma unroll
-    for (int i = 0; i < kRounds; ++i) n += __popcll(__ballot((early[i] >> rj) & 1ull));
-    pv = set_lane(pv, j, n);
-    rjv = set_lane(rjv, j, rj);
-  }
-  if (lane < rhi) atomicAdd(&s_cnt[lane], cv);
-  if (lane < nj) atomicAdd(&s_pos[lane], pv);
-  lds_barrier();
-
-  // 5. rows: lane r' sums the ranks below it; lane j gets the row on rank r_j
-  const int c = lane < rhi ? s_cnt[lane] : 0;
-  const int start = wave_inclusive_sum(c) - c;
-  int row = 0;
-  for (int j = 0; j < nj; ++j) row = set_lane(row, j, __builtin_amdgcn_readlane(start, __builtin_amdgcn_readlane(rjv, j)));
-  if (lane < nj) {
-    row += s_pos[lane];
-    if (row >= p.cap) {  // receive arrays smaller than the layout needs
-      if (lead && wave == 0) st |= kStBadSlot;
-      row = -1;
+      for (int i = 0; i < kRounds; ++i) {
+        const uint32_t a = (uint32_t)(rt.ranks[i] >> (8 * c)) & 0xffu;
+        const uint32_t e = (i * kRfThreads + tid < t) ? a : 0u;
+        alo += spread4(a & 15u);
+        ahi += spread4(a >> 4);
+        elo += spread4(e & 15u);
+        ehi += spread4(e >> 4);
+      }
+      const uint32_t sal = wave_sum(alo), sah = wave_sum(ahi);
+      const uint32_t sel = wave_sum(elo), seh = wave_sum(ehi);
+      if ((lane >> 3) == c) {
+        const int sh = 8 * (lane & 3);
+        cv = (int)(((lane & 4) ? sah : sal) >> sh & 0xffu);
+        pv = (int)(((lane & 4) ? seh : sel) >> sh & 0xffu);
+      }
     }
-  } else {
+    if (lane < 8 * nc) {
+      atomicAdd(&s_cnt[lane], cv);
+      atomicAdd(&s_pos[lane], pv);
+    }
+    // this workgroup's share of the receive counts
+    int ne;
+    const int ev = count_experts(p, rt, b, p.count_wgs, ne);
+    if (lane < ne) atomicAdd(&s_exp[lane], ev);
+  }
+  lds_barrier();
+  if (p.recv_count && tid < kRfDuties && b + tid * p.count_wgs < p.E)
+    p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
+
+  // 6. row of (t, r) in lane r: the tokens of the ranks below r (a scan over
+  //    the lanes) plus the tokens before t on r
+  const int n = s_cnt[lane];
+  int row = wave_inclusive_sum(n) - n + s_pos[lane];
+  const bool hit = (mt >> lane) & 1ull;
+  if (!hit) {
+    row = -1;
+  } else if (row >= p.cap) {  // receive arrays smaller than the layout needs
+    if (lead && wave == 0) st |= kStBadSlot;
     row = -1;
   }
 
-  // 6. the row chunk, once per rank reached
+  // 7. the row chunk, once per rank reached
   asm volatile("" : "+v"(val));
-  for (int j = 0; j < nj; ++j) {
-    const int s = __builtin_amdgcn_readlane(row, j);
+  for (uint64_t rest = mt; rest; rest &= rest - 1ull) {
+    const int s = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)rest) - 1);
     if (s >= 0 && s < p.rows) {
       if (lane_ok) __builtin_nontemporal_store(val, p.recv + (int64_t)s * p.nvec + v);
     } else if (s != -1 && lead && wave == 0) {
@@ -205,31 +263,35 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st) {
     }
   }
 
-  // 7. the token's handle entries (all 64 lanes of wave 0 take part in the
-  //    shuffles)
+  // 8. the token's handle entries
   if (lead && wave == 0) {
-    const int below = __popcll(mt & ((1ull << lane) - 1ull));  // lane = rank r
-    const int rrow = __shfl(row, below, 64);
-    if (lane < p.R) p.rank_slot[(int64_t)t * p.R + lane] = ((mt >> lane) & 1ull) ? rrow : -1;
-    if (lane < nj && row >= 0 && p.recv_src) p.recv_src[row] = t;
-    // entry (j, k) of the rows' local ids and weights in lane j*K + k (nj*K <= 64)
-    const int j = lane / K, k = lane - j * K;
-    const int jr = __shfl(row, j & 63, 64);
-    const int rj = __shfl(rjv, j & 63, 64);
-    const int rk = __shfl(tr, k, 64);
-    const int ek = __shfl((int)te, k, 64);
-    const float wk = __shfl(tw, k, 64);
-    if (j < nj && jr >= 0) {
-      const bool loc = rk == rj;  // the pair's expert lives on the row's rank
-      if (p.recv_idx) p.recv_idx[(int64_t)jr * K + k] = loc ? (int64_t)(ek - rj * p.L) : -1;
-      if (p.recv_w && p.w) p.recv_w[(int64_t)jr * K + k] = loc ? wk : 0.0f;
+    if (lane < p.R) p.rank_slot[(int64_t)t * p.R + lane] = row;
+    if (row >= 0 && p.recv_src) p.recv_src[row] = t;
+    // entry (j, k) of the rows' local ids and weights in lane j*K + k (at
+    // most 64 of them: a token reaches at most K ranks)
+    const int jl = lane / K;
+    int rj = -1, jr = -1, j = 0;
+    for (uint64_t rest = mt; rest; rest &= rest - 1ull, ++j) {
+      const int r = __ffsll((unsigned long long)rest) - 1;
+      const int rr = __builtin_amdgcn_readlane(row, r);
+      if (jl == j) {
+        rj = r;
+        jr = rr;
+      }
+    }
+    if (jr >= 0) {
+      const bool loc = tr == rj;  // the pair's expert lives on the row's rank
+      if (p.recv_idx) p.recv_idx[(int64_t)jr * K + kl] = loc ? te - (int64_t)rj * p.L : -1;
+      if (p.recv_w && p.w) p.recv_w[(int64_t)jr * K + kl] = loc ? tw : 0.0f;
     }
   }
   st &= ~kStBadExpert;  // every workgroup reads every id; the duty workgroups report
 }
 
+// Workgroups with no token: receive counts (b < count_wgs, written by the
+// kernel after its last barrier), or the rank offsets (b == count_wgs).
 template <int kRounds>
-__device__ void duty_workgroup(const RankFusedParams &p, int d, int &st) {
+__device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp) {
   __shared__ int32_t s_c[kRfWaves][64];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,27 +302,11 @@ __device__ void duty_workgroup(const RankFusedParams &p, int d, int &st) {
   } else {
     rt.empty();
   }
-  if (d < p.expert_wgs) {
-    // receive counts of experts d, d + D, ... (pairs, duplicates included)
-    const int D = p.expert_wgs;
-    const int nd = d < p.E ? (p.E - 1 - d) / D + 1 : 0;  // <= kRfDuties
-    int cv = 0;
-    for (int j = 0; j < nd; ++j) {
-      const int e = d + j * D;
-      int n = 0;
-#pragma unroll
-      for (int i = 0; i < kRounds; ++i)
-#pragma unroll
-        for (int k = 0; k < kRfMaxK; ++k) n += __popcll(__ballot(rt.id[i][k] == e));
-      cv = set_lane(cv, j, n);
-    }
-    s_c[wave][lane] = cv;
-    lds_barrier();
-    if (tid < nd && p.recv_count) {
-      int n = 0;
-      for (int w = 0; w < kRfWaves; ++w) n += s_c[w][tid];
-      p.recv_count[d + tid * D] = round_up(n, p.A);
-    }
+  lds_barrier();  // s_exp is zero
+  if (b < p.count_wgs) {
+    int ne;
+    const int ev = count_experts(p, rt, b, p.count_wgs, ne);
+    if (lane < ne) atomicAdd(&s_exp[lane], ev);
   } else {
     // rank offsets: exclusive sum of the tokens reaching each rank
     int cv = 0;
@@ -286,15 +332,21 @@ __device__ void duty_workgroup(const RankFusedParams &p, int d, int &st) {
 template <int kRounds>
 __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFusedParams p) {
   __shared__ int32_t s_status;
+  __shared__ int32_t s_exp[kRfDuties];  // pairs on this workgroup's experts
+  const int tid = threadIdx.x, b = blockIdx.x;
   int st = 0;
-  if (threadIdx.x == 0) s_status = 0;
-  if ((int)blockIdx.x < p.token_wgs)  // uniform per workgroup
-    token_workgroup<kRounds>(p, blockIdx.x, st);
+  if (tid == 0) s_status = 0;
+  if (tid < kRfDuties) s_exp[tid] = 0;
+  if (b < p.token_wgs)  // uniform per workgroup
+    token_workgroup<kRounds>(p, b, st, s_exp);
   else
-    duty_workgroup<kRounds>(p, blockIdx.x - p.token_wgs, st);
+    duty_workgroup<kRounds>(p, b, st, s_exp);
   if (st) atomicOr(&s_status, st);
   lds_barrier();
-  if (threadIdx.x == 0 && s_status && p.status) atomicOr(p.status, s_status);
+  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
+  if (b >= p.token_wgs && b < p.count_wgs && p.recv_count && tid < kRfDuties &&
+      b + tid * p.count_wgs < p.E)
+    p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
 }
 
 }  // namespace
@@ -337,8 +389,9 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   p.chunks_per_wg = (p.nchunk + groups - 1) / groups;  // <= kRfChunks = waves
   p.wg_per_token = (p.nchunk + p.chunks_per_wg - 1) / p.chunks_per_wg;
   p.token_wgs = T * p.wg_per_token;
-  p.expert_wgs = (E + kRfDuties - 1) / kRfDuties;
-  const dim3 grid((unsigned)(p.token_wgs + p.expert_wgs + 1)), block(kRfThreads);
+  const int need = (E + kRfDuties - 1) / kRfDuties;
+  p.count_wgs = p.token_wgs > need ? p.token_wgs : need;
+  const dim3 grid((unsigned)(p.count_wgs + 1)), block(kRfThreads);
   if (T <= kRfThreads)
     hipLaunchKernelGGL(rank_layout_dispatch_kernel<1>, grid, block, 0, s, p);
   else
