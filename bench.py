@@ -184,14 +184,14 @@ def graph_us_per_step(torch, stream, step_fns, reps):
     return start.elapsed_time(end) * 1e3 / (reps * len(step_fns))
 
 
-def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
-    """Low-latency padded path at 128 tokens per rank: layout + dispatch into
+def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
+    """Low-latency padded path at M tokens per rank: layout + dispatch into
     the [E, R*M, H] union of the receive buffers, then combine from it. Steps
-    rotate over 4 union buffers x 8 source stripes (> 512 MiB touched).
+    rotate over union buffers x 8 source stripes, enough for > 512 MiB of
+    touched bytes (at least 4 unions at M = 128).
     With fp8_flags, dispatch casts to E4M3 + per-128-channel scales
     (moe_ll_layout_dispatch_fp8) and combine reads a bf16 expert-output union
     of the same layout (filled once by a bf16 dispatch of the same batch)."""
-    M = 128
     w = mi.config_c3(M)
     E, R, K, T, H = w.E, w.R, w.K, w.T, w.H
     rows = capi.moe_ll_recv_rows(E, R, M)
@@ -200,13 +200,16 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     idx = torch.from_numpy(w.topk_idx).to(dev)
     wt = torch.from_numpy(w.topk_weights).to(dev)
     fp8 = fp8_flags is not None
-    unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(4)]
+    P = int((w.topk_idx >= 0).sum())
+    ab = algo_bytes(T, H, K, E, R, P, fp8_flags)
+    n_unions = max(4 if M == 128 else 1, math.ceil(512 * 2**20 / (ab["total"] * R)))
+    unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(n_unions)]
     if fp8:
         cols = capi.fp8_scale_cols(H, fp8_flags)
         sdt = torch.int32 if fp8_flags & capi.MOE_FP8_UE8M0 else torch.float32
-        qunions = [torch.empty(rows, H, dtype=torch.uint8, device=dev) for _ in range(4)]
+        qunions = [torch.empty(rows, H, dtype=torch.uint8, device=dev) for _ in range(n_unions)]
         sshape = (rows, cols) if fp8_flags & capi.MOE_FP8_SCALE_ROWS else (E, cols, R * M)
-        sunions = [torch.empty(sshape, dtype=sdt, device=dev) for _ in range(4)]
+        sunions = [torch.empty(sshape, dtype=sdt, device=dev) for _ in range(n_unions)]
     sets = []
     for ui, u in enumerate(unions):
         for s in range(R):
@@ -241,8 +244,7 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     us = graph_us_per_step(torch, stream, fns, 20)
     k_ld = graph_us_per_step(torch, stream, [(lambda z=z: ld(z)) for z in sets], 20)
     k_cb = graph_us_per_step(torch, stream, [(lambda z=z: cb(z)) for z in sets], 20)
-    P = int((w.topk_idx >= 0).sum())
-    ab = algo_bytes(T, H, K, E, R, P, fp8_flags)
+    n_sets = len(sets)
     del unions, sets
     if fp8:
         del qunions, sunions
@@ -250,8 +252,9 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None):
     name = "low-latency padded" + (f" FP8 (flags {fp8_flags}: "
                                    + ("row-major" if fp8_flags & 4 else "column-major")
                                    + " scales)" if fp8 else "")
-    res = {"workload": name + ": 128 tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
-                              "buffer [256, 8*128, 7168]",
+    res = {"workload": name + f": {M} tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
+                              f"buffer [256, 8*{M}, 7168]",
+           "buffer_sets": n_sets,
            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
            "kernels_us": {"ll_layout_dispatch" + ("_fp8" if fp8 else ""): round(k_ld, 3),
                           "combine": round(k_cb, 3)},
@@ -587,6 +590,19 @@ def main():
     if not args.no_rows:
         rows["low_latency_m128"] = row_low_latency(capi, mi, torch, np, dev, stream)
         log(f"low-latency row: {rows['low_latency_m128']['us_per_step']} us/step")
+        sweep = {}
+        for M in (16, 32, 64, 256, 512):
+            r = row_low_latency(capi, mi, torch, np, dev, stream, M=M)
+            sweep[str(M)] = {k: r[k] for k in ("us_per_step", "GB_per_s", "kernels_us",
+                                               "buffer_sets")}
+            log(f"low-latency M={M}: {r['us_per_step']} us/step")
+        m128 = rows["low_latency_m128"]
+        sweep["128"] = {k: m128[k] for k in ("us_per_step", "GB_per_s", "kernels_us",
+                                             "buffer_sets")}
+        rows["low_latency_sweep"] = {
+            "workload": "low-latency padded layout + dispatch + combine, M tokens per rank "
+                        "(T = M) x 7168, 256E top-8, 8 ranks",
+            "by_M": {k: sweep[k] for k in sorted(sweep, key=int)}}
         rows["low_latency_fp8_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, 0)
         log(f"low-latency FP8 row: {rows['low_latency_fp8_m128']['us_per_step']} us/step")
         rows["low_latency_fp8_rowscales_m128"] = row_low_latency(

@@ -79,8 +79,17 @@ int tokens_per_block(int K) { return kPairsPerBlock / K > 0 ? kPairsPerBlock / K
 
 bool one_block(const moe_shape *s) { return (int64_t)s->T * s->K <= kMaxPairsOneBlock; }
 
+// The counting kernel lays out batches of up to kMaxPairsFused pairs with
+// alignment 1 (low-latency layouts ignore the alignment) without a workspace.
+bool counted(const moe_shape *s, int mode) {
+  return (int64_t)s->T * s->K <= kMaxPairsFused && (mode == kModeLowLatency || s->A == 1);
+}
+
+// Workspace of the three-launch layout; 0 when no call with this shape takes
+// it (a low-latency call with A > 1 in the shape may be asked for one that it
+// does not use).
 size_t workspace_bytes(const moe_shape *s) {
-  if (one_block(s)) return 0;
+  if (one_block(s) || counted(s, kModeContiguous)) return 0;
   const int64_t tpb = tokens_per_block(s->K);
   const int64_t nb = (s->T + tpb - 1) / tpb;
   const int64_t ints = nb * s->E + nb * s->R + s->E;
@@ -99,7 +108,8 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
     if (M < 1 || s->T > M || src < 0 || src >= s->R) return MOE_ERR_LL;
     if ((int64_t)s->E * s->R * M >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   }
-  const size_t need = workspace_bytes(s);
+  const bool multi = !one_block(s) && !counted(s, mode);
+  const size_t need = multi ? workspace_bytes(s) : 0;
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
 
   std::memset(p, 0, sizeof(*p));
@@ -124,7 +134,7 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   p->row_src = out->row_src;
   p->status = out->status;
   p->recv_stats = out->recv_stats;
-  if (one_block(s)) {
+  if (!multi) {  // the counting kernel ignores these
     p->tokens_per_block = s->T > 0 ? s->T : 1;
     p->nblocks = 1;
   } else {

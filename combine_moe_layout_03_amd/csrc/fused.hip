@@ -48,7 +48,7 @@ constexpr int kCountMaxWaves = 16;
 constexpr int kCountingWaves = MOE_COUNTING_WAVES;
 constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * threads
 constexpr int kMaxDuties = 4;       // experts (and ranks) whose totals one workgroup writes
-constexpr int kLayoutOnlyThreads = 256;
+constexpr int kLayoutOnlyThreads = 512;
 constexpr int kNoId = -2;           // sentinel: matches no expert
 constexpr int kAboveAll = 0x7fffffff;  // sentinel: not below any expert
 

@@ -12,13 +12,16 @@ constexpr int kLayoutThreads = 1024;
 constexpr int kLayoutWaves = kLayoutThreads / 64;
 // Largest expert count (one expert per layout thread; per-wave counters in LDS).
 constexpr int kMaxExperts = 1024;
-// A batch of up to this many (token, k) pairs is laid out by one workgroup.
-constexpr int kMaxPairsOneBlock = 8192;
-// Above that, each workgroup of the first layout pass takes about this many pairs.
-constexpr int kPairsPerBlock = 1024;
-// Layout and dispatch share one launch when the batch has at most this many
-// pairs (every dispatch workgroup then re-derives the layout from L2).
-constexpr int kMaxPairsFused = 2048;
+// Batches of up to kMaxPairsFused pairs with alignment 1 (or low latency) are
+// laid out by counting, with or without the dispatch in the same launch (every
+// workgroup re-derives its slots from the routing in L2). Otherwise a batch of
+// up to kMaxPairsOneBlock pairs is laid out by one workgroup, and a larger one
+// by three launches whose first pass gives each workgroup about kPairsPerBlock
+// pairs (one workgroup's serial work grows with its pairs: at 4096 and 8192
+// pairs, the one-workgroup kernel took 18 and 27 us, three launches 15 and 13).
+constexpr int kMaxPairsFused = 4096;
+constexpr int kMaxPairsOneBlock = 1024;
+constexpr int kPairsPerBlock = 256;
 
 enum LayoutMode : int32_t {
   kModeContiguous = 0,  // aligned per-expert partitions of one receive buffer

@@ -13,11 +13,12 @@
 // a popcount and one leader lane per (wave, expert) touches LDS -- no atomics on
 // a hot expert's counter, whatever the skew. Each wave owns a contiguous segment
 // of pairs and a private row of uint16 counters in LDS; a per-expert prefix over
-// the 16 waves then gives every wave its starting rank. A batch of up to 8192
+// the 16 waves then gives every wave its starting rank. A batch of up to 1024
 // pairs is done by one workgroup; larger batches take three launches (per-block
 // counts and local ranks; one wave per expert for the prefix over blocks; a
 // per-pair fix-up whose workgroups each scan the per-expert totals), with no
-// inter-workgroup waiting.
+// inter-workgroup waiting. (Batches with alignment 1 of up to 4096 pairs take
+// the counting kernel of fused.hip instead.)
 #include "wave.hpp"
 
 namespace moe {
@@ -52,14 +53,26 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
   for (int r = tid; r < R; r += kLayoutThreads) s_rc[r] = 0;
   if (tid == 0) s_status = 0;
 
-  // Read the routing once; keep validated ids in LDS.
-  for (int i = tid; i < np; i += kLayoutThreads) {
-    const int64_t v = p.idx[p0 + i];
-    const bool ok = v >= 0 && v < E;
-    if (!ok && v != -1) st |= kStBadExpert;
-    s_ids[i] = ok ? (int16_t)v : (int16_t)-1;
+  // Read the routing once; keep validated ids in LDS. A thread's (at most
+  // kMaxPairsOneBlock / kLayoutThreads) loads are all issued before the first
+  // is used (addresses clamped into the batch), so they cost one latency.
+  constexpr int kIdsPerThread = kMaxPairsOneBlock / kLayoutThreads;
+  if (np > 0) {
+    int64_t v[kIdsPerThread];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u)
+      v[u] = p.idx[p0 + min(u * kLayoutThreads + tid, np - 1)];
+#pragma unroll
+    for (int u = 0; u < kIdsPerThread; ++u) {
+      const int i = u * kLayoutThreads + tid;
+      if (i < np) {
+        const bool ok = v[u] >= 0 && v[u] < E;
+        if (!ok && v[u] != -1) st |= kStBadExpert;
+        s_ids[i] = ok ? (int16_t)v[u] : (int16_t)-1;
+      }
+    }
   }
-  __syncthreads();
+  lds_barrier();
 
   // Per-wave counts over contiguous segments of 64-pair steps.
   const int seg = (((np + kLayoutWaves - 1) / kLayoutWaves) + 63) & ~63;
@@ -70,7 +83,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     const uint64_t peers = match_peers((uint32_t)e, e >= 0, p.id_bits);
     if (is_leader(peers)) s_wc[wave][e] += (uint16_t)__popcll(peers);
   }
-  __syncthreads();
+  lds_barrier();
 
   // Exclusive prefix over waves for each expert; block totals.
   for (int e = tid; e < E; e += kLayoutThreads) {
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     }
     s_cnt[e] = run;
   }
-  __syncthreads();
+  lds_barrier();
 
   // First slot of each expert.
   if (kOneBlock) {
@@ -116,7 +129,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     for (int e = tid; e < E; e += kLayoutThreads)
       p.ws_hist[(int64_t)e * p.nblocks + blockIdx.x] = s_cnt[e];
   }
-  __syncthreads();
+  lds_barrier();
 
   // Stable ranks: walk the same segments again; a wave's running counter per
   // expert starts at the prefix of the waves before it.
@@ -169,7 +182,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     }
   }
   if (st) atomicOr(&s_status, st);
-  __syncthreads();
+  lds_barrier();
 
   if (p.rank_token_count) {
     for (int r = tid; r < R; r += kLayoutThreads) {
@@ -180,17 +193,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     }
   }
   if (kOneBlock && p.row_src) {
-    if (p.mode == kModeContiguous) {
-      // alignment padding rows carry -1
-      for (int e = tid; e < E; e += kLayoutThreads) {
-        const int lo = s_base[e] + s_cnt[e], hi = s_base[e] + round_up(s_cnt[e], p.A);
-        for (int r = lo; r < hi; ++r) p.row_src[r] = -1;
-      }
-    } else {
-      const int64_t n = (int64_t)E * p.M;
-      for (int64_t i = tid; i < n; i += kLayoutThreads) {
-        const int e = (int)(i / p.M), j = (int)(i - (int64_t)e * p.M);
-        if (j >= s_cnt[e]) p.row_src[i] = -1;
+    // rows no pair fills carry -1: alignment padding, or the low-latency
+    // stripe rows past the received count; one wave per expert, its lanes
+    // over the rows
+    for (int e = wave; e < E; e += kLayoutWaves) {
+      const int c = s_cnt[e];
+      if (p.mode == kModeContiguous) {
+        const int hi = s_base[e] + round_up(c, p.A);
+        for (int r = s_base[e] + c + lane; r < hi; r += 64) p.row_src[r] = -1;
+      } else {
+        int32_t *stripe = p.row_src + (int64_t)e * p.M;
+        for (int j = min(c, p.M) + lane; j < p.M; j += 64) stripe[j] = -1;
       }
     }
   }
@@ -231,7 +244,7 @@ __global__ __launch_bounds__(64) void layout_prefix_kernel(LayoutParams p) {
 
 // Multi-block pass 3: every workgroup scans the per-expert totals into the
 // first row of each expert (cheap: E <= 1024), workgroup 0 writes the totals,
-// all workgroups share the padding rows, then each thread fixes one pair:
+// the workgroups share the unfilled rows, then each thread fixes one pair:
 // slot = first row of its expert + pairs of that expert in earlier blocks +
 // its rank inside its own block.
 constexpr int kFixupThreads = 256;
@@ -268,18 +281,26 @@ __global__ __launch_bounds__(kFixupThreads) void layout_fixup_kernel(LayoutParam
         if (p.offset) p.offset[e] = base;
       }
     }
-    // padding rows: expert e's share goes to workgroup e mod gridDim.x
-    if (p.row_src && (int)(e % gridDim.x) == (int)blockIdx.x) {
-      if (contiguous) {
-        for (int r = base + c; r < base + round_up(c, p.A); ++r) p.row_src[r] = -1;
-      } else {
-        for (int j2 = min(c, p.M); j2 < p.M; ++j2) p.row_src[(int64_t)e * p.M + j2] = -1;
-      }
-    }
     if (contiguous) run += round_up(c, p.A);
   }
   if (blockIdx.x == 0 && tid == 0 && p.offset) p.offset[E] = contiguous ? total : E * R * p.M;
-  __syncthreads();
+  lds_barrier();
+
+  // rows no pair fills carry -1 (alignment padding, or low-latency stripe rows
+  // past the received count): expert e's go to workgroup e mod gridDim.x,
+  // whose threads stride over them
+  if (p.row_src) {
+    for (int e = blockIdx.x; e < E; e += gridDim.x) {
+      const int c = p.ws_cnt[e];
+      if (contiguous) {
+        const int hi = s_base[e] + round_up(c, p.A);
+        for (int r = s_base[e] + c + tid; r < hi; r += kFixupThreads) p.row_src[r] = -1;
+      } else {
+        int32_t *stripe = p.row_src + (int64_t)e * p.M;
+        for (int j2 = min(c, p.M) + tid; j2 < p.M; j2 += kFixupThreads) stripe[j2] = -1;
+      }
+    }
+  }
 
   const int64_t i = (int64_t)blockIdx.x * kFixupThreads + tid;
   const int64_t n = (int64_t)p.T * p.K;
@@ -327,7 +348,7 @@ __global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kLayoutThreads) s_h[e] = 0;
   if (tid == 0) s_status = 0;
-  __syncthreads();
+  lds_barrier();
   int st = 0;
   const int i0 = blockIdx.x * per_block, i1 = min(n, i0 + per_block);
   for (int b = i0; b < i1; b += kLayoutThreads) {
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(kLayoutThreads) void expert_load_kernel(const int64
     if (is_leader(peers)) atomicAdd(&s_h[e], __popcll(peers));
   }
   if (st) atomicOr(&s_status, st);
-  __syncthreads();
+  lds_barrier();
   for (int e = tid; e < E; e += kLayoutThreads) {
     if (accumulate) {
       if (s_h[e]) atomicAdd(&load[e], s_h[e]);

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_small_kernel(RankPar
   }
   if (tid == 0) s_status = 0;
   for (int l = tid; l < p.L; l += kRankThreads) s_cnt[l] = 0;
-  __syncthreads();
+  lds_barrier();
   uint64_t m = 0, loc = 0;
   if (live) {
 #pragma unroll
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_small_kernel(RankPar
   }
   if (r != 0) st &= ~kStBadExpert;
   if (st) atomicOr(&s_status, st);
-  __syncthreads();
+  lds_barrier();
   if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
 }
 
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
   int st = 0;
   if (tid == 0) s_status = 0;
   for (int l = tid; l < p.L; l += kRankThreads) s_cnt[l] = 0;
-  __syncthreads();
+  lds_barrier();
 
   // pass 1: start of this rank's rows, local expert counts
   int before = 0;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
     block_exclusive_scan(n, s_wave, kRankWaves, &total);
     before += total;
   }
-  __syncthreads();
+  lds_barrier();
   if (p.recv_count)
     for (int l = tid; l < p.L; l += kRankThreads)
       p.recv_count[r * p.L + l] = round_up(s_cnt[l], p.A);
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p)
   }
   if (r != 0) st &= ~kStBadExpert;  // every workgroup sees the same ids; one reports
   if (st) atomicOr(&s_status, st);
-  __syncthreads();
+  lds_barrier();
   if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
 }
 

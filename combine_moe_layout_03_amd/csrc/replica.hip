@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void reroute_kernel(int32_t T, int32_t K, int3
     s_phys[2 * e] = replica_phys[2 * e];
     s_phys[2 * e + 1] = replica_phys[2 * e + 1];
   }
-  __syncthreads();
+  lds_barrier();
   if (!live) return;
   int64_t out = -1;
   int st = 0;

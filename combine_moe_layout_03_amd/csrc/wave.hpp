@@ -55,7 +55,9 @@ __device__ __forceinline__ int wave_token_chunk(int nchunk, int &t) {
 __device__ __forceinline__ int round_up(int c, int a) { return (c + a - 1) / a * a; }
 
 // Exclusive scan of one int per thread over a workgroup of nwaves wave64s
-// (s_wave holds at least nwaves ints). Every thread must call it.
+// (s_wave holds at least nwaves ints). Every thread must call it. Its barriers
+// order LDS only: the caller's outstanding global loads and stores stay in
+// flight.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int nwaves, int *total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   int x = v;
@@ -65,14 +67,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int nwav
     if (lane >= d) x += y;
   }
   if (lane == 63) s_wave[wave] = x;
-  __syncthreads();
+  lds_barrier();
   int before = 0, all = 0;
   for (int w = 0; w < nwaves; ++w) {
     const int s = s_wave[w];
     before += (w < wave) ? s : 0;
     all += s;
   }
-  __syncthreads();
+  lds_barrier();
   *total = all;
   return before + x - v;
 }

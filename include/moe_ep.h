@@ -126,8 +126,10 @@ int64_t moe_recv_rows_worst(const moe_shape *shape);
  * E*R*M rows. -1 for invalid arguments. */
 int64_t moe_ll_recv_rows(int32_t E, int32_t R, int32_t M);
 
-/* Device workspace bytes that moe_layout / moe_ll_layout need for this shape
- * (0 when the whole batch fits one workgroup). */
+/* Device workspace bytes that moe_layout / moe_ll_layout (and the layout +
+ * dispatch calls) need for this shape: 0 for at most 1024 pairs, or at most
+ * 4096 pairs with A = 1. (Low-latency calls ignore A but are asked for the
+ * workspace of the shape as given.) */
 size_t moe_layout_workspace_bytes(const moe_shape *shape);
 
 /* Contiguous dispatch layout (Buffer.get_dispatch_layout and the layout half of
@@ -155,10 +157,10 @@ int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank, const int
 /* Layout and dispatch in one call (Buffer.dispatch given topk_idx and no handle):
  * the same results as moe_layout followed by moe_dispatch -- every array of out
  * and every row of recv_x bit for bit -- and the same argument rules as those
- * two calls (shape->H is used). Batches of at most 2048 pairs run as a single
- * kernel in which each workgroup re-derives the layout from the routing while
- * its token rows load; larger batches launch the layout kernels, then the
- * scatter. A slot at or past recv_rows sets MOE_STATUS_BAD_SLOT and is not
+ * two calls (shape->H is used). Batches of at most 4096 pairs with A = 1 run
+ * as a single kernel in which each workgroup re-derives the layout from the
+ * routing while its token rows load; other batches launch the layout kernels,
+ * then the scatter. A slot at or past recv_rows sets MOE_STATUS_BAD_SLOT and is not
  * written. */
 int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx, const moe_layout_t *out,
                         const uint16_t *x, uint16_t *recv_x, int64_t recv_rows, void *ws,

@@ -48,6 +48,11 @@ def test_size_helpers(lib):
     assert lib.moe_ll_recv_rows(256, 8, 128) == 256 * 8 * 128
     assert lib.moe_ll_recv_rows(255, 8, 128) == -1
     assert lib.moe_layout_workspace_bytes(lib.make_shape(128, 7168, 256, 8, 8)) == 0
+    # no workspace up to 1024 pairs, or up to 4096 with alignment 1
+    assert lib.moe_layout_workspace_bytes(lib.make_shape(512, 7168, 256, 8, 8)) == 0
+    assert lib.moe_layout_workspace_bytes(lib.make_shape(128, 7168, 256, 8, 8, 32)) == 0
+    assert lib.moe_layout_workspace_bytes(lib.make_shape(129, 7168, 256, 8, 8, 32)) > 0
+    assert lib.moe_layout_workspace_bytes(lib.make_shape(513, 7168, 256, 8, 8)) > 0
     big = lib.make_shape(8192, 7168, 288, 8, 8)
     n = lib.moe_layout_workspace_bytes(big)
     assert n >= (64 * 288 + 64 * 8) * 4 and n % 256 == 0

@@ -85,6 +85,12 @@ CASES = {
     "rand_E1024_R64": lambda: mi.random_case(15, 256, 128, 1024, 64, 8, 1),
     "rand_K64_onefull": lambda: mi.random_case(16, 128, 32, 256, 8, 64, 1),  # 8192 pairs
     "rand_K64_multi": lambda: mi.random_case(17, 129, 32, 256, 8, 64, 1),  # 8256 pairs
+    # boundaries of the layout paths: one workgroup up to 1024 pairs (A > 1),
+    # counting up to 4096 (A = 1), three launches above
+    "rand_1024pairs": lambda: mi.random_case(23, 128, 64, 64, 8, 8, 1, neg_frac=0.02),
+    "rand_1025pairs": lambda: mi.random_case(24, 1025, 16, 16, 4, 1, 1),
+    "rand_4096pairs": lambda: mi.random_case(25, 512, 64, 256, 8, 8, 1),
+    "rand_4097pairs": lambda: mi.random_case(26, 4097, 16, 32, 4, 1, 1),
     "rand_8193pairs": lambda: mi.random_case(18, 8193, 16, 32, 4, 1, 1),
     "rand_all_neg": lambda: mi.random_case(19, 64, 64, 16, 4, 4, 1, neg_frac=1.0),
     "rand_bad_ids": lambda: mi.random_case(20, 100, 64, 32, 4, 4, 1, bad_frac=0.1),
