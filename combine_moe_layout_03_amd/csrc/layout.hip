@@ -33,7 +33,7 @@ template <bool kOneBlock>
 __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutParams p) {
   __shared__ int16_t s_ids[kMaxPairsOneBlock];     // validated ids, -1 = none (16 KiB)
   __shared__ uint16_t s_wc[kLayoutWaves][kMaxExperts];  // per-wave counters (32 KiB)
-  __shared__ int32_t s_base[kMaxExperts];          // first slot of each expert
+  __shared__ int32_t s_base[kMaxExperts + 1];      // first slot of each expert (+ end)
   __shared__ int32_t s_cnt[kMaxExperts];           // pairs per expert in this block
   __shared__ int32_t s_rc[kMaxExperts];            // tokens per rank in this block
   __shared__ int32_t s_wave[kLayoutWaves];
@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
         p.offset[e] = excl;
         if (e == E - 1) p.offset[E] = total;
         s_base[e] = excl;
+        if (e == E - 1) s_base[E] = total;
       } else {
         const int base = (e * R + p.src) * p.M;
         p.count[e] = min(c, p.M);
@@ -171,9 +172,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
       if (i < n) {
         const int tl = i / R;
         r = i - tl * R;
-        for (int k = 0; k < K; ++k) {
-          const int e = s_ids[tl * K + k];
-          hit |= (e >= 0) && (rank_of(e, p.l_magic) == r);
+        // eight LDS reads in flight at a time (indexes clamped into the token)
+        for (int k0 = 0; k0 < K; k0 += 8) {
+          int e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = s_ids[tl * K + min(k0 + j, K - 1)];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            hit |= (e[j] >= 0) && (rank_of(e[j], p.l_magic) == r);
         }
         if (p.in_rank) p.in_rank[(int64_t)t0 * R + i] = hit ? 1 : 0;
       }
@@ -193,17 +199,26 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
     }
   }
   if (kOneBlock && p.row_src) {
-    // rows no pair fills carry -1: alignment padding, or the low-latency
-    // stripe rows past the received count; one wave per expert, its lanes
-    // over the rows
-    for (int e = wave; e < E; e += kLayoutWaves) {
-      const int c = s_cnt[e];
-      if (p.mode == kModeContiguous) {
-        const int hi = s_base[e] + round_up(c, p.A);
-        for (int r = s_base[e] + c + lane; r < hi; r += 64) p.row_src[r] = -1;
-      } else {
-        int32_t *stripe = p.row_src + (int64_t)e * p.M;
-        for (int j = min(c, p.M) + lane; j < p.M; j += 64) stripe[j] = -1;
+    // Rows that hold no pair carry -1: the alignment padding after each
+    // expert's rows, or the low-latency stripe rows past its received count.
+    // Wave w takes experts w, w + 16, ...: its lanes read the experts' row
+    // ranges at once, then store each range with consecutive lanes.
+    for (int e0 = wave; e0 < E; e0 += kLayoutWaves * 64) {
+      const int e = e0 + lane * kLayoutWaves;
+      int lo = 0, hi = 0;
+      if (e < E) {
+        if (p.mode == kModeContiguous) {
+          lo = s_base[e] + s_cnt[e];
+          hi = s_base[e + 1];
+        } else {
+          lo = e * p.M + min(s_cnt[e], p.M);
+          hi = (e + 1) * p.M;
+        }
+      }
+      const int n = min(64, (E - e0 + kLayoutWaves - 1) / kLayoutWaves);
+      for (int j = 0; j < n; ++j) {
+        const int l = __builtin_amdgcn_readlane(lo, j), h = __builtin_amdgcn_readlane(hi, j);
+        for (int r = l + lane; r < h; r += 64) p.row_src[r] = -1;
       }
     }
   }
