@@ -61,6 +61,35 @@ def algo_bytes(T, H, K, E, R, P_valid, fp8_flags=None):
                 total=layout + dispatch + combine)
 
 
+def device_hbm_figures(dev_index):
+    """Memory bus width and clock as the HIP runtime reports them, and the peak
+    they imply for HBM3/HBM3E, which moves four transfers per reported clock
+    (bytes/s = 4 x clock x width / 8; the same rule gives MI300X's published
+    5.3 TB/s from its 1.3 GHz). The roofline uses the published 8 TB/s; this
+    is a cross-check reported beside it."""
+    import ctypes
+    path = "libamdhip64.so"
+    try:  # the HIP runtime torch already loaded, if any
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        hip = ctypes.CDLL(path)
+    except OSError:
+        return None
+    vals = {}
+    # hipDeviceAttributeMemoryBusWidth = 59, hipDeviceAttributeMemoryClockRate = 60
+    for name, attr in (("bus_width_bits", 59), ("memory_clock_khz", 60)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev_index) != 0:
+            return None
+        vals[name] = v.value
+    vals["implied_peak_GBps"] = round(4 * vals["memory_clock_khz"] * 1e3
+                                      * vals["bus_width_bits"] / 8 / 1e9, 1)
+    return vals
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
@@ -540,6 +569,12 @@ def main():
     us_step = ms * 1e3 / K
     value = ab["total"] / (us_step * 1e-6) / 1e9
     log(f"{mode}: {K} steps in {ms:.3f} ms -> {us_step:.2f} us/step, {value:.1f} GB/s")
+    # secondary: the same step on one buffer set over and over (caches warm)
+    warm_us = None
+    if not args.eager:
+        warm_us = graph_us_per_step(torch, stream, [(lambda: step(capi, sets[0], stream))] * S,
+                                    max(4, 400 // S))
+        log(f"warm (one buffer set): {warm_us:.2f} us/step")
 
     # per-kernel durations: each launch bracketed by events, rotating sets
     n = min(400, max(50, K // 4))
@@ -652,6 +687,8 @@ def main():
                    "timing": mode, "buffer_sets": S,
                    "footprint_MiB": round(S * probe.nbytes / 2**20, 1),
                    "algorithmic_bytes_per_step": ab["total"]},
+        "us_per_step_warm": round(warm_us, 3) if warm_us is not None else None,
+        "hbm_peak_reported_by_device": device_hbm_figures(dev.index or 0),
         "kernels_us": {k: round(v["mean_us"], 3) for k, v in kern.items()},
         "kernels_eager_event_us": {k: round(v["event_mean_us"], 3) for k, v in kern.items()},
         "roofline": roofline,
