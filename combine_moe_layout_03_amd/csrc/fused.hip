@@ -281,7 +281,10 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     //    each wave adds its counts for k into s_pre[k] / s_lt[k].
     // (an invalid ek = -1 matches no sentinel-coded id, so it needs no branch;
     // the below count is simply unused in the low-latency layout)
+    // (lane k also counts the token's earlier pairs with its own id, in the
+    // same pass)
     const int tokv = lane < K ? s_tok[lane] : -1;
+    int dup = 0;
     if (counting) {  // uniform per wave
       int prev = 0, ltv = 0;
 #pragma unroll 2
@@ -289,11 +292,14 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
         const int ek = __builtin_amdgcn_readlane(tokv, k);
         prev = set_lane(prev, k, ids.count_early_equal(ek));
         ltv = set_lane(ltv, k, ids.count_below(ek));
+        dup += (lane > k && tokv == ek) ? 1 : 0;
       }
       if (lane < K) {
         atomicAdd(&s_pre[lane], prev);
         if (!ll) atomicAdd(&s_lt[lane], ltv);
       }
+    } else {
+      for (int k = 0; k < K; ++k) dup += (lane > k && __builtin_amdgcn_readlane(tokv, k) == tokv);
     }
     lds_barrier();
 
@@ -301,8 +307,6 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     int out = -1, j = 0;
     {
       const int e = tokv;
-      int dup = 0;
-      for (int k = 0; k < K; ++k) dup += (k < lane && __builtin_amdgcn_readlane(tokv, k) == e);
       if (lane < K && e >= 0) {
         j = s_pre[lane] + dup;
         if (!ll) {
