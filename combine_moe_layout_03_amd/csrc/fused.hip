@@ -67,9 +67,6 @@ struct CountParams {
   int32_t RM, G;
 };
 
-// v with lane j replaced by the (uniform) value x
-__device__ __forceinline__ int set_lane(int v, int j, int x) { return lane_id() == j ? x : v; }
-
 __device__ __forceinline__ int valid_or_neg(int64_t v, int E, int &st) {
   const bool ok = v >= 0 && v < E;
   if (!ok && v != -1) st |= kStBadExpert;

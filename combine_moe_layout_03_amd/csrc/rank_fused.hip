@@ -54,8 +54,6 @@ struct RankFusedParams {
                       // workgroup count_wgs writes the rank offsets
 };
 
-__device__ __forceinline__ int set_lane(int v, int j, int x) { return lane_id() == j ? x : v; }
-
 // The routing as one lane sees it: tokens tid + 512 i (i < kRounds), their
 // valid ids (-1 otherwise) and their sets of ranks.
 template <int kRounds>
@@ -102,34 +100,6 @@ struct LaneTokens {
     }
   }
 };
-
-// Inclusive prefix sum over the lanes of a wave (every lane must call it):
-// a Hillis-Steele scan inside each 16-lane DPP row (row_shr by 1, 2, 4, 8),
-// then row 1 and 3 add the last lane of the row before (row_bcast:15) and
-// rows 2 and 3 the last lane of row 1 (row_bcast:31).
-__device__ __forceinline__ int wave_inclusive_sum(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
-  return x;
-}
-
-// Sum over the 64 lanes of a wave, wave-uniform (every lane must call it):
-// rotations inside each 16-lane row (by 8, 4, 2, 1) give every lane its row's
-// sum, then the four row sums are added.
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false);
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false);
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 32) +
-         (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
-}
 
 // Bits 0..3 of x to bits 0, 8, 16, 24: four one-byte counters that a sum over
 // a wave's lanes (at most 2 * 64 per byte here) cannot carry out of.

@@ -7,6 +7,37 @@ namespace moe {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// v with lane j replaced by the (uniform) value x
+__device__ __forceinline__ int set_lane(int v, int j, int x) { return lane_id() == j ? x : v; }
+
+// Inclusive prefix sum over the lanes of a wave (every lane must call it):
+// a Hillis-Steele scan inside each 16-lane DPP row (row_shr by 1, 2, 4, 8),
+// then row 1 and 3 add the last lane of the row before (row_bcast:15) and
+// rows 2 and 3 the last lane of row 1 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return x;
+}
+
+// Sum over the 64 lanes of a wave, wave-uniform (every lane must call it):
+// rotations inside each 16-lane row (by 8, 4, 2, 1) give every lane its row's
+// sum, then the four row sums are added.
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xf, 0xf, false);
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 32) +
+         (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+}
+
 // Lanes of this wave holding the same key (only lanes with valid = true take
 // part): one ballot per key bit, AND-ed -- gfx950 has no match instruction.
 // Every lane of the wave must call this (the ballots are wave-wide).
@@ -60,12 +91,7 @@ __device__ __forceinline__ int round_up(int c, int a) { return (c + a - 1) / a *
 // flight.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *s_wave, int nwaves, int *total) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  const int x = wave_inclusive_sum(v);
   if (lane == 63) s_wave[wave] = x;
   lds_barrier();
   int before = 0, all = 0;
