@@ -121,6 +121,14 @@ struct LaneIds {
     for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(early[r] == e));
     return n;
   }
+  // valid ids below e, plus ids equal to e before pair `before` (the two sets
+  // are disjoint): the contiguous slot of e's next pair, in one ballot per round
+  __device__ __forceinline__ int count_slot(int e) const {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(below[r] < e || early[r] == e));
+    return n;
+  }
   __device__ __forceinline__ int count_below(int e) const {
     int n = 0;
 #pragma unroll
@@ -226,8 +234,9 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 // kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast.
 template <bool kCopy, int kRounds, int kFp8>
 __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
-  __shared__ int32_t s_pre[64];   // per k: pairs with the same id before this token
-  __shared__ int32_t s_lt[64];    // per k: valid ids below it
+  // per k: pairs with the same id before this token, plus (contiguous layout)
+  // the valid ids below it
+  __shared__ int32_t s_pre[64];
   __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
   __shared__ int32_t s_status;
 
@@ -250,10 +259,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     const int t = kCopy ? b / f.wg_per_token : b;  // < T
     const bool token_lead = !kCopy || b % f.wg_per_token == 0;
     const int pbeg = t * K;
-    if (tid < 64) {
-      s_pre[tid] = 0;
-      s_lt[tid] = 0;
-    }
+    if (tid < 64) s_pre[tid] = 0;
 
     // 1. the routing first ...
     LaneIds<kRounds> ids;
@@ -274,27 +280,32 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     lds_barrier();
 
     // 3. per selected expert of this token: ids equal to it before the token,
-    //    and valid ids below it. The token's ids sit in lanes 0..K-1 of tokv;
-    //    each wave adds its counts for k into s_pre[k] / s_lt[k].
-    // (an invalid ek = -1 matches no sentinel-coded id, so it needs no branch;
-    // the below count is simply unused in the low-latency layout)
+    //    and (contiguous layout) valid ids below it, counted together. The
+    //    token's ids sit in lanes 0..K-1 of tokv; each wave adds its counts
+    //    for k into s_pre[k].
+    // (an invalid ek = -1 matches no sentinel-coded id, so it needs no branch)
     // (lane k also counts the token's earlier pairs with its own id, in the
     // same pass)
     const int tokv = lane < K ? s_tok[lane] : -1;
     int dup = 0;
     if (counting) {  // uniform per wave
-      int prev = 0, ltv = 0;
+      int prev = 0;
+      if (ll) {
 #pragma unroll 2
-      for (int k = 0; k < K; ++k) {
-        const int ek = __builtin_amdgcn_readlane(tokv, k);
-        prev = set_lane(prev, k, ids.count_early_equal(ek));
-        ltv = set_lane(ltv, k, ids.count_below(ek));
-        dup += (lane > k && tokv == ek) ? 1 : 0;
+        for (int k = 0; k < K; ++k) {
+          const int ek = __builtin_amdgcn_readlane(tokv, k);
+          prev = set_lane(prev, k, ids.count_early_equal(ek));
+          dup += (lane > k && tokv == ek) ? 1 : 0;
+        }
+      } else {
+#pragma unroll 2
+        for (int k = 0; k < K; ++k) {
+          const int ek = __builtin_amdgcn_readlane(tokv, k);
+          prev = set_lane(prev, k, ids.count_slot(ek));
+          dup += (lane > k && tokv == ek) ? 1 : 0;
+        }
       }
-      if (lane < K) {
-        atomicAdd(&s_pre[lane], prev);
-        if (!ll) atomicAdd(&s_lt[lane], ltv);
-      }
+      if (lane < K) atomicAdd(&s_pre[lane], prev);
     } else {
       for (int k = 0; k < K; ++k) dup += (lane > k && __builtin_amdgcn_readlane(tokv, k) == tokv);
     }
@@ -305,9 +316,9 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     {
       const int e = tokv;
       if (lane < K && e >= 0) {
-        j = s_pre[lane] + dup;
+        j = s_pre[lane] + dup;  // contiguous: the slot; low latency: the stripe row
         if (!ll) {
-          out = s_lt[lane] + j;
+          out = j;
         } else if (j < p.M) {
           out = (e * R + p.src) * p.M + j;
         } else if (wave == 0) {
