@@ -410,6 +410,44 @@ def row_replica_train(capi, mi, torch, np, dev, stream):
             "algorithmic_bytes": {"weight_sync": b_sync, "grad_reduce": b_red}}
 
 
+def row_config(capi, mi, torch, np, dev, stream, name):
+    """The standard step (layout + dispatch in one call, then combine) on
+    another configuration: c1 (64 tokens x 256, 16 experts top-2 on 4 ranks)
+    or c4 (4096 tokens x 4096, 64 experts top-6 Zipf(1.2) on 8 ranks).
+    Rotating buffer sets for >= 512 MiB touched (at most 64 sets)."""
+    w = mi.by_name(name)
+    probe = Workset(capi, w, dev)
+    S = min(64, max(2, math.ceil(512 * 2**20 / probe.nbytes)))
+    sets = [probe] + [Workset(capi, w, dev) for _ in range(S - 1)]
+    with torch.cuda.stream(stream):
+        for z in sets:
+            step(capi, z, stream)
+    torch.cuda.synchronize()
+    us = graph_us_per_step(torch, stream, [(lambda z=z: step(capi, z, stream)) for z in sets],
+                           max(4, 200 // S))
+    k_ld = graph_us_per_step(torch, stream, [(lambda z=z: capi.moe_layout_dispatch(
+        z.shape, z.idx, z.lay, z.x, z.recv, z.rows, z.ws, stream=stream)) for z in sets],
+        max(4, 200 // S))
+    k_cb = graph_us_per_step(torch, stream, [(lambda z=z: capi.moe_combine(
+        z.shape, z.recv, z.rows, z.lay.slot, z.w, z.out, None, None, stream=stream))
+        for z in sets], max(4, 200 // S))
+    P = int((w.topk_idx >= 0).sum())
+    ab = algo_bytes(w.T, w.H, w.K, w.E, w.R, P)
+    foot = S * probe.nbytes
+    del sets, probe
+    torch.cuda.empty_cache()
+    r_ld = (ab["layout"] + ab["dispatch"]) / k_ld / 1e3
+    r_cb = ab["combine"] / k_cb / 1e3
+    return {"workload": f"{w.name}: {w.T} tokens x {w.H}, {w.E} experts top-{w.K} on {w.R} ranks",
+            "buffer_sets": S, "footprint_MiB": round(foot / 2**20, 1),
+            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
+            "algorithmic_bytes_per_step": ab["total"],
+            "kernels_us": {"layout_dispatch": round(k_ld, 3), "combine": round(k_cb, 3)},
+            "roofline_layout_dispatch": {"achieved": round(r_ld, 1),
+                                         "frac": round(r_ld / HBM_PEAK_GBS, 4)},
+            "roofline_combine": {"achieved": round(r_cb, 1), "frac": round(r_cb / HBM_PEAK_GBS, 4)}}
+
+
 def row_replica(capi, mi, torch, np, dev, stream, n_ev):
     """Replica-expanded routing at full size (8192 tokens x 7168, 256 logical
     experts top-8 Zipf(1.0), 32 extra replicas): load -> plan -> reroute ->
@@ -646,6 +684,9 @@ def main():
             f"{rows['low_latency_fp8_rowscales_m128']['us_per_step']} us/step")
         rows["normal_mode_128x7168"] = row_normal(capi, mi, torch, np, dev, stream)
         log(f"normal-mode row: {rows['normal_mode_128x7168']['us_per_step']} us/step")
+        for cname in ("c1", "c4"):
+            rows[f"config_{cname}"] = row_config(capi, mi, torch, np, dev, stream, cname)
+            log(f"{cname} row: {rows[f'config_{cname}']['us_per_step']} us/step")
         rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
         log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
         rows["replica_train"] = row_replica_train(capi, mi, torch, np, dev, stream)
