@@ -195,9 +195,9 @@ class RankHandle:
     recv_rows: int
 
 
-def normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
-                    topk_weights: Optional[torch.Tensor], num_experts: int, num_ranks: int,
-                    expert_alignment: int = 1):
+def normal_dispatch(x: Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]],
+                    topk_idx: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                    num_experts: int, num_ranks: int, expert_alignment: int = 1):
     """Buffer.dispatch in normal mode: each token is sent once to every rank
     hosting one of its experts. Returns (recv_x [rows, H], recv_topk_idx
     [rows, K] rank-local ids or -1, recv_topk_weights [rows, K] or None,
@@ -205,18 +205,32 @@ def normal_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
     rank_offset [R+1] int32, handle). The receive buffers of the R ranks are
     one buffer sized for the worst case, T * min(K, R) rows; rank r's tokens
     are rows [rank_offset[r], rank_offset[r+1]) (device values, no host
-    read)."""
-    T, H = x.shape
+    read). x is bf16 [T, H], or (as on the page) a tuple of E4M3 codes
+    [T, H] and float scales [T, H/128]; then recv_x is the tuple of the
+    receive rows' codes and scales, each copied row for row."""
+    fp8 = isinstance(x, tuple)
+    xt = x[0] if fp8 else x
+    T, H = xt.shape
     K = topk_idx.shape[1]
     shape = capi.make_shape(T, H, num_experts, num_ranks, K, expert_alignment)
-    lay = capi.RankLayoutBuffers.empty(shape, x.device, weights=topk_weights is not None)
+    lay = capi.RankLayoutBuffers.empty(shape, xt.device, weights=topk_weights is not None)
     rows = max(lay.cap, 1)
-    recv_x = torch.empty(rows, H, dtype=x.dtype, device=x.device)
-    # layout and row copies in one call (one launch for batches of up to 1024 tokens)
-    capi.moe_rank_layout_dispatch(
-        shape, topk_idx.contiguous(),
-        topk_weights.contiguous() if topk_weights is not None else None, lay, x.contiguous(),
-        recv_x, lay.cap)
+    idx = topk_idx.contiguous()
+    wts = topk_weights.contiguous() if topk_weights is not None else None
+    if fp8:
+        # the layout, then the tuple's row copy over the [T, R] table of rank rows
+        xq, xs = x
+        capi.moe_rank_layout(shape, idx, wts, lay)
+        rq = torch.empty(rows, H, dtype=xq.dtype, device=xq.device)
+        rs = torch.empty(rows, H // capi.FP8_GROUP, dtype=torch.float32, device=xq.device)
+        rank_shape = capi.make_shape(T, H, num_experts, num_ranks, num_ranks, expert_alignment)
+        capi.moe_dispatch_fp8(rank_shape, xq.contiguous(), xs.contiguous(), lay.rank_slot,
+                              rq.view(torch.uint8), rs, lay.cap, lay.status)
+        recv_x = (rq, rs)
+    else:
+        recv_x = torch.empty(rows, H, dtype=xt.dtype, device=xt.device)
+        # layout and row copies in one call (one launch for batches of up to 1024 tokens)
+        capi.moe_rank_layout_dispatch(shape, idx, wts, lay, xt.contiguous(), recv_x, lay.cap)
     w = lay.recv_topk_weights.view(rows, K) if lay.recv_topk_weights is not None else None
     return (recv_x, lay.recv_topk_idx.view(rows, K), w, lay.recv_expert_count,
             lay.rank_offset, RankHandle(shape, lay, lay.cap))

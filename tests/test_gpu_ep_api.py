@@ -1,7 +1,8 @@
 """The page-named convenience calls (ep.py) end to end on the GPU, against the
 oracle: get_dispatch_layout + dispatch + combine, dispatch of an FP8 tuple,
-low_latency_dispatch (bf16 and FP8, with cumulative receive counts) and
-low_latency_combine (with an active-rank mask)."""
+low_latency_dispatch (bf16 and FP8, with cumulative receive counts),
+low_latency_combine (with an active-rank mask), and the normal-mode dispatch
+(bf16 and an FP8 tuple) and combine."""
 import numpy as np
 import pytest
 import torch
@@ -128,3 +129,23 @@ def test_normal_dispatch_and_combine(ep, orc):
                                                   "f32")["out_bf16"])
     want, _ = orc.combine_rank_weights(ref["rank_slot"], ref["recv_topk_weights"])
     assert np.array_equal(cw.cpu().numpy(), want)
+
+
+def test_normal_dispatch_fp8_tuple(ep, orc):
+    """Normal mode with x given as an (E4M3, scales) tuple: the rank rows
+    receive each token's codes and scales bit for bit."""
+    w = mi.config_c2()
+    qz = orc.quantize_fp8(w.x, 0)
+    xq = torch.from_numpy(qz["q"]).to(dev()).view(torch.float8_e4m3fn)
+    (rq, rs), ridx, rw, rcount, roff, h = ep.normal_dispatch(
+        (xq, to_dev(qz["scale"])), to_dev(w.topk_idx), to_dev(w.topk_weights), w.E, w.R, 1)
+    ref = orc.rank_layout(w.topk_idx, w.E, w.R, 1, w.topk_weights)
+    rows = ref["rows"]
+    assert np.array_equal(roff.cpu().numpy(), ref["rank_offset"])
+    assert np.array_equal(ridx.cpu().numpy()[:rows], ref["recv_topk_idx"])
+    wq, ws_, st = orc.dispatch_fp8_tuple(qz["q"], qz["scale"], ref["rank_slot"],
+                                         max(w.T * min(w.K, w.R), 1))
+    assert st == 0
+    assert np.array_equal(rq.view(torch.uint8).cpu().numpy()[:rows], wq[:rows])
+    assert np.array_equal(rs.cpu().numpy()[:rows].view(np.uint32), ws_[:rows].view(np.uint32))
+    assert np.array_equal(rq.view(torch.uint8).cpu().numpy()[:rows], qz["q"][ref["recv_src"]])
