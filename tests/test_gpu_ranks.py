@@ -109,6 +109,8 @@ CASES = [
     (8, 1024, 256, 64, 16, 8, 0.05, 0.1, 0.01),
     (9, 513, 7168, 256, 8, 8, 0.0, 0.0, 0.0),
     (10, 700, 1032, 128, 64, 5, 0.2, 0.2, 0.0),
+    (11, 300, 64, 8, 1, 4, 0.1, 0.1, 0.0),  # one rank
+    (12, 1024, 136, 1024, 64, 8, 0.02, 0.05, 0.01),  # the one-launch limits: T, E, R, K
 ]
 
 
