@@ -9,8 +9,10 @@
 //   #(valid pairs with id < e) + #(pairs before token t with id e)
 //   + #(earlier k of token t with id e),
 // and in the low-latency layout it is (e*R + src)*M plus the last two terms.
-// So a workgroup that serves token t needs just two counts per selected expert
-// over the whole routing -- no histogram, no scan, no cross-workgroup step.
+// The first two terms are disjoint sets of pairs, so a workgroup that serves
+// token t needs one count per selected expert over the whole routing (and in
+// the low-latency layout only the second) -- no histogram, no scan, no
+// cross-workgroup step; the third term comes from the token's own ids.
 // Each wave reads a few ids per lane (the routing is a few KiB and sits in
 // L2 after the first touch) and turns them into counts with ballot +
 // popcount, accumulated in scalar registers; the waves' partial counts meet
@@ -18,17 +20,19 @@
 // tokens per rank, empty low-latency stripe rows) are computed the same way by
 // a few extra "duty" workgroups that copy nothing, so the copying workgroups
 // only derive their own K slots. The id loads are unrolled over a compile-time
-// number of rounds and every count is one compare + ballot + popcount: at this
-// size the kernel is bound by each wave's serial instruction latency, not by
-// memory.
+// number of rounds (up to 8: 4096 pairs over 512 lanes) and every count is a
+// compare or two + ballot + popcount: at this size the counting is bound by
+// each wave's serial instruction latency, not by memory.
 //
 // With the copy, a workgroup of 8 waves owns up to 8 chunks (1 KiB each) of
 // one token row (a 7168-wide row is two workgroups of 7 copying waves, so the
 // row stores of 128 tokens leave from all 256 CUs; every wave also counts:
-// 512 lanes read a 1024-pair routing in two rounds). It requests the routing first and the row second, derives its K slots
-// while the (cold) row is still in flight, then stores the row K times -- as
+// 512 lanes read a 1024-pair routing in two rounds). It requests the routing
+// first and the row second, derives its K slots while the (cold) row is still
+// in flight, then stores the row K times -- as
 // bf16, or (low-latency FP8 dispatch) cast once to E4M3 with per-128-channel
-// scales (fp8.hpp) and stored as codes plus column-major scales.
+// scales (fp8.hpp) and stored as codes plus column-major (or row-major)
+// scales.
 #include "fp8.hpp"
 #include "wave.hpp"
 
