@@ -9,10 +9,11 @@
 //   #(valid pairs with id < e) + #(pairs before token t with id e)
 //   + #(earlier k of token t with id e),
 // and in the low-latency layout it is (e*R + src)*M plus the last two terms.
-// The first two terms are disjoint sets of pairs, so a workgroup that serves
-// token t needs one count per selected expert over the whole routing (and in
-// the low-latency layout only the second) -- no histogram, no scan, no
-// cross-workgroup step; the third term comes from the token's own ids.
+// The three terms together count the pairs ordered before (t, k) by the key
+// id * P + pair index, so a workgroup that serves token t needs one count per
+// selected expert over the whole routing, one compare per id; the low-latency
+// row counts the ids equal to e before the token and adds the token's own
+// earlier pairs -- no histogram, no scan, no cross-workgroup step.
 // Each wave reads a few ids per lane (the routing is a few KiB and sits in
 // L2 after the first touch) and turns them into counts with ballot +
 // popcount, accumulated in scalar registers; the waves' partial counts meet
@@ -85,6 +86,9 @@ template <int kRounds>
 struct LaneIds {
   int64_t raw[kRounds];
   int any[kRounds], early[kRounds], below[kRounds];
+  // (id, pair index) as one integer id * P + i, kAboveAll for no valid id:
+  // pairs order by expert, then by pair index, as the contiguous slots do
+  int key[kRounds];
 
   // request the ids; nothing waits for them here
   __device__ __forceinline__ void issue(const int64_t *idx, int P, int nthreads) {
@@ -104,6 +108,7 @@ struct LaneIds {
       any[r] = e >= 0 ? e : kNoId;
       early[r] = (e >= 0 && i < before) ? e : kNoId;
       below[r] = e >= 0 ? e : kAboveAll;
+      key[r] = e >= 0 ? e * P + i : kAboveAll;
       if (s_tok && i >= tok && i < tok + K && i < P) s_tok[i - tok] = e;
     }
   }
@@ -125,12 +130,12 @@ struct LaneIds {
     for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(early[r] == e));
     return n;
   }
-  // valid ids below e, plus ids equal to e before pair `before` (the two sets
-  // are disjoint): the contiguous slot of e's next pair, in one ballot per round
-  __device__ __forceinline__ int count_slot(int e) const {
+  // pairs whose key is below k: with k = e * P + i, the valid pairs with an id
+  // below e plus the pairs of e before pair i -- pair i's contiguous slot (A = 1)
+  __device__ __forceinline__ int count_key_below(int k) const {
     int n = 0;
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(below[r] < e || early[r] == e));
+    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(key[r] < k));
     return n;
   }
   __device__ __forceinline__ int count_below(int e) const {
@@ -238,9 +243,7 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 // kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast.
 template <bool kCopy, int kRounds, int kFp8>
 __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
-  // per k: pairs with the same id before this token, plus (contiguous layout)
-  // the valid ids below it
-  __shared__ int32_t s_pre[64];
+  __shared__ int32_t s_pre[64];  // per k: the slot (contiguous) or stripe row (low latency)
   __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
   __shared__ int32_t s_status;
 
@@ -283,13 +286,12 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     if (counting) ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
     lds_barrier();
 
-    // 3. per selected expert of this token: ids equal to it before the token,
-    //    and (contiguous layout) valid ids below it, counted together. The
-    //    token's ids sit in lanes 0..K-1 of tokv; each wave adds its counts
-    //    for k into s_pre[k].
-    // (an invalid ek = -1 matches no sentinel-coded id, so it needs no branch)
-    // (lane k also counts the token's earlier pairs with its own id, in the
-    // same pass)
+    // 3. per pair k of this token: (contiguous layout) the pairs ordered
+    //    before it by (expert, pair index), which is its slot; (low latency)
+    //    the pairs of its expert before the token, to which lane k adds the
+    //    token's own earlier pairs on it. The token's ids sit in lanes 0..K-1
+    //    of tokv; each wave adds its counts for k into s_pre[k]. (An invalid
+    //    ek = -1 gives an unused count, so it needs no branch.)
     const int tokv = lane < K ? s_tok[lane] : -1;
     int dup = 0;
     if (counting) {  // uniform per wave
@@ -302,15 +304,16 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           dup += (lane > k && tokv == ek) ? 1 : 0;
         }
       } else {
+        // the slot of pair (t, k) is the number of keys below its own key, so
+        // the token's earlier pairs on the same expert are counted too
 #pragma unroll 2
         for (int k = 0; k < K; ++k) {
           const int ek = __builtin_amdgcn_readlane(tokv, k);
-          prev = set_lane(prev, k, ids.count_slot(ek));
-          dup += (lane > k && tokv == ek) ? 1 : 0;
+          prev = set_lane(prev, k, ids.count_key_below(ek * P + pbeg + k));
         }
       }
       if (lane < K) atomicAdd(&s_pre[lane], prev);
-    } else {
+    } else if (ll) {
       for (int k = 0; k < K; ++k) dup += (lane > k && __builtin_amdgcn_readlane(tokv, k) == tokv);
     }
     lds_barrier();
@@ -320,7 +323,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     {
       const int e = tokv;
       if (lane < K && e >= 0) {
-        j = s_pre[lane] + dup;  // contiguous: the slot; low latency: the stripe row
+        j = s_pre[lane] + dup;  // contiguous (dup = 0): the slot; low latency: the stripe row
         if (!ll) {
           out = j;
         } else if (j < p.M) {
