@@ -360,6 +360,10 @@ FUSED_CASES = {k: v for k, v in CASES.items()
                if k not in ("rand_8193pairs", "rand_K64_onefull", "rand_K64_multi")}
 FUSED_CASES["rand_2048pairs"] = lambda: mi.random_case(70, 256, 520, 96, 8, 8, 1, neg_frac=0.05)
 FUSED_CASES["rand_2049pairs"] = lambda: mi.random_case(71, 2049, 64, 32, 4, 1, 1)
+# the counting kernel's largest keys: 1024 experts x 4096 pairs
+FUSED_CASES["rand_E1024_4096pairs"] = lambda: mi.random_case(72, 512, 64, 1024, 64, 8, 1,
+                                                             neg_frac=0.02, dup_frac=0.05,
+                                                             bad_frac=0.01)
 
 
 @pytest.mark.parametrize("name", sorted(FUSED_CASES))
