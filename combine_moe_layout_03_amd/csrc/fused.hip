@@ -10,10 +10,10 @@
 //   + #(earlier k of token t with id e),
 // and in the low-latency layout it is (e*R + src)*M plus the last two terms.
 // The three terms together count the pairs ordered before (t, k) by the key
-// id * P + pair index, so a workgroup that serves token t needs one count per
-// selected expert over the whole routing, one compare per id; the low-latency
-// row counts the ids equal to e before the token and adds the token's own
-// earlier pairs -- no histogram, no scan, no cross-workgroup step.
+// id * P + pair index, and the last two the keys in [e * P, e * P + tK + k),
+// so a workgroup that serves token t needs one count per selected expert over
+// the whole routing, one compare per id -- no histogram, no scan, no
+// cross-workgroup step.
 // Each wave reads a few ids per lane (the routing is a few KiB and sits in
 // L2 after the first touch) and turns them into counts with ballot +
 // popcount, accumulated in scalar registers; the waves' partial counts meet
@@ -79,16 +79,14 @@ __device__ __forceinline__ int valid_or_neg(int64_t v, int E, int &st) {
 }
 
 // The routing as seen by one lane: ids of pairs r*nthreads + tid for
-// r < kRounds, in the three forms the counts compare against (one compare
-// per ballot): any id (sentinel kNoId), ids of pairs before pair `before`
-// (kNoId otherwise), and valid ids for "below" tests (kAboveAll otherwise).
+// r < kRounds, in the three forms the counts compare against: any id
+// (sentinel kNoId), valid ids for "below" tests (kAboveAll otherwise), and
+// the key id * P + pair index (kAboveAll for no valid id), by which pairs
+// order as the slots do: by expert, then by pair index.
 template <int kRounds>
 struct LaneIds {
   int64_t raw[kRounds];
-  int any[kRounds], early[kRounds], below[kRounds];
-  // (id, pair index) as one integer id * P + i, kAboveAll for no valid id:
-  // pairs order by expert, then by pair index, as the contiguous slots do
-  int key[kRounds];
+  int any[kRounds], below[kRounds], key[kRounds];
 
   // request the ids; nothing waits for them here
   __device__ __forceinline__ void issue(const int64_t *idx, int P, int nthreads) {
@@ -99,23 +97,22 @@ struct LaneIds {
   }
   // wait for them and build the three forms; pairs [tok, tok + K) are also
   // written to s_tok (each pair is held by exactly one lane)
-  __device__ __forceinline__ void settle(int P, int E, int nthreads, int before, int tok,
+  __device__ __forceinline__ void settle(int P, int E, int nthreads, int tok,
                                          int K, int32_t *s_tok, int &st) {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int i = r * nthreads + (int)threadIdx.x;
       const int e = i < P ? valid_or_neg(raw[r], E, st) : -1;
       any[r] = e >= 0 ? e : kNoId;
-      early[r] = (e >= 0 && i < before) ? e : kNoId;
       below[r] = e >= 0 ? e : kAboveAll;
       key[r] = e >= 0 ? e * P + i : kAboveAll;
       if (s_tok && i >= tok && i < tok + K && i < P) s_tok[i - tok] = e;
     }
   }
-  __device__ __forceinline__ void load(const int64_t *idx, int P, int E, int nthreads, int before,
+  __device__ __forceinline__ void load(const int64_t *idx, int P, int E, int nthreads,
                                        int &st) {
     issue(idx, P, nthreads);
-    settle(P, E, nthreads, before, 0, 0, nullptr, st);
+    settle(P, E, nthreads, 0, 0, nullptr, st);
   }
   // wave-wide counts, as scalars
   __device__ __forceinline__ int count_equal(int e) const {
@@ -124,10 +121,14 @@ struct LaneIds {
     for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(any[r] == e));
     return n;
   }
-  __device__ __forceinline__ int count_early_equal(int e) const {
+  // pairs whose key lies in [lo, lo + width) (one unsigned compare each): with
+  // lo = e * P and width = i, the pairs of e before pair i -- its row in e's
+  // low-latency stripe
+  __device__ __forceinline__ int count_keys_in(int lo, int width) const {
     int n = 0;
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) n += __popcll(__ballot(early[r] == e));
+    for (int r = 0; r < kRounds; ++r)
+      n += __popcll(__ballot((uint32_t)key[r] - (uint32_t)lo < (uint32_t)width));
     return n;
   }
   // pairs whose key is below k: with k = e * P + i, the valid pairs with an id
@@ -162,11 +163,11 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
   const bool ll = p.mode == kModeLowLatency;
   LaneIds<kRounds> ids;
   if (P > 0) {
-    ids.load(p.idx, P, E, nthreads, 0, st);
+    ids.load(p.idx, P, E, nthreads, st);
   } else {
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-      ids.any[r] = ids.early[r] = kNoId;
+      ids.any[r] = kNoId;
       ids.below[r] = kAboveAll;
     }
   }
@@ -283,29 +284,25 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       lane_ok = wave < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
       val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
     }
-    if (counting) ids.settle(P, E, nthreads, pbeg, pbeg, K, s_tok, st);
+    if (counting) ids.settle(P, E, nthreads, pbeg, K, s_tok, st);
     lds_barrier();
 
     // 3. per pair k of this token: (contiguous layout) the pairs ordered
     //    before it by (expert, pair index), which is its slot; (low latency)
-    //    the pairs of its expert before the token, to which lane k adds the
-    //    token's own earlier pairs on it. The token's ids sit in lanes 0..K-1
-    //    of tokv; each wave adds its counts for k into s_pre[k]. (An invalid
-    //    ek = -1 gives an unused count, so it needs no branch.)
+    //    the pairs of its expert before it, its stripe row. The token's ids
+    //    sit in lanes 0..K-1 of tokv; each wave adds its counts for k into
+    //    s_pre[k]. (An invalid ek = -1 gives an unused count, so it needs no
+    //    branch.)
     const int tokv = lane < K ? s_tok[lane] : -1;
-    int dup = 0;
     if (counting) {  // uniform per wave
       int prev = 0;
       if (ll) {
 #pragma unroll 2
         for (int k = 0; k < K; ++k) {
           const int ek = __builtin_amdgcn_readlane(tokv, k);
-          prev = set_lane(prev, k, ids.count_early_equal(ek));
-          dup += (lane > k && tokv == ek) ? 1 : 0;
+          prev = set_lane(prev, k, ids.count_keys_in(ek * P, pbeg + k));
         }
       } else {
-        // the slot of pair (t, k) is the number of keys below its own key, so
-        // the token's earlier pairs on the same expert are counted too
 #pragma unroll 2
         for (int k = 0; k < K; ++k) {
           const int ek = __builtin_amdgcn_readlane(tokv, k);
@@ -313,8 +310,6 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
         }
       }
       if (lane < K) atomicAdd(&s_pre[lane], prev);
-    } else if (ll) {
-      for (int k = 0; k < K; ++k) dup += (lane > k && __builtin_amdgcn_readlane(tokv, k) == tokv);
     }
     lds_barrier();
 
@@ -323,7 +318,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     {
       const int e = tokv;
       if (lane < K && e >= 0) {
-        j = s_pre[lane] + dup;  // contiguous (dup = 0): the slot; low latency: the stripe row
+        j = s_pre[lane];  // contiguous: the slot; low latency: the stripe row
         if (!ll) {
           out = j;
         } else if (j < p.M) {
