@@ -360,6 +360,11 @@ FUSED_CASES = {k: v for k, v in CASES.items()
                if k not in ("rand_8193pairs", "rand_K64_onefull", "rand_K64_multi")}
 FUSED_CASES["rand_2048pairs"] = lambda: mi.random_case(70, 256, 520, 96, 8, 8, 1, neg_frac=0.05)
 FUSED_CASES["rand_2049pairs"] = lambda: mi.random_case(71, 2049, 64, 32, 4, 1, 1)
+# from 256 tokens on, one workgroup per token: 14 row chunks and a ragged
+# 2400-pair routing; and a row of 20 chunks, too wide for one workgroup
+FUSED_CASES["rand_T300_wide"] = lambda: mi.random_case(75, 300, 7168, 256, 8, 8, 1, neg_frac=0.02,
+                                                       dup_frac=0.02)
+FUSED_CASES["rand_T256_H10240"] = lambda: mi.random_case(76, 256, 10240, 256, 8, 8, 1)
 # the counting kernel's largest keys: 1024 experts x 4096 pairs
 FUSED_CASES["rand_E1024_4096pairs"] = lambda: mi.random_case(72, 512, 64, 1024, 64, 8, 1,
                                                              neg_frac=0.02, dup_frac=0.05,
@@ -410,6 +415,35 @@ def test_layout_dispatch_empty_and_overflow(capi, orc):
     got, recv_t, lay, shape = run_layout_dispatch(capi, w, ll=True, M=40, src=1)
     ref = orc.ll_layout(w.topk_idx, w.E, w.R, 40, 1)
     assert ref["status"] & 2
+    check_layout(got, ref, w, ll=True)
+    _gpu_rows_check(recv_t, to_dev(w.x), ref["slot"], w.T, w.K)
+
+
+@pytest.mark.parametrize("M", [256, 120])
+def test_ll_layout_dispatch_hot_stripe(capi, orc, M):
+    """A stripe with more pairs than a duty workgroup stages in LDS (64): its
+    later rows are stored one by one; at M = 120 the stripe also overflows."""
+    w = _hot(mi.random_case(77, 120, 64, 32, 4, 8, 1, neg_frac=0.03, dup_frac=0.05), 5, 0.2)
+    _announce(f"ll_layout_dispatch hot stripe M={M}")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, ll=True, M=M, src=2)
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, M, 2)
+    assert int(np.max(np.bincount(w.topk_idx[w.topk_idx >= 0], minlength=w.E))) > 64
+    check_layout(got, ref, w, ll=True)
+    _gpu_rows_check(recv_t, to_dev(w.x), ref["slot"], w.T, w.K)
+
+
+@pytest.mark.parametrize("T", [1, 2, 40])
+def test_ll_few_tokens_many_stripes(capi, orc, T):
+    """More stripes than the copying workgroups empty (8 each): the rest are
+    the duty workgroups', in the layout-only and the fused launch."""
+    w = mi.random_case(78 + T, T, 2048, 256, 8, 8, 1, neg_frac=0.05)
+    M = T + 3
+    ref = orc.ll_layout(w.topk_idx, w.E, w.R, M, 6)
+    _announce(f"ll_layout T={T} E=256 M={M}")
+    got, lay, shape = run_layout(capi, w, ll=True, M=M, src=6)
+    check_layout(got, ref, w, ll=True)
+    _announce(f"ll_layout_dispatch T={T} E=256 M={M}")
+    got, recv_t, lay, shape = run_layout_dispatch(capi, w, ll=True, M=M, src=6)
     check_layout(got, ref, w, ll=True)
     _gpu_rows_check(recv_t, to_dev(w.x), ref["slot"], w.T, w.K)
 
