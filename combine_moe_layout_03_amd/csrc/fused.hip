@@ -272,6 +272,12 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     // 1. the routing first ...
     LaneIds<kRounds> ids;
     if (counting) ids.issue(p.idx, P, nthreads);
+    //    Every wave's id loads leave before any wave's row load (a barrier
+    //    with no memory wait). Without it the routing reached a workgroup's
+    //    last wave 0.5 us after its first -- id loads issued after another
+    //    wave's cold row load came back after it -- and the barrier takes
+    //    0.4 us off the 128 x 7168 batch.
+    __builtin_amdgcn_s_barrier();
     // 2. ... then the row chunk this wave copies; it stays in flight while
     //    the slots are worked out. The load is unconditional (address clamped
     //    into the row): under a branch it would force an early wait.
@@ -295,19 +301,19 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     //    branch.)
     const int tokv = lane < K ? s_tok[lane] : -1;
     if (counting) {  // uniform per wave
+      // lane k: pair k's threshold key -- contiguous: e * P + pair index (its
+      // slot counts the keys below); low latency: e * P (its row counts the
+      // keys in [e * P, e * P + pair index)) -- so one lane read per k
+      const int thr = tokv * P + (ll ? 0 : pbeg + lane);
       int prev = 0;
       if (ll) {
 #pragma unroll 2
-        for (int k = 0; k < K; ++k) {
-          const int ek = __builtin_amdgcn_readlane(tokv, k);
-          prev = set_lane(prev, k, ids.count_keys_in(ek * P, pbeg + k));
-        }
+        for (int k = 0; k < K; ++k)
+          prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k));
       } else {
 #pragma unroll 2
-        for (int k = 0; k < K; ++k) {
-          const int ek = __builtin_amdgcn_readlane(tokv, k);
-          prev = set_lane(prev, k, ids.count_key_below(ek * P + pbeg + k));
-        }
+        for (int k = 0; k < K; ++k)
+          prev = set_lane(prev, k, ids.count_key_below(__builtin_amdgcn_readlane(thr, k)));
       }
       if (lane < K) atomicAdd(&s_pre[lane], prev);
     }

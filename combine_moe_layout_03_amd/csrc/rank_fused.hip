@@ -152,7 +152,11 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   LaneTokens<kRounds> rt;
   rt.issue(p);
   // 3. ... then the row chunk this wave copies, unconditionally (address
-  //    clamped into the row), so it stays in flight while the rows are derived
+  //    clamped into the row), so it stays in flight while the rows are derived.
+  //    Every wave's routing loads leave before any wave's row load (a barrier
+  //    with no memory wait): routing loads issued after another wave's cold
+  //    row load come back after it.
+  __builtin_amdgcn_s_barrier();
   const int chunk = (b % p.wg_per_token) * p.chunks_per_wg + wave;
   const int v = chunk * 64 + lane;
   const bool lane_ok = wave < p.chunks_per_wg && chunk < p.nchunk && v < p.nvec;
