@@ -241,6 +241,26 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
   }
 }
 
+// Lane k < K: pair (pbeg + k)'s count over the wave's ids, thr holding its
+// threshold key in lane k (see the kernel). KT > 0 fixes K at compile time so
+// the K lane reads, compares and ballots issue back to back.
+template <int KT, int kRounds>
+__device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr, int Kr,
+                                            int pbeg, bool ll) {
+  const int K = KT ? KT : Kr;
+  int prev = 0;
+  if (ll) {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k));
+  } else {
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      prev = set_lane(prev, k, ids.count_key_below(__builtin_amdgcn_readlane(thr, k)));
+  }
+  return prev;
+}
+
 // kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast.
 template <bool kCopy, int kRounds, int kFp8>
 __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
@@ -305,16 +325,8 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       // slot counts the keys below); low latency: e * P (its row counts the
       // keys in [e * P, e * P + pair index)) -- so one lane read per k
       const int thr = tokv * P + (ll ? 0 : pbeg + lane);
-      int prev = 0;
-      if (ll) {
-#pragma unroll 2
-        for (int k = 0; k < K; ++k)
-          prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k));
-      } else {
-#pragma unroll 2
-        for (int k = 0; k < K; ++k)
-          prev = set_lane(prev, k, ids.count_key_below(__builtin_amdgcn_readlane(thr, k)));
-      }
+      const int prev = K == 8 ? token_counts<8>(ids, thr, K, pbeg, ll)
+                              : token_counts<0>(ids, thr, K, pbeg, ll);
       if (lane < K) atomicAdd(&s_pre[lane], prev);
     }
     lds_barrier();
