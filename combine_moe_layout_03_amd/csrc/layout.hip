@@ -231,19 +231,25 @@ __global__ __launch_bounds__(64) void layout_prefix_kernel(LayoutParams p) {
   const int lane = lane_id(), nb = p.nblocks;
   const int g = blockIdx.x;
   if (g < p.E) {
+    // kPrefixLoads counts per lane are requested before the first is scanned
+    // (one load latency per 64 * kPrefixLoads blocks), each 64 by a DPP scan
+    constexpr int kPrefixLoads = 4;
     int32_t *h = p.ws_hist + (int64_t)g * nb;
     int carry = 0;
-    for (int b0 = 0; b0 < nb; b0 += 64) {
-      const int b = b0 + lane;
-      const int c = b < nb ? h[b] : 0;
-      int x = c;
+    for (int b0 = 0; b0 < nb; b0 += 64 * kPrefixLoads) {
+      int c[kPrefixLoads];
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
+      for (int j = 0; j < kPrefixLoads; ++j) {
+        const int b = b0 + 64 * j + lane;
+        c[j] = b < nb ? h[b] : 0;
       }
-      if (b < nb) h[b] = carry + x - c;
-      carry += __shfl(x, 63, 64);
+#pragma unroll
+      for (int j = 0; j < kPrefixLoads; ++j) {
+        const int b = b0 + 64 * j + lane;
+        const int x = wave_inclusive_sum(c[j]);
+        if (b < nb) h[b] = carry + x - c[j];
+        carry += __builtin_amdgcn_readlane(x, 63);
+      }
     }
     if (lane == 0) p.ws_cnt[g] = carry;
   } else if (p.rank_token_count) {
@@ -269,6 +275,13 @@ __global__ __launch_bounds__(kFixupThreads) void layout_fixup_kernel(LayoutParam
   __shared__ int32_t s_wave[kFixupThreads / 64];
   const int tid = threadIdx.x, E = p.E, R = p.R;
   const bool contiguous = p.mode == kModeContiguous;
+  // this thread's pair: its id and in-block rank are requested first, so they
+  // arrive while the expert totals are scanned (address clamped into the batch)
+  const int64_t i = (int64_t)blockIdx.x * kFixupThreads + tid;
+  const int64_t n = (int64_t)p.T * p.K;
+  const int64_t ic = i < n ? i : n - 1;
+  const int64_t v = p.idx[ic];
+  const int32_t local = p.slot[ic];
   // aligned exclusive scan over experts (E/256 consecutive experts per thread)
   const int per = (E + kFixupThreads - 1) / kFixupThreads;
   const int e0 = tid * per;
@@ -317,14 +330,11 @@ __global__ __launch_bounds__(kFixupThreads) void layout_fixup_kernel(LayoutParam
     }
   }
 
-  const int64_t i = (int64_t)blockIdx.x * kFixupThreads + tid;
-  const int64_t n = (int64_t)p.T * p.K;
   if (i < n) {
-    const int64_t v = p.idx[i];
     if (v >= 0 && v < E) {  // other pairs already hold slot -1
       const int e = (int)v;
       const int b = (int)((i / p.K) / p.tokens_per_block);
-      const int j = p.ws_hist[(int64_t)e * p.nblocks + b] + p.slot[i];
+      const int j = p.ws_hist[(int64_t)e * p.nblocks + b] + local;
       if (contiguous) {
         const int s = s_base[e] + j;
         p.slot[i] = s;
