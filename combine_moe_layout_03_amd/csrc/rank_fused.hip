@@ -64,12 +64,17 @@ struct LaneTokens {
 
   // request the ids (addresses clamped into the routing; T >= 1)
   __device__ __forceinline__ void issue(const RankFusedParams &p) {
+    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
       const int t = min(i * kRfThreads + (int)threadIdx.x, p.T - 1);
       const int64_t *row = p.idx + (int64_t)t * p.K;
 #pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) raw[i][k] = row[min(k, p.K - 1)];
+      for (int k = 0; k < kRfMaxK; ++k) {
+        raw[i][k] = -1;
+        // waves whose lanes hold no token (and ids past K) request nothing
+        if (i * kRfThreads + w0 < p.T && k < p.K) raw[i][k] = row[k];
+      }
     }
     // every id load stays ahead of whatever the caller issues next (a row load)
     __builtin_amdgcn_sched_barrier(0);
