@@ -88,10 +88,14 @@ struct LaneIds {
   int64_t raw[kRounds];
   int any[kRounds], below[kRounds], key[kRounds];
 
-  // request the ids; nothing waits for them here
-  __device__ __forceinline__ void issue(const int64_t *idx, int P, int nthreads) {
+  // request the ids of rounds r < nr (the rest read as "no id"); nothing
+  // waits for them here
+  __device__ __forceinline__ void issue(const int64_t *idx, int P, int nthreads, int nr = kRounds) {
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) raw[r] = idx[min(r * nthreads + (int)threadIdx.x, P - 1)];
+    for (int r = 0; r < kRounds; ++r) {
+      raw[r] = -1;
+      if (r == 0 || r < nr) raw[r] = idx[min(r * nthreads + (int)threadIdx.x, P - 1)];
+    }
     // every id load stays ahead of whatever the caller issues next (a row load)
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -124,11 +128,12 @@ struct LaneIds {
   // pairs whose key lies in [lo, lo + width) (one unsigned compare each): with
   // lo = e * P and width = i, the pairs of e before pair i -- its row in e's
   // low-latency stripe
-  __device__ __forceinline__ int count_keys_in(int lo, int width) const {
+  __device__ __forceinline__ int count_keys_in(int lo, int width, int nr = kRounds) const {
     int n = 0;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r)
-      n += __popcll(__ballot((uint32_t)key[r] - (uint32_t)lo < (uint32_t)width));
+      if (r == 0 || r < nr)  // (round 0 always counts)
+        n += __popcll(__ballot((uint32_t)key[r] - (uint32_t)lo < (uint32_t)width));
     return n;
   }
   // pairs whose key is below k: with k = e * P + i, the valid pairs with an id
@@ -246,13 +251,13 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 // the K lane reads, compares and ballots issue back to back.
 template <int KT, int kRounds>
 __device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr, int Kr,
-                                            int pbeg, bool ll) {
+                                            int pbeg, bool ll, int nr) {
   const int K = KT ? KT : Kr;
   int prev = 0;
   if (ll) {
 #pragma unroll
     for (int k = 0; k < K; ++k)
-      prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k));
+      prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k, nr));
   } else {
 #pragma unroll
     for (int k = 0; k < K; ++k)
@@ -291,7 +296,11 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
 
     // 1. the routing first ...
     LaneIds<kRounds> ids;
-    if (counting) ids.issue(p.idx, P, nthreads);
+    // A stripe row counts earlier pairs only, so in the low-latency layout
+    // the ids past this token's pairs are neither requested nor counted (on
+    // average half the routing); a contiguous slot counts every pair.
+    const int nr = ll ? (pbeg + K + nthreads - 1) / nthreads : kRounds;
+    if (counting) ids.issue(p.idx, P, nthreads, nr);
     //    Every wave's id loads leave before any wave's row load (a barrier
     //    with no memory wait). Without it the routing reached a workgroup's
     //    last wave 0.5 us after its first -- id loads issued after another
@@ -325,8 +334,8 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       // slot counts the keys below); low latency: e * P (its row counts the
       // keys in [e * P, e * P + pair index)) -- so one lane read per k
       const int thr = tokv * P + (ll ? 0 : pbeg + lane);
-      const int prev = K == 8 ? token_counts<8>(ids, thr, K, pbeg, ll)
-                              : token_counts<0>(ids, thr, K, pbeg, ll);
+      const int prev = K == 8 ? token_counts<8>(ids, thr, K, pbeg, ll, nr)
+                              : token_counts<0>(ids, thr, K, pbeg, ll, nr);
       if (lane < K) atomicAdd(&s_pre[lane], prev);
     }
     lds_barrier();
