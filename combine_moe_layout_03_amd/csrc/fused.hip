@@ -249,6 +249,13 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
 // Lane k < K: pair (pbeg + k)'s count over the wave's ids, thr holding its
 // threshold key in lane k (see the kernel). KT > 0 fixes K at compile time so
 // the K lane reads, compares and ballots issue back to back.
+// v with lane j (a compile-time constant) replaced by the wave-uniform x
+template <int j>
+__device__ __forceinline__ int write_lane(int v, int x) {
+  asm("v_writelane_b32 %0, %1, %2" : "=v"(v) : "s"(x), "i"(j), "0"(v));
+  return v;
+}
+
 template <int KT, int kRounds>
 __device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr, int Kr,
                                             int pbeg, bool ll, int nr) {
@@ -263,6 +270,33 @@ __device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr
     for (int k = 0; k < K; ++k)
       prev = set_lane(prev, k, ids.count_key_below(__builtin_amdgcn_readlane(thr, k)));
   }
+  return prev;
+}
+
+// The same for K = 8, written so the eight thresholds are read first and each
+// count lands in its lane with one v_writelane.
+template <int kRounds>
+__device__ __forceinline__ int token_counts8(const LaneIds<kRounds> &ids, int thr, int pbeg,
+                                             bool ll, int nr) {
+  int th[8], n[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) th[k] = __builtin_amdgcn_readlane(thr, k);
+  if (ll) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) n[k] = ids.count_keys_in(th[k], pbeg + k, nr);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) n[k] = ids.count_key_below(th[k]);
+  }
+  int prev = 0;
+  prev = write_lane<0>(prev, n[0]);
+  prev = write_lane<1>(prev, n[1]);
+  prev = write_lane<2>(prev, n[2]);
+  prev = write_lane<3>(prev, n[3]);
+  prev = write_lane<4>(prev, n[4]);
+  prev = write_lane<5>(prev, n[5]);
+  prev = write_lane<6>(prev, n[6]);
+  prev = write_lane<7>(prev, n[7]);
   return prev;
 }
 
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       // slot counts the keys below); low latency: e * P (its row counts the
       // keys in [e * P, e * P + pair index)) -- so one lane read per k
       const int thr = tokv * P + (ll ? 0 : pbeg + lane);
-      const int prev = K == 8 ? token_counts<8>(ids, thr, K, pbeg, ll, nr)
+      const int prev = K == 8 ? token_counts8(ids, thr, pbeg, ll, nr)
                               : token_counts<0>(ids, thr, K, pbeg, ll, nr);
       if (lane < K) atomicAdd(&s_pre[lane], prev);
     }
