@@ -419,12 +419,33 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       }
     } else if (kCopy) {
       asm volatile("" : "+v"(val));
-      for (int k = 0; k < K; ++k) {
-        const int s = __builtin_amdgcn_readlane(out, k);
-        if (s >= 0 && s < f.rows) {
-          if (lane_ok) __builtin_nontemporal_store(val, f.recv + (int64_t)s * f.nvec + v);
-        } else if (s != -1 && wave == 0) {
-          st |= kStBadSlot;  // receive buffer smaller than the layout needs
+      // slots are int32, so a 32-bit unsigned compare against the row count
+      // (clamped to INT32_MAX) tells valid slots (and -1 is never valid)
+      const uint32_t rows32 = f.rows < 0x7fffffff ? (uint32_t)f.rows : 0x7fffffffu;
+      u32x4 *dst = f.recv + v;
+      if (K == 8) {  // the eight slots first, then the stores back to back
+        int sl[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sl[k] = __builtin_amdgcn_readlane(out, k);
+        if (lane_ok) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((uint32_t)sl[k] < rows32)
+              __builtin_nontemporal_store(val, dst + (int64_t)sl[k] * f.nvec);
+        }
+        if (wave == 0) {  // receive buffer smaller than the layout needs
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((uint32_t)sl[k] >= rows32 && sl[k] != -1) st |= kStBadSlot;
+        }
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int sk = __builtin_amdgcn_readlane(out, k);
+          if ((uint32_t)sk < rows32) {
+            if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)sk * f.nvec);
+          } else if (sk != -1 && wave == 0) {
+            st |= kStBadSlot;  // receive buffer smaller than the layout needs
+          }
         }
       }
     }
