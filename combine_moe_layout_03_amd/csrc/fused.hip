@@ -399,22 +399,45 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       const int grp = chunk * 4 + (lane >> 4);
       uint32_t word = 0;
       if (kFp8 & kFp8Ue8m0) word = ue8m0_word(q.scale);
-      for (int k = 0; k < K; ++k) {
-        const int s = __builtin_amdgcn_readlane(out, k);
-        if (s >= 0 && s < f.rows) {
-          const int e = __builtin_amdgcn_readlane(tokv, k);
-          const int i = s - e * f.RM;  // row within the expert's R*M rows
-          if (lane_ok) __builtin_nontemporal_store(codes, f.q + (int64_t)s * f.nvec + v);
-          if (kFp8 & kFp8Ue8m0) {
-            if (lane == 0 && lane_ok)
-              f.ue[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.nchunk + chunk
-                                          : ((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
-          } else if ((lane & 15) == 0 && lane_ok) {
-            f.scale[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.G + grp
-                                           : ((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
+      const uint32_t rows32 = f.rows < 0x7fffffff ? (uint32_t)f.rows : 0x7fffffffu;
+      // pair k's codes, and its scale (or packed UE8M0 word) by one lane per group
+      auto put = [&](int s, int e) {
+        const int i = s - e * f.RM;  // row within the expert's R*M rows
+        __builtin_nontemporal_store(codes, f.q + (int64_t)s * f.nvec + v);
+        if (kFp8 & kFp8Ue8m0) {
+          if (lane == 0)
+            f.ue[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.nchunk + chunk
+                                        : ((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
+        } else if ((lane & 15) == 0) {
+          f.scale[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.G + grp
+                                         : ((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
+        }
+      };
+      if (K == 8) {  // the eight slots and experts first, then the stores back to back
+        int sl[8], ex[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          sl[k] = __builtin_amdgcn_readlane(out, k);
+          ex[k] = __builtin_amdgcn_readlane(tokv, k);
+        }
+        if (lane_ok) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((uint32_t)sl[k] < rows32) put(sl[k], ex[k]);
+        }
+        if (wave == 0) {  // receive buffer smaller than the layout needs
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((uint32_t)sl[k] >= rows32 && sl[k] != -1) st |= kStBadSlot;
+        }
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int sk = __builtin_amdgcn_readlane(out, k);
+          if ((uint32_t)sk < rows32) {
+            if (lane_ok) put(sk, __builtin_amdgcn_readlane(tokv, k));
+          } else if (sk != -1 && wave == 0) {
+            st |= kStBadSlot;  // receive buffer smaller than the layout needs
           }
-        } else if (s != -1 && wave == 0) {
-          st |= kStBadSlot;  // receive buffer smaller than the layout needs
         }
       }
     } else if (kCopy) {
