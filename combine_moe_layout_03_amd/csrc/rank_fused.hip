@@ -231,14 +231,33 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
     row = -1;
   }
 
-  // 7. the row chunk, once per rank reached
+  // 7. the row chunk, once per rank reached (row -1 for the others; rows are
+  //    int32, so one unsigned compare against the clamped row count)
   asm volatile("" : "+v"(val));
-  for (uint64_t rest = mt; rest; rest &= rest - 1ull) {
-    const int s = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)rest) - 1);
-    if (s >= 0 && s < p.rows) {
-      if (lane_ok) __builtin_nontemporal_store(val, p.recv + (int64_t)s * p.nvec + v);
-    } else if (s != -1 && lead && wave == 0) {
-      st |= kStBadSlot;  // receive buffer smaller than the layout needs
+  const uint32_t rows32 = p.rows < 0x7fffffff ? (uint32_t)p.rows : 0x7fffffffu;
+  u32x4 *dst = p.recv + v;
+  if (p.R == 8) {  // the eight rows first, then the stores back to back
+    int sl[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) sl[r] = __builtin_amdgcn_readlane(row, r);
+    if (lane_ok) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if ((uint32_t)sl[r] < rows32) __builtin_nontemporal_store(val, dst + (int64_t)sl[r] * p.nvec);
+    }
+    if (lead && wave == 0) {  // receive buffer smaller than the layout needs
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if ((uint32_t)sl[r] >= rows32 && sl[r] != -1) st |= kStBadSlot;
+    }
+  } else {
+    for (uint64_t rest = mt; rest; rest &= rest - 1ull) {
+      const int s = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)rest) - 1);
+      if ((uint32_t)s < rows32) {
+        if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)s * p.nvec);
+      } else if (s != -1 && lead && wave == 0) {
+        st |= kStBadSlot;  // receive buffer smaller than the layout needs
+      }
     }
   }
 
