@@ -16,21 +16,26 @@
 // its rows back, lanes 0..Kw-1, loaded alongside the rows.
 //
 // Both are HBM-bound streams with no data reuse, so the design is about
-// bytes in flight: a thread owns one 16-byte vector (8 bf16) of one token row,
-// a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors -- 1792
-// waves at 128 x 7168, seven per CU (dispatch in 4-wave workgroups, combine in
-// 1-wave workgroups, each measured best). Dispatch reads its
-// vector once and issues K 16-byte stores (non-temporal: the receive rows are
-// not re-read by this kernel). Combine issues all K 16-byte loads of a vector
-// before it sums, so K requests per lane are in flight at once, then adds in
-// ascending k in f32 with no fused multiply-add and rounds once to bf16
-// (round to nearest even, NaN -> 0x7FC0), stored non-temporally.
+// bytes in flight. Dispatch: a thread owns one 16-byte vector (8 bf16) of one
+// token row, a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors
+// -- 1792 waves at 128 x 7168, seven per CU, in 4-wave workgroups; it reads
+// its vector once and issues K 16-byte stores (non-temporal: the receive rows
+// are not re-read by this kernel). Combine: a thread owns 8 bytes (4 bf16), a
+// wave covers 512 bytes of a row, one wave per workgroup -- 3584 waves at
+// 128 x 7168. (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
+// 9.50 / 178 us, 8-byte lanes 9.31 / 171 us, 4-byte lanes 9.30 / 183 us; two
+// 16-byte vectors per lane 10.0 us: more waves hide more of the gather
+// latency.) It issues all K loads of its lane before it sums, so K requests
+// per lane are in flight at once, then adds in ascending k in f32 with no
+// fused multiply-add and rounds once to bf16 (round to nearest even, NaN ->
+// 0x7FC0), stored non-temporally.
 #include "wave.hpp"
 
 namespace moe {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -84,26 +89,32 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
-template <int KT, bool kWeights, bool kF32Out, bool kMask, bool kWsum>
-__global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ y, int64_t rows,
-                                                      const int32_t *__restrict__ slot,
-                                                      const float *__restrict__ w,
-                                                      u32x4 *__restrict__ out,
-                                                      f32x4 *__restrict__ out_f32, int32_t T,
-                                                      int32_t Kr, int32_t nvec, int32_t nchunk,
-                                                      CombineMask cm, RowWeightSum ws,
-                                                      int32_t *status) {
+// A lane of kDw dwords (2: 8 bytes, 4 bf16; 4: 16 bytes, 8 bf16).
+template <int kDw> struct Lane;
+template <> struct Lane<2> { typedef u32x2 T; };
+template <> struct Lane<4> { typedef u32x4 T; };
+
+template <int KT, bool kWeights, bool kF32Out, bool kMask, bool kWsum, int kDw>
+__global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T *__restrict__ y,
+                                                     int64_t rows, const int32_t *__restrict__ slot,
+                                                     const float *__restrict__ w,
+                                                     typename Lane<kDw>::T *__restrict__ out,
+                                                     f32x4 *__restrict__ out_f32, int32_t T,
+                                                     int32_t Kr, int32_t nq, int32_t nchunk,
+                                                     CombineMask cm, RowWeightSum ws,
+                                                     int32_t *status) {
 #pragma clang fp contract(off)
+  typedef typename Lane<kDw>::T VT;
   const int K = KT ? KT : Kr;
   int t;
-  const int v = wave_token_chunk(nchunk, t);
+  const int v = wave_token_chunk(nchunk, t);  // lane (kDw dwords) index in the row
   if (t >= T) return;
-  const bool lane_ok = v < nvec;
+  const bool lane_ok = v < nq;
   const int32_t *srow = slot + (int64_t)t * K;
   const float *wrow = kWeights ? w + (int64_t)t * K : nullptr;
-  float acc[8];
+  float acc[2 * kDw];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  for (int j = 0; j < 2 * kDw; ++j) acc[j] = 0.0f;
   int st = 0;
   // normal mode: the first wave of the token, lanes < Kw, sum the rows' weights
   const bool wsum_lane = kWsum && v < 64 && (int)(threadIdx.x & 63) < ws.Kw;
@@ -120,13 +131,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
       s[g] = in ? srow[k0 + g] : -1;
       wk[g] = (kWeights && in) ? wrow[k0 + g] : 1.0f;
     }
-    u32x4 val[G];
+    VT val[G];
     float rw[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       ok[g] = s[g] >= 0 && s[g] < rows;
-      val[g] = u32x4{0u, 0u, 0u, 0u};
-      if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nvec + v);
+      val[g] = VT(0u);
+      if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nq + v);
       rw[g] = 0.0f;
       if (kWsum && ok[g] && wsum_lane) rw[g] = ws.in[(int64_t)s[g] * ws.Kw + wl];
     }
@@ -144,31 +155,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const u32x4 *__restrict__ 
       if (!ok[g] || off[g]) continue;
       if (kWsum) wacc = wacc + rw[g];
       const float a = wk[g];
-      const u32x4 q = val[g];
-      acc[0] = acc[0] + a * bf16_lo(q.x);
-      acc[1] = acc[1] + a * bf16_hi(q.x);
-      acc[2] = acc[2] + a * bf16_lo(q.y);
-      acc[3] = acc[3] + a * bf16_hi(q.y);
-      acc[4] = acc[4] + a * bf16_lo(q.z);
-      acc[5] = acc[5] + a * bf16_hi(q.z);
-      acc[6] = acc[6] + a * bf16_lo(q.w);
-      acc[7] = acc[7] + a * bf16_hi(q.w);
+#pragma unroll
+      for (int d = 0; d < kDw; ++d) {
+        acc[2 * d] = acc[2 * d] + a * bf16_lo(val[g][d]);
+        acc[2 * d + 1] = acc[2 * d + 1] + a * bf16_hi(val[g][d]);
+      }
     }
   }
   if (kWsum && wsum_lane) ws.out[(int64_t)t * ws.Kw + wl] = wacc;
   if (lane_ok) {
-    const int64_t i = (int64_t)t * nvec + v;
-    u32x4 o;
-    o.x = to_bf16(acc[0]) | (to_bf16(acc[1]) << 16);
-    o.y = to_bf16(acc[2]) | (to_bf16(acc[3]) << 16);
-    o.z = to_bf16(acc[4]) | (to_bf16(acc[5]) << 16);
-    o.w = to_bf16(acc[6]) | (to_bf16(acc[7]) << 16);
+    const int64_t i = (int64_t)t * nq + v;
+    VT o;
+#pragma unroll
+    for (int d = 0; d < kDw; ++d) o[d] = to_bf16(acc[2 * d]) | (to_bf16(acc[2 * d + 1]) << 16);
     // non-temporal: the kernel does not read its output back (0.2 us per
     // step faster than a plain store at 128 x 7168)
     __builtin_nontemporal_store(o, out + i);
     if (kF32Out) {
-      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, out_f32 + 2 * i);
-      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, out_f32 + 2 * i + 1);
+#pragma unroll
+      for (int d = 0; d < kDw / 2; ++d)
+        __builtin_nontemporal_store(
+            f32x4{acc[4 * d], acc[4 * d + 1], acc[4 * d + 2], acc[4 * d + 3]},
+            out_f32 + (kDw / 2) * i + d);
     }
   }
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
@@ -192,13 +200,14 @@ hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, cons
                       const CombineMask &cm, int32_t *status, hipStream_t s) {
   // one wave per workgroup: measured faster than four (128 x 7168: 0.2 us per
   // step; 8192 x 7168: 2 us) -- the waves spread over the CUs evenly
-  const int32_t nchunk = (nvec + 63) / 64;
+  const int32_t nq = nvec * 2;  // 8-byte lanes per row
+  const int32_t nchunk = (nq + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
   const RowWeightSum none{nullptr, nullptr, 0};
-  hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM, false>), dim3((unsigned)waves), dim3(64), 0, s,
-                     reinterpret_cast<const u32x4 *>(y), rows, slot, w,
-                     reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
-                     nvec, nchunk, cm, none, status);
+  hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM, false, 2>), dim3((unsigned)waves), dim3(64), 0,
+                     s, reinterpret_cast<const u32x2 *>(y), rows, slot, w,
+                     reinterpret_cast<u32x2 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
+                     nq, nchunk, cm, none, status);
   return hipGetLastError();
 }
 
@@ -206,11 +215,13 @@ template <int KT, bool kF, bool kWs>
 hipError_t rank_combine_k(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
                           uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t nvec,
                           const RowWeightSum &ws, int32_t *status, hipStream_t s) {
+  // 16-byte lanes here: with the rows' weights summed back, measured faster
+  // than 8-byte lanes (128 x 7168: 4.96 vs 5.27 us)
   const int32_t nchunk = (nvec + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
   const CombineMask none{nullptr, nullptr, 0, 0};
-  hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs>), dim3((unsigned)waves), dim3(64), 0, s,
-                     reinterpret_cast<const u32x4 *>(y), rows, rank_slot, nullptr,
+  hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs, 4>), dim3((unsigned)waves), dim3(64),
+                     0, s, reinterpret_cast<const u32x4 *>(y), rows, rank_slot, nullptr,
                      reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, R,
                      nvec, nchunk, none, ws, status);
   return hipGetLastError();

@@ -71,11 +71,11 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// A wave owns 64 consecutive 16-byte vectors of one token row, so the token
-// index is wave-uniform: its K slots (and weights) arrive as scalar loads before
-// any vector memory operation, and the row's K stores or loads are issued back
-// to back without waiting on each other. Lanes past the row end (H/8 not a
-// multiple of 64) idle.
+// A wave owns 64 consecutive vectors (16 bytes in the dispatch, 8 in the
+// combine) of one token row, so the token index is wave-uniform: its K slots
+// (and weights) arrive as scalar loads before any vector memory operation, and
+// the row's K stores or loads are issued back to back without waiting on each
+// other. Lanes past the row end (vectors per row not a multiple of 64) idle.
 __device__ __forceinline__ int wave_token_chunk(int nchunk, int &t) {
   const int wid = __builtin_amdgcn_readfirstlane(
       (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
