@@ -48,12 +48,20 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int KT>
-__global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__ x,
+// A lane of kDw dwords (2: 8 bytes, 4 bf16; 4: 16 bytes, 8 bf16).
+template <int kDw> struct Lane;
+template <> struct Lane<2> { typedef u32x2 T; };
+template <> struct Lane<4> { typedef u32x4 T; };
+
+// nvec counts lanes (kDw dwords each) per row.
+template <int KT, int kDw>
+__global__ __launch_bounds__(256) void dispatch_kernel(const typename Lane<kDw>::T *__restrict__ x,
                                                        const int32_t *__restrict__ slot,
-                                                       u32x4 *__restrict__ recv, int32_t T,
-                                                       int32_t Kr, int32_t nvec, int32_t nchunk,
-                                                       int64_t rows, int32_t *status) {
+                                                       typename Lane<kDw>::T *__restrict__ recv,
+                                                       int32_t T, int32_t Kr, int32_t nvec,
+                                                       int32_t nchunk, int64_t rows,
+                                                       int32_t *status) {
+  typedef typename Lane<kDw>::T VT;
   const int K = KT ? KT : Kr;
   int t;
   const int v = wave_token_chunk(nchunk, t);
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__
   const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
   constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
-  u32x4 val = {0u, 0u, 0u, 0u};
+  VT val = VT(0u);
   if (lane_ok) val = __builtin_nontemporal_load(x + (int64_t)t * nvec + v);
   // the first group of slots is requested while the row load is in flight
   int32_t s[G];
@@ -88,11 +96,6 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const u32x4 *__restrict__
   }
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
-
-// A lane of kDw dwords (2: 8 bytes, 4 bf16; 4: 16 bytes, 8 bf16).
-template <int kDw> struct Lane;
-template <> struct Lane<2> { typedef u32x2 T; };
-template <> struct Lane<4> { typedef u32x4 T; };
 
 template <int KT, bool kWeights, bool kF32Out, bool kMask, bool kWsum, int kDw>
 __global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T *__restrict__ y,
@@ -182,13 +185,25 @@ __global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
+// Large batches copy in 8-byte lanes (twice the waves, more stores in flight:
+// 8192 x 7168 216 -> 202 us, the skewed 4096 x 4096 batch 56.3 -> 54.6 us);
+// small ones in 16-byte lanes (128 x 7168: 3.96 vs 4.06 us).
+constexpr int64_t kWideCopyWaves = 8192;  // 16-byte-lane waves from which 8-byte lanes pay
+
 template <int KT>
 hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                       int32_t K, int32_t nvec, int64_t rows, int32_t *status, hipStream_t s) {
   const int32_t nchunk = (nvec + 63) / 64;
+  if ((int64_t)T * nchunk >= kWideCopyWaves) {
+    const int32_t nq = nvec * 2, nchunk2 = (nq + 63) / 64;
+    const int64_t waves = (int64_t)T * nchunk2;
+    hipLaunchKernelGGL((dispatch_kernel<KT, 2>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
+                       reinterpret_cast<const u32x2 *>(x), slot, reinterpret_cast<u32x2 *>(recv),
+                       T, K, nq, nchunk2, rows, status);
+    return hipGetLastError();
+  }
   const int64_t waves = (int64_t)T * nchunk;
-  const unsigned blocks = (unsigned)((waves + 3) / 4);
-  hipLaunchKernelGGL(dispatch_kernel<KT>, dim3(blocks), dim3(256), 0, s,
+  hipLaunchKernelGGL((dispatch_kernel<KT, 4>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
                      reinterpret_cast<const u32x4 *>(x), slot, reinterpret_cast<u32x4 *>(recv),
                      T, K, nvec, nchunk, rows, status);
   return hipGetLastError();
