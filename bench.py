@@ -243,7 +243,8 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
     for ui, u in enumerate(unions):
         for s in range(R):
             z = dict(u=u, s=s, x=x.clone(), idx=idx.clone(), w=wt.clone(),
-                     lay=capi.LayoutBuffers.empty(shape, dev, ll_M=M, status=False),
+                     lay=capi.LayoutBuffers.empty(shape, dev, ll_M=M, status=False,
+                                                  rank_tables=False),
                      out=torch.empty(T, H, dtype=torch.int16, device=dev))
             if fp8:
                 z.update(q=qunions[ui], sc=sunions[ui])

@@ -185,7 +185,10 @@ class LayoutBuffers:
 
     @staticmethod
     def empty(shape: moe_shape, device, ll_M: Optional[int] = None, extras: bool = True,
-              status: bool = True) -> "LayoutBuffers":
+              status: bool = True, rank_tables: bool = True) -> "LayoutBuffers":
+        """extras: the optional outputs; rank_tables=False leaves out the
+        per-rank token counts and the token-rank table among them (what the
+        low-latency dispatch does not return)."""
         T, E, R, K = shape.T, shape.E, shape.R, shape.K
         i32 = dict(dtype=torch.int32, device=device)
         if ll_M is None:
@@ -196,9 +199,9 @@ class LayoutBuffers:
             count=torch.empty(E, **i32),
             offset=torch.empty(E + 1, **i32),
             slot=torch.empty(T * K, **i32),
-            rank_token_count=torch.empty(R, **i32) if extras else None,
+            rank_token_count=torch.empty(R, **i32) if extras and rank_tables else None,
             is_token_in_rank=torch.empty(T * R, dtype=torch.uint8, device=device)
-            if extras else None,
+            if extras and rank_tables else None,
             row_src=torch.empty(rows_src, **i32) if extras else None,
             status=torch.zeros(1, **i32) if status else None,
         )

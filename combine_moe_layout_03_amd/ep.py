@@ -139,7 +139,9 @@ def low_latency_dispatch(x: torch.Tensor, topk_idx: torch.Tensor,
     E, R = num_experts, num_ranks
     L = E // R
     shape = capi.make_shape(T, H, E, R, K, 1)
-    lay = capi.LayoutBuffers.empty(shape, x.device, ll_M=M)
+    # the low-latency handle: counts, slots, stripe offsets and source table
+    # (no per-rank token counts or token-rank table, as on the page)
+    lay = capi.LayoutBuffers.empty(shape, x.device, ll_M=M, rank_tables=False)
     lay.recv_stats = cumulative_local_expert_recv_stats
     rows = capi.moe_ll_recv_rows(E, R, M)
     ws = _workspace(shape, x.device)

@@ -76,6 +76,9 @@ def test_low_latency_dispatch_and_masked_combine(ep, orc, use_fp8, round_scale, 
                                            use_fp8=use_fp8, round_scale=round_scale,
                                            use_ue8m0=use_ue8m0, scale_rows=scale_rows)
     ll = orc.ll_layout(w.topk_idx, E, R, M, src)
+    # the low-latency handle carries no normal-path rank tables
+    assert h.layout.rank_token_count is None and h.layout.is_token_in_rank is None
+    assert np.array_equal(h.layout.row_src.cpu().numpy(), ll["row_src"])
     assert np.array_equal(cnt.cpu().numpy(), ll["recv_count"])
     assert np.array_equal(stats.cpu().numpy(), 10 + ll["recv_count"])
     rows = E * R * M
