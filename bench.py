@@ -91,10 +91,15 @@ def device_hbm_figures(dev_index):
 
 
 def kernel_source_hash():
+    """Hash of the measured kernels' code: comments and whitespace are left
+    out, so a comment edit does not invalidate the counter summary."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -12,8 +12,8 @@
 // The three terms together count the pairs ordered before (t, k) by the key
 // id * P + pair index, and the last two the keys in [e * P, e * P + tK + k),
 // so a workgroup that serves token t needs one count per selected expert over
-// the whole routing, one compare per id -- no histogram, no scan, no
-// cross-workgroup step.
+// the whole routing (low latency: over the pairs up to its own only), one
+// compare per id -- no histogram, no scan, no cross-workgroup step.
 // Each wave reads a few ids per lane (the routing is a few KiB and sits in
 // L2 after the first touch) and turns them into counts with ballot +
 // popcount, accumulated in scalar registers; the waves' partial counts meet
@@ -29,8 +29,9 @@
 // one token row (a 7168-wide row is two workgroups of 7 copying waves, so the
 // row stores of 128 tokens leave from all 256 CUs; every wave also counts:
 // 512 lanes read a 1024-pair routing in two rounds). It requests the routing
-// first and the row second, derives its K slots while the (cold) row is still
-// in flight, then stores the row K times -- as
+// first (every wave's, before any wave's row load) and the row second, derives
+// its K slots while the (cold) row is still in flight, then stores the row K
+// times, back to back -- as
 // bf16, or (low-latency FP8 dispatch) cast once to E4M3 with per-128-channel
 // scales (fp8.hpp) and stored as codes plus column-major (or row-major)
 // scales.
