@@ -532,8 +532,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not "
-                          "supported (the multi-GPU path is a design note, not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU: the logical ranks are "
+                          "partitions of one GPU's memory, so --gpus above 1 is not supported"}))
         sys.exit(2)
 
     import numpy as np
