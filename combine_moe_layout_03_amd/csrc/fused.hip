@@ -178,7 +178,8 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
     }
   }
   const int ndx = d < E ? (E - 1 - d) / D + 1 : 0;
-  const int ndr = d < R ? (R - 1 - d) / D + 1 : 0;
+  // (ranks only when their token counts are asked for)
+  const int ndr = (d < R && p.rank_token_count) ? (R - 1 - d) / D + 1 : 0;
   int cv = 0, lv = 0;  // lane j holds duty j's counts
   for (int j = 0; j < ndx; ++j) {
     const int ed = d + j * D;
