@@ -253,9 +253,6 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
   }
 }
 
-// Lane k < K: pair (pbeg + k)'s count over the wave's ids, thr holding its
-// threshold key in lane k (see the kernel). KT > 0 fixes K at compile time so
-// the K lane reads, compares and ballots issue back to back.
 // v with lane j (a compile-time constant) replaced by the wave-uniform x
 template <int j>
 __device__ __forceinline__ int write_lane(int v, int x) {
@@ -263,17 +260,16 @@ __device__ __forceinline__ int write_lane(int v, int x) {
   return v;
 }
 
-template <int KT, int kRounds>
-__device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr, int Kr,
+// Lane k < K: pair (pbeg + k)'s count over the wave's ids, thr holding its
+// threshold key in lane k (see the kernel).
+template <int kRounds>
+__device__ __forceinline__ int token_counts(const LaneIds<kRounds> &ids, int thr, int K,
                                             int pbeg, bool ll, int nr) {
-  const int K = KT ? KT : Kr;
   int prev = 0;
   if (ll) {
-#pragma unroll
     for (int k = 0; k < K; ++k)
       prev = set_lane(prev, k, ids.count_keys_in(__builtin_amdgcn_readlane(thr, k), pbeg + k, nr));
   } else {
-#pragma unroll
     for (int k = 0; k < K; ++k)
       prev = set_lane(prev, k, ids.count_key_below(__builtin_amdgcn_readlane(thr, k)));
   }
@@ -376,7 +372,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
       // keys in [e * P, e * P + pair index)) -- so one lane read per k
       const int thr = tokv * P + (ll ? 0 : pbeg + lane);
       const int prev = K == 8 ? token_counts8(ids, thr, pbeg, ll, nr)
-                              : token_counts<0>(ids, thr, K, pbeg, ll, nr);
+                              : token_counts(ids, thr, K, pbeg, ll, nr);
       if (lane < K) atomicAdd(&s_pre[lane], prev);
     }
     lds_barrier();
