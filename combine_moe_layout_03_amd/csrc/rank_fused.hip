@@ -70,10 +70,23 @@ struct LaneTokens {
       const int t = min(i * kRfThreads + (int)threadIdx.x, p.T - 1);
       const int64_t *row = p.idx + (int64_t)t * p.K;
 #pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) {
-        raw[i][k] = -1;
-        // waves whose lanes hold no token (and ids past K) request nothing
-        if (i * kRfThreads + w0 < p.T && k < p.K) raw[i][k] = row[k];
+      for (int k = 0; k < kRfMaxK; ++k) raw[i][k] = -1;
+      // waves whose lanes hold no token (and ids past K) request nothing
+      if (i * kRfThreads + w0 < p.T) {
+        if (p.K == kRfMaxK) {  // the token's 64-byte row in four 16-byte loads
+          typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
+          const i64x2 *row2 = reinterpret_cast<const i64x2 *>(row);
+#pragma unroll
+          for (int k = 0; k < kRfMaxK / 2; ++k) {
+            const i64x2 q = row2[k];
+            raw[i][2 * k] = q.x;
+            raw[i][2 * k + 1] = q.y;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < kRfMaxK; ++k)
+            if (k < p.K) raw[i][k] = row[k];
+        }
       }
     }
     // every id load stays ahead of whatever the caller issues next (a row load)
