@@ -18,11 +18,12 @@
 // Both are HBM-bound streams with no data reuse, so the design is about
 // bytes in flight. Dispatch: a thread owns one 16-byte vector (8 bf16) of one
 // token row, a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors
-// -- 1792 waves at 128 x 7168, seven per CU, in 4-wave workgroups; it reads
-// its vector once and issues K 16-byte stores (non-temporal: the receive rows
-// are not re-read by this kernel). Combine: a thread owns 8 bytes (4 bf16), a
-// wave covers 512 bytes of a row, one wave per workgroup -- 3584 waves at
-// 128 x 7168. (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
+// -- 1792 waves at 128 x 7168, seven per CU, in 4-wave workgroups (large
+// batches: 8-byte lanes, see dispatch_k); it reads its vector once and issues
+// K stores (non-temporal: the receive rows are not re-read by this kernel).
+// Combine: a thread owns 8 bytes (4 bf16), a wave covers 512 bytes of a row,
+// one wave per workgroup -- 3584 waves at 128 x 7168 (the normal-mode sum
+// keeps 16-byte lanes). (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
 // 9.50 / 178 us, 8-byte lanes 9.31 / 171 us, 4-byte lanes 9.30 / 183 us; two
 // 16-byte vectors per lane 10.0 us: more waves hide more of the gather
 // latency.) It issues all K loads of its lane before it sums, so K requests
