@@ -96,6 +96,9 @@ CASES = {
     "rand_bad_ids": lambda: mi.random_case(20, 100, 64, 32, 4, 4, 1, bad_frac=0.1),
     "rand_T1": lambda: mi.random_case(21, 1, 7168, 256, 8, 8, 1, distinct=True),
     "rand_hot_expert": lambda: _hot(mi.random_case(22, 3000, 64, 64, 8, 6, 1), 5, 0.9),
+    # 8200 row chunks of 1 KiB: the scatter's 8-byte lanes, a ragged last
+    # chunk (250 lanes a row) and K = 3 (no compile-time K)
+    "rand_wide_copy_ragged": lambda: mi.random_case(27, 4100, 1000, 64, 8, 3, 1, neg_frac=0.02),
 }
 
 
