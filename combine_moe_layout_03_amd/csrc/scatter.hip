@@ -22,8 +22,7 @@
 // batches: 8-byte lanes, see dispatch_k); it reads its vector once and issues
 // K stores (non-temporal: the receive rows are not re-read by this kernel).
 // Combine: a thread owns 8 bytes (4 bf16), a wave covers 512 bytes of a row,
-// one wave per workgroup -- 3584 waves at 128 x 7168 (the normal-mode sum
-// keeps 16-byte lanes). (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
+// one wave per workgroup -- 3584 waves at 128 x 7168. (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
 // 9.50 / 178 us, 8-byte lanes 9.31 / 171 us, 4-byte lanes 9.30 / 183 us; two
 // 16-byte vectors per lane 10.0 us: more waves hide more of the gather
 // latency.) It issues all K loads of its lane before it sums, so K requests
@@ -120,8 +119,13 @@ __global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T
 #pragma unroll
   for (int j = 0; j < 2 * kDw; ++j) acc[j] = 0.0f;
   int st = 0;
-  // normal mode: the first wave of the token, lanes < Kw, sum the rows' weights
-  const bool wsum_lane = kWsum && v < 64 && (int)(threadIdx.x & 63) < ws.Kw;
+  // normal mode: the first wave of the token (lanes < Kw) sums the rows'
+  // weights. Every lane of that wave loads (lanes past Kw repeat the last
+  // entry): a load under a per-lane condition makes the compiler merge its
+  // result, i.e. wait for it, before the next row load goes out (0.9 us per
+  // step here).
+  const bool wsum_wave = kWsum && v < 64;  // uniform: chunk 0
+  const bool wsum_lane = wsum_wave && (int)(threadIdx.x & 63) < ws.Kw;
   const int wl = kWsum ? min((int)(threadIdx.x & 63), ws.Kw - 1) : 0;
   float wacc = 0.0f;
   constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
@@ -137,13 +141,26 @@ __global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T
     }
     VT val[G];
     float rw[G];
+    // With the weight sum, loads under uniform branches only (lanes past the
+    // row end re-read its last lane, the same cache line, and store nothing):
+    // there a per-lane condition made the compiler wait between the loads.
+    // Without it the per-lane form measured slightly faster.
+    const int vc = lane_ok ? v : nq - 1;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       ok[g] = s[g] >= 0 && s[g] < rows;
       val[g] = VT(0u);
-      if (ok[g] && lane_ok) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nq + v);
+      if (kWsum) {
+        if (ok[g]) val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nq + vc);
+      } else if (ok[g] && lane_ok) {
+        val[g] = __builtin_nontemporal_load(y + (int64_t)s[g] * nq + v);
+      }
+    }
+    // the rows' weights after all row loads are out
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
       rw[g] = 0.0f;
-      if (kWsum && ok[g] && wsum_lane) rw[g] = ws.in[(int64_t)s[g] * ws.Kw + wl];
+      if (kWsum && ok[g] && wsum_wave) rw[g] = ws.in[(int64_t)s[g] * ws.Kw + wl];
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {  // masked ranks (scalar reads, rows already in flight)
@@ -231,15 +248,15 @@ template <int KT, bool kF, bool kWs>
 hipError_t rank_combine_k(const uint16_t *y, int64_t rows, const int32_t *rank_slot,
                           uint16_t *out, float *out_f32, int32_t T, int32_t R, int32_t nvec,
                           const RowWeightSum &ws, int32_t *status, hipStream_t s) {
-  // 16-byte lanes here: with the rows' weights summed back, measured faster
-  // than 8-byte lanes (128 x 7168: 4.96 vs 5.27 us)
-  const int32_t nchunk = (nvec + 63) / 64;
+  // 8-byte lanes, as the weighted combine (128 x 7168: 4.07 us; 16-byte lanes
+  // 4.18 us)
+  const int32_t nq = nvec * 2, nchunk = (nq + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
   const CombineMask none{nullptr, nullptr, 0, 0};
-  hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs, 4>), dim3((unsigned)waves), dim3(64),
-                     0, s, reinterpret_cast<const u32x4 *>(y), rows, rank_slot, nullptr,
-                     reinterpret_cast<u32x4 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, R,
-                     nvec, nchunk, none, ws, status);
+  hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs, 2>), dim3((unsigned)waves), dim3(64),
+                     0, s, reinterpret_cast<const u32x2 *>(y), rows, rank_slot, nullptr,
+                     reinterpret_cast<u32x2 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, R,
+                     nq, nchunk, none, ws, status);
   return hipGetLastError();
 }
 
