@@ -138,7 +138,7 @@ struct LaneIds {
     int n = 0;
 #pragma unroll
     for (int r = 0; r < kRounds; ++r)
-      if (r == 0 || r < nr)  // (round 0 always counts)
+      if (r == 0 || r < nr)  // (the first load round always counts)
         n += __popcll(__ballot((uint32_t)key[r] - (uint32_t)lo < (uint32_t)width));
     return n;
   }
