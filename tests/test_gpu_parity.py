@@ -164,7 +164,8 @@ def _gpu_rows_check(recv_t, x_t, slot, T, K):
 
 def test_c5_replica_path_full(capi, orc):
     """Replica workload at full size: reroute + layout + dispatch + combine;
-    combine equals the unreplicated path bit for bit."""
+    the combine of all 8192 tokens matches the oracle, and equals the
+    unreplicated path bit for bit."""
     w = mi.config_c5()
     _announce("c5 replica full size")
     C_ = w.replicas
@@ -203,12 +204,12 @@ def test_c5_replica_path_full(capi, orc):
     capi.moe_combine(shape, recv_t, rows, lay.slot, wt, out, o32, lay.status)
     torch.cuda.synchronize()
     _gpu_rows_check(recv_t, x_t, ref["slot"], w.T, w.K)
-    # sampled tokens against the oracle's own dispatch of the physical layout
+    # every token against the oracle's own dispatch of the physical layout:
+    # bf16 and f32 bit-exact against its f32 ascending-k sum, and within the
+    # 1e-2 / 1e-3 tolerance of its f64 sum
     rref, _ = orc.dispatch(w.x, ref["slot"], rows)
-    rng = np.random.default_rng(0)
-    toks = np.unique(np.concatenate([rng.choice(w.T, 512, replace=False), [0, w.T - 1]]))
-    check_combine(orc, np16(out), o32.cpu().numpy(), rref, ref["slot"], w.topk_weights,
-                  tokens=toks)
+    check_combine(orc, np16(out), o32.cpu().numpy(), rref, ref["slot"], w.topk_weights)
+    del rref
     # the unreplicated path gives the same bits
     sh2 = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
     lay2 = capi.LayoutBuffers.empty(sh2, dev())
