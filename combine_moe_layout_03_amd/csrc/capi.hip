@@ -47,6 +47,7 @@ int bits_for(int n) {  // bits needed to tell apart the values 0 .. n-1
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+bool aligned8(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 // FP8 flag set and the hidden sizes it needs: scales cover 128 channels, and
 // UE8M0 words pack four of them (and require power-of-two scales).
@@ -104,6 +105,7 @@ int layout_params(const moe_shape *s, int mode, int32_t M, int32_t src, const in
   if (!out || !out->count || (s->T > 0 && !out->slot)) return MOE_ERR_NULL;
   if (mode == kModeContiguous && !out->offset) return MOE_ERR_NULL;
   if (s->T > 0 && !idx) return MOE_ERR_NULL;
+  if (!aligned8(idx)) return MOE_ERR_ALIGN;
   if (mode == kModeLowLatency) {
     if (M < 1 || s->T > M || src < 0 || src >= s->R) return MOE_ERR_LL;
     if ((int64_t)s->E * s->R * M >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
@@ -213,7 +215,7 @@ MOE_API const char *moe_strerror(int code) {
     case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
     case MOE_ERR_CAPACITY: return "receive buffer size is invalid";
     case MOE_ERR_LL: return "low latency: T > M or src_rank outside [0, R)";
-    case MOE_ERR_ALIGN: return "a row pointer is not 16-byte aligned";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned as required (rows 16 bytes, ids 8)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
     case MOE_ERR_ARCH: return "current device is not gfx950";
@@ -340,6 +342,7 @@ MOE_API int moe_expert_load(int32_t T, int32_t K, int32_t E, const int64_t *topk
   if (T < 0 || K < 1 || K > 64 || E < 1 || E > kMaxExperts) return MOE_ERR_SHAPE;
   if ((int64_t)T * K >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (!load || (T > 0 && !topk_idx)) return MOE_ERR_NULL;
+  if (!aligned8(topk_idx)) return MOE_ERR_ALIGN;
   int rc = check_device();
   if (rc) return rc;
   return launch_expert_load(topk_idx, T, K, E, bits_for(E), load, status, stream) == hipSuccess
@@ -391,7 +394,8 @@ MOE_API int moe_combine_masked(const moe_shape *shape, const uint16_t *y, int64_
   if (recv_rows < 0) return MOE_ERR_CAPACITY;
   if (shape->T == 0) return MOE_OK;
   if (!slot || !out || !topk_idx || !rank_mask || (!y && recv_rows > 0)) return MOE_ERR_NULL;
-  if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32)) return MOE_ERR_ALIGN;
+  if (!aligned16(y) || !aligned16(out) || !aligned16(out_f32) || !aligned8(topk_idx))
+    return MOE_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   const uint64_t L = (uint64_t)(shape->E / shape->R);
@@ -416,6 +420,7 @@ MOE_API int moe_rank_layout(const moe_shape *shape, const int64_t *topk_idx,
   if (!out || !out->rank_offset || (shape->T > 0 && !out->rank_slot)) return MOE_ERR_NULL;
   if (shape->T > 0 && !topk_idx) return MOE_ERR_NULL;
   if (out->recv_topk_weights && !topk_weights && shape->T > 0) return MOE_ERR_NULL;
+  if (!aligned8(topk_idx)) return MOE_ERR_ALIGN;
   if (recv_cap < 0) return MOE_ERR_CAPACITY;
   rc = check_device();
   if (rc) return rc;
@@ -458,7 +463,7 @@ MOE_API int moe_rank_layout_dispatch(const moe_shape *shape, const int64_t *topk
   if (out->recv_topk_weights && !topk_weights && shape->T > 0) return MOE_ERR_NULL;
   if (recv_cap < 0 || recv_rows < 0) return MOE_ERR_CAPACITY;
   if (shape->T > 0 && (!x || (!recv_x && recv_rows > 0))) return MOE_ERR_NULL;
-  if (!aligned16(x) || !aligned16(recv_x)) return MOE_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(recv_x) || !aligned8(topk_idx)) return MOE_ERR_ALIGN;
   rc = check_device();
   if (rc) return rc;
   hipError_t e;
@@ -563,6 +568,7 @@ MOE_API int moe_reroute(int32_t T, int32_t K, int32_t E, const int64_t *topk_idx
   if ((int64_t)T * K >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
   if (T == 0) return MOE_OK;
   if (!topk_idx || !replica_count || !replica_phys || !phys_idx) return MOE_ERR_NULL;
+  if (!aligned8(topk_idx) || !aligned8(phys_idx)) return MOE_ERR_ALIGN;
   int rc = check_device();
   if (rc) return rc;
   return launch_reroute(T, K, E, topk_idx, replica_count, replica_phys, E_phys, phys_idx, status,

@@ -35,6 +35,7 @@ struct RankFusedParams {
   const int64_t *idx;  // [T*K]
   const float *w;      // [T*K] may be null
   int32_t T, K, E, R, L, A;
+  int32_t vec_ids;  // K == 8 and idx 16-byte aligned: a token's ids in four 16-byte loads
   uint64_t l_magic;
   int32_t *rank_slot;    // [T*R]
   int32_t *rank_offset;  // [R+1]
@@ -73,7 +74,7 @@ struct LaneTokens {
       for (int k = 0; k < kRfMaxK; ++k) raw[i][k] = -1;
       // waves whose lanes hold no token (and ids past K) request nothing
       if (i * kRfThreads + w0 < p.T) {
-        if (p.K == kRfMaxK) {  // the token's 64-byte row in four 16-byte loads
+        if (p.vec_ids) {  // the token's 64-byte row in four 16-byte loads
           typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
           const i64x2 *row2 = reinterpret_cast<const i64x2 *>(row);
 #pragma unroll
@@ -382,6 +383,8 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   p.R = R;
   p.L = E / R;
   p.A = A;
+  // (a routing view that starts at an odd int64 takes one load per id)
+  p.vec_ids = K == kRfMaxK && (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;
   p.l_magic = ((1ull << 32) + (uint64_t)p.L - 1) / (uint64_t)p.L;
   p.rank_slot = rank_slot;
   p.rank_offset = rank_offset;

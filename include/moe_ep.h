@@ -34,7 +34,10 @@
  *  - Row-major layouts everywhere. bf16 values travel as raw 16-bit patterns
  *    (uint16_t). Pointers to bf16 rows, f32 rows and the receive buffer must be
  *    16-byte aligned, and H must be a multiple of 8 (one 16-byte vector is
- *    8 bf16 values).
+ *    8 bf16 values). Routing pointers (topk_idx, phys_idx: int64) must be
+ *    8-byte aligned; MOE_ERR_ALIGN otherwise. (A 16-byte aligned routing lets
+ *    some kernels read a token's ids as 16-byte vectors; an 8-byte aligned one
+ *    that is not 16-byte aligned is read one id at a time, same results.)
  *  - Limits: 1 <= E <= 1024, 1 <= R, E % R == 0, 1 <= K <= 64,
  *    0 <= T, T*K + E*(A-1) < 2^31, 8 <= H <= 2^20, 1 <= A <= 2^16.
  */
@@ -58,7 +61,8 @@ extern "C" {
 #define MOE_ERR_SHAPE (-2)     /* a size is out of range or inconsistent */
 #define MOE_ERR_CAPACITY (-3)  /* receive buffer smaller than the worst case */
 #define MOE_ERR_LL (-4)        /* low latency: T > M, or src_rank not in [0, R) */
-#define MOE_ERR_ALIGN (-5)     /* a row pointer is not 16-byte aligned */
+#define MOE_ERR_ALIGN (-5)     /* a row pointer is not 16-byte aligned, or an id pointer
+                                  not 8-byte aligned */
 #define MOE_ERR_WORKSPACE (-6) /* workspace missing or smaller than required */
 #define MOE_ERR_LAUNCH (-7)    /* the HIP runtime refused a kernel launch */
 #define MOE_ERR_ARCH (-8)      /* the current device is not gfx950 */

@@ -276,3 +276,32 @@ def test_replica_move_checks(lib):
         assert f(16, 20, 8, d, d, None, None, None) == -1
         assert f(16, 20, 8, d, d, odd, None, None) == -5
         assert f(16, 20, 0, d, d, None, None, None) == 0  # nothing to move
+
+
+def test_routing_alignment_checks(lib):
+    """Routing pointers (int64 ids) must be 8-byte aligned; every call that
+    reads them says MOE_ERR_ALIGN before touching a device otherwise."""
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(260)  # 4-byte aligned only
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    lt = lib.moe_layout_t()
+    lt.count = lt.offset = lt.slot = d
+    assert raw.moe_layout(C.byref(s), odd, C.byref(lt), None, 0, None) == -5
+    assert raw.moe_ll_layout(C.byref(s), 4, 0, odd, C.byref(lt), None, 0, None) == -5
+    assert raw.moe_layout_dispatch(C.byref(s), odd, C.byref(lt), d, d, 8, None, 0, None) == -5
+    assert raw.moe_ll_layout_dispatch(C.byref(s), 4, 0, odd, C.byref(lt), d, d, 64, None, 0,
+                                      None) == -5
+    s512 = lib.make_shape(4, 512, 16, 4, 2, 1)
+    assert raw.moe_ll_layout_dispatch_fp8(C.byref(s512), 4, 0, odd, C.byref(lt), d, d, d, 64,
+                                          0, None, 0, None) == -5
+    assert raw.moe_expert_load(4, 2, 16, odd, d, None, None) == -5
+    assert raw.moe_combine_masked(C.byref(s), d, 8, d, odd, d, d, d, None, None, None) == -5
+    rl = lib.moe_rank_layout_t()
+    rl.rank_slot = rl.rank_offset = d
+    assert raw.moe_rank_layout(C.byref(s), odd, None, C.byref(rl), 8, None) == -5
+    assert raw.moe_rank_layout_dispatch(C.byref(s), odd, None, C.byref(rl), 8, d, d, 8,
+                                        None) == -5
+    assert raw.moe_reroute(4, 2, 16, odd, d, d, 20, d, None, None) == -5
+    assert raw.moe_reroute(4, 2, 16, d, d, d, 20, odd, None, None) == -5
+

@@ -30,10 +30,12 @@ def _announce(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None, fused=False, recv_rows=None):
+def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None, fused=False, recv_rows=None,
+                  odd_ids=False):
     """fused: moe_rank_layout_dispatch instead of moe_rank_layout followed by
     moe_rank_dispatch (same results); recv_rows: rows the receive buffer
-    passes (default: the layout's capacity)."""
+    passes (default: the layout's capacity); odd_ids: the routing is a view
+    starting one int64 into its buffer (8-byte but not 16-byte aligned)."""
     shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, A)
     lay = capi.RankLayoutBuffers.empty(shape, dev(), weights=weights, cap=cap)
     for t in (lay.rank_slot, lay.rank_offset, lay.recv_src, lay.recv_expert_count):
@@ -42,6 +44,11 @@ def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None, fused=False, rec
     if lay.recv_topk_weights is not None:
         lay.recv_topk_weights.fill_(float("nan"))
     idx = to_dev(w.topk_idx.astype(np.int64))
+    if odd_ids:
+        buf = torch.full((idx.numel() + 1,), -99, dtype=torch.int64, device=dev())
+        buf[1:] = idx.reshape(-1)
+        idx = buf[1:].view(w.T, w.K)
+        assert idx.data_ptr() % 16 == 8
     wt = to_dev(w.topk_weights) if weights else None
     nrecv = lay.cap if recv_rows is None else recv_rows
     recv = torch.full((max(nrecv, 1), w.H), SENTINEL, dtype=torch.int16, device=dev())
@@ -73,8 +80,8 @@ def run_rank_path(capi, w, A=1, cap=None, weights=True, y=None, fused=False, rec
     return got
 
 
-def check_rank_path(capi, orc, w, A=1, weights=True, fused=False):
-    got = run_rank_path(capi, w, A, weights=weights, fused=fused)
+def check_rank_path(capi, orc, w, A=1, weights=True, fused=False, odd_ids=False):
+    got = run_rank_path(capi, w, A, weights=weights, fused=fused, odd_ids=odd_ids)
     ref = orc.rank_layout(w.topk_idx, w.E, w.R, A, w.topk_weights if weights else None)
     for key in ("rank_slot", "rank_offset", "recv_src", "recv_topk_idx", "recv_expert_count"):
         assert np.array_equal(got[key], ref[key]), key
@@ -130,6 +137,18 @@ def test_rank_path_workloads(capi, orc, name, fused):
     w = mi.by_name(name)
     _announce(f"rank path {name} T={w.T} H={w.H} fused={fused}")
     check_rank_path(capi, orc, w, fused=fused)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
+@pytest.mark.parametrize("name", ["c2", "rand8"])
+def test_rank_path_unaligned_routing(capi, orc, name, fused):
+    """A routing view 8-byte but not 16-byte aligned: top-8 batches, which the
+    one-launch kernel reads as 16-byte vectors when aligned, give the same
+    results through per-id loads."""
+    w = mi.config_c2() if name == "c2" else mi.random_case(1324, 300, 136, 64, 16, 8, 1,
+                                                              neg_frac=0.05, dup_frac=0.1)
+    _announce(f"rank path, routing at an odd int64 offset, {name}, fused={fused}")
+    check_rank_path(capi, orc, w, fused=fused, odd_ids=True)
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "one_call"])
