@@ -34,15 +34,30 @@ FP8_SCALE_ROWS = 4
 FP8_GROUP = 128
 
 
-def build(out: str = LIB, mutant: Optional[int] = None) -> str:
-    """Compile oracle.c into a shared library (optionally with a planted mutant)."""
+LIB_OMP = os.path.join(_HERE, "liboracle_omp.so")
+
+
+def build(out: str = LIB, mutant: Optional[int] = None, openmp: bool = False,
+          extra: tuple = ()) -> str:
+    """Compile oracle.c into a shared library (optionally with a planted
+    mutant). openmp=True gives the build whose dispatch and combine token loops
+    run on several threads (the CPU baseline's all-cores leg); its results are
+    the same bit for bit. extra: more compiler flags (the sanitizer test)."""
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-Werror", "-o", out + ".tmp", SRC, "-lm"]
+           "-Wall", "-Wextra", "-Werror", *extra, "-o", out + ".tmp", SRC, "-lm"]
+    if openmp:
+        cmd.insert(1, "-fopenmp")
     if mutant is not None:
         cmd.insert(1, f"-DORACLE_MUTANT={int(mutant)}")
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_all() -> None:
+    """The normal build and the OpenMP build."""
+    build(LIB)
+    build(LIB_OMP, openmp=True)
 
 
 _P = C.c_void_p
@@ -64,6 +79,8 @@ class Oracle:
         lib = C.CDLL(path)
         self.lib = lib
         lib.oracle_mutant.restype = C.c_int
+        lib.oracle_threads.argtypes = [C.c_int]
+        lib.oracle_threads.restype = C.c_int
         lib.oracle_bf16_from_f32.argtypes = [_P, _P, _I64]
         lib.oracle_layout.argtypes = [_I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                       _I64, _P]
@@ -101,6 +118,11 @@ class Oracle:
     @property
     def mutant(self) -> int:
         return int(self.lib.oracle_mutant())
+
+    def threads(self, n: int = 0) -> int:
+        """Threads of the token loops: sets them when n > 0 (OpenMP build
+        only) and returns the count in force."""
+        return int(self.lib.oracle_threads(int(n)))
 
     # -- conversions --------------------------------------------------------
     def bf16_rne(self, f: np.ndarray) -> np.ndarray:
@@ -391,3 +413,17 @@ def get() -> Oracle:
             build()
         _default = Oracle(LIB)
     return _default
+
+
+_parallel: Optional[Oracle] = None
+
+
+def get_parallel() -> Oracle:
+    """The OpenMP build (same results; dispatch and combine split over
+    tokens); built on first use if absent."""
+    global _parallel
+    if _parallel is None:
+        if not os.path.exists(LIB_OMP):
+            build(LIB_OMP, openmp=True)
+        _parallel = Oracle(LIB_OMP)
+    return _parallel

@@ -49,6 +49,21 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* A second build with -fopenmp (used only to time the CPU baseline on all of
+ * the host's cores) splits the token loops of dispatch and combine over
+ * threads. Each token is still handled by one thread in the same order, so
+ * every result is the same bit for bit; the normal build ignores this. */
+#ifdef _OPENMP
+#include <omp.h>
+#define FOR_TOKENS _Pragma("omp parallel for schedule(static) reduction(|:st)")
+#define TOKEN_REGION _Pragma("omp parallel")
+#define TOKEN_SPLIT _Pragma("omp for schedule(static) reduction(|:st)")
+#else
+#define FOR_TOKENS
+#define TOKEN_REGION
+#define TOKEN_SPLIT
+#endif
+
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0
 #endif
@@ -59,6 +74,18 @@
 #define ST_BAD_REPLICA 8
 
 int oracle_mutant(void) { return ORACLE_MUTANT; }
+
+/* Threads the token loops may use: sets the count when n > 0, returns the
+ * count in force (1 in the normal build). */
+int oracle_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ */
 /* bf16 <-> f32                                                        */
@@ -334,17 +361,20 @@ int oracle_combine_rank_weights(int64_t T, int32_t K, int32_t R, const int32_t *
  * bit into its slot of the receive buffer. */
 int oracle_dispatch(int64_t T, int32_t H, int32_t K, const uint16_t *x, const int32_t *slot,
                     uint16_t *recv, int64_t rows, int32_t *status) {
+    int32_t st = 0;
+    FOR_TOKENS
     for (int64_t t = 0; t < T; ++t) {
         for (int32_t k = 0; k < K; ++k) {
             int32_t r = slot[t * K + k];
             if (r == -1) continue;
             if (r < -1 || r >= rows) {
-                if (status) *status |= ST_BAD_SLOT;
+                st |= ST_BAD_SLOT;
                 continue;
             }
             memcpy(recv + (int64_t)r * H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
         }
     }
+    if (status) *status |= st;
     return 0;
 }
 
@@ -374,6 +404,8 @@ static int32_t k_end(int32_t K) {
  * top-k weight, back into the token's row. Exact definition in double. */
 int oracle_combine_f64(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64_t rows,
                        const int32_t *slot, const float *w, double *out, int32_t *status) {
+    int32_t st = 0;
+    FOR_TOKENS
     for (int64_t t = 0; t < T; ++t) {
         double *o = out + t * (int64_t)H;
         for (int32_t h = 0; h < H; ++h) o[h] = 0.0;
@@ -381,7 +413,7 @@ int oracle_combine_f64(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64
             int32_t r = slot[t * K + k];
             if (r == -1) continue;
             if (r < -1 || r >= rows) {
-                if (status) *status |= ST_BAD_SLOT;
+                st |= ST_BAD_SLOT;
                 continue;
             }
             double wk = w ? (double)w[t * K + k_of(k, K)] : 1.0;
@@ -389,6 +421,7 @@ int oracle_combine_f64(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64
             for (int32_t h = 0; h < H; ++h) o[h] += wk * (double)bf16_to_f32(yr[h]);
         }
     }
+    if (status) *status |= st;
     return 0;
 }
 
@@ -397,29 +430,35 @@ int oracle_combine_f64(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64
 int oracle_combine_f32(int64_t T, int32_t H, int32_t K, const uint16_t *y, int64_t rows,
                        const int32_t *slot, const float *w, float *out_f32, uint16_t *out_bf16,
                        int32_t *status) {
-    float *acc = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
-    for (int64_t t = 0; t < T; ++t) {
-        for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
-        for (int32_t k = 0; k < k_end(K); ++k) {
-            int32_t r = slot[t * K + k];
-            if (r == -1) continue;
-            if (r < -1 || r >= rows) {
-                if (status) *status |= ST_BAD_SLOT;
-                continue;
+    int32_t st = 0;
+    TOKEN_REGION
+    {
+        float *acc = (float *)malloc(sizeof(float) * (size_t)(H > 0 ? H : 1));
+        TOKEN_SPLIT
+        for (int64_t t = 0; t < T; ++t) {
+            for (int32_t h = 0; h < H; ++h) acc[h] = 0.0f;
+            for (int32_t k = 0; k < k_end(K); ++k) {
+                int32_t r = slot[t * K + k];
+                if (r == -1) continue;
+                if (r < -1 || r >= rows) {
+                    st |= ST_BAD_SLOT;
+                    continue;
+                }
+                float wk = w ? w[t * K + k_of(k, K)] : 1.0f;
+                const uint16_t *yr = y + (int64_t)r * H;
+                for (int32_t h = 0; h < H; ++h) {
+                    float prod = wk * bf16_to_f32(yr[h]);
+                    acc[h] = acc[h] + prod;
+                }
             }
-            float wk = w ? w[t * K + k_of(k, K)] : 1.0f;
-            const uint16_t *yr = y + (int64_t)r * H;
             for (int32_t h = 0; h < H; ++h) {
-                float prod = wk * bf16_to_f32(yr[h]);
-                acc[h] = acc[h] + prod;
+                if (out_f32) out_f32[t * (int64_t)H + h] = acc[h];
+                if (out_bf16) out_bf16[t * (int64_t)H + h] = f32_to_bf16(acc[h]);
             }
         }
-        for (int32_t h = 0; h < H; ++h) {
-            if (out_f32) out_f32[t * (int64_t)H + h] = acc[h];
-            if (out_bf16) out_bf16[t * (int64_t)H + h] = f32_to_bf16(acc[h]);
-        }
+        free(acc);
     }
-    free(acc);
+    if (status) *status |= st;
     return 0;
 }
 
