@@ -13,18 +13,28 @@ The timed steps rotate over enough independent buffer sets (>= 512 MiB, twice
 the 256 MiB Infinity Cache) that no step finds its inputs in the
 memory-side cache from the previous visit. Steps are replayed from a HIP graph
 so host launch overhead does not throttle the GPU; the graph holds exactly the
-kernels an eager step launches.
+kernels an eager step launches. Before every timed region a short spin kernel
+keeps the GPU busy while the host queues the replays, so the region starts on
+a full queue whatever the step count.
 
-Prints one JSON line. See --help for options.
+Modes:
+  (default)            time the steps, print one JSON line
+  --profile-pass P     graph replays only, for rocprofv3 (P: standard | all):
+                       segments separated by marker launches, listed in
+                       --segments-out
+  --summarize DIR...   turn rocprofv3 CSV output (kernel trace, or counter
+                       passes) into the markdown summaries kept in profiles/
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -34,12 +44,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
 METRIC = "dispatch+combine µs & HBM GB/s (% of peak), 128 tok×7168 hidden, 256E top-8"
-KERNEL_SOURCES = ("combine_moe_layout_03_amd/csrc/scatter.hip",
-                  "combine_moe_layout_03_amd/csrc/fused.hip",
-                  "combine_moe_layout_03_amd/csrc/fp8.hpp",
-                  "combine_moe_layout_03_amd/csrc/layout.hip",
-                  "combine_moe_layout_03_amd/csrc/wave.hpp",
-                  "combine_moe_layout_03_amd/csrc/kernels.hpp")
+CSRC = os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_standard_128x7168.md")
+TRACE_ROWS_SUMMARY = os.path.join(ROOT, "profiles", "kernel_trace_rows.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+MARKER = (1, 1)  # marker launch between profile segments: 1 workgroup of 1 thread
 
 
 def log(msg):
@@ -91,141 +100,351 @@ def device_hbm_figures(dev_index):
 
 
 def kernel_source_hash():
-    """Hash of the measured kernels' code: comments and whitespace are left
-    out, so a comment edit does not invalidate the counter summary."""
+    """Hash of every kernel source (comments and whitespace left out, so a
+    comment edit does not invalidate the committed profile summaries)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel)) as f:
+    for path in sorted(glob.glob(os.path.join(CSRC, "*.hip")) +
+                       glob.glob(os.path.join(CSRC, "*.hpp"))):
+        with open(path) as f:
             src = f.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
+        h.update(os.path.basename(path).encode())
         h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic_c2.md")
+def read_summary(path):
+    """Machine-read lines `key: value` of a committed profile summary, or {}
+    if it is absent or was taken on other kernel sources."""
     if not os.path.exists(path):
-        return None
+        return {}
     txt = open(path).read()
-    m = re.search(r"kernel_source_hash:\s*([0-9a-f]+)", txt)
+    m = re.search(r"^kernel_source_hash:\s*([0-9a-f]+)", txt, re.M)
     if not m or m.group(1) != kernel_source_hash():
-        return None
-    m = re.search(rf"^traffic_bytes_{kernel}:\s*([0-9.]+)", txt, re.M)
-    return float(m.group(1)) if m else None
+        return {}
+    vals = {}
+    for m in re.finditer(r"^(trace_us|fetch_kib|write_kib)\s+(.+?):\s*([-0-9.eE]+)\s*$",
+                         txt, re.M):
+        vals[(m.group(1), m.group(2))] = float(m.group(3))
+    return vals
+
+
+# --------------------------------------------------------------------------
+# timing
+
+
+class Gate:
+    """A spin kernel ahead of a timed region: the GPU stays busy while the
+    host queues the region's launches, so the start event is followed by a
+    full queue (a 20-step region otherwise carries the graph launch's host
+    latency). torch.cuda._sleep spins for a number of GPU clock ticks; the
+    tick rate is measured once."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(1000)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            torch.cuda._sleep(2_000_000)
+            b.record(stream)
+        torch.cuda.synchronize()
+        self.ticks_per_us = 2_000_000 / max(a.elapsed_time(b) * 1e3, 1.0)
+
+    def hold(self, us):
+        self.torch.cuda._sleep(int(us * self.ticks_per_us))
+
+
+def timed_ms(torch, stream, gate, enqueue, launches, warm=None):
+    """Events around enqueue() on `stream`. Ahead of the start event: a spin
+    long enough for the host to queue `launches` kernel launches (5 us each,
+    0.2-50 ms), then warm(), untimed work of the same kind (so the region
+    starts in the steady state of a long run, not on a GPU that idled in the
+    spin)."""
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        gate.hold(min(50_000, max(200, 5 * launches)))
+        if warm is not None:
+            warm()
+        start.record(stream)
+        enqueue()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
+
+
+def hip_runtime():
+    """The HIP runtime library torch has loaded (ctypes)."""
+    import ctypes
+    path = "libamdhip64.so"
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    return ctypes.CDLL(path)
+
+
+class HipGraph:
+    """A HIP graph captured from `stream` with the runtime's own calls (no
+    torch graph wrapper: its replay launches two RNG-state fills before the
+    graph, which would land in the timed region)."""
+
+    _hip = None
+
+    def __init__(self, stream, fns):
+        import ctypes as C
+        if HipGraph._hip is None:
+            h = hip_runtime()
+            h.hipStreamBeginCapture.argtypes = [C.c_void_p, C.c_int]
+            h.hipStreamEndCapture.argtypes = [C.c_void_p, C.POINTER(C.c_void_p)]
+            h.hipGraphInstantiate.argtypes = [C.POINTER(C.c_void_p), C.c_void_p, C.c_void_p,
+                                              C.c_char_p, C.c_size_t]
+            h.hipGraphLaunch.argtypes = [C.c_void_p, C.c_void_p]
+            h.hipGraphExecDestroy.argtypes = [C.c_void_p]
+            h.hipGraphDestroy.argtypes = [C.c_void_p]
+            HipGraph._hip = h
+        h = HipGraph._hip
+        self.s = C.c_void_p(stream.cuda_stream)
+        self.graph, self.exec = C.c_void_p(), C.c_void_p()
+        self._check(h.hipStreamBeginCapture(self.s, 2), "hipStreamBeginCapture")  # relaxed
+        try:
+            for fn in fns:
+                fn()
+        finally:
+            rc = h.hipStreamEndCapture(self.s, C.byref(self.graph))
+        self._check(rc, "hipStreamEndCapture")
+        self._check(h.hipGraphInstantiate(C.byref(self.exec), self.graph, None, None, 0),
+                    "hipGraphInstantiate")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+
+    def replay(self):
+        self._check(HipGraph._hip.hipGraphLaunch(self.exec, self.s), "hipGraphLaunch")
+
+    def __del__(self):
+        h = HipGraph._hip
+        if h is not None and self.exec:
+            h.hipGraphExecDestroy(self.exec)
+            h.hipGraphDestroy(self.graph)
+            self.exec = None
+
+
+def capture(torch, stream, fns):
+    torch.cuda.synchronize()
+    return HipGraph(stream, fns)
+
+
+def graph_us(torch, stream, gate, fns, reps, launches=1):
+    """One HIP graph holding fns (one call each), replayed `reps` times
+    between events; microseconds per call."""
+    g = capture(torch, stream, fns)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+
+    def go():
+        for _ in range(reps):
+            g.replay()
+    ms = timed_ms(torch, stream, gate, go, reps * len(fns) * launches, warm=go)
+    del g
+    return ms * 1e3 / (reps * len(fns))
+
+
+# --------------------------------------------------------------------------
+# workloads ("rows"): per-set callables for one step and for each API call
+
+
+class Row:
+    """One measured configuration. step: per-set callables of one step;
+    calls: name -> per-set callables of one API call each; nbytes: name (and
+    "step") -> algorithmic bytes per call; main: the calls a step is made of
+    (the roofline takes the longest)."""
+
+    def __init__(self, key, workload, step, calls, nbytes, main, launches=2, reps=None,
+                 extra=None, holder=None):
+        self.key, self.workload = key, workload
+        self.step, self.calls, self.nbytes, self.main = step, calls, nbytes, main
+        self.launches = launches  # kernel launches per step
+        self.reps = reps
+        self.extra = extra or {}
+        self.holder = holder  # keeps the buffers alive
+
+    def release(self, torch):
+        self.step = self.calls = self.holder = None
+        torch.cuda.empty_cache()
+
+
+def n_sets(set_bytes, min_sets=2, max_sets=64):
+    return min(max_sets, max(min_sets, math.ceil(512 * 2**20 / set_bytes)))
+
+
+class Arena:
+    """Device buffers carved from one allocation (256-byte aligned pieces),
+    for comparing against one allocation per buffer."""
+
+    def __init__(self, torch, dev, nbytes):
+        self.torch = torch
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.off = 0
+
+    def empty(self, *shape, dtype):
+        n = math.prod(shape) * self.torch.empty((), dtype=dtype).element_size()
+        if self.off + n > self.buf.numel():
+            raise MemoryError("arena exhausted")
+        t = self.buf[self.off:self.off + n].view(dtype).view(*shape)
+        self.off += (n + 255) // 256 * 256
+        return t
 
 
 class Workset:
-    """One independent set of device buffers for a step."""
+    """One independent set of device buffers for a step of the standard kind
+    (layout + dispatch in one call, combine); from `arena` when given."""
 
-    def __init__(self, capi, w, dev):
+    def __init__(self, capi, w, dev, arena=None):
         import numpy as np
         import torch
 
+        def alloc(*shape, dtype):
+            if arena is None:
+                return torch.empty(*shape, dtype=dtype, device=dev)
+            return arena.empty(*shape, dtype=dtype)
+
+        def upload(a, dtype):
+            t = alloc(*a.shape, dtype=dtype)
+            t.copy_(torch.from_numpy(a))
+            return t
+
         self.shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, w.A)
-        self.x = torch.from_numpy(w.x.view(np.int16)).to(dev)
-        self.idx = torch.from_numpy(w.topk_idx).to(dev)
-        self.w = torch.from_numpy(w.topk_weights).to(dev)
-        self.lay = capi.LayoutBuffers.empty(self.shape, dev, status=False)
+        self.x = upload(w.x.view(np.int16), torch.int16)
+        self.idx = upload(w.topk_idx, torch.int64)
+        self.w = upload(w.topk_weights, torch.float32)
+        T, E, R, K = w.T, w.E, w.R, w.K
         self.rows = capi.moe_recv_rows_worst(self.shape)
-        self.recv = torch.empty(self.rows, w.H, dtype=torch.int16, device=dev)
-        self.out = torch.empty(w.T, w.H, dtype=torch.int16, device=dev)
+        self.lay = capi.LayoutBuffers(
+            count=alloc(E, dtype=torch.int32), offset=alloc(E + 1, dtype=torch.int32),
+            slot=alloc(T * K, dtype=torch.int32), rank_token_count=alloc(R, dtype=torch.int32),
+            is_token_in_rank=alloc(T * R, dtype=torch.uint8),
+            row_src=alloc(max(self.rows, 1), dtype=torch.int32))
+        self.recv = alloc(self.rows, w.H, dtype=torch.int16)
+        self.out = alloc(w.T, w.H, dtype=torch.int16)
         n = capi.moe_layout_workspace_bytes(self.shape)
-        self.ws = torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+        self.ws = alloc(n, dtype=torch.uint8) if n else None
         self.nbytes = sum(t.numel() * t.element_size() for t in
                           (self.x, self.idx, self.w, self.recv, self.out, self.lay.count,
                            self.lay.offset, self.lay.slot, self.lay.row_src))
 
 
-def step(capi, s, stream):
-    capi.moe_layout_dispatch(s.shape, s.idx, s.lay, s.x, s.recv, s.rows, s.ws, stream=stream)
-    capi.moe_combine(s.shape, s.recv, s.rows, s.lay.slot, s.w, s.out, None, None, stream=stream)
+def workset_bytes(w):
+    """Bytes of one Workset of workload w, with each piece rounded to 256."""
+    r = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    T, H, E, R, K = w.T, w.H, w.E, w.R, w.K
+    rows = T * K + E * (w.A - 1)
+    return (r(T * H * 2) + r(T * K * 8) + r(T * K * 4) + r(E * 4) + r((E + 1) * 4)
+            + r(T * K * 4) + r(R * 4) + r(T * R) + r(max(rows, 1) * 4) + r(rows * H * 2)
+            + r(T * H * 2) + r(1 << 22))
 
 
-def time_graph_steps(torch, graphs_full, graph_rem, reps, stream):
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+def standard_calls(capi, z, stream):
+    return {
+        "layout_dispatch": lambda: capi.moe_layout_dispatch(
+            z.shape, z.idx, z.lay, z.x, z.recv, z.rows, z.ws, stream=stream),
+        "combine": lambda: capi.moe_combine(
+            z.shape, z.recv, z.rows, z.lay.slot, z.w, z.out, None, None, stream=stream),
+        # reference: the same work as two separate kernels
+        "layout": lambda: capi.moe_layout(z.shape, z.idx, z.lay, z.ws, stream=stream),
+        "dispatch": lambda: capi.moe_dispatch(z.shape, z.x, z.lay.slot, z.recv, z.rows, None,
+                                              stream=stream),
+    }
+
+
+def row_standard_kind(capi, mi, torch, dev, stream, name, key, sets=0, arena=False):
+    """The standard step (layout + dispatch in one call, then combine) on a
+    workload: c2 (the headline), c1 or c4; rotating sets for >= 512 MiB.
+    arena: every set carved from one allocation."""
+    w = mi.by_name(name)
+    S = sets or n_sets(workset_bytes(w))
+    ar = Arena(torch, dev, S * workset_bytes(w)) if arena else None
+    zs = [Workset(capi, w, dev, ar) for _ in range(S)]
+    probe = zs[0]
     with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(reps):
-            graphs_full.replay()
-        if graph_rem is not None:
-            graph_rem.replay()
-        end.record(stream)
+        for z in zs:
+            c = standard_calls(capi, z, stream)
+            c["layout_dispatch"]()
+            c["combine"]()
     torch.cuda.synchronize()
-    return start.elapsed_time(end)  # ms
+    calls = {k: [standard_calls(capi, z, stream)[k] for z in zs]
+             for k in ("layout_dispatch", "combine", "layout", "dispatch")}
+    step = [(lambda z=z: (standard_calls(capi, z, stream)["layout_dispatch"](),
+                          standard_calls(capi, z, stream)["combine"]())) for z in zs]
+    P = int((w.topk_idx >= 0).sum())
+    ab = algo_bytes(w.T, w.H, w.K, w.E, w.R, P)
+    nb = {"layout_dispatch": ab["layout"] + ab["dispatch"], "combine": ab["combine"],
+          "layout": ab["layout"], "dispatch": ab["dispatch"] + 4 * P, "step": ab["total"]}
+    return Row(key, f"{w.name}: {w.T} tokens x {w.H}, {w.E} experts top-{w.K} on {w.R} ranks",
+               step, calls, nb, ("layout_dispatch", "combine"),
+               extra={"buffer_sets": S, "footprint_MiB": round(S * probe.nbytes / 2**20, 1),
+                      "one_allocation": bool(arena), "workload_obj": w}, holder=(zs, ar))
 
 
-def per_launch_event_times(torch, fn, n, stream):
-    """Each launch bracketed by its own pair of events (GPU timestamps)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    torch.cuda.synchronize()
-    for i in range(n):
-        evs[i][0].record(stream)
-        fn(i)
-        evs[i][1].record(stream)
-    torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)  # us
-    return dict(mean_us=sum(ts) / n, median_us=ts[n // 2], min_us=ts[0])
-
-
-def cpu_baseline(w, budget_s, gpu_out_bits):
-    """The oracle, as it stands, on this workload's step; single thread."""
-    import numpy as np
-
-    import oracle
-
-    orc = oracle.get()
-    reps = 0
-    t0 = time.perf_counter()
-    ref = None
-    while True:
-        lay = orc.layout(w.topk_idx, w.E, w.R, w.A)
-        recv, _ = orc.dispatch(w.x, lay["slot"], lay["rows"])
-        ref = orc.combine(recv, lay["slot"], w.topk_weights, "f64")["out_f64"]
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 100000:
-            break
-    # parity re-check of the timed GPU output against the oracle
-    got = (gpu_out_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    ok = bool(np.all(np.abs(got - ref) <= 1e-3 + 1e-2 * np.abs(ref)))
-    return reps, el, ok
-
-
-def graph_us_per_step(torch, stream, step_fns, reps):
-    """Capture one HIP graph holding one step per entry of step_fns, replay it
-    `reps` times between events; microseconds per step."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for fn in step_fns:
-            fn()
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+def row_floors(capi, floors, mi, torch, np, dev, stream):
+    """Floors at the standard shape (128 tokens x 7168, K = 8): the same bytes
+    as the two kernels with nothing data-dependent, and a launch with no work.
+    Rotating sets as for the real kernels."""
+    T, H, K = 128, 7168, 8
+    row = 2 * H
+    S = n_sets(T * row * (K + 1) * 2)
+    xs = [torch.randn(T, H, device=dev).to(torch.bfloat16).view(torch.int16) for _ in range(S)]
+    bc = [torch.empty(T * K, H, dtype=torch.int16, device=dev) for _ in range(S)]
+    go = [torch.empty(T, H, dtype=torch.int16, device=dev) for _ in range(S)]
+    ncopy = T * row * (K + 1) // 2  # 8.26 MB read + written: the dispatch's 16.5 MB moved
+    cs = [torch.empty(ncopy, dtype=torch.uint8, device=dev) for _ in range(S)]
+    cd = [torch.empty(ncopy, dtype=torch.uint8, device=dev) for _ in range(S)]
+    big_s = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
+    big_d = torch.empty_like(big_s)
+    s = stream
+    calls = {
+        "empty_1x64": [lambda: floors.empty(1, 64, s)] * S,
+        "empty_512x512": [lambda: floors.empty(512, 512, s)] * S,
+        "empty_3584x64": [lambda: floors.empty(3584, 64, s)] * S,
+        "bcast_128x7168x8": [(lambda i=i: floors.bcast(xs[i], bc[i], T, H, K, s))
+                             for i in range(S)],
+        "gather_128x7168x8": [(lambda i=i: floors.gather(bc[i], go[i], T, H, K, s))
+                              for i in range(S)],
+        "copy_8.26MB": [(lambda i=i: floors.copy(cs[i], cd[i], ncopy, s)) for i in range(S)],
+        "copy_256MiB": [lambda: floors.copy(big_s, big_d, big_s.numel(), s)] * 2,
+    }
     with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(reps):
-            g.replay()
-        end.record(stream)
+        for fns in calls.values():
+            for f in fns:
+                f()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e3 / (reps * len(step_fns))
+    nb = {"empty_1x64": 0, "empty_512x512": 0, "empty_3584x64": 0,
+          "bcast_128x7168x8": T * row * (K + 1), "gather_128x7168x8": T * row * (K + 1),
+          "copy_8.26MB": 2 * ncopy, "copy_256MiB": 2 * big_s.numel(), "step": 0}
+    return Row("floors", "floors at 128 tokens x 7168, top-8: empty launches, a broadcast copy "
+               "(one row read, 8 sequential row writes per token), a gather + sum (8 row reads "
+               "at computed addresses, one row write), plain copies", None, calls, nb, (),
+               extra={"buffer_sets": S}, holder=(xs, bc, go, cs, cd, big_s, big_d))
 
 
-def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
+def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128, masked=False):
     """Low-latency padded path at M tokens per rank: layout + dispatch into
     the [E, R*M, H] union of the receive buffers, then combine from it. Steps
     rotate over union buffers x 8 source stripes, enough for > 512 MiB of
     touched bytes (at least 4 unions at M = 128).
     With fp8_flags, dispatch casts to E4M3 + per-128-channel scales
     (moe_ll_layout_dispatch_fp8) and combine reads a bf16 expert-output union
-    of the same layout (filled once by a bf16 dispatch of the same batch)."""
+    of the same layout (filled once by a bf16 dispatch of the same batch).
+    masked: also the combine with an active-rank mask (no rank masked, and
+    rank 3 masked)."""
     w = mi.config_c3(M)
     E, R, K, T, H = w.E, w.R, w.K, w.T, w.H
     rows = capi.moe_ll_recv_rows(E, R, M)
@@ -238,12 +457,16 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
     ab = algo_bytes(T, H, K, E, R, P, fp8_flags)
     n_unions = max(4 if M == 128 else 1, math.ceil(512 * 2**20 / (ab["total"] * R)))
     unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(n_unions)]
+    qunions = sunions = None
     if fp8:
         cols = capi.fp8_scale_cols(H, fp8_flags)
         sdt = torch.int32 if fp8_flags & capi.MOE_FP8_UE8M0 else torch.float32
         qunions = [torch.empty(rows, H, dtype=torch.uint8, device=dev) for _ in range(n_unions)]
         sshape = (rows, cols) if fp8_flags & capi.MOE_FP8_SCALE_ROWS else (E, cols, R * M)
         sunions = [torch.empty(sshape, dtype=sdt, device=dev) for _ in range(n_unions)]
+    mask_none = torch.zeros(R, dtype=torch.int32, device=dev)
+    mask_one = torch.zeros(R, dtype=torch.int32, device=dev)
+    mask_one[3] = 1
     sets = []
     for ui, u in enumerate(unions):
         for s in range(R):
@@ -267,6 +490,10 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
         capi.moe_combine(shape, z["u"], rows, z["lay"].slot, z["w"], z["out"], None, None,
                          stream=stream)
 
+    def cbm(z, m):
+        capi.moe_combine_masked(shape, z["u"], rows, z["lay"].slot, z["idx"], z["w"], m,
+                                z["out"], None, None, stream=stream)
+
     with torch.cuda.stream(stream):
         for z in sets:
             if fp8:  # expert output: the bf16 rows of the same layout
@@ -274,30 +501,30 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128):
                                             rows, stream=stream)
             ld(z)
             cb(z)
+            if masked:
+                cbm(z, mask_none)
     torch.cuda.synchronize()
-    fns = [(lambda z=z: (ld(z), cb(z))) for z in sets]
-    us = graph_us_per_step(torch, stream, fns, 20)
-    k_ld = graph_us_per_step(torch, stream, [(lambda z=z: ld(z)) for z in sets], 20)
-    k_cb = graph_us_per_step(torch, stream, [(lambda z=z: cb(z)) for z in sets], 20)
-    n_sets = len(sets)
-    del unions, sets
-    if fp8:
-        del qunions, sunions
-    torch.cuda.empty_cache()
+    tag = "ll_layout_dispatch" + ("_fp8" if fp8 else "")
+    calls = {tag: [(lambda z=z: ld(z)) for z in sets],
+             "combine": [(lambda z=z: cb(z)) for z in sets]}
+    nb = {tag: ab["layout"] + ab["dispatch"], "combine": ab["combine"], "step": ab["total"]}
+    if masked:
+        calls["combine_masked_none"] = [(lambda z=z: cbm(z, mask_none)) for z in sets]
+        calls["combine_masked_rank3"] = [(lambda z=z: cbm(z, mask_one)) for z in sets]
+        # the ids and the mask are read besides combine's bytes; a masked rank's
+        # rows are not summed, but are still read (the row loads do not wait
+        # for the mask), so the same bytes move with one rank masked
+        nb["combine_masked_none"] = ab["combine"] + 8 * T * K + 4 * R
+        nb["combine_masked_rank3"] = ab["combine"] + 8 * T * K + 4 * R
     name = "low-latency padded" + (f" FP8 (flags {fp8_flags}: "
                                    + ("row-major" if fp8_flags & 4 else "column-major")
                                    + " scales)" if fp8 else "")
-    res = {"workload": name + f": {M} tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
-                              f"buffer [256, 8*{M}, 7168]",
-           "buffer_sets": n_sets,
-           "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
-           "kernels_us": {"ll_layout_dispatch" + ("_fp8" if fp8 else ""): round(k_ld, 3),
-                          "combine": round(k_cb, 3)},
-           "algorithmic_bytes_per_step": ab["total"]}
-    res["roofline_dispatch"] = {"achieved": round((ab["layout"] + ab["dispatch"]) / k_ld / 1e3, 1),
-                                "frac": round((ab["layout"] + ab["dispatch"]) / k_ld / 1e3
-                                              / HBM_PEAK_GBS, 4)}
-    return res
+    key = (f"low_latency_fp8_{'rowscales_' if fp8_flags & 4 else ''}m{M}" if fp8
+           else f"low_latency_m{M}")
+    return Row(key, name + f": {M} tokens/rank x 7168, 256E top-8, 8 ranks, union receive "
+                           f"buffer [256, 8*{M}, 7168]",
+               [(lambda z=z: (ld(z), cb(z))) for z in sets], calls, nb, (tag, "combine"),
+               extra={"buffer_sets": len(sets)}, holder=(unions, qunions, sunions, sets))
 
 
 def row_normal(capi, mi, torch, np, dev, stream):
@@ -343,122 +570,31 @@ def row_normal(capi, mi, torch, np, dev, stream):
             cmb(z)
     torch.cuda.synchronize()
     rows = int(sets[0]["lay"].rank_offset[R].item())
-    us = graph_us_per_step(torch, stream, [(lambda z=z: (lay_dsp(z), cmb(z))) for z in sets], 20)
-    us_two = graph_us_per_step(torch, stream,
-                               [(lambda z=z: (lay(z), dsp(z), cmb(z))) for z in sets], 20)
-    k = {n: graph_us_per_step(torch, stream, [(lambda z=z, f=f: f(z)) for z in sets], 20)
-         for n, f in (("rank_layout_dispatch", lay_dsp), ("rank_combine", cmb),
-                      ("rank_layout", lay), ("rank_dispatch", dsp))}
     b_layout = T * K * 12 + T * R * 4 + (R + 1) * 4 + rows * (4 + K * 12) + E * 4
     b_dispatch = T * 2 * H + rows * 2 * H
     b_combine = rows * 2 * H + T * 2 * H + T * R * 4 + rows * K * 4 + T * K * 4
-    total = b_layout + b_dispatch + b_combine
-    b_fused = b_layout + b_dispatch
-    del sets
-    torch.cuda.empty_cache()
-    return {"workload": "normal mode: 128 tokens x 7168, 256E top-8 on 8 ranks, one row per "
-                        "(token, rank): %d rows for %d pairs" % (rows, int((w.topk_idx >= 0).sum())),
-            "us_per_step": round(us, 3), "GB_per_s": round(total / us / 1e3, 1),
-            "us_per_step_layout_then_dispatch": round(us_two, 3),
-            "kernels_us": {n: round(v, 3) for n, v in k.items()},
-            "algorithmic_bytes_per_step": total,
-            "roofline_layout_dispatch": {
-                "achieved": round(b_fused / k["rank_layout_dispatch"] / 1e3, 1),
-                "frac": round(b_fused / k["rank_layout_dispatch"] / 1e3 / HBM_PEAK_GBS, 4)}}
+    calls = {"rank_layout_dispatch": [(lambda z=z: lay_dsp(z)) for z in sets],
+             "rank_combine": [(lambda z=z: cmb(z)) for z in sets],
+             "rank_layout": [(lambda z=z: lay(z)) for z in sets],
+             "rank_dispatch": [(lambda z=z: dsp(z)) for z in sets]}
+    nb = {"rank_layout_dispatch": b_layout + b_dispatch, "rank_combine": b_combine,
+          "rank_layout": b_layout, "rank_dispatch": b_dispatch + T * R * 4,
+          "step": b_layout + b_dispatch + b_combine}
+    return Row("normal_mode_128x7168",
+               "normal mode: 128 tokens x 7168, 256E top-8 on 8 ranks, one row per (token, "
+               "rank): %d rows for %d pairs" % (rows, int((w.topk_idx >= 0).sum())),
+               [(lambda z=z: (lay_dsp(z), cmb(z))) for z in sets], calls, nb,
+               ("rank_layout_dispatch", "rank_combine"),
+               extra={"buffer_sets": len(sets),
+                      "two_launch_step": [(lambda z=z: (lay(z), dsp(z), cmb(z))) for z in sets]},
+               holder=sets)
 
 
-def row_replica_train(capi, mi, torch, np, dev, stream):
-    """Replica weight sync and replica gradient reduction for the replica
-    workload's plan (256 logical experts, 32 replicas on 8 ranks), with one
-    7168 x 2048 matrix per expert (a stand-in: the pages give no expert size):
-    bf16 weights, f32 gradients, 288 physical experts."""
-    w5 = mi.config_c5(T=8192, H=8)
-    E, R, C = w5.E, w5.R, w5.replicas
-    Ep = E + C
-    S = 7168 * 2048
-    i32 = dict(dtype=torch.int32, device=dev)
-    idx = torch.from_numpy(w5.topk_idx).to(dev)
-    load = torch.empty(E, **i32)
-    rc = torch.empty(E, **i32)
-    rp = torch.empty(E, 2, **i32)
-    p2l = torch.empty(Ep, **i32)
-    capi.moe_expert_load(w5.T, w5.K, E, idx, load)
-    capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l)
-    w = torch.zeros(Ep * S, dtype=torch.int16, device=dev)
-    g = torch.zeros(Ep * S, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def timed(fn, n=5):
-        with torch.cuda.stream(stream):
-            fn()
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(n):
-                fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
-
-    t_sync = timed(lambda: capi.moe_replica_weight_sync(E, Ep, S, rc, rp, w, stream=stream))
-    t_red = timed(lambda: capi.moe_replica_grad_reduce(E, Ep, S, rc, rp, g, stream=stream))
-    b_sync = 2 * C * S * 2
-    b_red = 3 * C * S * 4
-    del w, g
-    torch.cuda.empty_cache()
-    return {"workload": "replica weight sync (bf16) and gradient reduction (f32), 256 experts + 32 "
-                        "replicas, one 7168x2048 matrix per expert",
-            "weight_sync_us": round(t_sync, 1), "grad_reduce_us": round(t_red, 1),
-            "weight_sync_GB_per_s": round(b_sync / t_sync / 1e3, 1),
-            "grad_reduce_GB_per_s": round(b_red / t_red / 1e3, 1),
-            "frac_weight_sync": round(b_sync / t_sync / 1e3 / HBM_PEAK_GBS, 4),
-            "frac_grad_reduce": round(b_red / t_red / 1e3 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": {"weight_sync": b_sync, "grad_reduce": b_red}}
-
-
-def row_config(capi, mi, torch, np, dev, stream, name):
-    """The standard step (layout + dispatch in one call, then combine) on
-    another configuration: c1 (64 tokens x 256, 16 experts top-2 on 4 ranks)
-    or c4 (4096 tokens x 4096, 64 experts top-6 Zipf(1.2) on 8 ranks).
-    Rotating buffer sets for >= 512 MiB touched (at most 64 sets)."""
-    w = mi.by_name(name)
-    probe = Workset(capi, w, dev)
-    S = min(64, max(2, math.ceil(512 * 2**20 / probe.nbytes)))
-    sets = [probe] + [Workset(capi, w, dev) for _ in range(S - 1)]
-    with torch.cuda.stream(stream):
-        for z in sets:
-            step(capi, z, stream)
-    torch.cuda.synchronize()
-    us = graph_us_per_step(torch, stream, [(lambda z=z: step(capi, z, stream)) for z in sets],
-                           max(4, 200 // S))
-    k_ld = graph_us_per_step(torch, stream, [(lambda z=z: capi.moe_layout_dispatch(
-        z.shape, z.idx, z.lay, z.x, z.recv, z.rows, z.ws, stream=stream)) for z in sets],
-        max(4, 200 // S))
-    k_cb = graph_us_per_step(torch, stream, [(lambda z=z: capi.moe_combine(
-        z.shape, z.recv, z.rows, z.lay.slot, z.w, z.out, None, None, stream=stream))
-        for z in sets], max(4, 200 // S))
-    P = int((w.topk_idx >= 0).sum())
-    ab = algo_bytes(w.T, w.H, w.K, w.E, w.R, P)
-    foot = S * probe.nbytes
-    del sets, probe
-    torch.cuda.empty_cache()
-    r_ld = (ab["layout"] + ab["dispatch"]) / k_ld / 1e3
-    r_cb = ab["combine"] / k_cb / 1e3
-    return {"workload": f"{w.name}: {w.T} tokens x {w.H}, {w.E} experts top-{w.K} on {w.R} ranks",
-            "buffer_sets": S, "footprint_MiB": round(foot / 2**20, 1),
-            "us_per_step": round(us, 3), "GB_per_s": round(ab["total"] / us / 1e3, 1),
-            "algorithmic_bytes_per_step": ab["total"],
-            "kernels_us": {"layout_dispatch": round(k_ld, 3), "combine": round(k_cb, 3)},
-            "roofline_layout_dispatch": {"achieved": round(r_ld, 1),
-                                         "frac": round(r_ld / HBM_PEAK_GBS, 4)},
-            "roofline_combine": {"achieved": round(r_cb, 1), "frac": round(r_cb / HBM_PEAK_GBS, 4)}}
-
-
-def row_replica(capi, mi, torch, np, dev, stream, n_ev):
+def row_replica(capi, mi, torch, np, dev, stream):
     """Replica-expanded routing at full size (8192 tokens x 7168, 256 logical
     experts top-8 Zipf(1.0), 32 extra replicas): load -> plan -> reroute ->
-    layout + dispatch over 288 physical experts -> combine. Also the large-batch
-    dispatch and combine kernels on their own (their HBM roofline)."""
+    layout + dispatch over 288 physical experts -> combine; and the calls on
+    their own. One buffer set (2.1 GB per step)."""
     w = mi.config_c5()
     E, R, K, T, H, C = w.E, w.R, w.K, w.T, w.H, w.replicas
     Ep = E + C
@@ -478,41 +614,434 @@ def row_replica(capi, mi, torch, np, dev, stream, n_ev):
     out = torch.empty(T, H, dtype=torch.int16, device=dev)
     ws = torch.empty(max(capi.moe_layout_workspace_bytes(shape), 1), dtype=torch.uint8,
                      device=dev)
+    s = stream
+    fns = {
+        "expert_load": lambda: capi.moe_expert_load(T, K, E, idx, load, None, stream=s),
+        "plan_replicas": lambda: capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l, stream=s),
+        "reroute": lambda: capi.moe_reroute(T, K, E, idx, rc, rp, Ep, phys, None, stream=s),
+        "layout": lambda: capi.moe_layout(shape, phys, lay, ws, stream=s),
+        "dispatch": lambda: capi.moe_dispatch(shape, x, lay.slot, recv, rows, None, stream=s),
+        "combine": lambda: capi.moe_combine(shape, recv, rows, lay.slot, wt, out, None, None,
+                                            stream=s),
+    }
 
     def step():
-        capi.moe_expert_load(T, K, E, idx, load, None, stream=stream)
-        capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l, stream=stream)
-        capi.moe_reroute(T, K, E, idx, rc, rp, Ep, phys, None, stream=stream)
-        capi.moe_layout_dispatch(shape, phys, lay, x, recv, rows, ws, stream=stream)
-        capi.moe_combine(shape, recv, rows, lay.slot, wt, out, None, None, stream=stream)
+        for k in ("expert_load", "plan_replicas", "reroute", "layout", "dispatch", "combine"):
+            fns[k]()
 
     with torch.cuda.stream(stream):
         step()
         step()
     torch.cuda.synchronize()
-    us = graph_us_per_step(torch, stream, [step], 10)
-    with torch.cuda.stream(stream):
-        k_d = per_launch_event_times(torch, lambda i: capi.moe_dispatch(
-            shape, x, lay.slot, recv, rows, None, stream=stream), n_ev // 4, stream)
-        k_c = per_launch_event_times(torch, lambda i: capi.moe_combine(
-            shape, recv, rows, lay.slot, wt, out, None, None, stream=stream), n_ev // 4, stream)
     P = T * K
     ab = algo_bytes(T, H, K, Ep, R, P)
-    reroute_bytes = P * 8 * 3 + E * 4 * 6 + Ep * 4
-    total = ab["total"] + reroute_bytes
-    rd = ab["dispatch"] / (k_d["mean_us"] * 1e-6) / 1e9
-    rcb = ab["combine"] / (k_c["mean_us"] * 1e-6) / 1e9
-    del recv, x, out
-    torch.cuda.empty_cache()
-    return {"workload": "replica-expanded: 8192 tokens x 7168, 256 logical experts top-8 "
-                        "Zipf(1.0) + 32 replicas = 288 physical on 8 ranks",
-            "us_per_step": round(us, 2), "GB_per_s": round(total / us / 1e3, 1),
-            "algorithmic_bytes_per_step": total,
-            "kernels_us": {"dispatch": round(k_d["mean_us"], 2),
-                           "combine": round(k_c["mean_us"], 2)},
-            "roofline_dispatch": {"achieved": round(rd, 1), "frac": round(rd / HBM_PEAK_GBS, 4)},
-            "roofline_combine": {"achieved": round(rcb, 1),
-                                 "frac": round(rcb / HBM_PEAK_GBS, 4)}}
+    nb = {"expert_load": P * 8 + E * 4, "plan_replicas": E * 4 * 4 + Ep * 4,
+          "reroute": P * 8 * 2 + E * 4 * 3, "layout": ab["layout"],
+          "dispatch": ab["dispatch"], "combine": ab["combine"]}
+    nb["step"] = sum(nb.values())
+    calls = {k: [f] for k, f in fns.items()}
+    return Row("replica_path_8192",
+               "replica-expanded: 8192 tokens x 7168, 256 logical experts top-8 Zipf(1.0) + 32 "
+               "replicas = 288 physical on 8 ranks", [step], calls, nb, ("dispatch", "combine"),
+               launches=8, reps=10, extra={"buffer_sets": 1},
+               holder=(x, idx, wt, load, rc, rp, p2l, phys, lay, recv, out, ws))
+
+
+def row_replica_train(capi, mi, torch, np, dev, stream):
+    """Replica weight sync and replica gradient reduction for the replica
+    workload's plan (256 logical experts, 32 replicas on 8 ranks), with one
+    7168 x 2048 matrix per expert (a stand-in: the pages give no expert size):
+    bf16 weights, f32 gradients, 288 physical experts."""
+    w5 = mi.config_c5(T=8192, H=8)
+    E, R, C = w5.E, w5.R, w5.replicas
+    Ep = E + C
+    S = 7168 * 2048
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.from_numpy(w5.topk_idx).to(dev)
+    load = torch.empty(E, **i32)
+    rc = torch.empty(E, **i32)
+    rp = torch.empty(E, 2, **i32)
+    p2l = torch.empty(Ep, **i32)
+    capi.moe_expert_load(w5.T, w5.K, E, idx, load)
+    capi.moe_plan_replicas(E, R, C, load, rc, rp, p2l)
+    wbuf = torch.zeros(Ep * S, dtype=torch.int16, device=dev)
+    g = torch.zeros(Ep * S, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    calls = {"weight_sync": [lambda: capi.moe_replica_weight_sync(E, Ep, S, rc, rp, wbuf,
+                                                                  stream=stream)],
+             "grad_reduce": [lambda: capi.moe_replica_grad_reduce(E, Ep, S, rc, rp, g,
+                                                                  stream=stream)]}
+    nb = {"weight_sync": 2 * C * S * 2, "grad_reduce": 3 * C * S * 4, "step": 0}
+    return Row("replica_train", "replica weight sync (bf16) and gradient reduction (f32), 256 "
+               "experts + 32 replicas, one 7168x2048 matrix per expert", None, calls, nb,
+               ("weight_sync", "grad_reduce"), reps=5, extra={"buffer_sets": 1},
+               holder=(idx, load, rc, rp, p2l, wbuf, g))
+
+
+# --------------------------------------------------------------------------
+# measuring a row
+
+
+def measure_row(torch, stream, gate, row, reps_hint, pmc, trace):
+    """Step time (graph replays of the rotating steps) and each call alone
+    (graph of one call per set); algorithmic GB/s and the fraction of peak;
+    HBM bytes from the committed counter summary; the committed trace's
+    kernel time per call."""
+    res = {"workload": row.workload}
+    res.update({k: v for k, v in row.extra.items()
+                if k not in ("workload_obj", "two_launch_step")})
+    S = len(next(iter(row.calls.values())))
+    reps = row.reps or max(4, reps_hint // max(S, 1))
+    if row.step:
+        us = graph_us(torch, stream, gate, row.step, reps, row.launches)
+        res["us_per_step"] = round(us, 3)
+        res["GB_per_s"] = round(row.nbytes["step"] / us / 1e3, 1)
+        res["algorithmic_bytes_per_step"] = row.nbytes["step"]
+    if "two_launch_step" in row.extra:
+        us2 = graph_us(torch, stream, gate, row.extra["two_launch_step"], reps, 3)
+        res["us_per_step_layout_then_dispatch"] = round(us2, 3)
+    kern = {}
+    for name, fns in row.calls.items():
+        us = graph_us(torch, stream, gate, fns, max(reps, 2) if len(fns) > 1 else reps)
+        nb = row.nbytes.get(name, 0)
+        d = {"us": round(us, 3), "algorithmic_bytes": nb}
+        if nb:
+            d["GB_per_s"] = round(nb / us / 1e3, 1)
+            d["frac"] = round(nb / us / 1e3 / HBM_PEAK_GBS, 4)
+        seg = f"{row.key}/{name}"
+        t = pmc.get(("traffic", seg))
+        d["traffic"] = round(t) if t is not None else None
+        if t is not None and nb:
+            d["traffic_ratio"] = round(t / nb, 3)
+        tr = trace.get(("trace_us", seg + " per_call"))
+        if tr is not None:
+            d["trace_us"] = round(tr, 3)
+        kern[name] = d
+    res["calls"] = kern
+    return res
+
+
+def pmc_traffic(summary):
+    """HBM bytes per call of each profiled segment: FETCH_SIZE and WRITE_SIZE
+    (KiB per call) scaled by what they read for a copy of known size (the
+    floor copy kernel)."""
+    out = {}
+    f_cal = summary.get(("fetch_kib", "floors/copy_256MiB per_call"))
+    w_cal = summary.get(("write_kib", "floors/copy_256MiB per_call"))
+    if not f_cal or not w_cal:
+        return out
+    true_kib = 256 * 1024
+    ff, fw = f_cal / true_kib, w_cal / true_kib
+    out["factors"] = (ff, fw)
+    for (kind, key), v in summary.items():
+        if kind != "fetch_kib" or not key.endswith(" per_call"):
+            continue
+        seg = key[:-len(" per_call")]
+        wv = summary.get(("write_kib", key))
+        if wv is None:
+            continue
+        out[("traffic", seg)] = (v / ff + wv / fw) * 1024
+    return out
+
+
+# --------------------------------------------------------------------------
+# CPU baseline
+
+
+def host_cpu_info():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(omp)) if omp and omp.isdigit() and int(omp) > 0 else affinity
+    return model, affinity, threads
+
+
+def cpu_baseline(w, budget_s, gpu_out_bits, total_bytes):
+    """The oracle as it stands on this workload's step, per phase (layout,
+    dispatch, float combine): once single-threaded, once on all the host
+    cores this process may use (the OpenMP build: dispatch and combine split
+    over tokens, the layout pass serial). Each leg's output is checked
+    against the timed GPU output (bit for bit against the float path, and
+    within 1e-2 / 1e-3 of the double sum)."""
+    import numpy as np
+
+    import oracle
+
+    model, affinity, threads = host_cpu_info()
+    legs = {}
+    ref64 = None
+    for leg, orc, nthr in (("single_thread", oracle.get(), 1),
+                           ("all_cores", oracle.get_parallel(), threads)):
+        used = orc.threads(nthr)
+        recv = None
+        t = {"layout": [], "dispatch": [], "combine": []}
+        t0 = time.perf_counter()
+        c = None
+        while True:
+            a = time.perf_counter()
+            lay = orc.layout(w.topk_idx, w.E, w.R, w.A)
+            b = time.perf_counter()
+            if recv is None or recv.shape[0] < lay["rows"]:
+                recv = np.empty((lay["rows"], w.H), np.uint16)
+            r, _ = orc.dispatch(w.x, lay["slot"], lay["rows"], out=recv[:lay["rows"]])
+            c_ = time.perf_counter()
+            c = orc.combine(r, lay["slot"], w.topk_weights, "f32")
+            d = time.perf_counter()
+            t["layout"].append(b - a)
+            t["dispatch"].append(c_ - b)
+            t["combine"].append(d - c_)
+            if d - t0 >= budget_s / 2 or len(t["layout"]) >= 100000:
+                break
+        if ref64 is None:
+            ref64 = orc.combine(r, lay["slot"], w.topk_weights, "f64")["out_f64"]
+        got = (gpu_out_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        ok = bool(np.array_equal(c["out_bf16"], gpu_out_bits)) and \
+            bool(np.all(np.abs(got - ref64) <= 1e-3 + 1e-2 * np.abs(ref64)))
+        n = len(t["layout"])
+        step = sum(sum(v) for v in t.values()) / n
+        legs[leg] = {"threads": used, "steps": n,
+                     "us": {k: round(statistics.median(v) * 1e6, 1) for k, v in t.items()},
+                     "us_per_step": round(step * 1e6, 1),
+                     "GB_per_s": round(total_bytes / step / 1e9, 3), "parity_ok": ok}
+        log(f"cpu oracle {leg} ({used} threads): {n} steps, {step * 1e6:.0f} us/step, "
+            f"parity {'ok' if ok else 'FAILED'}")
+    a = legs["all_cores"]
+    return {"value": a["GB_per_s"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+            "sample": f"{a['steps']} full steps (layout, dispatch, float combine) of the "
+                      f"standard 128x7168 batch on {a['threads']} threads, and "
+                      f"{legs['single_thread']['steps']} on 1 thread, about "
+                      f"{budget_s / 2:.0f} s each; per-phase medians in legs",
+            "cpu_model": model, "affinity_cores": affinity, "legs": legs,
+            "parity_ok": all(v["parity_ok"] for v in legs.values())}
+
+
+# --------------------------------------------------------------------------
+# floor kernels (libmoe_floors.so, measurement only)
+
+
+class Floors:
+    def __init__(self):
+        import ctypes as C
+
+        from combine_moe_layout_03_amd import build as hb
+
+        if not os.path.exists(hb.FLOOR_LIB):
+            raise ImportError(f"{hb.FLOOR_LIB} is not built; run __graft_entry__.build()")
+        self.C = C
+        lib = C.CDLL(hb.FLOOR_LIB)
+        P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
+        lib.moe_floor_empty.argtypes = [I32, I32, P]
+        lib.moe_floor_bcast.argtypes = [P, P, I32, I32, I32, P]
+        lib.moe_floor_gather.argtypes = [P, P, I32, I32, I32, P]
+        lib.moe_floor_copy.argtypes = [P, P, I64, P]
+        self.lib = lib
+
+    @staticmethod
+    def _s(stream):
+        import ctypes as C
+        return C.c_void_p(stream.cuda_stream)
+
+    def _ok(self, rc, fn):
+        if rc != 0:
+            raise RuntimeError(f"{fn} failed ({rc})")
+
+    def empty(self, wgs, threads, stream):
+        self._ok(self.lib.moe_floor_empty(wgs, threads, self._s(stream)), "moe_floor_empty")
+
+    def bcast(self, x, out, T, H, K, stream):
+        self._ok(self.lib.moe_floor_bcast(x.data_ptr(), out.data_ptr(), T, H, K,
+                                          self._s(stream)), "moe_floor_bcast")
+
+    def gather(self, y, out, T, H, K, stream):
+        self._ok(self.lib.moe_floor_gather(y.data_ptr(), out.data_ptr(), T, H, K,
+                                           self._s(stream)), "moe_floor_gather")
+
+    def copy(self, src, dst, nbytes, stream):
+        self._ok(self.lib.moe_floor_copy(src.data_ptr(), dst.data_ptr(), nbytes,
+                                         self._s(stream)), "moe_floor_copy")
+
+
+# --------------------------------------------------------------------------
+# profile pass and summaries
+
+
+def profile_pass(args, capi, floors, mi, torch, np, dev, stream):
+    """Graph replays only: for each segment (a row's step, or one call of a
+    row alone), a marker launch, the segment's graph, another marker. A
+    kernel trace or a counter pass thus sees exactly the timed launches
+    between each pair of markers (buffer set-up runs outside them). The
+    segment list goes to --segments-out."""
+    segs = []
+    mark = lambda: floors.empty(MARKER[0], MARKER[1], stream)  # noqa: E731
+
+    def run(seg, fns, calls, reps=1):
+        g = capture(torch, stream, fns)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            mark()
+            for _ in range(reps):
+                g.replay()
+            mark()
+        torch.cuda.synchronize()
+        del g
+        segs.append({"name": seg, "calls": calls * reps})
+        log(f"segment {seg}: {calls * reps} calls")
+
+    def do_row(row, step_reps=1, call_reps=1, only_step=False):
+        if row.step:
+            run(f"{row.key}/step", row.step, len(row.step), step_reps)
+        if not only_step:
+            for name, fns in row.calls.items():
+                run(f"{row.key}/{name}", fns, len(fns), call_reps)
+        row.release(torch)
+
+    std = row_standard_kind(capi, mi, torch, dev, stream, "c2", "standard", args.sets,
+                            args.arena)
+    if args.profile_pass == "standard":
+        S = len(std.step)
+        do_row(std, step_reps=max(1, args.steps // S), only_step=True)
+    else:
+        do_row(std)
+        do_row(row_floors(capi, floors, mi, torch, np, dev, stream))
+        for M in mi.C3_SWEEP:
+            do_row(row_low_latency(capi, mi, torch, np, dev, stream, M=M, masked=True))
+        for fl in (0, capi.MOE_FP8_SCALE_ROWS):
+            do_row(row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=fl))
+        do_row(row_normal(capi, mi, torch, np, dev, stream))
+        for name in ("c1", "c4"):
+            do_row(row_standard_kind(capi, mi, torch, dev, stream, name, f"config_{name}"))
+        do_row(row_replica(capi, mi, torch, np, dev, stream))
+        do_row(row_replica_train(capi, mi, torch, np, dev, stream))
+    torch.cuda.synchronize()
+    os.makedirs(os.path.dirname(os.path.abspath(args.segments_out)), exist_ok=True)
+    with open(args.segments_out, "w") as f:
+        json.dump({"segments": segs, "kernel_source_hash": kernel_source_hash()}, f, indent=1)
+    log(f"profile pass done: {len(segs)} segments -> {args.segments_out}")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(r, *names):
+    for n in names:
+        if n in r and r[n] != "":
+            return r[n]
+    return None
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").strip()
+    name = re.sub(r"^moe::", "", name)
+    return re.sub(r"\([^()]*\)$", "", name).strip()  # drop the argument list
+
+
+def _dispatches(d):
+    """Dispatches of one rocprofv3 CSV output dir, in dispatch order: name,
+    grid and workgroup size (threads), and the duration (kernel trace) or the
+    counter values (counter collection; a counter repeated for one dispatch
+    is counted once)."""
+    disp = {}
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in _csv_rows(path):
+            e = disp.setdefault(int(_col(r, "Dispatch_Id", "Correlation_Id")), {})
+            e["name"] = _col(r, "Kernel_Name")
+            e["grid"] = int(float(_col(r, "Grid_Size_X", "Grid_Size") or 0))
+            e["wg"] = int(float(_col(r, "Workgroup_Size_X", "Workgroup_Size") or 0))
+            e["dur"] = (int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in _csv_rows(path):
+            e = disp.setdefault(int(_col(r, "Dispatch_Id", "Correlation_Id")), {})
+            e["name"] = _col(r, "Kernel_Name")
+            e["grid"] = int(float(_col(r, "Grid_Size", "Grid_Size_X") or 0))
+            e["wg"] = int(float(_col(r, "Workgroup_Size", "Workgroup_Size_X") or 0))
+            e.setdefault("ctr", {}).setdefault(_col(r, "Counter_Name"),
+                                               float(_col(r, "Counter_Value")))
+    return [disp[i] for i in sorted(disp)]
+
+
+def _segments(es, names):
+    """Split dispatches at the marker launches: segment i lies between marker
+    2i and marker 2i + 1 (what runs between segments belongs to none)."""
+    marks = [j for j, e in enumerate(es)
+             if "floor_empty_kernel" in (e.get("name") or "") and e["grid"] == MARKER[0] * MARKER[1]
+             and e["wg"] == MARKER[1]]
+    if len(marks) != 2 * len(names):
+        raise SystemExit(f"found {len(marks)} markers for {len(names)} segments")
+    return {n: es[marks[2 * i] + 1: marks[2 * i + 1]] for i, n in enumerate(names)}
+
+
+def summarize(dirs, segments_path):
+    """Aggregate each segment of rocprofv3 CSV output (a kernel trace, or one
+    counter pass per dir): per kernel (name, grid, workgroup) the launches and
+    the mean/median/min duration or the mean counter values, and per call of
+    the segment the totals. Prints markdown with machine-read
+    `kind segment: value` lines."""
+    seg = json.load(open(segments_path))
+    names = [s["name"] for s in seg["segments"]]
+    calls = {s["name"]: s["calls"] for s in seg["segments"]}
+    per_dir = [_segments(_dispatches(d), names) for d in dirs]
+    lines, mach = [], []
+    for sname in names:
+        lines.append(f"\n### {sname} ({calls[sname]} calls)\n")
+        groups = {}  # (kernel, grid, wg) -> {"dur": [...], counter: [...]}
+        for segs in per_dir:
+            for e in segs[sname]:
+                g = groups.setdefault((_short(e["name"]), e["grid"], e["wg"]), {})
+                g.setdefault("n", []).append(1)
+                if "dur" in e:
+                    g.setdefault("dur", []).append(e["dur"])
+                for c, v in e.get("ctr", {}).items():
+                    g.setdefault(c, []).append(v)
+        cnames = sorted({c for g in groups.values() for c in g if c not in ("n", "dur")})
+        has_dur = any("dur" in g for g in groups.values())
+        head = ["kernel", "grid (threads)", "workgroup", "launches"]
+        if has_dur:
+            head += ["mean µs", "median µs", "min µs"]
+        head += [f"{c} KiB (mean)" for c in cnames]
+        lines.append("| " + " | ".join(head) + " |")
+        lines.append("|" + "---|" * len(head))
+        tot = {c: 0.0 for c in cnames}
+        tot_dur = 0.0
+        for (kn, grid, wg), g in sorted(groups.items(), key=lambda kv: -len(kv[1]["n"])):
+            n = len(g.get("dur", [])) or max(len(g.get(c, [])) for c in cnames)
+            cells = [f"`{kn}`", str(grid), str(wg), str(n)]
+            if has_dur:
+                ds = g.get("dur", [])
+                cells += ([f"{statistics.mean(ds):.3f}", f"{statistics.median(ds):.3f}",
+                           f"{min(ds):.3f}"] if ds else ["—"] * 3)
+                if ds:
+                    tot_dur += sum(ds)
+                    mach.append(f"trace_us {sname} {kn}@{grid}: {statistics.mean(ds):.4f}")
+            for c in cnames:
+                v = g.get(c, [])
+                tot[c] += sum(v)
+                cells.append(f"{statistics.mean(v):.1f}" if v else "—")
+            lines.append("| " + " | ".join(cells) + " |")
+        if has_dur:
+            mach.append(f"trace_us {sname} per_call: {tot_dur / calls[sname]:.4f}")
+        for c in cnames:
+            kind = {"FETCH_SIZE": "fetch_kib", "WRITE_SIZE": "write_kib"}.get(c, c.lower())
+            mach.append(f"{kind} {sname} per_call: {tot[c] / calls[sname]:.2f}")
+    print("\n".join(lines))
+    print("\nMachine-read by bench.py (valid only while the kernel sources hash to the value "
+          "below):\n")
+    print(f"kernel_source_hash: {seg['kernel_source_hash']}")
+    for m in mach:
+        print(m)
+
+
+# --------------------------------------------------------------------------
 
 
 def main():
@@ -522,14 +1051,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--sets", type=int, default=0,
                     help="rotating buffer sets (0: enough for >= 512 MiB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=16.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the low-latency and replica-path measurements")
-    ap.add_argument("--profile-pass", action="store_true",
-                    help="short fixed run for rocprofv3: warm-up, copy calibration, steps")
+                    help="only the standard step (no floors, other rows)")
+    ap.add_argument("--profile-pass", choices=("standard", "all"), default=None,
+                    help="graph replays only, for rocprofv3")
+    ap.add_argument("--segments-out", default=os.path.join(ROOT, "gpurun_out", "segments.json"))
+    ap.add_argument("--summarize", nargs="+", metavar="DIR", default=None,
+                    help="rocprofv3 CSV output dirs to summarise (with --segments)")
+    ap.add_argument("--segments", default=None)
+    ap.add_argument("--arena", action="store_true",
+                    help="carve the standard step's buffer sets from one allocation")
     args = ap.parse_args()
+
+    if args.summarize:
+        summarize(args.summarize, args.segments or args.segments_out)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU: the logical ranks are "
@@ -546,172 +1084,131 @@ def main():
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device {props.name} {getattr(props, 'gcnArchName', '?')} CUs={props.multi_processor_count}")
-
-    w = mi.config_c2()
-    P_valid = int((w.topk_idx >= 0).sum())
-    ab = algo_bytes(w.T, w.H, w.K, w.E, w.R, P_valid)
-    probe = Workset(capi, w, dev)
-    S = args.sets or max(2, math.ceil(512 * 2**20 / probe.nbytes))
-    sets = [probe] + [Workset(capi, w, dev) for _ in range(S - 1)]
-    log(f"workload {w.name}: {S} buffer sets x {probe.nbytes / 2**20:.1f} MiB")
     stream = torch.cuda.Stream()  # default priority
-
-    # eager warm-up (also runs the one-time device check outside any capture)
-    with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(capi, sets[i % S], stream)
-    torch.cuda.synchronize()
-    ref_out = sets[0].out.clone()
+    floors = Floors()
 
     if args.profile_pass:
-        # calibration copy of known size for the PMC counters, then steps
-        a = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
+        # the library's one-time device check, on a shape whose kernels the
+        # timed ones do not share (top-1)
+        t1 = capi.make_shape(1, 8, 1, 1, 1, 1)
+        lb = capi.LayoutBuffers.empty(t1, dev)
+        xx = torch.zeros(1, 8, dtype=torch.int16, device=dev)
+        rr = torch.empty(1, 8, dtype=torch.int16, device=dev)
+        capi.moe_layout_dispatch(t1, torch.zeros(1, 1, dtype=torch.int64, device=dev), lb, xx,
+                                 rr, 1, stream=stream)
         torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            for i in range(args.steps):
-                step(capi, sets[i % S], stream)
-        torch.cuda.synchronize()
-        log(f"profile pass done: 3 x copy of 256 MiB, {args.steps} steps")
+        profile_pass(args, capi, floors, mi, torch, np, dev, stream)
         return
 
+    gate = Gate(torch, stream)
+    pmc = pmc_traffic(read_summary(PMC_SUMMARY))
+    trace = {}
+    trace.update(read_summary(TRACE_ROWS_SUMMARY))
+    trace.update(read_summary(TRACE_SUMMARY))
+
+    # ---- the headline: the standard step, exactly --steps of them ----
+    std = row_standard_kind(capi, mi, torch, dev, stream, "c2", "standard", args.sets,
+                            args.arena)
+    w = std.extra["workload_obj"]
+    zs = std.holder[0]
+    S = len(zs)
+    ab = algo_bytes(w.T, w.H, w.K, w.E, w.R, int((w.topk_idx >= 0).sum()))
+    log(f"workload {w.name}: {S} buffer sets, {std.extra['footprint_MiB']} MiB")
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            std.step[i % S]()
+    torch.cuda.synchronize()
+    ref_out = zs[0].out.clone()
     K = args.steps
-    if args.eager:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
-            start = torch.cuda.Event(enable_timing=True)
-            end = torch.cuda.Event(enable_timing=True)
-            start.record(stream)
-            for i in range(K):
-                step(capi, sets[i % S], stream)
-            end.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(end)
-        mode = "eager"
-    else:
-        g_full = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_full, stream=stream):
-            for i in range(S):
-                step(capi, sets[i], stream)
-        rem = K % S
-        g_rem = None
-        if rem:
-            g_rem = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_rem, stream=stream):
-                for i in range(rem):
-                    step(capi, sets[i], stream)
-        # graph warm-up replays, then check they reproduce the eager output
-        for _ in range(3):
+    g_full = capture(torch, stream, std.step)
+    rem = K % S
+    g_rem = capture(torch, stream, std.step[:rem]) if rem else None
+    for _ in range(3):
+        g_full.replay()
+        if g_rem is not None:
+            g_rem.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(zs[0].out, ref_out), "graph replay differs from the eager step"
+
+    def go():
+        for _ in range(K // S):
             g_full.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(sets[0].out, ref_out), "graph replay differs from eager step"
-        ms = time_graph_steps(torch, g_full, g_rem, K // S, stream)
-        mode = "hip_graph"
+        if g_rem is not None:
+            g_rem.replay()
+
+    def warm():  # untimed steps ahead of the start event: about 2 ms of them
+        for _ in range(max(2, math.ceil(200 / S))):
+            g_full.replay()
+    ms = timed_ms(torch, stream, gate, go, 2 * K, warm=warm)
     us_step = ms * 1e3 / K
     value = ab["total"] / (us_step * 1e-6) / 1e9
-    log(f"{mode}: {K} steps in {ms:.3f} ms -> {us_step:.2f} us/step, {value:.1f} GB/s")
+    log(f"hip_graph: {K} steps in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s")
+    del g_full, g_rem
     # secondary: the same step on one buffer set over and over (caches warm)
-    warm_us = None
-    if not args.eager:
-        warm_us = graph_us_per_step(torch, stream, [(lambda: step(capi, sets[0], stream))] * S,
-                                    max(4, 400 // S))
-        log(f"warm (one buffer set): {warm_us:.2f} us/step")
+    warm_us = graph_us(torch, stream, gate, [std.step[0]] * S, max(4, 400 // S), 2)
+    log(f"warm (one buffer set): {warm_us:.3f} us/step")
+    std_res = measure_row(torch, stream, gate, std, 400, pmc, trace)
+    out_bits = zs[0].out.cpu().numpy().view(np.uint16)
+    assert np.array_equal(out_bits, ref_out.cpu().numpy().view(np.uint16))
+    std.release(torch)
 
-    # per-kernel durations: each launch bracketed by events, rotating sets
-    n = min(400, max(50, K // 4))
-
-    def ev(fn):
-        with torch.cuda.stream(stream):
-            return per_launch_event_times(torch, fn, n, stream)
-
-    def z(i):
-        return sets[i % S]
-
-    # primary: each kernel alone, one HIP graph of S launches over the rotating
-    # sets, events around the replays (the configuration of the timed steps);
-    # secondary: every launch bracketed by its own event pair (adds the launch
-    # latency of an eager launch)
-    fns = {
-        "layout_dispatch": lambda i: capi.moe_layout_dispatch(
-            z(i).shape, z(i).idx, z(i).lay, z(i).x, z(i).recv, z(i).rows, z(i).ws,
-            stream=stream),
-        "combine": lambda i: capi.moe_combine(
-            z(i).shape, z(i).recv, z(i).rows, z(i).lay.slot, z(i).w, z(i).out, None, None,
-            stream=stream),
-        # reference: the same work as two separate kernels
-        "layout": lambda i: capi.moe_layout(z(i).shape, z(i).idx, z(i).lay, z(i).ws,
-                                            stream=stream),
-        "dispatch": lambda i: capi.moe_dispatch(z(i).shape, z(i).x, z(i).lay.slot, z(i).recv,
-                                                z(i).rows, None, stream=stream),
-    }
-    kern = {}
-    for name, fn in fns.items():
-        g_us = graph_us_per_step(torch, stream, [(lambda i=i, fn=fn: fn(i)) for i in range(S)],
-                                 max(4, n // S))
-        e = ev(fn)
-        kern[name] = {"mean_us": g_us, "event_mean_us": e["mean_us"],
-                      "event_median_us": e["median_us"]}
-    kbytes = {"layout_dispatch": ab["layout"] + ab["dispatch"], "combine": ab["combine"],
-              "layout": ab["layout"], "dispatch": ab["dispatch"]}
-    dom = max(("layout_dispatch", "combine"), key=lambda k: kern[k]["mean_us"])
-    dur = kern[dom]["mean_us"]
-    achieved = kbytes[dom] / (dur * 1e-6) / 1e9
-    traffic = read_traffic(dom)
+    # roofline: the longer of the step's two kernels, live duration from the
+    # event-timed graph of that call alone
+    kc = std_res["calls"]
+    dom = max(std.main, key=lambda k: kc[k]["us"])
+    dur = kc[dom]["us"]
+    achieved = kc[dom]["algorithmic_bytes"] / (dur * 1e-6) / 1e9
+    tr_step = {k[1].split(" ", 1)[1]: v for k, v in trace.items()
+               if k[0] == "trace_us" and k[1].startswith("standard/step ")}
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "algorithmic_bytes": kbytes[dom],
-                "duration_us": round(dur, 3)}
+                "traffic": kc[dom]["traffic"], "algorithmic_bytes": kc[dom]["algorithmic_bytes"],
+                "duration_us": dur,
+                "trace_mean_us_in_step": {k: round(v, 3) for k, v in tr_step.items()} or None}
 
     rows = {}
     if not args.no_rows:
-        rows["low_latency_m128"] = row_low_latency(capi, mi, torch, np, dev, stream)
-        log(f"low-latency row: {rows['low_latency_m128']['us_per_step']} us/step")
-        sweep = {}
-        for M in (16, 32, 64, 256, 512):
-            r = row_low_latency(capi, mi, torch, np, dev, stream, M=M)
-            sweep[str(M)] = {k: r[k] for k in ("us_per_step", "GB_per_s", "kernels_us",
-                                               "buffer_sets")}
-            log(f"low-latency M={M}: {r['us_per_step']} us/step")
-        m128 = rows["low_latency_m128"]
-        sweep["128"] = {k: m128[k] for k in ("us_per_step", "GB_per_s", "kernels_us",
-                                             "buffer_sets")}
+        rlist = [lambda: row_floors(capi, floors, mi, torch, np, dev, stream)]
+        for M in mi.C3_SWEEP:
+            rlist.append(lambda M=M: row_low_latency(capi, mi, torch, np, dev, stream, M=M,
+                                                     masked=True))
+        for fl in (0, capi.MOE_FP8_SCALE_ROWS):
+            rlist.append(lambda fl=fl: row_low_latency(capi, mi, torch, np, dev, stream,
+                                                       fp8_flags=fl))
+        rlist.append(lambda: row_normal(capi, mi, torch, np, dev, stream))
+        for name in ("c1", "c4"):
+            rlist.append(lambda name=name: row_standard_kind(capi, mi, torch, dev, stream, name,
+                                                             f"config_{name}"))
+        rlist.append(lambda: row_replica(capi, mi, torch, np, dev, stream))
+        rlist.append(lambda: row_replica_train(capi, mi, torch, np, dev, stream))
+        for make in rlist:
+            row = make()
+            rows[row.key] = measure_row(torch, stream, gate, row, 200, pmc, trace)
+            log(f"row {row.key}: " + ", ".join(f"{k} {v['us']} us" for k, v in
+                                               rows[row.key]["calls"].items()))
+            row.release(torch)
+        # the low-latency sweep and the masked combine, side by side
+        sweep, masked = {}, {}
+        for M in mi.C3_SWEEP:
+            r = rows.pop(f"low_latency_m{M}")
+            c = r["calls"]
+            sweep[str(M)] = {k: r[k] for k in ("us_per_step", "GB_per_s", "buffer_sets")}
+            sweep[str(M)]["calls"] = {k: c[k] for k in ("ll_layout_dispatch", "combine")}
+            masked[str(M)] = {k: c[k] for k in ("combine", "combine_masked_none",
+                                                "combine_masked_rank3")}
+            if M == 128:
+                rows["low_latency_m128"] = dict(r, calls=sweep["128"]["calls"])
         rows["low_latency_sweep"] = {
             "workload": "low-latency padded layout + dispatch + combine, M tokens per rank "
-                        "(T = M) x 7168, 256E top-8, 8 ranks",
-            "by_M": {k: sweep[k] for k in sorted(sweep, key=int)}}
-        rows["low_latency_fp8_m128"] = row_low_latency(capi, mi, torch, np, dev, stream, 0)
-        log(f"low-latency FP8 row: {rows['low_latency_fp8_m128']['us_per_step']} us/step")
-        rows["low_latency_fp8_rowscales_m128"] = row_low_latency(
-            capi, mi, torch, np, dev, stream, capi.MOE_FP8_SCALE_ROWS)
-        log(f"low-latency FP8 row-major scales: "
-            f"{rows['low_latency_fp8_rowscales_m128']['us_per_step']} us/step")
-        rows["normal_mode_128x7168"] = row_normal(capi, mi, torch, np, dev, stream)
-        log(f"normal-mode row: {rows['normal_mode_128x7168']['us_per_step']} us/step")
-        for cname in ("c1", "c4"):
-            rows[f"config_{cname}"] = row_config(capi, mi, torch, np, dev, stream, cname)
-            log(f"{cname} row: {rows[f'config_{cname}']['us_per_step']} us/step")
-        rows["replica_path_8192"] = row_replica(capi, mi, torch, np, dev, stream, n)
-        log(f"replica row: {rows['replica_path_8192']['us_per_step']} us/step")
-        rows["replica_train"] = row_replica_train(capi, mi, torch, np, dev, stream)
-        log(f"replica sync/reduce row: {rows['replica_train']['weight_sync_us']} / "
-            f"{rows['replica_train']['grad_reduce_us']} us")
-
-    torch.cuda.synchronize()
-    out_bits = sets[0].out.cpu().numpy().view(np.uint16)
-    assert np.array_equal(out_bits, ref_out.cpu().numpy().view(np.uint16))
+                        "(T = M) x 7168, 256E top-8, 8 ranks", "by_M": sweep}
+        rows["masked_combine"] = {
+            "workload": "low-latency combine at M tokens per rank x 7168 (256E top-8, 8 ranks): "
+                        "plain, with an active-rank mask of no masked rank, and with rank 3 "
+                        "masked (its pairs are left out of the sum)", "by_M": masked}
 
     cpu = None
     if not args.no_cpu_baseline:
-        reps, el, ok = cpu_baseline(w, args.cpu_seconds, out_bits)
-        cpu_v = ab["total"] * reps / el / 1e9
-        cpu = {"value": round(cpu_v, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{reps} full steps (layout+dispatch+combine f64) of the same "
-                         f"128x7168 batch in {el:.1f} s, single thread",
-               "us_per_step": round(el / reps * 1e6, 1), "parity_ok": ok}
-        log(f"cpu oracle: {reps} steps in {el:.1f}s, parity {'ok' if ok else 'FAILED'}")
+        cpu = cpu_baseline(w, args.cpu_seconds, out_bits, ab["total"])
 
     res = {
         "metric": METRIC,
@@ -731,13 +1228,14 @@ def main():
         "config": {"workload": "standard: 128 tokens x 7168 hidden bf16, 256 experts on 8 "
                                "logical ranks, top-8 uniform, softmax weights, identity expert",
                    "T": w.T, "H": w.H, "E": w.E, "R": w.R, "K": w.K, "A": w.A,
-                   "timing": mode, "buffer_sets": S,
-                   "footprint_MiB": round(S * probe.nbytes / 2**20, 1),
+                   "timing": "hip_graph", "buffer_sets": S,
+                   "footprint_MiB": std.extra["footprint_MiB"],
                    "algorithmic_bytes_per_step": ab["total"]},
-        "us_per_step_warm": round(warm_us, 3) if warm_us is not None else None,
+        "us_per_step_warm": round(warm_us, 3),
         "hbm_peak_reported_by_device": device_hbm_figures(dev.index or 0),
-        "kernels_us": {k: round(v["mean_us"], 3) for k, v in kern.items()},
-        "kernels_eager_event_us": {k: round(v["event_mean_us"], 3) for k, v in kern.items()},
+        "kernels_us": {k: v["us"] for k, v in kc.items()},
+        "standard_calls": kc,
+        "pmc_calibration_factors": list(pmc["factors"]) if "factors" in pmc else None,
         "roofline": roofline,
         "rows": rows,
         "cpu_baseline": cpu,

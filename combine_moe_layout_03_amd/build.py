@@ -15,6 +15,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_ep.so")
 SOURCES = ["capi.hip", "layout.hip", "fused.hip", "scatter.hip", "fp8.hip", "ranks.hip",
            "rank_fused.hip", "replica.hip"]
+# floor kernels for the benchmark (measurement only; not part of the C ABI)
+FLOOR_LIB = os.path.join(PKG, "libmoe_floors.so")
+FLOOR_SOURCES = ["floors.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -29,19 +32,26 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(out: str, sources, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build libmoe_ep.so")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"hipcc failed to build {os.path.basename(out)}")
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """libmoe_ep.so (the library) and libmoe_floors.so (the benchmark's floor
+    kernels)."""
+    _hipcc(FLOOR_LIB, FLOOR_SOURCES, verbose)
+    return _hipcc(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":
