@@ -20,7 +20,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_ep.so")
 
-MOE_ABI_VERSION = 4  # the version the binding is written against
+MOE_ABI_VERSION = 5  # the version the binding is written against
+MOE_STATIC_SCRATCH_BYTES = 4 << 20
 
 MOE_STATUS_BAD_EXPERT = 1
 MOE_STATUS_LL_OVERFLOW = 2
@@ -69,6 +70,7 @@ def _load():
         "moe_layout": (C.c_int, [P, P, P, P, SZ, P]),
         "moe_ll_layout": (C.c_int, [P, I32, I32, P, P, P, SZ, P]),
         "moe_layout_dispatch": (C.c_int, [P, P, P, P, P, I64, P, SZ, P]),
+        "moe_layout_dispatch_static": (C.c_int, [P, P, P, P, P, I64, P]),
         "moe_ll_layout_dispatch": (C.c_int, [P, I32, I32, P, P, P, P, I64, P, SZ, P]),
         "moe_expert_load": (C.c_int, [I32, I32, I32, P, P, P, P]),
         "moe_dispatch": (C.c_int, [P, P, P, P, I64, P, P]),
@@ -99,6 +101,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_abi_version", "moe_strerror", "moe_recv_rows_worst", "moe_ll_recv_rows",
             "moe_layout_workspace_bytes", "moe_layout", "moe_ll_layout", "moe_layout_dispatch",
+            "moe_layout_dispatch_static",
             "moe_ll_layout_dispatch", "moe_expert_load",
             "moe_dispatch", "moe_combine", "moe_plan_replicas", "moe_reroute",
             "moe_quantize_fp8", "moe_ll_layout_dispatch_fp8", "moe_ll_dispatch_fp8",
@@ -332,6 +335,20 @@ def moe_layout_dispatch(shape: moe_shape, topk_idx: torch.Tensor, out: LayoutBuf
     return _check("moe_layout_dispatch", _lib.moe_layout_dispatch(
         C.byref(shape), idx, C.byref(st), _dev(x, "x", _BF16_LIKE, T * H),
         _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows), wsp, wsn,
+        _stream(stream)))
+
+
+def moe_layout_dispatch_static(shape: moe_shape, topk_idx: torch.Tensor, out: LayoutBuffers,
+                               x: torch.Tensor, recv_x: torch.Tensor, recv_rows: int,
+                               stream=None) -> int:
+    """moe_layout_dispatch without a workspace argument: the library's static
+    per-GPU scratch serves the batches that need one (nothing is allocated)."""
+    T, H, K = shape.T, shape.H, shape.K
+    idx = _dev(topk_idx, "topk_idx", (torch.int64,), T * K)
+    st = out._struct(shape, None)
+    return _check("moe_layout_dispatch_static", _lib.moe_layout_dispatch_static(
+        C.byref(shape), idx, C.byref(st), _dev(x, "x", _BF16_LIKE, T * H),
+        _dev(recv_x, "recv_x", _BF16_LIKE, int(recv_rows) * H), int(recv_rows),
         _stream(stream)))
 
 

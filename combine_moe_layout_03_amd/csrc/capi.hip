@@ -25,6 +25,14 @@ constexpr int kMaxDevices = 64;
 constexpr int kMaxRanksNormal = 64;  // a token's set of ranks is one 64-bit mask
 std::atomic<int> g_arch[kMaxDevices];  // 0 = not checked yet, 1 = gfx950, 2 = other
 
+// Layout workspace of moe_layout_dispatch_static, for callers that cannot
+// allocate: one array per GPU, held until the process ends. In host code its
+// name stands for no device address; the address comes from
+// hipGetSymbolAddress, once per device, kept in g_scratch.
+static_assert(MOE_STATIC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+std::atomic<uintptr_t> g_scratch[kMaxDevices];  // 0 = not looked up yet
+
 // The kernels are compiled for gfx950 only; refuse any other current device.
 int check_device() {
   int dev = -1;
@@ -37,6 +45,22 @@ int check_device() {
     if (dev < kMaxDevices) g_arch[dev].store(state, std::memory_order_relaxed);
   }
   return state == 1 ? MOE_OK : MOE_ERR_ARCH;
+}
+
+// Device address of the current device's scratch array (looked up on the first
+// call on each device, with that device current). NULL if the lookup fails.
+void *device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  uintptr_t a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    a = reinterpret_cast<uintptr_t>(ptr);
+    g_scratch[dev].store(a, std::memory_order_release);
+  }
+  return reinterpret_cast<void *>(a);
 }
 
 int bits_for(int n) {  // bits needed to tell apart the values 0 .. n-1
@@ -221,6 +245,8 @@ MOE_API const char *moe_strerror(int code) {
     case MOE_ERR_ARCH: return "current device is not gfx950";
     case MOE_ERR_DEVICE: return "HIP runtime query failed";
     case MOE_ERR_FLAGS: return "unsupported FP8 flag combination";
+    case MOE_ERR_SCRATCH:
+      return "shape needs a larger layout workspace than the static scratch holds";
     default: return "unknown error code";
   }
 }
@@ -257,6 +283,24 @@ MOE_API int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx,
                                 hipStream_t stream) {
   return layout_dispatch_common(shape, kModeContiguous, 0, 0, topk_idx, out, x, recv_x,
                                 recv_rows, nullptr, ws, ws_bytes, stream);
+}
+
+MOE_API int moe_layout_dispatch_static(const moe_shape *shape, const int64_t *topk_idx,
+                                       const moe_layout_t *out, const uint16_t *x,
+                                       uint16_t *recv_x, int64_t recv_rows, hipStream_t stream) {
+  int rc = check_shape(shape, true);
+  if (rc) return rc;
+  const size_t need = workspace_bytes(shape);
+  if (need == 0)  // counted or one-workgroup layout: no scratch
+    return layout_dispatch_common(shape, kModeContiguous, 0, 0, topk_idx, out, x, recv_x,
+                                  recv_rows, nullptr, nullptr, 0, stream);
+  if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  rc = check_device();
+  if (rc) return rc;
+  void *ws = device_scratch();
+  if (!ws) return MOE_ERR_DEVICE;
+  return layout_dispatch_common(shape, kModeContiguous, 0, 0, topk_idx, out, x, recv_x,
+                                recv_rows, nullptr, ws, MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 MOE_API int moe_ll_layout_dispatch(const moe_shape *shape, int32_t M, int32_t src_rank,

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Host-side return codes. */
 #define MOE_OK 0
@@ -68,6 +68,11 @@ extern "C" {
 #define MOE_ERR_ARCH (-8)      /* the current device is not gfx950 */
 #define MOE_ERR_DEVICE (-9)    /* the HIP runtime could not be queried */
 #define MOE_ERR_FLAGS (-10)    /* an unsupported FP8 flag combination */
+#define MOE_ERR_SCRATCH (-11)  /* the layout workspace would exceed MOE_STATIC_SCRATCH_BYTES */
+
+/* Size of the library's static per-GPU layout workspace
+ * (moe_layout_dispatch_static). */
+#define MOE_STATIC_SCRATCH_BYTES (4u << 20)
 
 /* FP8 cast options (Buffer.low_latency_dispatch: round_scale, use_ue8m0). */
 #define MOE_FP8_ROUND_SCALE 1 /* scales rounded up to powers of two */
@@ -169,6 +174,22 @@ int moe_ll_layout(const moe_shape *shape, int32_t M, int32_t src_rank, const int
 int moe_layout_dispatch(const moe_shape *shape, const int64_t *topk_idx, const moe_layout_t *out,
                         const uint16_t *x, uint16_t *recv_x, int64_t recv_rows, void *ws,
                         size_t ws_bytes, hipStream_t stream);
+
+/* moe_layout_dispatch for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same results,
+ * bit for bit. Batches that need a layout workspace (moe_layout_workspace_bytes
+ * > 0) use a static array of MOE_STATIC_SCRATCH_BYTES that the library holds on
+ * each GPU until the process ends; a shape that needs more returns
+ * MOE_ERR_SCRATCH before anything is enqueued. Nothing is allocated or freed,
+ * and nothing in the array needs clearing between calls. All calls on one GPU
+ * share that array: calls that may overlap on one GPU (other streams, other
+ * host threads without ordering) race on it and must be serialised, for
+ * example on one stream. MOE_ERR_DEVICE if the array's address cannot be
+ * looked up. */
+int moe_layout_dispatch_static(const moe_shape *shape, const int64_t *topk_idx,
+                               const moe_layout_t *out, const uint16_t *x, uint16_t *recv_x,
+                               int64_t recv_rows, hipStream_t stream);
 
 /* Low-latency layout and dispatch in one call: the same results as moe_ll_layout
  * followed by moe_dispatch (recv_rows is normally moe_ll_recv_rows(E, R, M)). */

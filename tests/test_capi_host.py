@@ -26,7 +26,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 26, declared
+    assert len(declared) == 27, declared
     assert sorted(lib.EXPORTED) == declared
     raw = C.CDLL(lib.LIB_PATH)
     for name in declared:
@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strerror(lib):
     assert lib.moe_abi_version() == lib.MOE_ABI_VERSION
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         assert lib.moe_strerror(code) != "unknown error code"
     assert lib.moe_strerror(-99) == "unknown error code"
 
@@ -305,3 +305,27 @@ def test_routing_alignment_checks(lib):
     assert raw.moe_reroute(4, 2, 16, odd, d, d, 20, d, None, None) == -5
     assert raw.moe_reroute(4, 2, 16, d, d, d, 20, odd, None, None) == -5
 
+
+def test_static_scratch_entry_checks(lib):
+    """The no-allocation layout + dispatch rejects, on the host, a shape whose
+    layout workspace would not fit the static scratch, and otherwise checks
+    its arguments as moe_layout_dispatch does."""
+    raw = _raw(lib)
+    d = C.c_void_p(256)
+    odd = C.c_void_p(258)
+    lt = lib.moe_layout_t()
+    lt.count = lt.offset = lt.slot = d
+    # 200000 tokens x top-8 over 1024 experts on 64 ranks: 6250 first-pass
+    # blocks x (1024 + 64) + 1024 ints = 27 MB of workspace > 4 MiB
+    big = lib.make_shape(200000, 8, 1024, 64, 8, 1)
+    assert lib.moe_layout_workspace_bytes(big) > lib.MOE_STATIC_SCRATCH_BYTES
+    assert raw.moe_layout_dispatch_static(C.byref(big), d, C.byref(lt), d, d, 1600000,
+                                          None) == -11
+    s = lib.make_shape(4, 12, 16, 4, 2, 1)  # H % 8
+    assert raw.moe_layout_dispatch_static(C.byref(s), d, C.byref(lt), d, d, 8, None) == -2
+    s = lib.make_shape(4, 16, 16, 4, 2, 1)
+    assert raw.moe_layout_dispatch_static(C.byref(s), d, C.byref(lt), odd, d, 8, None) == -5
+    assert raw.moe_layout_dispatch_static(C.byref(s), d, C.byref(lt), None, d, 8, None) == -1
+    assert raw.moe_layout_dispatch_static(C.byref(s), d, C.byref(lt), d, d, -1, None) == -3
+    assert raw.moe_layout_dispatch_static(None, d, C.byref(lt), d, d, 8, None) == -1
+    assert lib.moe_strerror(-11) != "unknown error code"
