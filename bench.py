@@ -157,15 +157,57 @@ class Gate:
         self.torch.cuda._sleep(int(us * self.ticks_per_us))
 
 
+class HipEvent:
+    """A timing event created with hipEventDisableSystemFence: recording it
+    takes a GPU timestamp without the system-scope cache writeback and
+    invalidation a default event performs, which would otherwise be charged
+    to the region it closes (a fixed cost per region, 6% of a 20-step run)."""
+
+    _hip = None
+
+    def __init__(self):
+        import ctypes as C
+        if HipEvent._hip is None:
+            h = hip_runtime()
+            h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+            h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+            h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+            h.hipEventDestroy.argtypes = [C.c_void_p]
+            HipEvent._hip = h
+        self.ev = C.c_void_p()
+        rc = HipEvent._hip.hipEventCreateWithFlags(C.byref(self.ev), 0x20000000)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        import ctypes as C
+        rc = HipEvent._hip.hipEventRecord(self.ev, C.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both complete)."""
+        import ctypes as C
+        ms = C.c_float()
+        rc = HipEvent._hip.hipEventElapsedTime(C.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+            self.ev = None
+
+
 def timed_ms(torch, stream, gate, enqueue, launches, warm=None):
-    """Events around enqueue() on `stream`. Ahead of the start event: a spin
-    long enough for the host to queue `launches` kernel launches (5 us each,
-    0.2-50 ms), then warm(), untimed work of the same kind (so the region
-    starts in the steady state of a long run, not on a GPU that idled in the
-    spin)."""
+    """Events around enqueue() on `stream`, with the device synchronised
+    before and after. Ahead of the start event: a spin long enough for the
+    host to queue `launches` kernel launches (5 us each, 0.2-50 ms), then
+    warm(), untimed work of the same kind (so the region starts in the steady
+    state of a long run, not on a GPU that idled in the spin)."""
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    start, end = HipEvent(), HipEvent()
     with torch.cuda.stream(stream):
         gate.hold(min(50_000, max(200, 5 * launches)))
         if warm is not None:
@@ -895,12 +937,15 @@ def profile_pass(args, capi, floors, mi, torch, np, dev, stream):
         segs.append({"name": seg, "calls": calls * reps})
         log(f"segment {seg}: {calls * reps} calls")
 
-    def do_row(row, step_reps=1, call_reps=1, only_step=False):
+    def do_row(row, step_reps=None, only_step=False):
+        # about 100 calls per segment (at least 2 replays), one replay of the
+        # largest rows' graphs
+        reps = lambda n: step_reps or (1 if row.reps else max(2, math.ceil(100 / n)))  # noqa
         if row.step:
-            run(f"{row.key}/step", row.step, len(row.step), step_reps)
+            run(f"{row.key}/step", row.step, len(row.step), reps(len(row.step)))
         if not only_step:
             for name, fns in row.calls.items():
-                run(f"{row.key}/{name}", fns, len(fns), call_reps)
+                run(f"{row.key}/{name}", fns, len(fns), reps(len(fns)))
         row.release(torch)
 
     std = row_standard_kind(capi, mi, torch, dev, stream, "c2", "standard", args.sets,
@@ -941,9 +986,18 @@ def _col(r, *names):
 
 
 def _short(name):
+    """Kernel name without return type, namespaces and argument list."""
     name = name.replace("(anonymous namespace)::", "").strip()
+    name = re.sub(r"^void ", "", name)
     name = re.sub(r"^moe::", "", name)
-    return re.sub(r"\([^()]*\)$", "", name).strip()  # drop the argument list
+    if name.endswith(")"):  # drop the (balanced) argument list
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    return name.strip()
 
 
 def _dispatches(d):
@@ -985,15 +1039,17 @@ def summarize(dirs, segments_path):
     """Aggregate each segment of rocprofv3 CSV output (a kernel trace, or one
     counter pass per dir): per kernel (name, grid, workgroup) the launches and
     the mean/median/min duration or the mean counter values, and per call of
-    the segment the totals. Prints markdown with machine-read
-    `kind segment: value` lines."""
+    the segment the totals. Prints one markdown table (a row per segment and
+    kernel) and machine-read `kind segment: value` lines (per call; per
+    kernel too where a segment runs several kernels)."""
     seg = json.load(open(segments_path))
     names = [s["name"] for s in seg["segments"]]
     calls = {s["name"]: s["calls"] for s in seg["segments"]}
     per_dir = [_segments(_dispatches(d), names) for d in dirs]
-    lines, mach = [], []
+    table, mach = [], []
+    cn_all, has_dur = set(), False
+    agg = {}
     for sname in names:
-        lines.append(f"\n### {sname} ({calls[sname]} calls)\n")
         groups = {}  # (kernel, grid, wg) -> {"dur": [...], counter: [...]}
         for segs in per_dir:
             for e in segs[sname]:
@@ -1001,39 +1057,45 @@ def summarize(dirs, segments_path):
                 g.setdefault("n", []).append(1)
                 if "dur" in e:
                     g.setdefault("dur", []).append(e["dur"])
+                    has_dur = True
                 for c, v in e.get("ctr", {}).items():
                     g.setdefault(c, []).append(v)
-        cnames = sorted({c for g in groups.values() for c in g if c not in ("n", "dur")})
-        has_dur = any("dur" in g for g in groups.values())
-        head = ["kernel", "grid (threads)", "workgroup", "launches"]
-        if has_dur:
-            head += ["mean µs", "median µs", "min µs"]
-        head += [f"{c} KiB (mean)" for c in cnames]
-        lines.append("| " + " | ".join(head) + " |")
-        lines.append("|" + "---|" * len(head))
+                    cn_all.add(c)
+        agg[sname] = groups
+    cnames = sorted(cn_all)
+    head = ["segment", "calls", "kernel", "grid", "wg", "launches"]
+    if has_dur:
+        head += ["mean µs", "median µs", "min µs"]
+    head += [f"{c} KiB" for c in cnames]
+    table.append("| " + " | ".join(head) + " |")
+    table.append("|" + "---|" * len(head))
+    for sname in names:
+        groups = agg[sname]
         tot = {c: 0.0 for c in cnames}
         tot_dur = 0.0
+        multi = len(groups) > 1
         for (kn, grid, wg), g in sorted(groups.items(), key=lambda kv: -len(kv[1]["n"])):
-            n = len(g.get("dur", [])) or max(len(g.get(c, [])) for c in cnames)
-            cells = [f"`{kn}`", str(grid), str(wg), str(n)]
+            n = len(g.get("dur", [])) or max([len(g.get(c, [])) for c in cnames] or [0])
+            cells = [sname, str(calls[sname]), f"`{kn}`", str(grid), str(wg), str(n)]
             if has_dur:
                 ds = g.get("dur", [])
                 cells += ([f"{statistics.mean(ds):.3f}", f"{statistics.median(ds):.3f}",
                            f"{min(ds):.3f}"] if ds else ["—"] * 3)
                 if ds:
                     tot_dur += sum(ds)
-                    mach.append(f"trace_us {sname} {kn}@{grid}: {statistics.mean(ds):.4f}")
+                    if multi:
+                        mach.append(f"trace_us {sname} {kn}@{grid}: {statistics.mean(ds):.4f}")
             for c in cnames:
                 v = g.get(c, [])
                 tot[c] += sum(v)
                 cells.append(f"{statistics.mean(v):.1f}" if v else "—")
-            lines.append("| " + " | ".join(cells) + " |")
+            table.append("| " + " | ".join(cells) + " |")
         if has_dur:
             mach.append(f"trace_us {sname} per_call: {tot_dur / calls[sname]:.4f}")
         for c in cnames:
             kind = {"FETCH_SIZE": "fetch_kib", "WRITE_SIZE": "write_kib"}.get(c, c.lower())
             mach.append(f"{kind} {sname} per_call: {tot[c] / calls[sname]:.2f}")
-    print("\n".join(lines))
+    print("\n".join(table))
     print("\nMachine-read by bench.py (valid only while the kernel sources hash to the value "
           "below):\n")
     print(f"kernel_source_hash: {seg['kernel_source_hash']}")

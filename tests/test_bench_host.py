@@ -92,6 +92,8 @@ def test_trace_summary_segments(tmp_path, segs):
         pytest.approx(4.0)
     # launches outside a pair of markers belong to no segment
     assert "warm" not in txt and "setup" not in txt and "after" not in txt
+    assert bench._short("void moe::(anonymous namespace)::combine_kernel<8, true>(moe::Lane<2>::T "
+                        "const*, float __vector(4)*, int)") == "combine_kernel<8, true>"
 
 
 def test_pmc_summary_and_scaling(tmp_path, segs):
