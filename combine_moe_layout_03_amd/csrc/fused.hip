@@ -44,22 +44,20 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kCountMaxWaves = 16;
-// Waves of a copying workgroup that also read the routing and count; the rest
-// only copy. Fewer counting waves share the SIMDs less (the counting is issue
-// bound), at the price of more id rounds each.
-#ifndef MOE_COUNTING_WAVES
-#define MOE_COUNTING_WAVES 8
-#endif
-constexpr int kCountingWaves = MOE_COUNTING_WAVES;
-constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * threads
+// Every workgroup of the kernel has 8 waves: a copying workgroup owns at most
+// 8 row chunks (one per wave, or two per wave for large batches), and every
+// wave reads its share of the routing and counts. A compile-time block size
+// spares the wave a load of the launch's block size and makes the lane
+// arithmetic shifts.
+constexpr int kCountWaves = 8;
+constexpr int kCountThreads = 64 * kCountWaves;
+constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * 512
 // Experts (and ranks) whose totals one duty workgroup writes. One each: the
 // duty workgroups' last stores tend to end the kernel (they queue behind the
 // row stores of the copying workgroup sharing the CU), and a shorter duty ends
 // sooner (4 -> 1: low latency 5.12 -> 4.89 us at 128 tokens, 18.1 -> 17.1 us
 // at 512; the standard batch unchanged).
 constexpr int kMaxDuties = 1;
-constexpr int kLayoutOnlyThreads = 512;
 constexpr int kNoId = -2;           // sentinel: matches no expert
 constexpr int kAboveAll = 0x7fffffff;  // sentinel: not below any expert
 
@@ -69,6 +67,7 @@ struct CountParams {
   u32x4 *recv;
   int64_t rows;
   int32_t nvec, nchunk, chunks_per_wg, wg_per_token;
+  uint64_t wpt_magic;  // ceil(2^32 / wg_per_token): token of workgroup b = (b * magic) >> 32
   int32_t token_wgs;  // workgroups [0, token_wgs) serve tokens, the rest do duties
   int32_t duty_wgs;
   // FP8 output (kFp8 >= 0): codes, scales, rows per expert, scale groups per row
@@ -163,13 +162,13 @@ struct LaneIds {
 // of ranks d, d+D, ...; empty low-latency stripe rows.
 template <int kRounds>
 __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
-  __shared__ int32_t s_c[kCountMaxWaves][kMaxDuties];
-  __shared__ int32_t s_l[kCountMaxWaves][kMaxDuties];
-  __shared__ int32_t s_r[kCountMaxWaves][kMaxDuties];
+  __shared__ int32_t s_c[kCountWaves][kMaxDuties];
+  __shared__ int32_t s_l[kCountWaves][kMaxDuties];
+  __shared__ int32_t s_r[kCountWaves][kMaxDuties];
   __shared__ uint8_t s_mark[kMaxPairsFused];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
+  constexpr int nthreads = kCountThreads, nwaves = kCountWaves;
   const int E = p.E, R = p.R, K = p.K, T = p.T, L = p.L, P = T * K;
   const bool ll = p.mode == kModeLowLatency;
   LaneIds<kRounds> ids;
@@ -303,31 +302,36 @@ __device__ __forceinline__ int token_counts8(const LaneIds<kRounds> &ids, int th
   return prev;
 }
 
-// kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast.
-template <bool kCopy, int kRounds, int kFp8>
-__global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(CountParams f) {
+// kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast. kCpw: row
+// chunks per copying wave (2 only for bf16 rows).
+template <bool kCopy, int kRounds, int kFp8, int kCpw>
+__global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams f) {
   __shared__ int32_t s_pre[64];  // per k: the slot (contiguous) or stripe row (low latency)
   __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
-  __shared__ int32_t s_status;
 
   const LayoutParams &p = f.lp;
   const int tid = threadIdx.x, lane = lane_id();
   const int b = blockIdx.x;
   int st = 0;
-  if (tid == 0) s_status = 0;
 
   if (b >= f.token_wgs) {  // uniform per workgroup
     duty_workgroup<kRounds>(p, b - f.token_wgs, f.duty_wgs, st);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // the last wave writes the token's handle entries and reports its bad
+    // slots: with 7 row chunks in 8 waves it copies nothing, so those stores
+    // do not queue behind a row's K stores
+    constexpr int hw = kCountWaves - 1;
     // lanes that read the routing and count (all of them without the copy)
-    const int nthreads = kCopy ? min((int)blockDim.x, kCountingWaves * 64) : (int)blockDim.x;
-    const bool counting = tid < nthreads;
+    constexpr int nthreads = kCountThreads;
+    constexpr bool counting = true;
     const int E = p.E, R = p.R, K = p.K, T = p.T;
     const int P = T * K;
     const bool ll = p.mode == kModeLowLatency;
-    const int t = kCopy ? b / f.wg_per_token : b;  // < T
-    const bool token_lead = !kCopy || b % f.wg_per_token == 0;
+    // b / wg_per_token, exact while b * wg_per_token < 2^32
+    const int t = kCopy ? (int)(((uint64_t)(uint32_t)b * f.wpt_magic) >> 32) : b;  // < T
+    const int part = b - t * (kCopy ? f.wg_per_token : 1);  // workgroup within the token
+    const bool token_lead = part == 0;
     const int pbeg = t * K;
     if (tid < 64) s_pre[tid] = 0;
 
@@ -347,14 +351,19 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     // 2. ... then the row chunk this wave copies; it stays in flight while
     //    the slots are worked out. The load is unconditional (address clamped
     //    into the row): under a branch it would force an early wait.
-    u32x4 val = {0u, 0u, 0u, 0u};
+    static_assert(kCpw == 1 || kFp8 < 0, "two chunks per wave for bf16 rows only");
+    u32x4 val = {0u, 0u, 0u, 0u}, val2 = {0u, 0u, 0u, 0u};
     int v = 0, chunk = 0;
-    bool lane_ok = false;
+    bool lane_ok = false, lane_ok2 = false;
     if (kCopy) {
-      chunk = (b % f.wg_per_token) * f.chunks_per_wg + wave;
+      chunk = part * f.chunks_per_wg + wave * kCpw;
       v = chunk * 64 + lane;
-      lane_ok = wave < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
+      lane_ok = wave * kCpw < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
       val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
+      if (kCpw == 2) {  // the wave's second chunk, 64 vectors further
+        lane_ok2 = wave * kCpw + 1 < f.chunks_per_wg && chunk + 1 < f.nchunk && v + 64 < f.nvec;
+        val2 = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v + 64, f.nvec - 1));
+      }
     }
     if (counting) ids.settle(P, E, nthreads, pbeg, K, s_tok, st);
     lds_barrier();
@@ -387,7 +396,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           out = j;
         } else if (j < p.M) {
           out = (e * R + p.src) * p.M + j;
-        } else if (wave == 0) {
+        } else if (wave == hw) {
           st |= kStOverflow;
         }
       }
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           for (int k = 0; k < 8; ++k)
             if ((uint32_t)sl[k] < rows32) put(sl[k], ex[k]);
         }
-        if (wave == 0) {  // receive buffer smaller than the layout needs
+        if (wave == hw) {  // receive buffer smaller than the layout needs
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if ((uint32_t)sl[k] >= rows32 && sl[k] != -1) st |= kStBadSlot;
@@ -438,13 +447,14 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           const int sk = __builtin_amdgcn_readlane(out, k);
           if ((uint32_t)sk < rows32) {
             if (lane_ok) put(sk, __builtin_amdgcn_readlane(tokv, k));
-          } else if (sk != -1 && wave == 0) {
+          } else if (sk != -1 && wave == hw) {
             st |= kStBadSlot;  // receive buffer smaller than the layout needs
           }
         }
       }
     } else if (kCopy) {
       asm volatile("" : "+v"(val));
+      if (kCpw == 2) asm volatile("" : "+v"(val2));
       // slots are int32, so a 32-bit unsigned compare against the row count
       // (clamped to INT32_MAX) tells valid slots (and -1 is never valid)
       const uint32_t rows32 = f.rows < 0x7fffffff ? (uint32_t)f.rows : 0x7fffffffu;
@@ -459,7 +469,13 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
             if ((uint32_t)sl[k] < rows32)
               __builtin_nontemporal_store(val, dst + (int64_t)sl[k] * f.nvec);
         }
-        if (wave == 0) {  // receive buffer smaller than the layout needs
+        if (kCpw == 2 && lane_ok2) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((uint32_t)sl[k] < rows32)
+              __builtin_nontemporal_store(val2, dst + (int64_t)sl[k] * f.nvec + 64);
+        }
+        if (wave == hw) {  // receive buffer smaller than the layout needs
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if ((uint32_t)sl[k] >= rows32 && sl[k] != -1) st |= kStBadSlot;
@@ -469,16 +485,17 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
           const int sk = __builtin_amdgcn_readlane(out, k);
           if ((uint32_t)sk < rows32) {
             if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)sk * f.nvec);
-          } else if (sk != -1 && wave == 0) {
+            if (kCpw == 2 && lane_ok2)
+              __builtin_nontemporal_store(val2, dst + (int64_t)sk * f.nvec + 64);
+          } else if (sk != -1 && wave == hw) {
             st |= kStBadSlot;  // receive buffer smaller than the layout needs
           }
         }
       }
     }
 
-    // 6. this token's handle entries, written after the row so the wait for
-    //    the row load does not also wait for them
-    if (token_lead && wave == 0) {
+    // 6. this token's handle entries
+    if (token_lead && wave == hw) {
       if (lane < K) {
         p.slot[pbeg + lane] = out;
         if (out >= 0 && p.row_src)
@@ -497,41 +514,43 @@ __global__ __launch_bounds__(64 * kCountMaxWaves) void count_layout_kernel(Count
     // every workgroup reads every id; the duty workgroups report bad ones
     st &= ~kStBadExpert;
   }
-  if (st) atomicOr(&s_status, st);
-  lds_barrier();
-  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
+  // error bits (rare) go straight to the status word: no barrier at the end,
+  // so each wave leaves as soon as its own work is out
+  if (st && p.status) atomicOr(p.status, st);
 }
 
-template <bool kCopy, int kFp8>
+template <bool kCopy, int kFp8, int kCpw = 1>
 hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const CountParams &f) {
   if (rounds <= 1)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8, kCpw>), grid, block, 0, s, f);
   else if (rounds <= 2)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2, kFp8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2, kFp8, kCpw>), grid, block, 0, s, f);
   else if (rounds <= 4)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4, kFp8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4, kFp8, kCpw>), grid, block, 0, s, f);
   else
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8, kFp8>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8, kFp8, kCpw>), grid, block, 0, s, f);
   return hipGetLastError();
 }
 
-// Waves of a copying workgroup: its row chunks (at most kCopyChunks), padded up to
-// kCopyWaves so the routing is read in fewer rounds per wave (extra waves only count).
-// Measured on the 128 x 7168, top-8 batch: 8 chunks in 8-wave workgroups beat
-// one 16-wave workgroup per token (5.7 vs 6.1 us): twice the CUs issue the row
-// stores, and the counting still takes two rounds.
-constexpr int kCopyChunks = 8;
-constexpr int kCopyWaves = 8;
+// Row chunks of a copying workgroup: at most 8, one per wave (for large
+// batches 16, two per wave). Measured on the 128 x 7168, top-8 batch: 8 chunks
+// in 8-wave workgroups beat one 16-wave workgroup per token (5.7 vs 6.1 us):
+// twice the CUs issue the row stores, and the counting still takes two rounds.
+constexpr int kCopyChunks = kCountWaves;
+// From this many tokens on (bf16 rows), a copying wave takes two chunks, so a
+// token's row needs half the workgroups: the batch's workgroups then fit the
+// GPU at once and each token's routing is counted once, not twice (512
+// low-latency tokens x 7168: 14.8 vs 15.9 us; at 256 tokens it measured
+// slower, 8.1 vs 7.8 us).
+#ifndef MOE_TWO_CHUNK_TOKENS
+#define MOE_TWO_CHUNK_TOKENS 512
+#endif
 
-int copy_chunks(int32_t H) {
+// Row chunks of one workgroup (cpw: chunks per copying wave).
+int copy_chunks(int32_t H, int cpw = 1) {
   const int nchunk = (H / 8 + 63) / 64;
-  const int groups = (nchunk + kCopyChunks - 1) / kCopyChunks;
+  const int groups = (nchunk + cpw * kCopyChunks - 1) / (cpw * kCopyChunks);
   return (nchunk + groups - 1) / groups;
-}
-
-int copy_threads(int32_t H) {
-  const int c = copy_chunks(H);
-  return 64 * (c > kCopyWaves ? c : kCopyWaves);
 }
 
 }  // namespace
@@ -540,10 +559,8 @@ bool count_layout_fits(const LayoutParams &lp, int32_t H, bool copy) {
   if (lp.mode == kModeContiguous && lp.A != 1) return false;
   const int64_t P = (int64_t)lp.T * lp.K;
   if (P > kMaxPairsFused) return false;
-  int threads = (copy && lp.T > 0) ? copy_threads(H) : kLayoutOnlyThreads;
-  if (copy && lp.T > 0 && threads > kCountingWaves * 64) threads = kCountingWaves * 64;
-  // the batch must fit kCountMaxRounds rounds of the counting lanes
-  return P <= (int64_t)kCountMaxRounds * threads;
+  // the batch must fit kCountMaxRounds rounds of the 512 counting lanes
+  return P <= (int64_t)kCountMaxRounds * kCountThreads;
 }
 
 hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16_t *recv,
@@ -562,18 +579,18 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
   f.duty_wgs = (need + kMaxDuties - 1) / kMaxDuties;
   const int P = lp.T * lp.K;
   if (x && lp.T > 0) {
+    const int cpw = (!fp8 && lp.T >= MOE_TWO_CHUNK_TOKENS) ? 2 : 1;
     f.nvec = H / 8;
     f.nchunk = (f.nvec + 63) / 64;
-    const int threads = copy_threads(H);
-    f.chunks_per_wg = copy_chunks(H);
+    f.chunks_per_wg = copy_chunks(H, cpw);  // <= cpw * 8: one or two per wave
     f.wg_per_token = (f.nchunk + f.chunks_per_wg - 1) / f.chunks_per_wg;
+    f.wpt_magic = ((1ull << 32) + (uint64_t)f.wg_per_token - 1) / f.wg_per_token;
     f.token_wgs = lp.T * f.wg_per_token;
-    // token workgroups count with kCountingWaves waves, duty workgroups with all
-    // of theirs; the rounds template covers the larger need
-    const int counting = threads < kCountingWaves * 64 ? threads : kCountingWaves * 64;
-    const int rounds = (P + counting - 1) / counting;
-    const dim3 grid((unsigned)(f.token_wgs + f.duty_wgs)), block(threads);
-    if (!fp8) return launch_rounds<true, -1>(rounds, grid, block, s, f);
+    const int rounds = (P + kCountThreads - 1) / kCountThreads;
+    const dim3 grid((unsigned)(f.token_wgs + f.duty_wgs)), block(kCountThreads);
+    if (!fp8)
+      return cpw == 2 ? launch_rounds<true, -1, 2>(rounds, grid, block, s, f)
+                      : launch_rounds<true, -1>(rounds, grid, block, s, f);
     constexpr int R1 = kFp8RoundScale, U = kFp8Ue8m0, SR = kFp8ScaleRows;
     switch (fp8->flags) {
       case 0: return launch_rounds<true, 0>(rounds, grid, block, s, f);
@@ -584,11 +601,13 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
       default: return launch_rounds<true, SR | R1 | U>(rounds, grid, block, s, f);
     }
   }
-  f.nvec = f.nchunk = f.chunks_per_wg = f.wg_per_token = 0;
+  f.nvec = f.nchunk = f.chunks_per_wg = 0;
+  f.wg_per_token = 1;
+  f.wpt_magic = 0;
   f.token_wgs = lp.T;
-  const int rounds = (P + kLayoutOnlyThreads - 1) / kLayoutOnlyThreads;
+  const int rounds = (P + kCountThreads - 1) / kCountThreads;
   return launch_rounds<false, -1>(rounds, dim3((unsigned)(f.token_wgs + f.duty_wgs)),
-                                  dim3(kLayoutOnlyThreads), s, f);
+                                  dim3(kCountThreads), s, f);
 }
 
 }  // namespace moe

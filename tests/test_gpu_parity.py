@@ -364,11 +364,17 @@ FUSED_CASES = {k: v for k, v in CASES.items()
                if k not in ("rand_8193pairs", "rand_K64_onefull", "rand_K64_multi")}
 FUSED_CASES["rand_2048pairs"] = lambda: mi.random_case(70, 256, 520, 96, 8, 8, 1, neg_frac=0.05)
 FUSED_CASES["rand_2049pairs"] = lambda: mi.random_case(71, 2049, 64, 32, 4, 1, 1)
-# from 256 tokens on, one workgroup per token: 14 row chunks and a ragged
-# 2400-pair routing; and a row of 20 chunks, too wide for one workgroup
+# wide rows: 300 tokens of 14 row chunks with a ragged 2400-pair routing,
+# 256 tokens of 20 chunks; from 512 tokens on each copying wave takes two
+# chunks and a row needs one workgroup (14 chunks), or two of 10 (20 chunks)
 FUSED_CASES["rand_T300_wide"] = lambda: mi.random_case(75, 300, 7168, 256, 8, 8, 1, neg_frac=0.02,
                                                        dup_frac=0.02)
 FUSED_CASES["rand_T256_H10240"] = lambda: mi.random_case(76, 256, 10240, 256, 8, 8, 1)
+FUSED_CASES["rand_T512_wide"] = lambda: mi.random_case(78, 512, 7168, 256, 8, 8, 1, neg_frac=0.01,
+                                                       dup_frac=0.02)
+FUSED_CASES["rand_T512_H10240"] = lambda: mi.random_case(79, 512, 10240, 64, 8, 8, 1,
+                                                         neg_frac=0.02)
+FUSED_CASES["rand_T600_H1000"] = lambda: mi.random_case(80, 600, 1000, 64, 8, 6, 1, neg_frac=0.02)
 # the counting kernel's largest keys: 1024 experts x 4096 pairs
 FUSED_CASES["rand_E1024_4096pairs"] = lambda: mi.random_case(72, 512, 64, 1024, 64, 8, 1,
                                                              neg_frac=0.02, dup_frac=0.05,
