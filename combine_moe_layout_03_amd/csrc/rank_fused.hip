@@ -49,6 +49,7 @@ struct RankFusedParams {
   u32x4 *recv;     // [rows, nvec]
   int64_t rows;
   int32_t nvec, nchunk, chunks_per_wg, wg_per_token;
+  uint64_t wpt_magic;  // ceil(2^32 / wg_per_token)
   int32_t token_wgs;  // [0, token_wgs) serve tokens
   int32_t count_wgs;  // [0, count_wgs) also count experts b, b + count_wgs, ... (at most
                       // kRfDuties each); workgroups [token_wgs, count_wgs) only do that;
@@ -151,8 +152,14 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   __shared__ int32_t s_pos[64];  // per rank: tokens before t reaching it
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = b / p.wg_per_token;  // < T
-  const bool lead = b % p.wg_per_token == 0;
+  // b / wg_per_token by the reciprocal (exact while b * wg_per_token < 2^32)
+  const int t = (int)(((uint64_t)(uint32_t)b * p.wpt_magic) >> 32);  // < T
+  const int part = b - t * p.wg_per_token;  // workgroup within the token
+  const bool lead = part == 0;
+  // the last wave writes the handle entries and reports bad rows: it copies
+  // nothing for 7168-wide rows (7 chunks), so those stores do not queue behind
+  // a row's stores
+  constexpr int hw = kRfWaves - 1;
   const int K = p.K;
   if (tid < 64) {
     s_cnt[tid] = 0;
@@ -176,7 +183,7 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   //    with no memory wait): routing loads issued after another wave's cold
   //    row load come back after it.
   __builtin_amdgcn_s_barrier();
-  const int chunk = (b % p.wg_per_token) * p.chunks_per_wg + wave;
+  const int chunk = part * p.chunks_per_wg + wave;
   const int v = chunk * 64 + lane;
   const bool lane_ok = wave < p.chunks_per_wg && chunk < p.nchunk && v < p.nvec;
   u32x4 val = __builtin_nontemporal_load(p.x + (int64_t)t * p.nvec + min(v, p.nvec - 1));
@@ -241,7 +248,7 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   if (!hit) {
     row = -1;
   } else if (row >= p.cap) {  // receive arrays smaller than the layout needs
-    if (lead && wave == 0) st |= kStBadSlot;
+    if (lead && wave == hw) st |= kStBadSlot;
     row = -1;
   }
 
@@ -259,7 +266,7 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
       for (int r = 0; r < 8; ++r)
         if ((uint32_t)sl[r] < rows32) __builtin_nontemporal_store(val, dst + (int64_t)sl[r] * p.nvec);
     }
-    if (lead && wave == 0) {  // receive buffer smaller than the layout needs
+    if (lead && wave == hw) {  // receive buffer smaller than the layout needs
 #pragma unroll
       for (int r = 0; r < 8; ++r)
         if ((uint32_t)sl[r] >= rows32 && sl[r] != -1) st |= kStBadSlot;
@@ -269,14 +276,14 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
       const int s = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)rest) - 1);
       if ((uint32_t)s < rows32) {
         if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)s * p.nvec);
-      } else if (s != -1 && lead && wave == 0) {
+      } else if (s != -1 && lead && wave == hw) {
         st |= kStBadSlot;  // receive buffer smaller than the layout needs
       }
     }
   }
 
   // 8. the token's handle entries
-  if (lead && wave == 0) {
+  if (lead && wave == hw) {
     if (lane < p.R) p.rank_slot[(int64_t)t * p.R + lane] = row;
     if (row >= 0 && p.recv_src) p.recv_src[row] = t;
     // entry (j, k) of the rows' local ids and weights in lane j*K + k (at
@@ -343,22 +350,21 @@ __device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t
 
 template <int kRounds>
 __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFusedParams p) {
-  __shared__ int32_t s_status;
   __shared__ int32_t s_exp[kRfDuties];  // pairs on this workgroup's experts
   const int tid = threadIdx.x, b = blockIdx.x;
   int st = 0;
-  if (tid == 0) s_status = 0;
   if (tid < kRfDuties) s_exp[tid] = 0;
-  if (b < p.token_wgs)  // uniform per workgroup
+  if (b < p.token_wgs) {  // uniform per workgroup
     token_workgroup<kRounds>(p, b, st, s_exp);
-  else
+  } else {
     duty_workgroup<kRounds>(p, b, st, s_exp);
-  if (st) atomicOr(&s_status, st);
-  lds_barrier();
-  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
-  if (b >= p.token_wgs && b < p.count_wgs && p.recv_count && tid < kRfDuties &&
-      b + tid * p.count_wgs < p.E)
-    p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
+    lds_barrier();  // every wave's receive counts are in s_exp
+    if (b < p.count_wgs && p.recv_count && tid < kRfDuties && b + tid * p.count_wgs < p.E)
+      p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
+  }
+  // error bits (rare) go straight to the status word: no barrier ends a token
+  // workgroup, so each wave leaves as soon as its own work is out
+  if (st && p.status) atomicOr(p.status, st);
 }
 
 }  // namespace
@@ -402,6 +408,7 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   const int groups = (p.nchunk + kRfChunks - 1) / kRfChunks;
   p.chunks_per_wg = (p.nchunk + groups - 1) / groups;  // <= kRfChunks = waves
   p.wg_per_token = (p.nchunk + p.chunks_per_wg - 1) / p.chunks_per_wg;
+  p.wpt_magic = ((1ull << 32) + (uint64_t)p.wg_per_token - 1) / p.wg_per_token;
   p.token_wgs = T * p.wg_per_token;
   const int need = (E + kRfDuties - 1) / kRfDuties;
   p.count_wgs = p.token_wgs > need ? p.token_wgs : need;
