@@ -195,8 +195,9 @@ class HipEvent:
         return ms.value
 
     def __del__(self):
-        if HipEvent._hip is not None and self.ev:
-            HipEvent._hip.hipEventDestroy(self.ev)
+        h = getattr(HipEvent, "_hip", None) if HipEvent is not None else None
+        if h is not None and self.ev:
+            h.hipEventDestroy(self.ev)
             self.ev = None
 
 
@@ -272,7 +273,7 @@ class HipGraph:
         self._check(HipGraph._hip.hipGraphLaunch(self.exec, self.s), "hipGraphLaunch")
 
     def __del__(self):
-        h = HipGraph._hip
+        h = getattr(HipGraph, "_hip", None) if HipGraph is not None else None
         if h is not None and self.exec:
             h.hipGraphExecDestroy(self.exec)
             h.hipGraphDestroy(self.graph)
@@ -481,7 +482,7 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128, mas
     """Low-latency padded path at M tokens per rank: layout + dispatch into
     the [E, R*M, H] union of the receive buffers, then combine from it. Steps
     rotate over union buffers x 8 source stripes, enough for > 512 MiB of
-    touched bytes (at least 4 unions at M = 128).
+    touched bytes (at least 4 unions from M = 128 on).
     With fp8_flags, dispatch casts to E4M3 + per-128-channel scales
     (moe_ll_layout_dispatch_fp8) and combine reads a bf16 expert-output union
     of the same layout (filled once by a bf16 dispatch of the same batch).
@@ -497,7 +498,10 @@ def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128, mas
     fp8 = fp8_flags is not None
     P = int((w.topk_idx >= 0).sum())
     ab = algo_bytes(T, H, K, E, R, P, fp8_flags)
-    n_unions = max(4 if M == 128 else 1, math.ceil(512 * 2**20 / (ab["total"] * R)))
+    # at least 4 unions from M = 128 on (the large rows' timings otherwise
+    # vary by several percent from one process to the next with where the
+    # one union lands in memory)
+    n_unions = max(4 if M >= 128 else 1, math.ceil(512 * 2**20 / (ab["total"] * R)))
     unions = [torch.empty(rows, H, dtype=torch.int16, device=dev) for _ in range(n_unions)]
     qunions = sunions = None
     if fp8:
@@ -1123,6 +1127,8 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 CSV output dirs to summarise (with --segments)")
     ap.add_argument("--segments", default=None)
+    ap.add_argument("--only-rows", default=None, metavar="REGEX",
+                    help="measure only the rows whose key matches")
     ap.add_argument("--arena", action="store_true",
                     help="carve the standard step's buffer sets from one allocation")
     args = ap.parse_args()
@@ -1198,9 +1204,13 @@ def main():
         if g_rem is not None:
             g_rem.replay()
 
-    def warm():  # untimed steps ahead of the start event: about 2 ms of them
-        for _ in range(max(2, math.ceil(200 / S))):
-            g_full.replay()
+    def warm():
+        # untimed steps ahead of the start event, about 2 ms of them, from the
+        # graph the region starts with (the first launch of a graph after
+        # another one costs a few us more, once per region)
+        g0, n0 = (g_full, S) if K >= S else (g_rem, rem)
+        for _ in range(max(2, math.ceil(200 / n0))):
+            g0.replay()
     ms = timed_ms(torch, stream, gate, go, 2 * K, warm=warm)
     us_step = ms * 1e3 / K
     value = ab["total"] / (us_step * 1e-6) / 1e9
@@ -1245,6 +1255,9 @@ def main():
         rlist.append(lambda: row_replica_train(capi, mi, torch, np, dev, stream))
         for make in rlist:
             row = make()
+            if args.only_rows and not re.search(args.only_rows, row.key):
+                row.release(torch)
+                continue
             rows[row.key] = measure_row(torch, stream, gate, row, 200, pmc, trace)
             log(f"row {row.key}: " + ", ".join(f"{k} {v['us']} us" for k, v in
                                                rows[row.key]["calls"].items()))
@@ -1252,6 +1265,8 @@ def main():
         # the low-latency sweep and the masked combine, side by side
         sweep, masked = {}, {}
         for M in mi.C3_SWEEP:
+            if f"low_latency_m{M}" not in rows:
+                continue
             r = rows.pop(f"low_latency_m{M}")
             c = r["calls"]
             sweep[str(M)] = {k: r[k] for k in ("us_per_step", "GB_per_s", "buffer_sets")}

@@ -52,12 +52,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kCountWaves = 8;
 constexpr int kCountThreads = 64 * kCountWaves;
 constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * 512
-// Experts (and ranks) whose totals one duty workgroup writes. One each: the
-// duty workgroups' last stores tend to end the kernel (they queue behind the
-// row stores of the copying workgroup sharing the CU), and a shorter duty ends
-// sooner (4 -> 1: low latency 5.12 -> 4.89 us at 128 tokens, 18.1 -> 17.1 us
-// at 512; the standard batch unchanged).
-constexpr int kMaxDuties = 1;
+// Experts (and ranks) whose totals one duty workgroup writes: one each for
+// batches of at most kManyPairs pairs -- the duty workgroups' last stores
+// tend to end the kernel (they queue behind the row stores of the copying
+// workgroup sharing the CU), and a shorter duty ends sooner (4 -> 1: low
+// latency 5.12 -> 4.89 us at 128 tokens); kMaxDuties each above, where every
+// duty workgroup reading the whole routing from L2 is what costs.
+constexpr int kMaxDuties = 4;
+constexpr int kManyPairs = 2048;
 constexpr int kNoId = -2;           // sentinel: matches no expert
 constexpr int kAboveAll = 0x7fffffff;  // sentinel: not below any expert
 
@@ -576,7 +578,8 @@ hipError_t launch_count_layout(const LayoutParams &lp, const uint16_t *x, uint16
   f.RM = fp8 ? fp8->rows_per_expert : 0;
   f.G = H / kFp8Group;
   const int need = (lp.E > lp.R ? lp.E : lp.R);
-  f.duty_wgs = (need + kMaxDuties - 1) / kMaxDuties;
+  const int duties = (int64_t)lp.T * lp.K > kManyPairs ? kMaxDuties : 1;
+  f.duty_wgs = (need + duties - 1) / duties;
   const int P = lp.T * lp.K;
   if (x && lp.T > 0) {
     const int cpw = (!fp8 && lp.T >= MOE_TWO_CHUNK_TOKENS) ? 2 : 1;
