@@ -385,14 +385,15 @@ class Workset:
                            self.lay.offset, self.lay.slot, self.lay.row_src))
 
 
-def workset_bytes(w):
-    """Bytes of one Workset of workload w, with each piece rounded to 256."""
+def workset_bytes(w, ws_bytes):
+    """Device bytes of one Workset of workload w (each piece rounded up to 256
+    as the arena places them); ws_bytes: its layout workspace."""
     r = lambda n: (n + 255) // 256 * 256  # noqa: E731
     T, H, E, R, K = w.T, w.H, w.E, w.R, w.K
     rows = T * K + E * (w.A - 1)
     return (r(T * H * 2) + r(T * K * 8) + r(T * K * 4) + r(E * 4) + r((E + 1) * 4)
             + r(T * K * 4) + r(R * 4) + r(T * R) + r(max(rows, 1) * 4) + r(rows * H * 2)
-            + r(T * H * 2) + r(1 << 22))
+            + r(T * H * 2) + r(ws_bytes))
 
 
 def standard_calls(capi, z, stream):
@@ -413,8 +414,10 @@ def row_standard_kind(capi, mi, torch, dev, stream, name, key, sets=0, arena=Fal
     workload: c2 (the headline), c1 or c4; rotating sets for >= 512 MiB.
     arena: every set carved from one allocation."""
     w = mi.by_name(name)
-    S = sets or n_sets(workset_bytes(w))
-    ar = Arena(torch, dev, S * workset_bytes(w)) if arena else None
+    nws = capi.moe_layout_workspace_bytes(capi.make_shape(w.T, w.H, w.E, w.R, w.K, w.A))
+    per_set = workset_bytes(w, nws)
+    S = sets or n_sets(per_set)
+    ar = Arena(torch, dev, S * per_set) if arena else None
     zs = [Workset(capi, w, dev, ar) for _ in range(S)]
     probe = zs[0]
     with torch.cuda.stream(stream):

@@ -143,3 +143,21 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+def test_rotating_sets_cover_twice_the_infinity_cache(name):
+    """The standard-kind rows rotate over enough buffer sets that a step's
+    inputs were last touched >= 512 MiB of traffic ago (twice the 256 MB
+    memory-side cache), capped at 64 sets for the tiny batch."""
+    import moe_inputs as mi
+    from combine_moe_layout_03_amd import capi
+    w = mi.by_name(name)
+    nws = capi.moe_layout_workspace_bytes(capi.make_shape(w.T, w.H, w.E, w.R, w.K, w.A))
+    per_set = bench.workset_bytes(w, nws)
+    S = bench.n_sets(per_set)
+    assert S * per_set >= 512 * 2**20 or S == 64
+    # the set's own device bytes: x, routing, weights, layout arrays, receive
+    # buffer, output (and workspace), each rounded to 256
+    rows = w.T * w.K + w.E * (w.A - 1)
+    assert per_set >= w.T * w.H * 2 * 2 + rows * w.H * 2 + w.T * w.K * 16
