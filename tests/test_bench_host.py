@@ -161,3 +161,17 @@ def test_rotating_sets_cover_twice_the_infinity_cache(name):
     # buffer, output (and workspace), each rounded to 256
     rows = w.T * w.K + w.E * (w.A - 1)
     assert per_set >= w.T * w.H * 2 * 2 + rows * w.H * 2 + w.T * w.K * 16
+
+
+def test_phase_instrumentation_applies(tmp_path):
+    """bench_phases.py's instrumented copy still finds every anchor in the
+    current kernel sources (it stops with SystemExit otherwise), and leaves
+    the library's own sources untouched."""
+    import bench_phases
+    before = open(os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip")).read()
+    bench_phases.instrument(str(tmp_path))
+    got = open(tmp_path / "combine_moe_layout_03_amd" / "csrc" / "fused.hip").read()
+    assert got.count("STAMP(") == 9 and "moe_debug_stamps" in got
+    assert "moe_debug_fstamps" in open(tmp_path / "combine_moe_layout_03_amd" / "csrc" /
+                                       "floors.hip").read()
+    assert open(os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip")).read() == before
