@@ -30,8 +30,8 @@ PKG = "combine_moe_layout_03_amd"
 FUSED_STAMPS = [
     ("  const int b = blockIdx.x;\n  int st = 0;\n",
      "  unsigned long long ts[8] = {0, 0, 0, 0, 0, 0, 0, 0};\n  STAMP(0);\n"),
-    ("    if (counting) ids.issue(p.idx, P, nthreads, nr);\n", "    STAMP(1);\n"),
-    ("      val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));\n",
+    ("    if (counting) ids.issue(hidx, P, nthreads, nr);\n", "    STAMP(1);\n"),
+    ("      val = __builtin_nontemporal_load(hx + (int64_t)t * hnvec + min(v, hnvec - 1));\n",
      "      STAMP(2);\n"),
     ("    if (counting) ids.settle(P, E, nthreads, pbeg, K, s_tok, st);\n    lds_barrier();\n",
      "    STAMP(3);\n"),

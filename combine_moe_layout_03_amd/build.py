@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     "-Wall",
     # packed f32 ops off: the compiler must not form v_pk_{add,mul,fma}_f32
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # leading scalar and pointer kernel arguments preloaded into registers at
+    # launch (no round trip to the argument buffer before the first loads;
+    # the combine measured 4.74 vs 4.83 us at 128 x 7168)
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 
 

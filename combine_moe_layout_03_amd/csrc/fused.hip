@@ -306,8 +306,16 @@ __device__ __forceinline__ int token_counts8(const LaneIds<kRounds> &ids, int th
 
 // kFp8: -1 copies bf16 rows; otherwise the FP8 flags of the cast. kCpw: row
 // chunks per copying wave (2 only for bf16 rows).
+//
+// The values a token workgroup needs before its first loads come first, as
+// scalar arguments (copies of fields of f), so the launch can preload them
+// into registers (the library is built with kernel-argument preloading): the
+// routing and row loads need no round trip to the argument buffer.
 template <bool kCopy, int kRounds, int kFp8, int kCpw>
-__global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams f) {
+__global__ __launch_bounds__(kCountThreads) void count_layout_kernel(
+    const int64_t *hidx, const u32x4 *hx, uint64_t hmagic, int32_t hT, int32_t hK, int32_t hE,
+    int32_t hmode, int32_t htoken_wgs, int32_t hwpt, int32_t hcpw, int32_t hnchunk,
+    int32_t hnvec, CountParams f) {
   __shared__ int32_t s_pre[64];  // per k: the slot (contiguous) or stripe row (low latency)
   __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
 
@@ -316,8 +324,8 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
   const int b = blockIdx.x;
   int st = 0;
 
-  if (b >= f.token_wgs) {  // uniform per workgroup
-    duty_workgroup<kRounds>(p, b - f.token_wgs, f.duty_wgs, st);
+  if (b >= htoken_wgs) {  // uniform per workgroup
+    duty_workgroup<kRounds>(p, b - htoken_wgs, f.duty_wgs, st);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // the last wave writes the token's handle entries and reports its bad
@@ -327,12 +335,12 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
     // lanes that read the routing and count (all of them without the copy)
     constexpr int nthreads = kCountThreads;
     constexpr bool counting = true;
-    const int E = p.E, R = p.R, K = p.K, T = p.T;
+    const int E = hE, R = p.R, K = hK, T = hT;
     const int P = T * K;
-    const bool ll = p.mode == kModeLowLatency;
+    const bool ll = hmode == kModeLowLatency;
     // b / wg_per_token, exact while b * wg_per_token < 2^32
-    const int t = kCopy ? (int)(((uint64_t)(uint32_t)b * f.wpt_magic) >> 32) : b;  // < T
-    const int part = b - t * (kCopy ? f.wg_per_token : 1);  // workgroup within the token
+    const int t = kCopy ? (int)(((uint64_t)(uint32_t)b * hmagic) >> 32) : b;  // < T
+    const int part = b - t * (kCopy ? hwpt : 1);  // workgroup within the token
     const bool token_lead = part == 0;
     const int pbeg = t * K;
     if (tid < 64) s_pre[tid] = 0;
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
     // the ids past this token's pairs are neither requested nor counted (on
     // average half the routing); a contiguous slot counts every pair.
     const int nr = ll ? (pbeg + K + nthreads - 1) / nthreads : kRounds;
-    if (counting) ids.issue(p.idx, P, nthreads, nr);
+    if (counting) ids.issue(hidx, P, nthreads, nr);
     //    Every wave's id loads leave before any wave's row load (a barrier
     //    with no memory wait). Without it the routing reached a workgroup's
     //    last wave 0.5 us after its first -- id loads issued after another
@@ -358,13 +366,13 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
     int v = 0, chunk = 0;
     bool lane_ok = false, lane_ok2 = false;
     if (kCopy) {
-      chunk = part * f.chunks_per_wg + wave * kCpw;
+      chunk = part * hcpw + wave * kCpw;
       v = chunk * 64 + lane;
-      lane_ok = wave * kCpw < f.chunks_per_wg && chunk < f.nchunk && v < f.nvec;
-      val = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v, f.nvec - 1));
+      lane_ok = wave * kCpw < hcpw && chunk < hnchunk && v < hnvec;
+      val = __builtin_nontemporal_load(hx + (int64_t)t * hnvec + min(v, hnvec - 1));
       if (kCpw == 2) {  // the wave's second chunk, 64 vectors further
-        lane_ok2 = wave * kCpw + 1 < f.chunks_per_wg && chunk + 1 < f.nchunk && v + 64 < f.nvec;
-        val2 = __builtin_nontemporal_load(f.x + (int64_t)t * f.nvec + min(v + 64, f.nvec - 1));
+        lane_ok2 = wave * kCpw + 1 < hcpw && chunk + 1 < hnchunk && v + 64 < hnvec;
+        val2 = __builtin_nontemporal_load(hx + (int64_t)t * hnvec + min(v + 64, hnvec - 1));
       }
     }
     if (counting) ids.settle(P, E, nthreads, pbeg, K, s_tok, st);
@@ -417,11 +425,11 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
       // pair k's codes, and its scale (or packed UE8M0 word) by one lane per group
       auto put = [&](int s, int e) {
         const int i = s - e * f.RM;  // row within the expert's R*M rows
-        __builtin_nontemporal_store(codes, f.q + (int64_t)s * f.nvec + v);
+        __builtin_nontemporal_store(codes, f.q + (int64_t)s * hnvec + v);
         if (kFp8 & kFp8Ue8m0) {
           if (lane == 0)
-            f.ue[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.nchunk + chunk
-                                        : ((int64_t)e * f.nchunk + chunk) * f.RM + i] = word;
+            f.ue[(kFp8 & kFp8ScaleRows) ? (int64_t)s * hnchunk + chunk
+                                        : ((int64_t)e * hnchunk + chunk) * f.RM + i] = word;
         } else if ((lane & 15) == 0) {
           f.scale[(kFp8 & kFp8ScaleRows) ? (int64_t)s * f.G + grp
                                          : ((int64_t)e * f.G + grp) * f.RM + i] = q.scale;
@@ -469,13 +477,13 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if ((uint32_t)sl[k] < rows32)
-              __builtin_nontemporal_store(val, dst + (int64_t)sl[k] * f.nvec);
+              __builtin_nontemporal_store(val, dst + (int64_t)sl[k] * hnvec);
         }
         if (kCpw == 2 && lane_ok2) {
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if ((uint32_t)sl[k] < rows32)
-              __builtin_nontemporal_store(val2, dst + (int64_t)sl[k] * f.nvec + 64);
+              __builtin_nontemporal_store(val2, dst + (int64_t)sl[k] * hnvec + 64);
         }
         if (wave == hw) {  // receive buffer smaller than the layout needs
 #pragma unroll
@@ -486,9 +494,9 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
         for (int k = 0; k < K; ++k) {
           const int sk = __builtin_amdgcn_readlane(out, k);
           if ((uint32_t)sk < rows32) {
-            if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)sk * f.nvec);
+            if (lane_ok) __builtin_nontemporal_store(val, dst + (int64_t)sk * hnvec);
             if (kCpw == 2 && lane_ok2)
-              __builtin_nontemporal_store(val2, dst + (int64_t)sk * f.nvec + 64);
+              __builtin_nontemporal_store(val2, dst + (int64_t)sk * hnvec + 64);
           } else if (sk != -1 && wave == hw) {
             st |= kStBadSlot;  // receive buffer smaller than the layout needs
           }
@@ -523,14 +531,18 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(CountParams
 
 template <bool kCopy, int kFp8, int kCpw = 1>
 hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const CountParams &f) {
+#define MOE_COUNT_ARGS                                                                       \
+  f.lp.idx, f.x, f.wpt_magic, f.lp.T, f.lp.K, f.lp.E, f.lp.mode, f.token_wgs, f.wg_per_token, \
+      f.chunks_per_wg, f.nchunk, f.nvec, f
   if (rounds <= 1)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8, kCpw>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8, kCpw>), grid, block, 0, s, MOE_COUNT_ARGS);
   else if (rounds <= 2)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2, kFp8, kCpw>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 2, kFp8, kCpw>), grid, block, 0, s, MOE_COUNT_ARGS);
   else if (rounds <= 4)
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4, kFp8, kCpw>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 4, kFp8, kCpw>), grid, block, 0, s, MOE_COUNT_ARGS);
   else
-    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8, kFp8, kCpw>), grid, block, 0, s, f);
+    hipLaunchKernelGGL((count_layout_kernel<kCopy, 8, kFp8, kCpw>), grid, block, 0, s, MOE_COUNT_ARGS);
+#undef MOE_COUNT_ARGS
   return hipGetLastError();
 }
 
