@@ -35,7 +35,6 @@ struct RankFusedParams {
   const int64_t *idx;  // [T*K]
   const float *w;      // [T*K] may be null
   int32_t T, K, E, R, L, A;
-  int32_t vec_ids;  // K == 8 and idx 16-byte aligned: a token's ids in four 16-byte loads
   uint64_t l_magic;
   int32_t *rank_slot;    // [T*R]
   int32_t *rank_offset;  // [R+1]
@@ -56,68 +55,77 @@ struct RankFusedParams {
                       // workgroup count_wgs writes the rank offsets
 };
 
-// The routing as one lane sees it: tokens tid + 512 i (i < kRounds), their
-// valid ids (-1 otherwise) and their sets of ranks.
-template <int kRounds>
+// The routing in two views. Read as it lies in memory -- pair i * 512 + tid
+// in round i, one 8-byte load per pair, every wave taking part, so each load
+// instruction covers 512 contiguous bytes -- a lane keeps its pairs' valid ids
+// (for the receive counts) and writes their ranks, one byte each, into an LDS
+// table with one 8-byte row per token. After a barrier a lane reads the rows
+// of tokens tid + 512 j (j < kRounds) and holds those tokens' sets of ranks.
+// (Each lane reading its own token's 64 bytes as four 16-byte loads, from
+// two waves only, brought the routing in 0.36 us later and the row chunk,
+// which returns behind it, as much later.) kPairRounds, the pair rounds
+// compiled, is the launch's ceil(T * K / 512) rounded up to a power of two:
+// the few-microsecond kernel pays for every instruction-cache line its waves
+// run through, so no unused round is unrolled.
+template <int kRounds, int kPairRounds>
 struct LaneTokens {
-  int64_t raw[kRounds][kRfMaxK];
-  int id[kRounds][kRfMaxK];
+  int64_t raw[kPairRounds];
+  int pid[kPairRounds];  // the id of pair i * 512 + tid if valid, else -1
   uint64_t ranks[kRounds];
 
-  // request the ids (addresses clamped into the routing; T >= 1)
-  __device__ __forceinline__ void issue(const RankFusedParams &p) {
-    const int w0 = __builtin_amdgcn_readfirstlane((int)threadIdx.x & ~63);
+  // request the pairs (addresses clamped into the routing)
+  __device__ __forceinline__ void issue(const int64_t *idx, int P) {
+    const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      const int t = min(i * kRfThreads + (int)threadIdx.x, p.T - 1);
-      const int64_t *row = p.idx + (int64_t)t * p.K;
-#pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) raw[i][k] = -1;
-      // waves whose lanes hold no token (and ids past K) request nothing
-      if (i * kRfThreads + w0 < p.T) {
-        if (p.vec_ids) {  // the token's 64-byte row in four 16-byte loads
-          typedef int64_t i64x2 __attribute__((ext_vector_type(2)));
-          const i64x2 *row2 = reinterpret_cast<const i64x2 *>(row);
-#pragma unroll
-          for (int k = 0; k < kRfMaxK / 2; ++k) {
-            const i64x2 q = row2[k];
-            raw[i][2 * k] = q.x;
-            raw[i][2 * k + 1] = q.y;
-          }
-        } else {
-#pragma unroll
-          for (int k = 0; k < kRfMaxK; ++k)
-            if (k < p.K) raw[i][k] = row[k];
-        }
-      }
+    for (int i = 0; i < kPairRounds; ++i) {
+      raw[i] = -1;
+      if (i * kRfThreads < P) raw[i] = idx[min(i * kRfThreads + tid, P - 1)];  // uniform
     }
     // every id load stays ahead of whatever the caller issues next (a row load)
     __builtin_amdgcn_sched_barrier(0);
   }
-  __device__ __forceinline__ void settle(const RankFusedParams &p, int &st) {
+  // validate the pairs (bad ids flagged) and write their rank bytes (0xff:
+  // no expert) into row q / K, byte q mod K of the table
+  __device__ __forceinline__ void settle(const RankFusedParams &p, int P, uint8_t *s_rk,
+                                         int &st) {
+    const int tid = threadIdx.x;
+    // q / K by a multiply: the reciprocal's error times q stays under
+    // 2^13 / 2^18 = 1/32 for q < P <= 2^13, below the 1/K >= 1/8 gap
+    // between q / K and the next integer; q * kmag < 2^32
+    const uint32_t kmag = (1u << 18) / (uint32_t)p.K + 1u;
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      const bool live = i * kRfThreads + (int)threadIdx.x < p.T;
-      uint64_t m = 0;
-#pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) {
-        const int64_t e = raw[i][k];
-        const bool in = live && k < p.K;
-        const bool ok = in && e >= 0 && e < p.E;
-        if (in && !ok && e != -1) st |= kStBadExpert;
-        id[i][k] = ok ? (int)e : -1;
-        if (ok) m |= 1ull << rank_of((int)e, p.l_magic);
+    for (int i = 0; i < kPairRounds; ++i) {
+      const int q = i * kRfThreads + tid;
+      const bool in = q < P;
+      const int64_t e = raw[i];
+      const bool ok = in && e >= 0 && e < p.E;
+      if (in && !ok && e != -1) st |= kStBadExpert;
+      pid[i] = ok ? (int)e : -1;
+      if (in) {
+        const int tt = (int)(((uint32_t)q * kmag) >> 18);
+        s_rk[tt * kRfMaxK + (q - tt * p.K)] =
+            ok ? (uint8_t)rank_of((int)e, p.l_magic) : (uint8_t)0xffu;
       }
-      ranks[i] = m;
     }
   }
-  __device__ __forceinline__ void empty() {
+  // after the barrier that follows every settle: the sets of ranks
+  __device__ __forceinline__ void gather(const RankFusedParams &p, const uint8_t *s_rk) {
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) {
-      ranks[i] = 0;
-#pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) id[i][k] = -1;
+    for (int j = 0; j < kRounds; ++j) {
+      const int tt = j * kRfThreads + (int)threadIdx.x;
+      ranks[j] = tt < p.T ? rank_set(*reinterpret_cast<const uint64_t *>(s_rk + tt * kRfMaxK), p.K)
+                          : 0ull;
     }
+  }
+  // the set of ranks of a token's row of rank bytes (the first K of them)
+  static __device__ __forceinline__ uint64_t rank_set(uint64_t row, int K) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int k = 0; k < kRfMaxK; ++k) {
+      const uint32_t r = (uint32_t)(row >> (8 * k)) & 0xffu;
+      if (k < K && r != 0xffu) m |= 1ull << r;
+    }
+    return m;
   }
 };
 
@@ -128,26 +136,26 @@ __device__ __forceinline__ uint32_t spread4(uint32_t x) { return (x * 0x00204081
 // This wave's pairs on experts b, b + G, ... (lane j: the j-th of them; at
 // most kRfDuties), for the aligned receive counts. Every lane of the wave must
 // call it.
-template <int kRounds>
+template <int kRounds, int kPR>
 __device__ __forceinline__ int count_experts(const RankFusedParams &p,
-                                             const LaneTokens<kRounds> &rt, int b, int G,
-                                             int &ne) {
+                                             const LaneTokens<kRounds, kPR> &rt, int P, int b,
+                                             int G, int &ne) {
   ne = b < p.E ? (p.E - 1 - b) / G + 1 : 0;
   int cv = 0;
   for (int j = 0; j < ne; ++j) {
     const int e = b + j * G;
     int n = 0;
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i)
-#pragma unroll
-      for (int k = 0; k < kRfMaxK; ++k) n += __popcll(__ballot(rt.id[i][k] == e));
+    for (int i = 0; i < kPR; ++i)
+      if (i * kRfThreads < P) n += __popcll(__ballot(rt.pid[i] == e));  // uniform
     cv = set_lane(cv, j, n);
   }
   return cv;
 }
 
-template <int kRounds>
-__device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp) {
+template <int kRounds, int kPR>
+__device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp,
+                                uint8_t *s_rk) {
   __shared__ int32_t s_cnt[64];  // per rank: tokens reaching it
   __shared__ int32_t s_pos[64];  // per rank: tokens before t reaching it
   const int tid = threadIdx.x, lane = lane_id();
@@ -160,24 +168,16 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   // nothing for 7168-wide rows (7 chunks), so those stores do not queue behind
   // a row's stores
   constexpr int hw = kRfWaves - 1;
-  const int K = p.K;
+  const int K = p.K, P = p.T * K;
   if (tid < 64) {
     s_cnt[tid] = 0;
     s_pos[tid] = 0;
   }
 
-  // 1. pair (t, lane mod K) and its weight (lanes 0..K-1 hold the token's K
-  //    pairs; without weights the load reads id bits, unused: no branch
-  //    around it) ...
-  const int kl = lane % K;
-  const int64_t *trow = p.idx + (int64_t)t * K;
-  const int64_t te = trow[kl];
-  const float *wsrc = p.w ? p.w : reinterpret_cast<const float *>(p.idx);
-  const float tw = wsrc[(int64_t)t * K + kl];
-  // 2. ... the routing ...
-  LaneTokens<kRounds> rt;
-  rt.issue(p);
-  // 3. ... then the row chunk this wave copies, unconditionally (address
+  // 1. the routing first ...
+  LaneTokens<kRounds, kPR> rt;
+  rt.issue(p.idx, P);
+  // 2. ... then the row chunk this wave copies, unconditionally (address
   //    clamped into the row), so it stays in flight while the rows are derived.
   //    Every wave's routing loads leave before any wave's row load (a barrier
   //    with no memory wait): routing loads issued after another wave's cold
@@ -189,20 +189,21 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   u32x4 val = __builtin_nontemporal_load(p.x + (int64_t)t * p.nvec + min(v, p.nvec - 1));
   __builtin_amdgcn_sched_barrier(0);  // nothing below waits before the row load is issued
 
-  // 4. the token's set of ranks (uniform)
-  const bool tok = te >= 0 && te < p.E;
-  const int tr = tok ? rank_of((int)te, p.l_magic) : -1;  // rank of pair `lane` (lane < K)
-  uint64_t mt = 0;
-  for (int k = 0; k < K; ++k) {
-    const int rk = __builtin_amdgcn_readlane(tr, k);
-    if (rk >= 0) mt |= 1ull << rk;
-  }
+  // 3. the rank table; after the barrier each lane takes its tokens' sets of
+  //    ranks, and every lane the row of token t: its set of ranks (uniform)
+  //    and, in lane j, the rank of pair j mod K (-1: no expert)
+  rt.settle(p, P, s_rk, st);
+  lds_barrier();  // the rank table is whole, the LDS counters are zero
+  rt.gather(p, s_rk);
+  const int kl = lane % K;
+  const uint64_t trow = *reinterpret_cast<const uint64_t *>(s_rk + t * kRfMaxK);
+  const uint32_t trk = (uint32_t)(trow >> (8 * kl)) & 0xffu;
+  const int tr = trk == 0xffu ? -1 : (int)trk;
+  const uint64_t mt = LaneTokens<kRounds, kPR>::rank_set(trow, K);
   const int rhi = mt ? 63 - __builtin_clzll(mt) : 0;  // highest rank reached
   const int nc = (rhi >> 3) + 1;                       // 8-rank groups up to it
-  lds_barrier();  // the LDS counters are zero
-  rt.settle(p, st);
 
-  // 5. per rank r of the first nc groups, this wave's tokens reaching r and
+  // 4. per rank r of the first nc groups, this wave's tokens reaching r and
   //    its tokens before t reaching r: one byte counter per rank, summed over
   //    the wave by DPP; lane r takes rank r's counts. Waves that hold no token
   //    add nothing.
@@ -231,16 +232,17 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
       atomicAdd(&s_cnt[lane], cv);
       atomicAdd(&s_pos[lane], pv);
     }
-    // this workgroup's share of the receive counts
+  }
+  {  // this workgroup's share of the receive counts (every wave holds pairs)
     int ne;
-    const int ev = count_experts(p, rt, b, p.count_wgs, ne);
+    const int ev = count_experts(p, rt, P, b, p.count_wgs, ne);
     if (lane < ne) atomicAdd(&s_exp[lane], ev);
   }
   lds_barrier();
   if (p.recv_count && tid < kRfDuties && b + tid * p.count_wgs < p.E)
     p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
 
-  // 6. row of (t, r) in lane r: the tokens of the ranks below r (a scan over
+  // 5. row of (t, r) in lane r: the tokens of the ranks below r (a scan over
   //    the lanes) plus the tokens before t on r
   const int n = s_cnt[lane];
   int row = wave_inclusive_sum(n) - n + s_pos[lane];
@@ -252,7 +254,7 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
     row = -1;
   }
 
-  // 7. the row chunk, once per rank reached (row -1 for the others; rows are
+  // 6. the row chunk, once per rank reached (row -1 for the others; rows are
   //    int32, so one unsigned compare against the clamped row count)
   asm volatile("" : "+v"(val));
   const uint32_t rows32 = p.rows < 0x7fffffff ? (uint32_t)p.rows : 0x7fffffffu;
@@ -282,8 +284,11 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
     }
   }
 
-  // 8. the token's handle entries
+  // 7. the token's handle entries; the pairs' ids and weights are read here,
+  //    by this wave only (a CU returns loads in issue order, so read ahead of
+  //    the routing they would hold it back)
   if (lead && wave == hw) {
+    const int64_t te = p.idx[(int64_t)t * K + kl];
     if (lane < p.R) p.rank_slot[(int64_t)t * p.R + lane] = row;
     if (row >= 0 && p.recv_src) p.recv_src[row] = t;
     // entry (j, k) of the rows' local ids and weights in lane j*K + k (at
@@ -301,7 +306,7 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
     if (jr >= 0) {
       const bool loc = tr == rj;  // the pair's expert lives on the row's rank
       if (p.recv_idx) p.recv_idx[(int64_t)jr * K + kl] = loc ? te - (int64_t)rj * p.L : -1;
-      if (p.recv_w && p.w) p.recv_w[(int64_t)jr * K + kl] = loc ? tw : 0.0f;
+      if (p.recv_w && p.w) p.recv_w[(int64_t)jr * K + kl] = loc ? p.w[(int64_t)t * K + kl] : 0.0f;
     }
   }
   st &= ~kStBadExpert;  // every workgroup reads every id; the duty workgroups report
@@ -309,22 +314,21 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
 
 // Workgroups with no token: receive counts (b < count_wgs, written by the
 // kernel after its last barrier), or the rank offsets (b == count_wgs).
-template <int kRounds>
-__device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp) {
+template <int kRounds, int kPR>
+__device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp,
+                               uint8_t *s_rk) {
   __shared__ int32_t s_c[kRfWaves][64];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  LaneTokens<kRounds> rt;
-  if (p.T > 0) {
-    rt.issue(p);
-    rt.settle(p, st);
-  } else {
-    rt.empty();
-  }
-  lds_barrier();  // s_exp is zero
+  const int P = p.T * p.K;  // 0 for an empty batch: nothing is read
+  LaneTokens<kRounds, kPR> rt;
+  rt.issue(p.idx, P);
+  rt.settle(p, P, s_rk, st);
+  lds_barrier();  // the rank table is whole, s_exp is zero
+  rt.gather(p, s_rk);
   if (b < p.count_wgs) {
     int ne;
-    const int ev = count_experts(p, rt, b, p.count_wgs, ne);
+    const int ev = count_experts(p, rt, P, b, p.count_wgs, ne);
     if (lane < ne) atomicAdd(&s_exp[lane], ev);
   } else {
     // rank offsets: exclusive sum of the tokens reaching each rank
@@ -348,16 +352,18 @@ __device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t
   }
 }
 
-template <int kRounds>
+template <int kRounds, int kPR>
 __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFusedParams p) {
   __shared__ int32_t s_exp[kRfDuties];  // pairs on this workgroup's experts
+  // per token its pairs' ranks, one byte each (0xff: no expert), 8 per row
+  __shared__ __align__(8) uint8_t s_rk[kRfMaxTokens * kRfMaxK];
   const int tid = threadIdx.x, b = blockIdx.x;
   int st = 0;
   if (tid < kRfDuties) s_exp[tid] = 0;
   if (b < p.token_wgs) {  // uniform per workgroup
-    token_workgroup<kRounds>(p, b, st, s_exp);
+    token_workgroup<kRounds, kPR>(p, b, st, s_exp, s_rk);
   } else {
-    duty_workgroup<kRounds>(p, b, st, s_exp);
+    duty_workgroup<kRounds, kPR>(p, b, st, s_exp, s_rk);
     lds_barrier();  // every wave's receive counts are in s_exp
     if (b < p.count_wgs && p.recv_count && tid < kRfDuties && b + tid * p.count_wgs < p.E)
       p.recv_count[b + tid * p.count_wgs] = round_up(s_exp[tid], p.A);
@@ -389,8 +395,6 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   p.R = R;
   p.L = E / R;
   p.A = A;
-  // (a routing view that starts at an odd int64 takes one load per id)
-  p.vec_ids = K == kRfMaxK && (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;
   p.l_magic = ((1ull << 32) + (uint64_t)p.L - 1) / (uint64_t)p.L;
   p.rank_slot = rank_slot;
   p.rank_offset = rank_offset;
@@ -413,10 +417,27 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   const int need = (E + kRfDuties - 1) / kRfDuties;
   p.count_wgs = p.token_wgs > need ? p.token_wgs : need;
   const dim3 grid((unsigned)(p.count_wgs + 1)), block(kRfThreads);
-  if (T <= kRfThreads)
-    hipLaunchKernelGGL(rank_layout_dispatch_kernel<1>, grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL(rank_layout_dispatch_kernel<2>, grid, block, 0, s, p);
+  // pair rounds: ceil(T * K / 512) rounded up to a power of two (T * K <= 8192)
+  const int pr = (T * K + kRfThreads - 1) / kRfThreads;
+  if (T <= kRfThreads) {
+    if (pr <= 1)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 1>), grid, block, 0, s, p);
+    else if (pr <= 2)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 2>), grid, block, 0, s, p);
+    else if (pr <= 4)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 4>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 8>), grid, block, 0, s, p);
+  } else {
+    if (pr <= 2)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 2>), grid, block, 0, s, p);
+    else if (pr <= 4)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 4>), grid, block, 0, s, p);
+    else if (pr <= 8)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 8>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 16>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 
