@@ -310,12 +310,13 @@ __device__ __forceinline__ int token_counts8(const LaneIds<kRounds> &ids, int th
 // The values a token workgroup needs before its first loads come first, as
 // scalar arguments (copies of fields of f), so the launch can preload them
 // into registers (the library is built with kernel-argument preloading): the
-// routing and row loads need no round trip to the argument buffer.
+// routing and row loads need no round trip to the argument buffer. The launch
+// preloads 14 dwords (up to hnchunk); hE is read after the row load is issued.
 template <bool kCopy, int kRounds, int kFp8, int kCpw>
 __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(
-    const int64_t *hidx, const u32x4 *hx, uint64_t hmagic, int32_t hT, int32_t hK, int32_t hE,
-    int32_t hmode, int32_t htoken_wgs, int32_t hwpt, int32_t hcpw, int32_t hnchunk,
-    int32_t hnvec, CountParams f) {
+    const int64_t *hidx, const u32x4 *hx, uint64_t hmagic, int32_t hT, int32_t hK,
+    int32_t hmode, int32_t htoken_wgs, int32_t hwpt, int32_t hcpw, int32_t hnvec,
+    int32_t hnchunk, int32_t hE, CountParams f) {
   __shared__ int32_t s_pre[64];  // per k: the slot (contiguous) or stripe row (low latency)
   __shared__ int32_t s_tok[64];   // this token's ids (-1 = none)
 
@@ -324,7 +325,9 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(
   const int b = blockIdx.x;
   int st = 0;
 
-  if (b >= htoken_wgs) {  // uniform per workgroup
+  // uniform per workgroup; the token path is laid out first, so a token
+  // wave's first instructions follow the entry in the instruction cache
+  if (__builtin_expect(b >= htoken_wgs, 0)) {
     duty_workgroup<kRounds>(p, b - htoken_wgs, f.duty_wgs, st);
   } else {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -532,8 +535,8 @@ __global__ __launch_bounds__(kCountThreads) void count_layout_kernel(
 template <bool kCopy, int kFp8, int kCpw = 1>
 hipError_t launch_rounds(int rounds, dim3 grid, dim3 block, hipStream_t s, const CountParams &f) {
 #define MOE_COUNT_ARGS                                                                       \
-  f.lp.idx, f.x, f.wpt_magic, f.lp.T, f.lp.K, f.lp.E, f.lp.mode, f.token_wgs, f.wg_per_token, \
-      f.chunks_per_wg, f.nchunk, f.nvec, f
+  f.lp.idx, f.x, f.wpt_magic, f.lp.T, f.lp.K, f.lp.mode, f.token_wgs, f.wg_per_token,        \
+      f.chunks_per_wg, f.nvec, f.nchunk, f.lp.E, f
   if (rounds <= 1)
     hipLaunchKernelGGL((count_layout_kernel<kCopy, 1, kFp8, kCpw>), grid, block, 0, s, MOE_COUNT_ARGS);
   else if (rounds <= 2)

@@ -98,20 +98,26 @@ __global__ __launch_bounds__(256) void dispatch_kernel(const typename Lane<kDw>:
 }
 
 template <int KT, bool kWeights, bool kF32Out, bool kMask, bool kWsum, int kDw>
-__global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T *__restrict__ y,
-                                                     int64_t rows, const int32_t *__restrict__ slot,
+// One wave per workgroup; the token of wave b is b / nchunk, by the
+// host-computed reciprocal tmagic where that is exact (0: a division). The
+// arguments a wave needs before its first loads lead, so the launch preloads
+// them into registers (14 dwords, up to w): a read of the argument buffer
+// before the slot load put a round trip ahead of every row load.
+__global__ __launch_bounds__(64) void combine_kernel(const int32_t *__restrict__ slot,
+                                                     const typename Lane<kDw>::T *__restrict__ y,
+                                                     uint64_t tmagic, int64_t rows, int32_t T,
+                                                     int32_t nq, int32_t nchunk, int32_t Kr,
                                                      const float *__restrict__ w,
                                                      typename Lane<kDw>::T *__restrict__ out,
-                                                     f32x4 *__restrict__ out_f32, int32_t T,
-                                                     int32_t Kr, int32_t nq, int32_t nchunk,
-                                                     CombineMask cm, RowWeightSum ws,
-                                                     int32_t *status) {
+                                                     f32x4 *__restrict__ out_f32, CombineMask cm,
+                                                     RowWeightSum ws, int32_t *status) {
 #pragma clang fp contract(off)
   typedef typename Lane<kDw>::T VT;
   const int K = KT ? KT : Kr;
-  int t;
-  const int v = wave_token_chunk(nchunk, t);  // lane (kDw dwords) index in the row
+  const int b = blockIdx.x;
+  const int t = tmagic ? (int)(((uint64_t)(uint32_t)b * tmagic) >> 32) : b / nchunk;
   if (t >= T) return;
+  const int v = (b - t * nchunk) * 64 + (int)(threadIdx.x & 63);  // lane (kDw dwords) in the row
   const bool lane_ok = v < nq;
   const int32_t *srow = slot + (int64_t)t * K;
   const float *wrow = kWeights ? w + (int64_t)t * K : nullptr;
@@ -203,6 +209,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const typename Lane<kDw>::T
   if (st && status && (threadIdx.x & 63) == 0) atomicOr(status, st);
 }
 
+// ceil(2^32 / d): (b * m) >> 32 == b / d for every b < waves while
+// waves * d < 2^32 (the error b * (m - 2^32 / d) / 2^32 < b / 2^32 stays under
+// 1 / d); 0 beyond, where the kernel divides.
+uint64_t token_magic(int64_t waves, int32_t d) {
+  if ((uint64_t)waves * (uint64_t)d >= (1ull << 32)) return 0;
+  return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d;
+}
+
 // Large batches copy in 8-byte lanes (twice the waves, more stores in flight:
 // 8192 x 7168 216 -> 202 us, the skewed 4096 x 4096 batch 56.3 -> 54.6 us);
 // small ones in 16-byte lanes (128 x 7168: 3.96 vs 4.06 us).
@@ -238,9 +252,9 @@ hipError_t combine_k3(const uint16_t *y, int64_t rows, const int32_t *slot, cons
   const int64_t waves = (int64_t)T * nchunk;
   const RowWeightSum none{nullptr, nullptr, 0};
   hipLaunchKernelGGL((combine_kernel<KT, kW, kF, kM, false, 2>), dim3((unsigned)waves), dim3(64), 0,
-                     s, reinterpret_cast<const u32x2 *>(y), rows, slot, w,
-                     reinterpret_cast<u32x2 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, K,
-                     nq, nchunk, cm, none, status);
+                     s, slot, reinterpret_cast<const u32x2 *>(y), token_magic(waves, nchunk), rows,
+                     T, nq, nchunk, K, w, reinterpret_cast<u32x2 *>(out),
+                     reinterpret_cast<f32x4 *>(out_f32), cm, none, status);
   return hipGetLastError();
 }
 
@@ -254,9 +268,10 @@ hipError_t rank_combine_k(const uint16_t *y, int64_t rows, const int32_t *rank_s
   const int64_t waves = (int64_t)T * nchunk;
   const CombineMask none{nullptr, nullptr, 0, 0};
   hipLaunchKernelGGL((combine_kernel<KT, false, kF, false, kWs, 2>), dim3((unsigned)waves), dim3(64),
-                     0, s, reinterpret_cast<const u32x2 *>(y), rows, rank_slot, nullptr,
-                     reinterpret_cast<u32x2 *>(out), reinterpret_cast<f32x4 *>(out_f32), T, R,
-                     nq, nchunk, none, ws, status);
+                     0, s, rank_slot, reinterpret_cast<const u32x2 *>(y),
+                     token_magic(waves, nchunk), rows, T, nq, nchunk, R, nullptr,
+                     reinterpret_cast<u32x2 *>(out), reinterpret_cast<f32x4 *>(out_f32), none, ws,
+                     status);
   return hipGetLastError();
 }
 
