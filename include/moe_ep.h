@@ -35,9 +35,8 @@
  *    (uint16_t). Pointers to bf16 rows, f32 rows and the receive buffer must be
  *    16-byte aligned, and H must be a multiple of 8 (one 16-byte vector is
  *    8 bf16 values). Routing pointers (topk_idx, phys_idx: int64) must be
- *    8-byte aligned; MOE_ERR_ALIGN otherwise. (A 16-byte aligned routing lets
- *    some kernels read a token's ids as 16-byte vectors; an 8-byte aligned one
- *    that is not 16-byte aligned is read one id at a time, same results.)
+ *    8-byte aligned (the kernels read them as 8-byte words); MOE_ERR_ALIGN
+ *    otherwise.
  *  - Limits: 1 <= E <= 1024, 1 <= R, E % R == 0, 1 <= K <= 64,
  *    0 <= T, T*K + E*(A-1) < 2^31, 8 <= H <= 2^20, 1 <= A <= 2^16.
  */
