@@ -117,7 +117,7 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
                               hipStream_t s);
 // Normal-mode layout and dispatch in one launch (rank_fused.hip), for
 // T <= 1024, K <= 8, R <= 64: the results of launch_rank_layout followed by
-// the rank scatter.
+// the rank scatter. With x null, the layout alone (no row read or written).
 bool rank_layout_dispatch_fits(int32_t T, int32_t K, int32_t R);
 hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32_t T, int32_t K,
                                        int32_t E, int32_t R, int32_t A, int32_t *rank_slot,

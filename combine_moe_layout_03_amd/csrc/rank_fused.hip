@@ -153,7 +153,9 @@ __device__ __forceinline__ int count_experts(const RankFusedParams &p,
   return cv;
 }
 
-template <int kRounds, int kPR>
+// kCopy false: the layout alone (no row chunk read or stored; one workgroup
+// per token).
+template <bool kCopy, int kRounds, int kPR>
 __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_t *s_exp,
                                 uint8_t *s_rk) {
   __shared__ int32_t s_cnt[64];  // per rank: tokens reaching it
@@ -182,12 +184,17 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
   //    Every wave's routing loads leave before any wave's row load (a barrier
   //    with no memory wait): routing loads issued after another wave's cold
   //    row load come back after it.
-  __builtin_amdgcn_s_barrier();
-  const int chunk = part * p.chunks_per_wg + wave;
-  const int v = chunk * 64 + lane;
-  const bool lane_ok = wave < p.chunks_per_wg && chunk < p.nchunk && v < p.nvec;
-  u32x4 val = __builtin_nontemporal_load(p.x + (int64_t)t * p.nvec + min(v, p.nvec - 1));
-  __builtin_amdgcn_sched_barrier(0);  // nothing below waits before the row load is issued
+  u32x4 val = {0u, 0u, 0u, 0u};
+  int v = 0;
+  bool lane_ok = false;
+  if (kCopy) {
+    __builtin_amdgcn_s_barrier();
+    const int chunk = part * p.chunks_per_wg + wave;
+    v = chunk * 64 + lane;
+    lane_ok = wave < p.chunks_per_wg && chunk < p.nchunk && v < p.nvec;
+    val = __builtin_nontemporal_load(p.x + (int64_t)t * p.nvec + min(v, p.nvec - 1));
+    __builtin_amdgcn_sched_barrier(0);  // nothing below waits before the row load is issued
+  }
 
   // 3. the rank table; after the barrier each lane takes its tokens' sets of
   //    ranks, and every lane the row of token t: its set of ranks (uniform)
@@ -256,10 +263,11 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
 
   // 6. the row chunk, once per rank reached (row -1 for the others; rows are
   //    int32, so one unsigned compare against the clamped row count)
-  asm volatile("" : "+v"(val));
-  const uint32_t rows32 = p.rows < 0x7fffffff ? (uint32_t)p.rows : 0x7fffffffu;
-  u32x4 *dst = p.recv + v;
-  if (p.R == 8) {  // the eight rows first, then the stores back to back
+  if (!kCopy) {
+  } else if (p.R == 8) {  // the eight rows first, then the stores back to back
+    asm volatile("" : "+v"(val));
+    const uint32_t rows32 = p.rows < 0x7fffffff ? (uint32_t)p.rows : 0x7fffffffu;
+    u32x4 *dst = p.recv + v;
     int sl[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) sl[r] = __builtin_amdgcn_readlane(row, r);
@@ -274,6 +282,9 @@ __device__ void token_workgroup(const RankFusedParams &p, int b, int &st, int32_
         if ((uint32_t)sl[r] >= rows32 && sl[r] != -1) st |= kStBadSlot;
     }
   } else {
+    asm volatile("" : "+v"(val));
+    const uint32_t rows32 = p.rows < 0x7fffffff ? (uint32_t)p.rows : 0x7fffffffu;
+    u32x4 *dst = p.recv + v;
     for (uint64_t rest = mt; rest; rest &= rest - 1ull) {
       const int s = __builtin_amdgcn_readlane(row, __ffsll((unsigned long long)rest) - 1);
       if ((uint32_t)s < rows32) {
@@ -352,7 +363,7 @@ __device__ void duty_workgroup(const RankFusedParams &p, int b, int &st, int32_t
   }
 }
 
-template <int kRounds, int kPR>
+template <bool kCopy, int kRounds, int kPR>
 __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFusedParams p) {
   __shared__ int32_t s_exp[kRfDuties];  // pairs on this workgroup's experts
   // per token its pairs' ranks, one byte each (0xff: no expert), 8 per row
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFu
   int st = 0;
   if (tid < kRfDuties) s_exp[tid] = 0;
   if (b < p.token_wgs) {  // uniform per workgroup
-    token_workgroup<kRounds, kPR>(p, b, st, s_exp, s_rk);
+    token_workgroup<kCopy, kRounds, kPR>(p, b, st, s_exp, s_rk);
   } else {
     duty_workgroup<kRounds, kPR>(p, b, st, s_exp, s_rk);
     lds_barrier();  // every wave's receive counts are in s_exp
@@ -371,6 +382,32 @@ __global__ __launch_bounds__(kRfThreads) void rank_layout_dispatch_kernel(RankFu
   // error bits (rare) go straight to the status word: no barrier ends a token
   // workgroup, so each wave leaves as soon as its own work is out
   if (st && p.status) atomicOr(p.status, st);
+}
+
+// The kernel instance for the batch: pair rounds ceil(T * K / 512) rounded up
+// to a power of two (T * K <= 8192).
+template <bool kCopy>
+void launch_rounds(const RankFusedParams &p, dim3 grid, dim3 block, hipStream_t s) {
+  const int pr = (p.T * p.K + kRfThreads - 1) / kRfThreads;
+  if (p.T <= kRfThreads) {
+    if (pr <= 1)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 1, 1>), grid, block, 0, s, p);
+    else if (pr <= 2)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 1, 2>), grid, block, 0, s, p);
+    else if (pr <= 4)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 1, 4>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 1, 8>), grid, block, 0, s, p);
+  } else {
+    if (pr <= 2)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 2, 2>), grid, block, 0, s, p);
+    else if (pr <= 4)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 2, 4>), grid, block, 0, s, p);
+    else if (pr <= 8)
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 2, 8>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((rank_layout_dispatch_kernel<kCopy, 2, 16>), grid, block, 0, s, p);
+  }
 }
 
 }  // namespace
@@ -407,37 +444,20 @@ hipError_t launch_rank_layout_dispatch(const int64_t *idx, const float *w, int32
   p.x = reinterpret_cast<const u32x4 *>(x);
   p.recv = reinterpret_cast<u32x4 *>(recv);
   p.rows = rows;
-  p.nvec = H / 8;
+  p.nvec = x ? H / 8 : 0;
   p.nchunk = (p.nvec + 63) / 64;
   const int groups = (p.nchunk + kRfChunks - 1) / kRfChunks;
-  p.chunks_per_wg = (p.nchunk + groups - 1) / groups;  // <= kRfChunks = waves
-  p.wg_per_token = (p.nchunk + p.chunks_per_wg - 1) / p.chunks_per_wg;
+  p.chunks_per_wg = x ? (p.nchunk + groups - 1) / groups : 0;  // <= kRfChunks = waves
+  p.wg_per_token = x ? (p.nchunk + p.chunks_per_wg - 1) / p.chunks_per_wg : 1;
   p.wpt_magic = ((1ull << 32) + (uint64_t)p.wg_per_token - 1) / p.wg_per_token;
   p.token_wgs = T * p.wg_per_token;
   const int need = (E + kRfDuties - 1) / kRfDuties;
   p.count_wgs = p.token_wgs > need ? p.token_wgs : need;
   const dim3 grid((unsigned)(p.count_wgs + 1)), block(kRfThreads);
-  // pair rounds: ceil(T * K / 512) rounded up to a power of two (T * K <= 8192)
-  const int pr = (T * K + kRfThreads - 1) / kRfThreads;
-  if (T <= kRfThreads) {
-    if (pr <= 1)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 1>), grid, block, 0, s, p);
-    else if (pr <= 2)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 2>), grid, block, 0, s, p);
-    else if (pr <= 4)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 4>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<1, 8>), grid, block, 0, s, p);
-  } else {
-    if (pr <= 2)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 2>), grid, block, 0, s, p);
-    else if (pr <= 4)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 4>), grid, block, 0, s, p);
-    else if (pr <= 8)
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 8>), grid, block, 0, s, p);
-    else
-      hipLaunchKernelGGL((rank_layout_dispatch_kernel<2, 16>), grid, block, 0, s, p);
-  }
+  if (x)
+    launch_rounds<true>(p, grid, block, s);
+  else
+    launch_rounds<false>(p, grid, block, s);
   return hipGetLastError();
 }
 

@@ -7,7 +7,9 @@
 // weights). The scatter and the row sum are the pair kernels run over the
 // [T, R] table of rank rows instead of the [T, K] table of expert slots.
 //
-// Layout: one workgroup per rank r. A thread takes one token per pass, reads
+// Layout (batches of more than 1024 tokens, or K > 8; smaller ones take the
+// one-launch kernel of rank_fused.hip without its row copy): one workgroup
+// per rank r. A thread takes one token per pass, reads
 // its K ids and forms the set of ranks it reaches as a 64-bit mask (so
 // duplicates collapse). Pass 1 sums, over all tokens, the ranks below r that
 // each reaches (popcount of the masked bits) -- the start of rank r's rows --
@@ -75,83 +77,8 @@ __device__ __forceinline__ uint64_t token_ranks(const RankParams &p, int t, int 
   return m;
 }
 
-// One pass for a batch of at most kRankThreads tokens and K <= 8: every
-// thread loads its token's ids and weights once, up front (one memory
-// latency), and keeps them in registers for both scans.
-__global__ __launch_bounds__(kRankThreads) void rank_layout_small_kernel(RankParams p) {
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_wave[kRankWaves];
-  __shared__ int32_t s_status;
-  const int tid = threadIdx.x, r = blockIdx.x;
-  const uint64_t below = (1ull << r) - 1ull;  // r < 64
-  const int t = tid;
-  const bool live = t < p.T;
-  const int tc = live ? t : 0;
-  int st = 0;
-  IdChunk c;
-  float wk[8];
-  if (p.T > 0) {
-    c.load(p, tc, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wk[j] = p.w ? p.w[(int64_t)tc * p.K + min(j, p.K - 1)] : 0.0f;
-  }
-  if (tid == 0) s_status = 0;
-  for (int l = tid; l < p.L; l += kRankThreads) s_cnt[l] = 0;
-  lds_barrier();
-  uint64_t m = 0, loc = 0;
-  if (live) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t e = c.e[j];
-      if (j >= p.K) break;
-      if (e >= 0 && e < p.E) {
-        const int rr = rank_of((int)e, p.l_magic);
-        m |= 1ull << rr;
-        if (rr == r) {
-          loc |= 1ull << j;
-          atomicAdd(&s_cnt[(int)e - r * p.L], 1);
-        }
-      } else if (e != -1) {
-        st |= kStBadExpert;
-      }
-    }
-  }
-  int before = 0;
-  block_exclusive_scan(__popcll(m & below), s_wave, kRankWaves, &before);
-  const int hit = (int)((m >> r) & 1ull);
-  int total = 0;
-  const int pos = block_exclusive_scan(hit, s_wave, kRankWaves, &total);
-  if (p.recv_count)
-    for (int l = tid; l < p.L; l += kRankThreads)
-      p.recv_count[r * p.L + l] = round_up(s_cnt[l], p.A);
-  if (live) {
-    int row = hit ? before + pos : -1;
-    if (row >= p.cap) {
-      st |= kStBadSlot;
-      row = -1;
-    }
-    p.rank_slot[(int64_t)t * p.R + r] = row;
-    if (row >= 0) {
-      if (p.recv_src) p.recv_src[row] = t;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= p.K) break;
-        const bool l = (loc >> j) & 1ull;
-        if (p.recv_idx) p.recv_idx[(int64_t)row * p.K + j] = l ? c.e[j] - (int64_t)r * p.L : -1;
-        if (p.recv_w && p.w) p.recv_w[(int64_t)row * p.K + j] = l ? wk[j] : 0.0f;
-      }
-    }
-  }
-  if (tid == 0) {
-    p.rank_offset[r] = before;
-    if (r == p.R - 1) p.rank_offset[p.R] = before + total;
-  }
-  if (r != 0) st &= ~kStBadExpert;
-  if (st) atomicOr(&s_status, st);
-  lds_barrier();
-  if (tid == 0 && s_status && p.status) atomicOr(p.status, s_status);
-}
-
+// Batches of more than 1024 tokens, or K > 8 (smaller ones take the
+// layout-only instance of the one-launch kernel in rank_fused.hip).
 __global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(RankParams p) {
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_wave[kRankWaves];
@@ -233,6 +160,12 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
                               int32_t *rank_offset, int32_t *recv_src, int64_t *recv_idx,
                               float *recv_w, int32_t *recv_count, int64_t cap, int32_t *status,
                               hipStream_t s) {
+  // batches the one-launch normal-mode kernel takes: its layout-only instance
+  // (one workgroup per token instead of one per rank)
+  if (rank_layout_dispatch_fits(T, K, R))
+    return launch_rank_layout_dispatch(idx, w, T, K, E, R, A, rank_slot, rank_offset, recv_src,
+                                       recv_idx, recv_w, recv_count, cap, status, nullptr,
+                                       nullptr, 0, 0, s);
   RankParams p;
   p.idx = idx;
   p.w = w;
@@ -251,10 +184,7 @@ hipError_t launch_rank_layout(const int64_t *idx, const float *w, int32_t T, int
   p.recv_count = recv_count;
   p.cap = cap;
   p.status = status;
-  if (T <= kRankThreads && K <= 8)
-    hipLaunchKernelGGL(rank_layout_small_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
-  else
-    hipLaunchKernelGGL(rank_layout_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
+  hipLaunchKernelGGL(rank_layout_kernel, dim3((unsigned)R), dim3(kRankThreads), 0, s, p);
   return hipGetLastError();
 }
 
