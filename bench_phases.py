@@ -207,7 +207,7 @@ def main():
         print("# Per-phase timestamps, standard workload (128 x 7168 bf16, 256 experts top-8)\n")
         print("Instrumented copy of the kernels (bench_phases.py): each wave reads the GPU's "
               "100 MHz\nreal-time counter at the phase boundaries; 10 replays, the last step's "
-              "kernel of each.")
+              "kernel of each.\n\n    python3 bench_phases.py    (repository root, one MI355X)")
         sys.stdout.flush()
         r = subprocess.run([sys.executable, "-c", CHILD, tmp])
         sys.exit(r.returncode)
