@@ -67,13 +67,11 @@ FLOOR_NEW = """  u32x4 val = __builtin_nontemporal_load(x + (int64_t)t * nvec + 
   ts[6] = ts[7] = __builtin_amdgcn_s_memrealtime();
   if ((threadIdx.x & 63) == 0 && wid < 4096 * 16)
     for (int i = 0; i < 8; ++i) g_fstamps[wid][i] = ts[i];"""
-FLOOR_START_OLD = """                                                          int32_t nchunk) {
-  const int wid = __builtin_amdgcn_readfirstlane(
+FLOOR_START_OLD = """  const int wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
 """
-FLOOR_START_NEW = """                                                          int32_t nchunk) {
-  unsigned long long ts[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+FLOOR_START_NEW = """  unsigned long long ts[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   ts[0] = __builtin_amdgcn_s_memrealtime();
-  const int wid = __builtin_amdgcn_readfirstlane(
+  const int wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
 """
 FLOOR_TABLE = ("namespace {\n\ntypedef uint32_t u32x4",
                "__device__ unsigned long long g_fstamps[4096 * 16][8];\nnamespace {\n\n"

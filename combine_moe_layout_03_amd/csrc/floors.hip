@@ -17,7 +17,9 @@
 // Launch shapes follow the real kernels: one wave per (token, 1 KiB of the
 // row) in 256-thread workgroups for the broadcast (as the stand-alone
 // scatter), one wave per (token, 512 B) in one-wave workgroups for the gather
-// (as the combine); non-temporal loads and stores throughout.
+// (as the combine); non-temporal loads and stores throughout. A wave's token
+// comes from a host-computed reciprocal (an integer division per wave cost the
+// gather 0.2 us).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,12 +36,11 @@ __global__ void floor_empty_kernel() {}
 
 // One wave per (token, 64 vectors of 16 bytes); t is wave-uniform.
 __global__ __launch_bounds__(256) void floor_bcast_kernel(const u32x4 *__restrict__ x,
-                                                          u32x4 *__restrict__ out, int32_t T,
-                                                          int32_t K, int32_t nvec,
+                                                          u32x4 *__restrict__ out, uint64_t magic,
+                                                          int32_t T, int32_t K, int32_t nvec,
                                                           int32_t nchunk) {
-  const int wid = __builtin_amdgcn_readfirstlane(
-      (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
-  const int t = wid / nchunk;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int t = (int)(((uint64_t)(uint32_t)wid * magic) >> 32);
   if (t >= T) return;
   const int v = (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
   if (v >= nvec) return;
@@ -56,11 +57,11 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 
 // One wave per (token, 64 lanes of 8 bytes); rows t*K .. t*K + K-1.
 __global__ __launch_bounds__(64) void floor_gather_kernel(const u32x2 *__restrict__ y,
-                                                          u32x2 *__restrict__ out, int32_t T,
-                                                          int32_t K, int32_t nq,
+                                                          u32x2 *__restrict__ out, uint64_t magic,
+                                                          int32_t T, int32_t K, int32_t nq,
                                                           int32_t nchunk) {
   const int wid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
-  const int t = wid / nchunk;
+  const int t = (int)(((uint64_t)(uint32_t)wid * magic) >> 32);
   if (t >= T) return;
   const int v = (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
   if (v >= nq) return;
@@ -99,6 +100,10 @@ __global__ __launch_bounds__(256) void floor_copy_kernel(const u32x4 *__restrict
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ceil(2^32 / d): (w * m) >> 32 == w / d for every w < waves while waves * d
+// < 2^32 (the callers check it)
+uint64_t recip(int32_t d) { return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d; }
+
 int ok(hipError_t e) { return e == hipSuccess ? 0 : -7; }
 
 }  // namespace
@@ -120,9 +125,10 @@ FLOOR_API int moe_floor_bcast(const uint16_t *x, uint16_t *out, int32_t T, int32
   if (!aligned16(x) || !aligned16(out)) return -5;
   const int32_t nvec = H / 8, nchunk = (nvec + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
+  if ((waves + 3) / 4 * 4 * (int64_t)nchunk >= ((int64_t)1 << 32)) return -2;
   hipLaunchKernelGGL(floor_bcast_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x4 *>(out), T, K,
-                     nvec, nchunk);
+                     reinterpret_cast<const u32x4 *>(x), reinterpret_cast<u32x4 *>(out),
+                     recip(nchunk), T, K, nvec, nchunk);
   return ok(hipGetLastError());
 }
 
@@ -135,9 +141,10 @@ FLOOR_API int moe_floor_gather(const uint16_t *y, uint16_t *out, int32_t T, int3
   if (!aligned16(y) || !aligned16(out)) return -5;
   const int32_t nq = H / 4, nchunk = (nq + 63) / 64;
   const int64_t waves = (int64_t)T * nchunk;
+  if (waves * (int64_t)nchunk >= ((int64_t)1 << 32)) return -2;
   hipLaunchKernelGGL(floor_gather_kernel, dim3((unsigned)waves), dim3(64), 0, s,
-                     reinterpret_cast<const u32x2 *>(y), reinterpret_cast<u32x2 *>(out), T, K,
-                     nq, nchunk);
+                     reinterpret_cast<const u32x2 *>(y), reinterpret_cast<u32x2 *>(out),
+                     recip(nchunk), T, K, nq, nchunk);
   return ok(hipGetLastError());
 }
 
