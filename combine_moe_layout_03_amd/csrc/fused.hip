@@ -19,8 +19,8 @@
 // popcount, accumulated in scalar registers; the waves' partial counts meet
 // in LDS once. The totals the handle also needs (count and offset per expert,
 // tokens per rank, empty low-latency stripe rows) are computed the same way by
-// a few extra "duty" workgroups that copy nothing, so the copying workgroups
-// only derive their own K slots. The id loads are unrolled over a compile-time
+// extra "duty" workgroups that copy nothing (one per expert for batches of up
+// to 2048 pairs), so the copying workgroups only derive their own K slots. The id loads are unrolled over a compile-time
 // number of rounds (up to 8: 4096 pairs over 512 lanes) and every count is a
 // compare or two + ballot + popcount: at this size the counting is bound by
 // each wave's serial instruction latency, not by memory.
@@ -55,9 +55,11 @@ constexpr int kCountMaxRounds = 8;  // ids per lane; the batch needs P <= 8 * 51
 // Experts (and ranks) whose totals one duty workgroup writes: one each for
 // batches of at most kManyPairs pairs -- the duty workgroups' last stores
 // tend to end the kernel (they queue behind the row stores of the copying
-// workgroup sharing the CU), and a shorter duty ends sooner (4 -> 1: low
-// latency 5.12 -> 4.89 us at 128 tokens); kMaxDuties each above, where every
-// duty workgroup reading the whole routing from L2 is what costs.
+// workgroup sharing the CU), and a shorter duty ends sooner (128 x 7168 with
+// 1, 4, 8 experts each: 4.35, 4.65, 4.95 us); kMaxDuties each above, where
+// every duty workgroup reading the whole routing from L2 is what costs. (The
+// totals done by the token workgroups after their stores instead cost 1.3 us:
+// that code then runs late, from cold instruction caches.)
 constexpr int kMaxDuties = 4;
 constexpr int kManyPairs = 2048;
 constexpr int kNoId = -2;           // sentinel: matches no expert
