@@ -54,18 +54,22 @@ template <> struct Lane<2> { typedef u32x2 T; };
 template <> struct Lane<4> { typedef u32x4 T; };
 
 // nvec counts lanes (kDw dwords each) per row.
+// Four waves per workgroup; the wave's token by the host reciprocal tmagic
+// where exact (0: a division). The arguments needed before the first loads
+// lead, so the launch preloads them (as in the combine).
 template <int KT, int kDw>
-__global__ __launch_bounds__(256) void dispatch_kernel(const typename Lane<kDw>::T *__restrict__ x,
-                                                       const int32_t *__restrict__ slot,
+__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t *__restrict__ slot,
+                                                       const typename Lane<kDw>::T *__restrict__ x,
+                                                       uint64_t tmagic, int64_t rows, int32_t T,
+                                                       int32_t nvec, int32_t nchunk, int32_t Kr,
                                                        typename Lane<kDw>::T *__restrict__ recv,
-                                                       int32_t T, int32_t Kr, int32_t nvec,
-                                                       int32_t nchunk, int64_t rows,
                                                        int32_t *status) {
   typedef typename Lane<kDw>::T VT;
   const int K = KT ? KT : Kr;
-  int t;
-  const int v = wave_token_chunk(nchunk, t);
+  const int wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int t = tmagic ? (int)(((uint64_t)(uint32_t)wid * tmagic) >> 32) : wid / nchunk;
   if (t >= T) return;
+  const int v = (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
   const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
   constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
@@ -230,14 +234,14 @@ hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, in
     const int32_t nq = nvec * 2, nchunk2 = (nq + 63) / 64;
     const int64_t waves = (int64_t)T * nchunk2;
     hipLaunchKernelGGL((dispatch_kernel<KT, 2>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                       reinterpret_cast<const u32x2 *>(x), slot, reinterpret_cast<u32x2 *>(recv),
-                       T, K, nq, nchunk2, rows, status);
+                       slot, reinterpret_cast<const u32x2 *>(x), token_magic(waves + 3, nchunk2),
+                       rows, T, nq, nchunk2, K, reinterpret_cast<u32x2 *>(recv), status);
     return hipGetLastError();
   }
   const int64_t waves = (int64_t)T * nchunk;
   hipLaunchKernelGGL((dispatch_kernel<KT, 4>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                     reinterpret_cast<const u32x4 *>(x), slot, reinterpret_cast<u32x4 *>(recv),
-                     T, K, nvec, nchunk, rows, status);
+                     slot, reinterpret_cast<const u32x4 *>(x), token_magic(waves + 3, nchunk), rows,
+                     T, nvec, nchunk, K, reinterpret_cast<u32x4 *>(recv), status);
   return hipGetLastError();
 }
 
