@@ -117,6 +117,26 @@ def test_path_parity(capi, orc, name, A):
     full_case(capi, orc, w, A=A)
 
 
+def test_max_row_width(capi, orc):
+    """H = 2^20, the widest row the library takes, with 256 tokens: the
+    scatter's and the combine's grids reach b * d = 2^32 (b: wave, d: waves
+    per row), so a wave's token comes from a division there instead of the
+    host reciprocal (exact only below that bound). Rows bit-exact, combine
+    against the oracle on every token."""
+    w = mi.random_case(28, 256, 1 << 20, 8, 2, 1, 1)
+    _announce("max row width: T=256 H=2^20 E=8 R=2 K=1")
+    got, lay, shape = run_layout(capi, w)
+    ref = orc.layout(w.topk_idx, w.E, w.R, 1)
+    check_layout(got, ref, w)
+    rows = ref["rows"]
+    recv, o16, _, st = run_dispatch_combine(capi, w, shape, lay, rows, f32=False)
+    rref, _ = orc.dispatch(w.x, ref["slot"], rows, fill=SENTINEL)
+    assert np.array_equal(recv[:rows], rref), "dispatched rows"
+    del recv
+    check_combine(orc, o16, None, rref, ref["slot"], w.topk_weights)
+    assert st == ref["status"]
+
+
 def test_unweighted_combine(capi, orc):
     w = mi.config_c2()
     _announce("c2 unweighted")

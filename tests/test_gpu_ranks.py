@@ -118,6 +118,9 @@ CASES = [
     (10, 700, 1032, 128, 64, 5, 0.2, 0.2, 0.0),
     (11, 300, 64, 8, 1, 4, 0.1, 0.1, 0.0),  # one rank
     (12, 1024, 136, 1024, 64, 8, 0.02, 0.05, 0.01),  # the one-launch limits: T, E, R, K
+    # two tokens per lane with few pairs: 2 and 4 pair rounds
+    (13, 600, 64, 16, 4, 1, 0.1, 0.0, 0.0),
+    (14, 600, 136, 32, 8, 3, 0.05, 0.1, 0.0),
 ]
 
 
