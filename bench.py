@@ -455,6 +455,12 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
     cd = [torch.empty(ncopy, dtype=torch.uint8, device=dev) for _ in range(S)]
     big_s = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
     big_d = torch.empty_like(big_s)
+    # the same two floors at 512 tokens (the low-latency sweep's largest batch)
+    T5 = 512
+    S5 = n_sets(T5 * row * (K + 1) * 2)
+    xs5 = [torch.randn(T5, H, device=dev).to(torch.bfloat16).view(torch.int16) for _ in range(S5)]
+    bc5 = [torch.empty(T5 * K, H, dtype=torch.int16, device=dev) for _ in range(S5)]
+    go5 = [torch.empty(T5, H, dtype=torch.int16, device=dev) for _ in range(S5)]
     s = stream
     calls = {
         "empty_1x64": [lambda: floors.empty(1, 64, s)] * S,
@@ -466,6 +472,10 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
                               for i in range(S)],
         "copy_8.26MB": [(lambda i=i: floors.copy(cs[i], cd[i], ncopy, s)) for i in range(S)],
         "copy_256MiB": [lambda: floors.copy(big_s, big_d, big_s.numel(), s)] * 2,
+        "bcast_512x7168x8": [(lambda i=i: floors.bcast(xs5[i], bc5[i], T5, H, K, s))
+                             for i in range(S5)],
+        "gather_512x7168x8": [(lambda i=i: floors.gather(bc5[i], go5[i], T5, H, K, s))
+                              for i in range(S5)],
     }
     with torch.cuda.stream(stream):
         for fns in calls.values():
@@ -474,11 +484,15 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
     torch.cuda.synchronize()
     nb = {"empty_1x64": 0, "empty_512x512": 0, "empty_3584x64": 0,
           "bcast_128x7168x8": T * row * (K + 1), "gather_128x7168x8": T * row * (K + 1),
-          "copy_8.26MB": 2 * ncopy, "copy_256MiB": 2 * big_s.numel(), "step": 0}
+          "copy_8.26MB": 2 * ncopy, "copy_256MiB": 2 * big_s.numel(),
+          "bcast_512x7168x8": T5 * row * (K + 1), "gather_512x7168x8": T5 * row * (K + 1),
+          "step": 0}
     return Row("floors", "floors at 128 tokens x 7168, top-8: empty launches, a broadcast copy "
                "(one row read, 8 sequential row writes per token), a gather + sum (8 row reads "
-               "at computed addresses, one row write), plain copies", None, calls, nb, (),
-               extra={"buffer_sets": S}, holder=(xs, bc, go, cs, cd, big_s, big_d))
+               "at computed addresses, one row write), plain copies; the broadcast and the "
+               "gather also at 512 tokens", None, calls, nb, (),
+               extra={"buffer_sets": S, "buffer_sets_512": S5},
+               holder=(xs, bc, go, cs, cd, big_s, big_d, xs5, bc5, go5))
 
 
 def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128, masked=False):
