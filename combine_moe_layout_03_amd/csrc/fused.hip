@@ -173,7 +173,7 @@ __device__ void duty_workgroup(const LayoutParams &p, int d, int D, int &st) {
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int nthreads = kCountThreads, nwaves = kCountWaves;
-  const int E = p.E, R = p.R, K = p.K, T = p.T, L = p.L, P = T * K;
+  const int E = p.E, R = p.R, K = p.K, T = p.T, P = T * K;
   const bool ll = p.mode == kModeLowLatency;
   LaneIds<kRounds> ids;
   if (P > 0) {

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_block_kernel(LayoutPara
 
   // Which ranks each token reaches, and distinct tokens per rank.
   if (p.in_rank || p.rank_token_count) {
-    const int L = p.L, n = nt * R;
+    const int n = nt * R;
     for (int b = 0; b < n; b += kLayoutThreads) {
       const int i = b + tid;
       bool hit = false;
