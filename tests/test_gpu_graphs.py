@@ -154,3 +154,32 @@ def test_graph_replica_route(capi, orc):
                  [load, rc, phys, lay.slot, out])
     ref_load, _ = orc.expert_load(w.topk_idx, E)
     assert np.array_equal(load.cpu().numpy(), ref_load)
+
+
+def test_graph_layout_dispatch_static(capi, orc):
+    """moe_layout_dispatch_static, the entry point for callers that cannot
+    allocate, captured in a graph at a size whose layout runs in three
+    launches over the library's static per-GPU scratch: every replay equals
+    the eager call, and that call equals the oracle."""
+    w = mi.random_case(31, 1100, 256, 64, 8, 8, 1, neg_frac=0.02)  # 8800 pairs
+    shape = capi.make_shape(w.T, w.H, w.E, w.R, w.K, 1)
+    assert capi.moe_layout_workspace_bytes(shape) > 0
+    _announce(f"graph: static-scratch layout + dispatch, T={w.T} K={w.K}")
+    idx, x = to_dev(w.topk_idx), to_dev(w.x)
+    lay = capi.LayoutBuffers.empty(shape, dev())
+    rows = capi.moe_recv_rows_worst(shape)
+    recv = torch.full((rows, w.H), -7, dtype=torch.int16, device=dev())
+
+    def step(s):
+        capi.moe_layout_dispatch_static(shape, idx, lay, x, recv, rows, stream=s)
+
+    # (row_src past the rows in use is never written, so it is compared but not poisoned)
+    ref = replay_check(step, [lay.slot, lay.count, lay.offset, lay.row_src, recv],
+                       [lay.slot, lay.count, lay.offset])
+    o = orc.layout(w.topk_idx, w.E, w.R, 1)
+    assert np.array_equal(ref[0].cpu().numpy().reshape(w.T, w.K), o["slot"])
+    assert np.array_equal(ref[1].cpu().numpy(), o["count"])
+    assert np.array_equal(ref[2].cpu().numpy(), o["offset"])
+    r = o["rows"]
+    rref, _ = orc.dispatch(w.x, o["slot"], r, fill=-7 & 0xFFFF)
+    assert np.array_equal(ref[4].cpu().numpy()[:r].view(np.uint16), rref.view(np.uint16))
