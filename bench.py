@@ -36,6 +36,7 @@ import os
 import re
 import statistics
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -1140,7 +1141,8 @@ def main():
                     help="only the standard step (no floors, other rows)")
     ap.add_argument("--profile-pass", choices=("standard", "all"), default=None,
                     help="graph replays only, for rocprofv3")
-    ap.add_argument("--segments-out", default=os.path.join(ROOT, "gpurun_out", "segments.json"))
+    ap.add_argument("--segments-out", default=os.path.join(tempfile.gettempdir(), "moe_segments.json"),
+                    help="where --profile-pass writes its segment list (markers between them)")
     ap.add_argument("--summarize", nargs="+", metavar="DIR", default=None,
                     help="rocprofv3 CSV output dirs to summarise (with --segments)")
     ap.add_argument("--segments", default=None)
