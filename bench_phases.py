@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Per-phase timestamps of the fused layout + dispatch kernel and of the
 broadcast floor kernel, on the standard workload (128 tokens x 7168 bf16,
-256 experts top-8) replayed from a HIP graph over rotating buffer sets.
+256 experts top-8) replayed from a HIP graph over rotating buffer sets; and
+of the same kernel in the low-latency layout at 128 tokens per rank, bf16 and
+FP8 (row-major and column-major scales).
 
 An instrumented copy of the two kernel sources is built into a temporary
 directory (the library's own sources and build are left alone): each wave
@@ -11,7 +13,8 @@ replay. The copy differs from the library only by those reads and stores.
 
 Phases (each wave, from its own first instruction): the id loads issued, the
 row-chunk load issued, the ids arrived (first barrier), the counting done
-(second barrier), the row arrived, the row stores issued, the wave's end.
+(second barrier), the row arrived, (FP8) the cast done, the row stores issued,
+the wave's end.
 
     python3 bench_phases.py            (needs an MI355X; prints a markdown table)
 """
@@ -29,7 +32,7 @@ PKG = "combine_moe_layout_03_amd"
 # (anchor in fused.hip, text inserted after it)
 FUSED_STAMPS = [
     ("  const int b = blockIdx.x;\n  int st = 0;\n",
-     "  unsigned long long ts[8] = {0, 0, 0, 0, 0, 0, 0, 0};\n  STAMP(0);\n"),
+     "  unsigned long long ts[10] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0};\n  STAMP(0);\n"),
     ("    if (counting) ids.issue(hidx, P, nthreads, nr);\n", "    STAMP(1);\n"),
     ("      val = __builtin_nontemporal_load(hx + (int64_t)t * hnvec + min(v, hnvec - 1));\n",
      "      STAMP(2);\n"),
@@ -39,14 +42,19 @@ FUSED_STAMPS = [
      "    STAMP(4);\n"),
     ("      asm volatile(\"\" : \"+v\"(val));\n      if (kCpw == 2) asm volatile(\"\" : \"+v\"(val2));\n",
      "      STAMP(5);\n"),
+    # the FP8 branch: the row arrived, the cast done
+    ("    if (kCopy && kFp8 >= 0) {\n      asm volatile(\"\" : \"+v\"(val));\n", "      STAMP(5);\n"),
+    ("      const u32x2 codes = {q.lo, q.hi};\n",
+     "      asm volatile(\"\" :: \"v\"(codes.x), \"v\"(codes.y), \"v\"(q.scale));\n"
+     "      STAMP(8);\n"),
 ]
 FUSED_BEFORE = [("    // 6. this token's handle entries", "    STAMP(6);\n")]
 FUSED_END = ("  if (st && p.status) atomicOr(p.status, st);\n}",
              "  if (st && p.status) atomicOr(p.status, st);\n  STAMP(7);\n"
              "  if (lane_id() == 0 && b < 4096)\n"
-             "    for (int i = 0; i < 8; ++i) g_stamps[b * 16 + (tid >> 6)][i] = ts[i];\n}")
+             "    for (int i = 0; i < 10; ++i) g_stamps[b * 16 + (tid >> 6)][i] = ts[i];\n}")
 TABLE = ("namespace moe {\nnamespace {\n",
-         "namespace moe {\n__device__ unsigned long long g_stamps[4096 * 16][8];\nnamespace {\n"
+         "namespace moe {\n__device__ unsigned long long g_stamps[4096 * 16][10];\nnamespace {\n"
          "#define STAMP(i) ts[i] = __builtin_amdgcn_s_memrealtime()\n")
 FUSED_EXPORT = """
 extern "C" __attribute__((visibility("default"))) int moe_debug_stamps(void *dst, size_t bytes) {
@@ -162,7 +170,8 @@ g = bench.capture(torch, stream, std.step)
 for _ in range(20):
     g.replay()
 torch.cuda.synchronize()
-buf = np.zeros((4096 * 16, 8), np.uint64)
+buf = np.zeros((4096 * 16, 10), np.uint64)
+fbuf = np.zeros((4096 * 16, 8), np.uint64)
 reps = []
 for _ in range(REPS):
     g.replay(); torch.cuda.synchronize()
@@ -186,10 +195,39 @@ torch.cuda.synchronize()
 reps = []
 for _ in range(REPS):
     g2.replay(); torch.cuda.synchronize()
-    assert flib.moe_debug_fstamps(buf.ctypes.data, buf.nbytes) == 0
-    reps.append(buf[:1792].copy())
+    assert flib.moe_debug_fstamps(fbuf.ctypes.data, fbuf.nbytes) == 0
+    reps.append(fbuf[:1792].copy())
 table("broadcast floor (same bytes, computed destinations): 1792 waves", reps, 1, 1792,
       [(2, "row load issued"), (5, "row in"), (6, "row stores issued"), (7, "end")])
+del g2, xs, bc
+torch.cuda.empty_cache()
+
+# the low-latency layout at 128 tokens per rank: bf16, FP8 with row-major and
+# with column-major (the page's format) scales
+common = [(1, "id loads issued"), (2, "row load issued"), (3, "ids in (first barrier)"),
+          (4, "counted (second barrier)"), (5, "row in")]
+for flags, name, call in ((None, "bf16", "ll_layout_dispatch"),
+                          (4, "FP8, row-major scales", "ll_layout_dispatch_fp8"),
+                          (0, "FP8, column-major scales", "ll_layout_dispatch_fp8")):
+    row = bench.row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=flags, M=128)
+    g3 = bench.capture(torch, stream, row.calls[call])
+    for _ in range(20):
+        g3.replay()
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(REPS):
+        g3.replay(); torch.cuda.synchronize()
+        assert lib.moe_debug_stamps(buf.ctypes.data, buf.nbytes) == 0
+        reps.append(buf[:256 * 16].copy())
+    extra = [] if flags is None else [(8, "cast done")]
+    table(f"low-latency layout + dispatch, 128 tokens per rank, {name} (graph of "
+          f"{len(row.calls[call])} calls over rotating receive unions; the last call's kernel of "
+          f"{REPS} replays): 256 token workgroups x 8 waves", reps, 8, 256,
+          common + extra + [(6, "row stores issued"), (7, "end")])
+    del g3
+    row.release(torch)
+    del row
+    torch.cuda.empty_cache()
 '''
 
 
@@ -202,7 +240,8 @@ def main():
         if not b.PKG.startswith(tmp):
             raise SystemExit("instrumented build would overwrite the library")
         b.build()
-        print("# Per-phase timestamps, standard workload (128 x 7168 bf16, 256 experts top-8)\n")
+        print("# Per-phase timestamps, standard and low-latency workloads (128 tokens x 7168, "
+              "256 experts top-8)\n")
         print("Instrumented copy of the kernels (bench_phases.py): each wave reads the GPU's "
               "100 MHz\nreal-time counter at the phase boundaries; 10 replays, the last step's "
               "kernel of each.\n\n    python3 bench_phases.py    (repository root, one MI355X)")

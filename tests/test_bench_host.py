@@ -171,7 +171,7 @@ def test_phase_instrumentation_applies(tmp_path):
     before = open(os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip")).read()
     bench_phases.instrument(str(tmp_path))
     got = open(tmp_path / "combine_moe_layout_03_amd" / "csrc" / "fused.hip").read()
-    assert got.count("STAMP(") == 9 and "moe_debug_stamps" in got
+    assert got.count("STAMP(") == 11 and "moe_debug_stamps" in got and "STAMP(8)" in got
     assert "moe_debug_fstamps" in open(tmp_path / "combine_moe_layout_03_amd" / "csrc" /
                                        "floors.hip").read()
     assert open(os.path.join(ROOT, "combine_moe_layout_03_amd", "csrc", "fused.hip")).read() == before
