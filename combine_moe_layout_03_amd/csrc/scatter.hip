@@ -17,10 +17,10 @@
 //
 // Both are HBM-bound streams with no data reuse, so the design is about
 // bytes in flight. Dispatch: a thread owns one 16-byte vector (8 bf16) of one
-// token row, a wave covers 1 KiB of a row, and the grid covers T * H/8 vectors
-// -- 1792 waves at 128 x 7168, seven per CU, in 4-wave workgroups (large
-// batches: 8-byte lanes, see dispatch_k); it reads its vector once and issues
-// K stores (non-temporal: the receive rows are not re-read by this kernel).
+// token row, a workgroup one 1 KiB chunk of a row, and its two (or four)
+// waves each read the chunk and store it to half (a quarter) of the token's K
+// slots -- 896 workgroups of two waves at 128 x 7168 -- with non-temporal
+// stores (the receive rows are not re-read by this kernel).
 // Combine: a thread owns 8 bytes (4 bf16), a wave covers 512 bytes of a row,
 // one wave per workgroup -- 3584 waves at 128 x 7168. (Measured per step at 128 x 7168 / at 8192 x 7168: 16-byte lanes
 // 9.50 / 178 us, 8-byte lanes 9.31 / 171 us, 4-byte lanes 9.30 / 183 us; two
@@ -53,41 +53,42 @@ template <int kDw> struct Lane;
 template <> struct Lane<2> { typedef u32x2 T; };
 template <> struct Lane<4> { typedef u32x4 T; };
 
-// nvec counts lanes (kDw dwords each) per row.
-// Four waves per workgroup; the wave's token by the host reciprocal tmagic
-// where exact (0: a division). The arguments needed before the first loads
-// lead, so the launch preloads them (as in the combine).
-template <int KT, int kDw>
-__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t *__restrict__ slot,
-                                                       const typename Lane<kDw>::T *__restrict__ x,
-                                                       uint64_t tmagic, int64_t rows, int32_t T,
-                                                       int32_t nvec, int32_t nchunk, int32_t Kr,
-                                                       typename Lane<kDw>::T *__restrict__ recv,
-                                                       int32_t *status) {
-  typedef typename Lane<kDw>::T VT;
+// One workgroup per (token, 1 KiB chunk of its row) of kS waves; wave j stores
+// the chunk to the token's slots j, j + kS, ... Every wave reads the chunk
+// (a plain load: after the first wave's, from L2) and has K / kS stores per
+// lane in flight instead of K. Against one wave per chunk storing all K (four
+// chunks per workgroup): 8192 x 7168 rows to random slots 219 -> 181 us (two
+// waves) / 179 us (four); the skewed 4096 x 4096 batch (K = 6) 45.5 -> 38.5 /
+// 37.3 us; 128 x 7168 3.82 -> 3.71 / 3.97 us. The token of workgroup b is
+// b / nchunk, by the host reciprocal tmagic where exact (0: a division).
+template <int KT, int kS>
+__global__ __launch_bounds__(64 * kS) void dispatch_kernel(
+    const int32_t *__restrict__ slot, const u32x4 *__restrict__ x, uint64_t tmagic, int64_t rows,
+    int32_t T, int32_t nvec, int32_t nchunk, int32_t Kr, u32x4 *__restrict__ recv,
+    int32_t *status) {
   const int K = KT ? KT : Kr;
-  const int wid = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  const int t = tmagic ? (int)(((uint64_t)(uint32_t)wid * tmagic) >> 32) : wid / nchunk;
+  const int b = blockIdx.x;
+  const int t = tmagic ? (int)(((uint64_t)(uint32_t)b * tmagic) >> 32) : b / nchunk;
   if (t >= T) return;
-  const int v = (wid - t * nchunk) * 64 + (int)(threadIdx.x & 63);
+  const int j = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int v = (b - t * nchunk) * 64 + (int)(threadIdx.x & 63);
   const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
-  constexpr int G = (KT > 0 && KT < 8) ? KT : 8;
-  VT val = VT(0u);
-  if (lane_ok) val = __builtin_nontemporal_load(x + (int64_t)t * nvec + v);
-  // the first group of slots is requested while the row load is in flight
+  // slots per wave and group: all of them for a compile-time K
+  constexpr int G = KT > 0 ? (KT + kS - 1) / kS : 4;
+  u32x4 val = x[(int64_t)t * nvec + min(v, nvec - 1)];
   int32_t s[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) s[g] = (g < K) ? srow[g] : -1;
+  for (int g = 0; g < G; ++g) s[g] = (j + g * kS < K) ? srow[j + g * kS] : -1;
   // Settle the row load once here: without this the compiler re-waits on it
   // before every (conditional) store, and on gfx950 such a wait also drains
-  // the stores already issued, serialising the K copies.
+  // the stores already issued, serialising the copies.
   asm volatile("" : "+v"(val));
   int st = 0;
-  for (int k0 = 0; k0 < K; k0 += G) {
-    if (k0 > 0) {
+  for (int k0 = j; k0 < K; k0 += G * kS) {
+    if (k0 > j) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = (k0 + g < K) ? srow[k0 + g] : -1;
+      for (int g = 0; g < G; ++g) s[g] = (k0 + g * kS < K) ? srow[k0 + g * kS] : -1;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -221,28 +222,29 @@ uint64_t token_magic(int64_t waves, int32_t d) {
   return ((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d;
 }
 
-// Large batches copy in 8-byte lanes (twice the waves, more stores in flight:
-// 8192 x 7168 216 -> 202 us, the skewed 4096 x 4096 batch 56.3 -> 54.6 us);
-// small ones in 16-byte lanes (128 x 7168: 3.96 vs 4.06 us).
-constexpr int64_t kWideCopyWaves = 8192;  // 16-byte-lane waves from which 8-byte lanes pay
+// Four waves per chunk for K >= 4 from kWideChunks (token, chunk) pairs on,
+// else two (one for K = 1).
+constexpr int64_t kWideChunks = 8192;
+
+template <int KT, int kS>
+hipError_t dispatch_ks(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
+                       int32_t K, int32_t nvec, int32_t nchunk, int64_t rows, int32_t *status,
+                       hipStream_t s) {
+  const int64_t wgs = (int64_t)T * nchunk;
+  hipLaunchKernelGGL((dispatch_kernel<KT, kS>), dim3((unsigned)wgs), dim3(64 * kS), 0, s, slot,
+                     reinterpret_cast<const u32x4 *>(x), token_magic(wgs, nchunk), rows, T, nvec,
+                     nchunk, K, reinterpret_cast<u32x4 *>(recv), status);
+  return hipGetLastError();
+}
 
 template <int KT>
 hipError_t dispatch_k(const uint16_t *x, const int32_t *slot, uint16_t *recv, int32_t T,
                       int32_t K, int32_t nvec, int64_t rows, int32_t *status, hipStream_t s) {
   const int32_t nchunk = (nvec + 63) / 64;
-  if ((int64_t)T * nchunk >= kWideCopyWaves) {
-    const int32_t nq = nvec * 2, nchunk2 = (nq + 63) / 64;
-    const int64_t waves = (int64_t)T * nchunk2;
-    hipLaunchKernelGGL((dispatch_kernel<KT, 2>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                       slot, reinterpret_cast<const u32x2 *>(x), token_magic(waves + 3, nchunk2),
-                       rows, T, nq, nchunk2, K, reinterpret_cast<u32x2 *>(recv), status);
-    return hipGetLastError();
-  }
-  const int64_t waves = (int64_t)T * nchunk;
-  hipLaunchKernelGGL((dispatch_kernel<KT, 4>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s,
-                     slot, reinterpret_cast<const u32x4 *>(x), token_magic(waves + 3, nchunk), rows,
-                     T, nvec, nchunk, K, reinterpret_cast<u32x4 *>(recv), status);
-  return hipGetLastError();
+  if (K >= 4 && (int64_t)T * nchunk >= kWideChunks)
+    return dispatch_ks<KT, 4>(x, slot, recv, T, K, nvec, nchunk, rows, status, s);
+  if (K >= 2) return dispatch_ks<KT, 2>(x, slot, recv, T, K, nvec, nchunk, rows, status, s);
+  return dispatch_ks<KT, 1>(x, slot, recv, T, K, nvec, nchunk, rows, status, s);
 }
 
 template <int KT, bool kW, bool kF, bool kM>
