@@ -456,6 +456,9 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
     cd = [torch.empty(ncopy, dtype=torch.uint8, device=dev) for _ in range(S)]
     big_s = torch.empty(256 * 2**20, dtype=torch.uint8, device=dev)
     big_d = torch.empty_like(big_s)
+    # a copy four times the 256 MB Infinity Cache each way: the streaming rate
+    huge_s = torch.empty(2**30, dtype=torch.uint8, device=dev)
+    huge_d = torch.empty_like(huge_s)
     # the same two floors at 512 tokens (the low-latency sweep's largest batch)
     T5 = 512
     S5 = n_sets(T5 * row * (K + 1) * 2)
@@ -471,11 +474,16 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
                              for i in range(S)],
         "gather_128x7168x8": [(lambda i=i: floors.gather(bc[i], go[i], T, H, K, s))
                               for i in range(S)],
+        "bcast2_128x7168x8": [(lambda i=i: floors.bcast_split(xs[i], bc[i], T, H, K, 2, s))
+                              for i in range(S)],
         "copy_8.26MB": [(lambda i=i: floors.copy(cs[i], cd[i], ncopy, s)) for i in range(S)],
         "copy_256MiB": [lambda: floors.copy(big_s, big_d, big_s.numel(), s)] * 2,
+        "copy_1GiB": [lambda: floors.copy(huge_s, huge_d, huge_s.numel(), s)] * 2,
         "bcast_512x7168x8": [(lambda i=i: floors.bcast(xs5[i], bc5[i], T5, H, K, s))
                              for i in range(S5)],
         "gather_512x7168x8": [(lambda i=i: floors.gather(bc5[i], go5[i], T5, H, K, s))
+                              for i in range(S5)],
+        "bcast2_512x7168x8": [(lambda i=i: floors.bcast_split(xs5[i], bc5[i], T5, H, K, 2, s))
                               for i in range(S5)],
     }
     with torch.cuda.stream(stream):
@@ -485,15 +493,19 @@ def row_floors(capi, floors, mi, torch, np, dev, stream):
     torch.cuda.synchronize()
     nb = {"empty_1x64": 0, "empty_512x512": 0, "empty_3584x64": 0,
           "bcast_128x7168x8": T * row * (K + 1), "gather_128x7168x8": T * row * (K + 1),
+          "bcast2_128x7168x8": T * row * (K + 1),
           "copy_8.26MB": 2 * ncopy, "copy_256MiB": 2 * big_s.numel(),
+          "copy_1GiB": 2 * huge_s.numel(),
           "bcast_512x7168x8": T5 * row * (K + 1), "gather_512x7168x8": T5 * row * (K + 1),
+          "bcast2_512x7168x8": T5 * row * (K + 1),
           "step": 0}
     return Row("floors", "floors at 128 tokens x 7168, top-8: empty launches, a broadcast copy "
-               "(one row read, 8 sequential row writes per token), a gather + sum (8 row reads "
-               "at computed addresses, one row write), plain copies; the broadcast and the "
-               "gather also at 512 tokens", None, calls, nb, (),
+               "(one row read, 8 sequential row writes per token; also with 2 waves per 1 KiB "
+               "chunk, each storing half the rows), a gather + sum (8 row "
+               "reads at computed addresses, one row write), plain copies; the broadcast and "
+               "the gather also at 512 tokens", None, calls, nb, (),
                extra={"buffer_sets": S, "buffer_sets_512": S5},
-               holder=(xs, bc, go, cs, cd, big_s, big_d, xs5, bc5, go5))
+               holder=(xs, bc, go, cs, cd, big_s, big_d, huge_s, huge_d, xs5, bc5, go5))
 
 
 def row_low_latency(capi, mi, torch, np, dev, stream, fp8_flags=None, M=128, masked=False):
@@ -904,6 +916,7 @@ class Floors:
         P, I32, I64 = C.c_void_p, C.c_int32, C.c_int64
         lib.moe_floor_empty.argtypes = [I32, I32, P]
         lib.moe_floor_bcast.argtypes = [P, P, I32, I32, I32, P]
+        lib.moe_floor_bcast_split.argtypes = [P, P, I32, I32, I32, I32, P]
         lib.moe_floor_gather.argtypes = [P, P, I32, I32, I32, P]
         lib.moe_floor_copy.argtypes = [P, P, I64, P]
         self.lib = lib
@@ -923,6 +936,10 @@ class Floors:
     def bcast(self, x, out, T, H, K, stream):
         self._ok(self.lib.moe_floor_bcast(x.data_ptr(), out.data_ptr(), T, H, K,
                                           self._s(stream)), "moe_floor_bcast")
+
+    def bcast_split(self, x, out, T, H, K, S, stream):
+        self._ok(self.lib.moe_floor_bcast_split(x.data_ptr(), out.data_ptr(), T, H, K, S,
+                                                self._s(stream)), "moe_floor_bcast_split")
 
     def gather(self, y, out, T, H, K, stream):
         self._ok(self.lib.moe_floor_gather(y.data_ptr(), out.data_ptr(), T, H, K,

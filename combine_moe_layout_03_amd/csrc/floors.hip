@@ -12,14 +12,21 @@
 //   moe_floor_gather  out[t] = bf16(sum over k of y[t*K + k]): the combine's
 //                     bytes (K row reads, one row write per token) with
 //                     computed row addresses -- no slot or weight read.
+//   moe_floor_bcast_split  the same broadcast by S waves per 1 KiB chunk, wave
+//                     j storing rows j, j + S, ... (the stand-alone scatter's
+//                     shape).
 //   moe_floor_copy    a contiguous copy: the plain streaming rate.
 //
-// Launch shapes follow the real kernels: one wave per (token, 1 KiB of the
-// row) in 256-thread workgroups for the broadcast (as the stand-alone
-// scatter), one wave per (token, 512 B) in one-wave workgroups for the gather
-// (as the combine); non-temporal loads and stores throughout. A wave's token
-// comes from a host-computed reciprocal (an integer division per wave cost the
-// gather 0.2 us).
+// Launch shapes: one wave per (token, 1 KiB of the row) in 256-thread
+// workgroups for the broadcast (the copying waves of the fused layout +
+// dispatch kernel store all K rows of a chunk so), one workgroup of S waves
+// per (token, 1 KiB) for the split broadcast, one wave per (token, 512 B) in
+// one-wave workgroups for the gather (as the combine; the gather split over
+// two or four waves per chunk, each loading a share of the K rows and wave 0
+// summing them through LDS, measured 4.76 / 4.81 against 4.59 us at 128 x 7168
+// x 8); non-temporal stores throughout. A wave's token comes from a
+// host-computed reciprocal (an integer division per wave cost the gather
+// 0.2 us).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,6 +54,24 @@ __global__ __launch_bounds__(256) void floor_bcast_kernel(const u32x4 *__restric
   const u32x4 val = __builtin_nontemporal_load(x + (int64_t)t * nvec + v);
   u32x4 *dst = out + (int64_t)t * K * nvec + v;
   for (int k = 0; k < K; ++k) __builtin_nontemporal_store(val, dst + (int64_t)k * nvec);
+}
+
+// One workgroup of kS waves per (token, 64 vectors of 16 bytes); wave j
+// stores rows j, j + kS, ... The chunk is read by every wave (plain loads:
+// after the first, from L2).
+template <int kS>
+__global__ __launch_bounds__(64 * kS) void floor_bcast_split_kernel(
+    const u32x4 *__restrict__ x, u32x4 *__restrict__ out, uint64_t magic, int32_t T, int32_t K,
+    int32_t nvec, int32_t nchunk) {
+  const int b = blockIdx.x;
+  const int t = (int)(((uint64_t)(uint32_t)b * magic) >> 32);
+  if (t >= T) return;
+  const int j = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int v = (b - t * nchunk) * 64 + (int)(threadIdx.x & 63);
+  if (v >= nvec) return;
+  const u32x4 val = x[(int64_t)t * nvec + v];
+  u32x4 *dst = out + (int64_t)t * K * nvec + v;
+  for (int k = j; k < K; k += kS) __builtin_nontemporal_store(val, dst + (int64_t)k * nvec);
 }
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -83,19 +108,15 @@ __global__ __launch_bounds__(64) void floor_gather_kernel(const u32x2 *__restric
   __builtin_nontemporal_store(o, out + (int64_t)t * nq + v);
 }
 
-// Grid-stride copy of n 16-byte vectors, four in flight per thread.
+// Copy of n 16-byte vectors, one per thread and grid stride, up to 65536
+// workgroups. (Four vectors in flight per thread over at most 8192 workgroups
+// streamed a 1 GiB copy at 5.0 TB/s; one per thread over 65536 workgroups at
+// 5.9 TB/s.)
 __global__ __launch_bounds__(256) void floor_copy_kernel(const u32x4 *__restrict__ src,
                                                          u32x4 *__restrict__ dst, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    u32x4 a[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = __builtin_nontemporal_load(src + i + j * stride);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(a[j], dst + i + j * stride);
-  }
-  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -132,6 +153,30 @@ FLOOR_API int moe_floor_bcast(const uint16_t *x, uint16_t *out, int32_t T, int32
   return ok(hipGetLastError());
 }
 
+// The broadcast by S waves per chunk; S in {1, 2, 4, 8}.
+FLOOR_API int moe_floor_bcast_split(const uint16_t *x, uint16_t *out, int32_t T, int32_t H,
+                                    int32_t K, int32_t S, hipStream_t s) {
+  if (T < 1 || H < 8 || H % 8 != 0 || K < 1 || K > kMaxK) return -2;
+  if (S != 1 && S != 2 && S != 4 && S != 8) return -2;
+  if ((int64_t)T * (H / 8) >= ((int64_t)1 << 31)) return -2;
+  if (!x || !out) return -1;
+  if (!aligned16(x) || !aligned16(out)) return -5;
+  const int32_t nvec = H / 8, nchunk = (nvec + 63) / 64;
+  const int64_t wgs = (int64_t)T * nchunk;
+  if (wgs * (int64_t)nchunk >= ((int64_t)1 << 32)) return -2;
+  const u32x4 *xv = reinterpret_cast<const u32x4 *>(x);
+  u32x4 *ov = reinterpret_cast<u32x4 *>(out);
+  const dim3 g((unsigned)wgs), w((unsigned)(64 * S));
+  const uint64_t m = recip(nchunk);
+  switch (S) {
+    case 1: hipLaunchKernelGGL(floor_bcast_split_kernel<1>, g, w, 0, s, xv, ov, m, T, K, nvec, nchunk); break;
+    case 2: hipLaunchKernelGGL(floor_bcast_split_kernel<2>, g, w, 0, s, xv, ov, m, T, K, nvec, nchunk); break;
+    case 4: hipLaunchKernelGGL(floor_bcast_split_kernel<4>, g, w, 0, s, xv, ov, m, T, K, nvec, nchunk); break;
+    default: hipLaunchKernelGGL(floor_bcast_split_kernel<8>, g, w, 0, s, xv, ov, m, T, K, nvec, nchunk);
+  }
+  return ok(hipGetLastError());
+}
+
 // y [T*K, H] bf16 -> out [T, H] bf16; H % 8 == 0, 1 <= K <= 8.
 FLOOR_API int moe_floor_gather(const uint16_t *y, uint16_t *out, int32_t T, int32_t H,
                                int32_t K, hipStream_t s) {
@@ -154,8 +199,8 @@ FLOOR_API int moe_floor_copy(const void *src, void *dst, int64_t bytes, hipStrea
   if (!src || !dst) return -1;
   if (!aligned16(src) || !aligned16(dst)) return -5;
   const int64_t n = bytes / 16;
-  int64_t wgs = (n + 1023) / 1024;  // four vectors per thread
-  if (wgs > 8192) wgs = 8192;
+  int64_t wgs = (n + 255) / 256;  // one vector per thread
+  if (wgs > 65536) wgs = 65536;
   hipLaunchKernelGGL(floor_copy_kernel, dim3((unsigned)wgs), dim3(256), 0, s,
                      static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst), n);
   return ok(hipGetLastError());
