@@ -11,11 +11,13 @@ when timing starts.
 
 The timed steps rotate over enough independent buffer sets (>= 512 MiB, twice
 the 256 MiB Infinity Cache) that no step finds its inputs in the
-memory-side cache from the previous visit. Steps are replayed from a HIP graph
-so host launch overhead does not throttle the GPU; the graph holds exactly the
-kernels an eager step launches. Before every timed region a short spin kernel
-keeps the GPU busy while the host queues the replays, so the region starts on
-a full queue whatever the step count.
+memory-side cache from the previous visit. Before every timed region a spin
+kernel keeps the GPU busy while the host queues the region's launches, so the
+region starts on a full queue whatever the step count: the headline's steps
+are the library's calls issued onto the stream (up to 1000 steps; beyond, one
+HIP graph of all of them), each call alone is timed as a HIP graph of a few
+hundred calls. A graph launch costs the GPU about 6 us of its own, so no
+region is made of many short graphs.
 
 Modes:
   (default)            time the steps, print one JSON line
@@ -202,16 +204,17 @@ class HipEvent:
             self.ev = None
 
 
-def timed_ms(torch, stream, gate, enqueue, launches, warm=None):
+def timed_ms(torch, stream, gate, enqueue, launches, warm=None, hold_us=None):
     """Events around enqueue() on `stream`, with the device synchronised
     before and after. Ahead of the start event: a spin long enough for the
-    host to queue `launches` kernel launches (5 us each, 0.2-50 ms), then
-    warm(), untimed work of the same kind (so the region starts in the steady
-    state of a long run, not on a GPU that idled in the spin)."""
+    host to queue the region (hold_us, else 5 us per graph launch of
+    `launches` kernels, 0.2-50 ms), then warm(), untimed work of the same
+    kind (so the region starts in the steady state of a long run, not on a
+    GPU that idled in the spin)."""
     torch.cuda.synchronize()
     start, end = HipEvent(), HipEvent()
     with torch.cuda.stream(stream):
-        gate.hold(min(50_000, max(200, 5 * launches)))
+        gate.hold(hold_us if hold_us is not None else min(50_000, max(200, 5 * launches)))
         if warm is not None:
             warm()
         start.record(stream)
@@ -286,20 +289,32 @@ def capture(torch, stream, fns):
     return HipGraph(stream, fns)
 
 
+# Calls per captured graph in graph_us: a graph launch costs the GPU about
+# 6 us of its own (the runtime's packets around the graph: a region of N
+# standard steps measured 9.5 + 8.73 N us as one graph, 3.2 + 14.8 N us as one
+# graph per step), so each graph holds a few hundred calls.
+GRAPH_CALLS = 600
+# Headline regions up to this many steps are timed as stream launches.
+EAGER_STEPS = 1000
+
+
 def graph_us(torch, stream, gate, fns, reps, launches=1):
-    """One HIP graph holding fns (one call each), replayed `reps` times
-    between events; microseconds per call."""
-    g = capture(torch, stream, fns)
+    """fns (one call each) captured m times over into one HIP graph (m <=
+    reps, about GRAPH_CALLS calls), replayed until about reps rounds of fns
+    are done, between events; microseconds per call."""
+    m = max(1, min(reps, math.ceil(GRAPH_CALLS / len(fns))))
+    n = max(1, round(reps / m))
+    g = capture(torch, stream, list(fns) * m)
     for _ in range(2):
         g.replay()
     torch.cuda.synchronize()
 
     def go():
-        for _ in range(reps):
+        for _ in range(n):
             g.replay()
-    ms = timed_ms(torch, stream, gate, go, reps * len(fns) * launches, warm=go)
+    ms = timed_ms(torch, stream, gate, go, n * len(fns) * launches, warm=go)
     del g
-    return ms * 1e3 / (reps * len(fns))
+    return ms * 1e3 / (n * m * len(fns))
 
 
 # --------------------------------------------------------------------------
@@ -956,20 +971,20 @@ class Floors:
 
 def profile_pass(args, capi, floors, mi, torch, np, dev, stream):
     """Graph replays only: for each segment (a row's step, or one call of a
-    row alone), a marker launch, the segment's graph, another marker. A
-    kernel trace or a counter pass thus sees exactly the timed launches
-    between each pair of markers (buffer set-up runs outside them). The
-    segment list goes to --segments-out."""
+    row alone), a marker launch, one HIP graph of all the segment's calls
+    (reps rounds over the buffer sets), another marker. A kernel trace or a
+    counter pass thus sees exactly the timed launches between each pair of
+    markers (buffer set-up runs outside them). The segment list goes to
+    --segments-out."""
     segs = []
     mark = lambda: floors.empty(MARKER[0], MARKER[1], stream)  # noqa: E731
 
     def run(seg, fns, calls, reps=1):
-        g = capture(torch, stream, fns)
+        g = capture(torch, stream, list(fns) * reps)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             mark()
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             mark()
         torch.cuda.synchronize()
         del g
@@ -1224,34 +1239,45 @@ def main():
     torch.cuda.synchronize()
     ref_out = zs[0].out.clone()
     K = args.steps
-    g_full = capture(torch, stream, std.step)
-    rem = K % S
-    g_rem = capture(torch, stream, std.step[:rem]) if rem else None
-    for _ in range(3):
-        g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
-    torch.cuda.synchronize()
-    assert torch.equal(zs[0].out, ref_out), "graph replay differs from the eager step"
+    # The K steps cycle over the S buffer sets. Up to EAGER_STEPS steps they
+    # are the library's calls issued straight onto the stream, behind a spin
+    # that lets the host queue all of them first (a region of N steps so
+    # measured 0.9 + 8.89 N us); beyond that, one HIP graph of all K steps
+    # (9.5 + 8.73 N us: its launch carries a fixed cost, which a long region
+    # amortises). Replaying a graph per buffer set instead added about 6 us
+    # per graph launch: 9.3 us per step over 20 steps, 8.99 over 2000.
+    if K <= EAGER_STEPS:
+        timing = "stream"
 
-    def go():
-        for _ in range(K // S):
-            g_full.replay()
-        if g_rem is not None:
-            g_rem.replay()
+        def one_pass():
+            for i in range(S):
+                std.step[i]()
+        # the host's enqueue cost per step, with the GPU held busy meanwhile
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            gate.hold(20_000)
+            t0 = time.perf_counter()
+            one_pass()
+            host_us = (time.perf_counter() - t0) * 1e6 / S
+        torch.cuda.synchronize()
+        assert torch.equal(zs[0].out, ref_out), "the steps' output changed between passes"
 
-    def warm():
-        # untimed steps ahead of the start event, about 2 ms of them, from the
-        # graph the region starts with (the first launch of a graph after
-        # another one costs a few us more, once per region)
-        g0, n0 = (g_full, S) if K >= S else (g_rem, rem)
-        for _ in range(max(2, math.ceil(200 / n0))):
-            g0.replay()
-    ms = timed_ms(torch, stream, gate, go, 2 * K, warm=warm)
+        def go():
+            for i in range(K):
+                std.step[i % S]()
+        ms = timed_ms(torch, stream, gate, go, 2 * K, warm=one_pass,
+                      hold_us=min(200_000, 1000 + 3 * host_us * (K + S)))
+    else:
+        timing = "one_graph"
+        g_all = capture(torch, stream, [std.step[i % S] for i in range(K)])
+        g_all.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(zs[0].out, ref_out), "graph replay differs from the eager step"
+        ms = timed_ms(torch, stream, gate, g_all.replay, 2 * K, warm=g_all.replay)
+        del g_all
     us_step = ms * 1e3 / K
     value = ab["total"] / (us_step * 1e-6) / 1e9
-    log(f"hip_graph: {K} steps in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s")
-    del g_full, g_rem
+    log(f"step ({timing}): {K} steps in {ms:.3f} ms -> {us_step:.3f} us/step, {value:.1f} GB/s")
     # secondary: the same step on one buffer set over and over (caches warm)
     warm_us = graph_us(torch, stream, gate, [std.step[0]] * S, max(4, 400 // S), 2)
     log(f"warm (one buffer set): {warm_us:.3f} us/step")
@@ -1341,7 +1367,7 @@ def main():
         "config": {"workload": "standard: 128 tokens x 7168 hidden bf16, 256 experts on 8 "
                                "logical ranks, top-8 uniform, softmax weights, identity expert",
                    "T": w.T, "H": w.H, "E": w.E, "R": w.R, "K": w.K, "A": w.A,
-                   "timing": "hip_graph", "buffer_sets": S,
+                   "timing": timing, "buffer_sets": S,
                    "footprint_MiB": std.extra["footprint_MiB"],
                    "algorithmic_bytes_per_step": ab["total"]},
         "us_per_step_warm": round(warm_us, 3),
