@@ -96,9 +96,20 @@ CASES = {
     "rand_bad_ids": lambda: mi.random_case(20, 100, 64, 32, 4, 4, 1, bad_frac=0.1),
     "rand_T1": lambda: mi.random_case(21, 1, 7168, 256, 8, 8, 1, distinct=True),
     "rand_hot_expert": lambda: _hot(mi.random_case(22, 3000, 64, 64, 8, 6, 1), 5, 0.9),
-    # 8200 row chunks of 1 KiB: the scatter's 8-byte lanes, a ragged last
-    # chunk (250 lanes a row) and K = 3 (no compile-time K)
+    # the scatter: one workgroup per (token, 1 KiB chunk), two waves each
+    # storing half the slots, four from 8192 chunks on when K >= 4. 8200
+    # chunks with a ragged last chunk (125 vectors a row) and K = 3 (no
+    # compile-time K, still two waves)
     "rand_wide_copy_ragged": lambda: mi.random_case(27, 4100, 1000, 64, 8, 3, 1, neg_frac=0.02),
+    # four waves, no compile-time K: wave 0 takes slots 0 and 4
+    "rand_split4_K5_ragged": lambda: mi.random_case(28, 4100, 1000, 64, 8, 5, 1, neg_frac=0.02),
+    # four waves, K = 20: each wave's slots come in two groups of four
+    "rand_split4_K20": lambda: mi.random_case(29, 2100, 2048, 64, 8, 20, 1),
+    # either side of the 8192-chunk switch at K = 8 (two chunks a row)
+    "rand_split2_K8_8190": lambda: mi.random_case(30, 4095, 1000, 256, 8, 8, 1),
+    "rand_split4_K8_8192": lambda: mi.random_case(31, 4096, 1000, 256, 8, 8, 1),
+    # K = 1: one wave per chunk, 16400 chunks
+    "rand_split1_K1": lambda: mi.random_case(32, 8200, 1024, 32, 4, 1, 1),
 }
 
 
