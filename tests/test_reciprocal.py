@@ -34,8 +34,8 @@ def test_small_divisors_exhaustive_near_zero_and_bound():
 
 
 def test_row_chunk_divisors():
-    # chunks per token row: 1 KiB chunks (dispatch, 16-byte lanes), 512 B
-    # (combine, 8-byte lanes) and 2 KiB (8-byte-lane dispatch) for H = 8..2^20
+    # chunks per token row: 1 KiB chunks (the scatter and the fused kernels,
+    # 16-byte lanes) and 512 B (the combine, 8-byte lanes) for H = 8..2^20
     rng = random.Random(5)
     ds = set()
     for H in [8, 256, 1000, 4096, 7168, 1 << 16, 1 << 20] + [8 * rng.randrange(1, 1 << 17)
