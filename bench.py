@@ -774,8 +774,8 @@ def row_replica_train(capi, mi, torch, np, dev, stream):
 
 
 def measure_row(torch, stream, gate, row, reps_hint, pmc, trace):
-    """Step time (graph replays of the rotating steps) and each call alone
-    (graph of one call per set); algorithmic GB/s and the fraction of peak;
+    """Step time (one graph of a few hundred of the rotating steps) and each
+    call alone (likewise); algorithmic GB/s and the fraction of peak;
     HBM bytes from the committed counter summary; the committed trace's
     kernel time per call."""
     res = {"workload": row.workload}
