@@ -1188,6 +1188,10 @@ def main():
         summarize(args.summarize, args.segments or args.segments_out)
         return
 
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be at least 1 and --warmup at least 0"}))
+        sys.exit(2)
+
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU: the logical ranks are "
                           "partitions of one GPU's memory, so --gpus above 1 is not supported"}))

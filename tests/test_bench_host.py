@@ -145,6 +145,14 @@ def test_multi_gpu_refused():
     assert r.returncode == 2 and "one GPU" in r.stdout
 
 
+@pytest.mark.parametrize("args", [["--steps", "0"], ["--warmup", "-1"]])
+def test_bad_step_counts_refused(args):
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "--steps" in r.stdout
+
+
 @pytest.mark.parametrize("name", ["c1", "c2", "c4"])
 def test_rotating_sets_cover_twice_the_infinity_cache(name):
     """The standard-kind rows rotate over enough buffer sets that a step's
