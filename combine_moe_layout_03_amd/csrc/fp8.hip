@@ -43,6 +43,9 @@ __global__ __launch_bounds__(256) void ll_quant_dispatch_kernel(
   const int chunk = (v - lane) >> 6;
   const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
+  // slots are int32: the unsigned compare against the row count clamped to
+  // INT32_MAX stays scalar, and -1 never passes it
+  const uint32_t rows32 = rows < 0x7fffffff ? (uint32_t)rows : 0x7fffffffu;
   constexpr int GS = (KT > 0 && KT < 8) ? KT : 8;
   // unconditional, clamped load (H % 128 == 0, so a 16-lane group is either
   // inside the row or wholly past its end and never stored)
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(256) void ll_quant_dispatch_kernel(
 #pragma unroll
     for (int g = 0; g < GS; ++g) {
       const int r = s[g];
-      if (r >= 0 && r < rows) {
+      if ((uint32_t)r < rows32) {
         const int e = r / RM;  // scalar
         const int i = r - e * RM;
         if (lane_ok) __builtin_nontemporal_store(codes, recv_q + (int64_t)r * nvec + v);
@@ -127,6 +130,9 @@ __global__ __launch_bounds__(256) void fp8_copy_dispatch_kernel(
   const int g = chunk * 8 + (lane & 7);
   const bool scale_ok = lane < 8 && g < G;
   const int32_t *srow = slot + (int64_t)t * K;
+  // slots are int32: the unsigned compare against the row count clamped to
+  // INT32_MAX stays scalar, and -1 never passes it
+  const uint32_t rows32 = rows < 0x7fffffff ? (uint32_t)rows : 0x7fffffffu;
   constexpr int GS = (KT > 0 && KT < 8) ? KT : 8;
   u32x4 val = __builtin_nontemporal_load(xq + (int64_t)t * nvec + min(v, nvec - 1));
   float sc = xs[(int64_t)t * G + min(g, G - 1)];
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(256) void fp8_copy_dispatch_kernel(
 #pragma unroll
     for (int j = 0; j < GS; ++j) {
       const int r = s[j];
-      if (r >= 0 && r < rows) {
+      if ((uint32_t)r < rows32) {
         if (lane_ok) __builtin_nontemporal_store(val, rq + (int64_t)r * nvec + v);
         if (scale_ok) rs[(int64_t)r * G + g] = sc;
       } else if (r != -1) {

@@ -74,6 +74,9 @@ __global__ __launch_bounds__(64 * kS) void dispatch_kernel(
   const int v = (b - t * nchunk) * 64 + (int)(threadIdx.x & 63);
   const bool lane_ok = v < nvec;
   const int32_t *srow = slot + (int64_t)t * K;
+  // a 32-bit unsigned compare against the row count clamped to INT32_MAX
+  // keeps the slot tests scalar (slots are int32; -1 never passes)
+  const uint32_t rows32 = rows < 0x7fffffff ? (uint32_t)rows : 0x7fffffffu;
   // slots per wave and group: all of them for a compile-time K
   constexpr int G = KT > 0 ? (KT + kS - 1) / kS : 4;
   u32x4 val = x[(int64_t)t * nvec + min(v, nvec - 1)];
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(64 * kS) void dispatch_kernel(
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      if (s[g] >= 0 && s[g] < rows) {
+      if ((uint32_t)s[g] < rows32) {
         if (lane_ok) __builtin_nontemporal_store(val, recv + (int64_t)s[g] * nvec + v);
       } else if (s[g] != -1) {
         st |= kStBadSlot;
